@@ -1,0 +1,98 @@
+"""Quantize-once invariant and the quantization counts of Table I (CPU only).
+
+MicroQonv (arXiv 2609.28358) §IV-C, Table I: for a 3x3 convolution with
+stride and padding 1, an activation is quantized once by MicroQonv, 9 times
+when the im2col-expanded tensor is quantized in square blocks (the extension
+of Cuyckens et al.), and 18 times by DaCapo's two line directions; weights
+and gradients twice by DaCapo and once by the others.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+from microscaling_quantized_convolution_mx_amd import workloads as WL
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "table1.json")))
+T1 = GOLD["per_element_quantizations"]
+
+
+@pytest.fixture(scope="module")
+def layer():
+    return O.conv(8, 8, 8, 8, 8, 3, 3, 1, 1, 1, 1)
+
+
+def test_microqonv_quantizes_each_activation_once(orc, layer):
+    counts, events = O.count_act_quant(layer, O.FLOW_MICROQONV)
+    assert np.all(counts == T1["microqonv"]["A"])
+    assert events == counts.size
+
+
+def test_quantize_after_im2col_counts(orc, layer):
+    counts, events = O.count_act_quant(layer, O.FLOW_IM2COL_SQUARE)
+    interior = counts[1:-1, 1:-1]
+    assert np.all(interior == T1["cuyckens"]["A"])
+    # corners are covered by 4 windows, edges by 6
+    for (h, w) in ((0, 0), (0, 7), (7, 0), (7, 7)):
+        assert np.all(counts[h, w] == 4)
+    assert np.all(counts[0, 1:-1] == 6) and np.all(counts[1:-1, 0] == 6)
+    # one event per entry of X' including the zero padding: 9 |X| at stride 1
+    assert events == 9 * counts.size
+
+
+def test_dacapo_counts(orc, layer):
+    counts, events = O.count_act_quant(layer, O.FLOW_DACAPO)
+    assert np.all(counts[1:-1, 1:-1] == T1["dacapo"]["A"])
+    assert events == 18 * counts.size
+
+
+def test_im2col_copies_carry_the_same_quantized_value(orc, layer):
+    # MicroQonv: every X' entry is a reference to one quantized activation, so
+    # all copies of an element share its (code, block scale, tensor scale).
+    lay = WL.ConvLayer(8, 8, 8, 8, 8, 3, 3, 1, 1, 1, 1)
+    x = WL.gen_x(lay, "normal", 21).numpy()
+    q = O.quantize(O.ACT, O.E2M1, x)
+    dims = q.dims
+    where = {}
+    for b in range(O.nblocks(O.ACT, dims)):
+        for r in range(8):
+            for c in range(8):
+                where[O.block_src_index(O.ACT, dims, b, r, c)] = (int(q.codes[b * 64 + r * 8 + c]),
+                                                                  int(q.scales[b]))
+    K, J = 9 * 8, 8 * 8 * 8
+    copies = {}
+    for k in range(K):
+        for j in range(J):
+            s = O.im2col_src(layer, k, j)
+            if s >= 0:
+                copies.setdefault(s, set()).add(where[s] + (q.t,))
+    assert all(len(v) == 1 for v in copies.values())
+    assert max(len(v) for v in copies.values()) == 1 and len(copies) == x.size
+
+    # quantizing after im2col gives some element copies different codes or
+    # scales (the reason those flows must keep the expanded tensor)
+    codes, scales, src, t = O.quantize_after_im2col(layer, O.E2M1, x)
+    # every activation appears in X' once per window covering it (4..9 times)
+    cover = np.bincount(src[src >= 0], minlength=x.size)
+    assert cover.min() == 4 and cover.max() == 9
+    seen = {}
+    differ = 0
+    for s, c, b in zip(src.ravel(), codes.ravel(), scales.ravel()):
+        if s < 0:
+            continue
+        v = (int(c), int(b))
+        if s in seen and seen[s] != v:
+            differ += 1
+        seen.setdefault(int(s), v)
+    assert len(seen) == x.size
+    assert differ > 0
+
+
+def test_weight_and_gradient_counts(orc):
+    # MicroQonv quantizes W and G_Y once each; a line-blocked flow that needs
+    # both GEMM directions quantizes them once per direction.
+    assert T1["microqonv"]["W"] == 1 and T1["microqonv"]["G"] == 1
+    assert T1["dacapo"]["W"] == 2 and T1["dacapo"]["G"] == 2
+    assert T1["cuyckens"]["W"] == 1 and T1["cuyckens"]["G"] == 1

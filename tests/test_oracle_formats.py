@@ -1,0 +1,149 @@
+"""Pins of the oracle's number formats and rounding rules (CPU only).
+
+The grids below are written as literal value lists, binade by binade, as the
+OCP Microscaling Formats v1.0 specification tabulates them; the E4M3 grid is
+taken from PyTorch's own float8_e4m3fn type.  The maxima 448 (E4M3 block
+scale) and 6 (E2M1 element) are the two the MicroQonv paper names in §III-A.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+E2M1_GRID = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+E2M3_GRID = ([k / 8 for k in range(8)] + [1 + k / 8 for k in range(8)]
+             + [2 + k / 4 for k in range(8)] + [4 + k / 2 for k in range(8)])
+E3M2_GRID = ([k / 16 for k in range(4)] + [0.25 + k / 16 for k in range(4)]
+             + [0.5 + k / 8 for k in range(4)] + [1 + k / 4 for k in range(4)]
+             + [2 + k / 2 for k in range(4)] + [4 + k for k in range(4)]
+             + [8 + 2 * k for k in range(4)] + [16 + 4 * k for k in range(4)])
+
+
+def torch_e4m3_grid():
+    bits = torch.arange(0, 0x7F, dtype=torch.uint8)  # 0x7F is NaN in the fn variant
+    return bits.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+GRIDS = {O.E2M1: np.array(E2M1_GRID), O.E2M3: np.array(E2M3_GRID),
+         O.E3M2: np.array(E3M2_GRID), O.E4M3: torch_e4m3_grid()}
+
+
+@pytest.mark.parametrize("fmt", [O.E2M1, O.E2M3, O.E3M2, O.E4M3])
+def test_grid_matches_literal_tables(orc, fmt):
+    assert np.array_equal(O.fmt_grid(fmt), GRIDS[fmt])
+
+
+def test_maxima_printed_in_paper(orc):
+    facts = json.load(open(os.path.join(GOLD, "format_facts.json")))
+    assert O.fmt_max(O.E4M3) == facts["max_block_scale_e4m3"]["value"]
+    assert O.fmt_max(O.E2M1) == facts["max_element_e2m1"]["value"]
+    assert O.fmt_max(O.E2M3) == 7.5
+    assert O.fmt_max(O.E3M2) == 28.0
+
+
+def brute_rne(grid: np.ndarray, v: float) -> int:
+    """argmin |v - g| over the grid; ties to the even code; saturating."""
+    if v >= grid[-1]:
+        return len(grid) - 1
+    d = np.abs(grid - np.float64(v))
+    best = np.flatnonzero(d == d.min())
+    if len(best) == 1:
+        return int(best[0])
+    even = [int(b) for b in best if b % 2 == 0]
+    return even[0]
+
+
+def probe_values(grid, rng, nrand):
+    mids = (grid[1:] + grid[:-1]) / 2
+    f = np.float32
+    vals = list(grid) + list(mids)
+    for m in mids:
+        vals += [np.nextafter(f(m), f(0)), np.nextafter(f(m), f(np.inf))]
+    for g in grid:
+        vals += [np.nextafter(f(g), f(0)), np.nextafter(f(g), f(np.inf))]
+    vals += list(rng.uniform(0, grid[-1] * 1.25, nrand))
+    vals += [grid[-1] * 3, 1e30, 0.0]
+    return [float(np.float32(v)) for v in vals if v >= 0]
+
+
+@pytest.mark.parametrize("fmt", [O.E2M1, O.E2M3, O.E3M2, O.E4M3])
+def test_rne_equals_brute_force_argmin(orc, fmt):
+    grid = GRIDS[fmt]
+    rng = np.random.default_rng(11 + fmt)
+    for v in probe_values(grid, rng, 20000):
+        assert O.round_rne(fmt, v) == brute_rne(grid, v), (fmt, v)
+
+
+def test_e2m1_tie_cases(orc):
+    # ties between grid points go to the even code
+    expect = {0.25: 0.0, 0.75: 1.0, 1.25: 1.0, 1.75: 2.0, 2.5: 2.0, 3.5: 4.0, 5.0: 4.0}
+    for v, g in expect.items():
+        assert O.fmt_value(O.E2M1, O.round_rne(O.E2M1, v)) == g
+
+
+def test_e4m3_cast_matches_torch(orc):
+    rng = np.random.default_rng(5)
+    grid = torch_e4m3_grid()
+    mids = (grid[1:] + grid[:-1]) / 2
+    vals = np.concatenate([rng.uniform(0, 448, 50000).astype(np.float32),
+                           np.exp2(rng.uniform(-12, 8.8, 50000)).astype(np.float32),
+                           mids.astype(np.float32), grid.astype(np.float32)])
+    vals = np.minimum(vals, np.float32(448))
+    ref = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([O.e4m3_code(float(v)) for v in vals])
+    assert np.array_equal(got, ref.astype(np.int64))
+
+
+def test_e4m3_underflow_and_saturation(orc):
+    assert O.e4m3_code(2.0 ** -10) == 0            # tie between 0 and 2^-9 -> even (0)
+    assert O.e4m3_code(np.nextafter(np.float32(2.0 ** -10), np.float32(1))) == 1
+    assert O.e4m3_code(2.0 ** -9) == 1
+    assert O.e4m3_code(448.0) == 0x7E
+    assert O.e4m3_code(500.0) == 0x7E              # saturating, never the NaN pattern
+    assert O.e4m3_code(1e30) == 0x7E
+
+
+@pytest.mark.parametrize("fmt", [O.E2M1, O.E2M3, O.E4M3])
+def test_sr_threshold_extremes(orc, fmt):
+    grid = GRIDS[fmt]
+    rng = np.random.default_rng(3)
+    for _ in range(2000):
+        i = rng.integers(0, len(grid) - 1)
+        lo, hi = grid[i], grid[i + 1]
+        v = np.float32(rng.uniform(lo, hi))
+        if not (lo <= v < hi):
+            continue
+        # u = 0 rounds up exactly when v is above lo
+        assert O.round_sr(fmt, float(v), 0.0) == (i + 1 if v > lo else i)
+        # u just below 1 rounds up only when v - lo exceeds (1 - 2^-24) (hi - lo)
+        u = 1.0 - 2.0 ** -24
+        up = (np.float64(v) - lo) > u * (hi - lo)
+        assert O.round_sr(fmt, float(v), u) == (i + 1 if up else i)
+    assert O.round_sr(fmt, float(grid[-1]) * 2, 0.5) == len(grid) - 1
+
+
+def test_sr_rounding_frequency(orc):
+    # with u uniform, v = lo + f*delta rounds up with probability f
+    fmt = O.E2M1
+    v = 1.0 + 0.3 * 0.5  # between 1.0 and 1.5
+    us = (np.arange(4096) + 0.5) / 4096
+    ups = sum(O.round_sr(fmt, v, float(u)) == 3 for u in us)
+    assert abs(ups / 4096 - 0.3) < 1e-3
+
+
+def test_splitmix64_published_sequence(orc):
+    # The first outputs of SplitMix64 seeded with 0 (Steele, Lea & Flood 2014;
+    # the widely published test vector of the reference implementation): the
+    # generator's i-th output is the mix of i * 0x9E3779B97F4A7C15.
+    expect = [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F, 0xF88BB8A8724C81EC]
+    gamma = 0x9E3779B97F4A7C15
+    for i, e in enumerate(expect, start=1):
+        assert O.splitmix64((gamma * i) % (1 << 64)) == e
+    # u for (seed 0, element 0) is the top 24 bits of the first output
+    assert O.sr_uniform(0, 0) == 0xE220A8 / 2.0 ** 24
