@@ -1,0 +1,162 @@
+/*
+ * mxconv.h -- C ABI of the MicroQonv microscaling convolution hot path on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Source of the method: "MicroQonv: Reshaping Convolution Tensors for
+ * Efficient Microscaling in Training and Inference" (Facq, Ben Ali, Sentieys;
+ * arXiv 2609.28358).  Each convolution tensor is quantized exactly once, in
+ * square 8x8 blocks, into a channel-batch-first layout, and the same quantized
+ * tensors feed the three training GEMMs through an implicit im2col that never
+ * reaches device memory (§IV-A, §IV-B).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every pointer argument except the descriptor and mx_qtensor structs
+ *   themselves (which live in host memory) is a DEVICE pointer.  The caller
+ *   allocates and owns all buffers; the library allocates nothing, keeps no
+ *   global state and may be called from several host threads.
+ * - fp32 tensors and code buffers must be 16-byte aligned; scale buffers,
+ *   tensor_scale and amax 4-byte aligned.  Sources and destinations must not
+ *   overlap.
+ * - Arguments are validated synchronously on the host before anything is
+ *   enqueued; a negative mx_status is returned and nothing runs.  On MX_OK the
+ *   work has been enqueued on `stream` (asynchronous; 0 = null stream).
+ *   MX_ERR_LAUNCH reports a HIP launch error.
+ * - Layouts (N, the batch, is always the fastest index):
+ *     activation X, its gradient dX ........ fp32 [H][W][C_in][N]
+ *     output Y, output gradient dY ......... fp32 [Ho][Wo][C_out][N]
+ *     weight W (FP32 master copy), dW ...... fp32 OIHW [C_out][C_in][K_h][K_w]
+ *   with Ho = (H + 2 pad_h - K_h) / stride_h + 1 (likewise Wo).  The
+ *   convolution is a cross-correlation with zero padding.
+ * - Quantized tensors (mx_qtensor) are stored block by block:
+ *     ACT    blocks [H][W][C_in/8][N/8],    in-block order [c][n]
+ *     GRAD   blocks [Ho][Wo][C_out/8][N/8], in-block order [c][n]
+ *     WEIGHT blocks [K_h][K_w][C_out/8][C_in/8], in-block order [co][ci]
+ *   codes: E2M1 2 per byte (element 2j in the low nibble), E2M3 a
+ *   little-endian 6-bit stream (48 bytes per block), E4M3 1 byte each; the
+ *   sign is the top bit of each code.  scales: one E4M3 byte per block, in
+ *   block order.  tensor_scale: one fp32.  amax: one fp32, max |x|.
+ * - C_in, C_out and N must be multiples of 8 (zero-pad otherwise: padding
+ *   changes neither the amax nor any result) and block must be 8.  N may be 0.
+ */
+#ifndef MXCONV_H
+#define MXCONV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MX_OK = 0,
+  MX_ERR_NULL = -1,      /* a required pointer is NULL */
+  MX_ERR_SHAPE = -2,     /* bad dimension, stride, padding, or not a multiple of 8 */
+  MX_ERR_FORMAT = -3,    /* unknown element format */
+  MX_ERR_BLOCK = -4,     /* block size other than 8 */
+  MX_ERR_ALIGN = -5,     /* misaligned pointer */
+  MX_ERR_WORKSPACE = -6, /* workspace missing or too small */
+  MX_ERR_ROLE = -7,      /* unknown tensor role */
+  MX_ERR_LAUNCH = -8,    /* HIP reported a launch error */
+  MX_ERR_ROUND = -9      /* unknown rounding mode */
+} mx_status;
+
+/* Element formats; the block scale is always E4M3 and the tensor scale fp32
+ * (the NVFP4-style two-level scaling of §II-D / §III-A, with FP6 and FP8
+ * element variants of §IV-D, §IV-E and §VI-B). */
+typedef enum { MX_E2M1 = 1, MX_E2M3 = 2, MX_E4M3 = 3 } mx_elem_fmt;
+
+/* Which tensor of the layer a quantization applies to (§IV-B: activations
+ * blocked over (C_in, N), weights over (C_out, C_in), output gradients over
+ * (C_out, N)). */
+typedef enum { MX_ROLE_ACT = 0, MX_ROLE_WEIGHT = 1, MX_ROLE_GRAD = 2 } mx_role;
+
+/* Element rounding (§III-A: nearest for activations and weights, stochastic
+ * for gradients). */
+typedef enum { MX_RNE = 0, MX_SR = 1 } mx_round;
+
+/* One convolution layer (the problem statement of §II-A). */
+typedef struct {
+  int32_t n, c_in, c_out, h, w, k_h, k_w, stride_h, stride_w, pad_h, pad_w;
+  int32_t elem_fmt; /* mx_elem_fmt */
+  int32_t block;    /* must be 8 (8x8 square blocks, §IV-B) */
+} mx_conv_desc;
+
+/* A quantized tensor: device pointers owned by the caller. */
+typedef struct {
+  void* codes;         /* packed element codes, mx_code_bytes() bytes */
+  uint8_t* scales;     /* E4M3 block scales, mx_scale_bytes() bytes */
+  float* tensor_scale; /* one fp32: T */
+  float* amax;         /* one fp32: max |x| of the source */
+} mx_qtensor;
+
+/* Bytes of packed codes / block scales of the tensor of `role` (0 on an
+ * invalid descriptor or role). */
+size_t mx_code_bytes(const mx_conv_desc* desc, mx_role role);
+size_t mx_scale_bytes(const mx_conv_desc* desc, mx_role role);
+
+/* Bytes of device workspace mx_conv_wgrad needs for this layer (0 on an
+ * invalid descriptor). */
+size_t mx_wgrad_workspace_bytes(const mx_conv_desc* desc);
+
+/* Quantize one fp32 tensor into 8x8 microscaling blocks (§III-A, §IV-B).
+ *   T     = amax / (448 * max_elem)
+ *   B     = E4M3_RNE_sat(blockamax / (max_elem * T))      one per 8x8 block
+ *   code  = Round(|x| / (B * T)) on the element grid, sign = sign of x
+ * Round is nearest-even (MX_RNE) or stochastic (MX_SR): round up iff
+ * u * (hi - lo) < v - lo with u the top 24 bits of
+ * SplitMix64(seed ^ 0x9E3779B97F4A7C15 * (i + 1)), i the element's linear
+ * index in `src`.  Every fp32 step is one correctly rounded IEEE operation.
+ *   src        fp32 tensor of `role` in the layout above
+ *   dst        quantized tensor: codes, scales, tensor_scale and amax written
+ *   amax_given 0: *dst->amax is computed here (max |x|, two passes over src);
+ *              1: *dst->amax already holds the amax to use (e.g. a
+ *              statistic carried over from a previous step); not written
+ * Non-finite input (Inf/NaN, or a non-finite given amax) is reported in-band:
+ * *tensor_scale = NaN, every scale byte 0x7F (E4M3 NaN), all codes 0. */
+mx_status mx_quantize_cbf(const mx_conv_desc* desc, mx_role role, const float* src,
+                          const mx_qtensor* dst, mx_round rounding, uint64_t seed,
+                          int amax_given, hipStream_t stream);
+
+/* Forward convolution Y = W_f . X' (§II-C, §IV-B) with X' the channel-batch-
+ * first im2col of the quantized activation, formed on chip only.
+ *   wq  quantized weight (role WEIGHT), xq quantized activation (role ACT)
+ *   y   fp32 [Ho][Wo][C_out][N], overwritten
+ * Products of dequantized elements are exact; sums are fp32. */
+mx_status mx_conv_fwd(const mx_conv_desc* desc, const mx_qtensor* wq, const mx_qtensor* xq,
+                      float* y, hipStream_t stream);
+
+/* Data gradient dX = col2im(W_f^T . dY) (§II-A "transposed kernels",
+ * §IV-B), evaluated in gather form: each dX element sums exactly the
+ * products col2im would add into it.
+ *   wq quantized weight, dyq quantized output gradient (role GRAD)
+ *   dx fp32 [H][W][C_in][N], overwritten */
+mx_status mx_conv_dgrad(const mx_conv_desc* desc, const mx_qtensor* wq, const mx_qtensor* dyq,
+                        float* dx, hipStream_t stream);
+
+/* Weight gradient dW = dY . X'^T accumulated over the batch (§II-A, §IV-B).
+ *   dyq quantized output gradient, xq quantized activation
+ *   dw        fp32 OIHW, overwritten
+ *   workspace device buffer of at least mx_wgrad_workspace_bytes(desc) bytes
+ *             (partial sums of the split reduction; contents on return are
+ *             unspecified).  The reduction order is fixed: results are
+ *             bit-reproducible run to run. */
+mx_status mx_conv_wgrad(const mx_conv_desc* desc, const mx_qtensor* dyq, const mx_qtensor* xq,
+                        float* dw, void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Fake-quantized fp32 values (-1)^s * fl32(fl32(g * B) * T) (§III-A), written
+ * in the fp32 layout of `role`. */
+mx_status mx_dequantize(const mx_conv_desc* desc, mx_role role, const mx_qtensor* q, float* dst,
+                        hipStream_t stream);
+
+/* Static description of a status code. */
+const char* mx_status_str(mx_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXCONV_H */

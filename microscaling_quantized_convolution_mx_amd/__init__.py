@@ -1,0 +1,195 @@
+"""MicroQonv microscaling convolution hot path for AMD MI355X (gfx950).
+
+Thin ctypes binding of ``libmxconv.so`` (C ABI in ``include/mxconv.h``): the
+functions below have the same names as the C entry points and only marshal
+arguments -- every step of the computation runs in the HIP kernels.  PyTorch
+is used for device memory and streams.  There is no CPU fallback: if the
+library is missing, or a call fails, an exception is raised.
+
+Method: "MicroQonv: Reshaping Convolution Tensors for Efficient Microscaling in
+Training and Inference" (arXiv 2609.28358): quantize each convolution tensor
+once in 8x8 microscaling blocks in a channel-batch-first layout (§IV-A,
+§IV-B) and run the forward, data-gradient and weight-gradient GEMMs on the
+quantized tensors through an implicit im2col.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmxconv.so")
+
+MX_E2M1, MX_E2M3, MX_E4M3 = 1, 2, 3
+MX_ROLE_ACT, MX_ROLE_WEIGHT, MX_ROLE_GRAD = 0, 1, 2
+MX_RNE, MX_SR = 0, 1
+
+STATUS = {0: "MX_OK", -1: "MX_ERR_NULL", -2: "MX_ERR_SHAPE", -3: "MX_ERR_FORMAT",
+          -4: "MX_ERR_BLOCK", -5: "MX_ERR_ALIGN", -6: "MX_ERR_WORKSPACE", -7: "MX_ERR_ROLE",
+          -8: "MX_ERR_LAUNCH", -9: "MX_ERR_ROUND"}
+
+EXPORTS = ("mx_code_bytes", "mx_scale_bytes", "mx_wgrad_workspace_bytes", "mx_quantize_cbf",
+           "mx_conv_fwd", "mx_conv_dgrad", "mx_conv_wgrad", "mx_dequantize", "mx_status_str")
+
+
+class MxError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({status_str(status)})")
+
+
+class mx_conv_desc(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_int32) for f in
+                ("n", "c_in", "c_out", "h", "w", "k_h", "k_w", "stride_h", "stride_w",
+                 "pad_h", "pad_w", "elem_fmt", "block")]
+
+    @property
+    def h_out(self) -> int:
+        return (self.h + 2 * self.pad_h - self.k_h) // self.stride_h + 1
+
+    @property
+    def w_out(self) -> int:
+        return (self.w + 2 * self.pad_w - self.k_w) // self.stride_w + 1
+
+
+class mx_qtensor(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("tensor_scale", ctypes.c_void_p), ("amax", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmxconv.so (built by build.py); raises if it is absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: run __graft_entry__.build() "
+                           "(or python -m microscaling_quantized_convolution_mx_amd.build)")
+    L = ctypes.CDLL(LIB_PATH)
+    D = ctypes.POINTER(mx_conv_desc)
+    Q = ctypes.POINTER(mx_qtensor)
+    P = ctypes.c_void_p
+    for f in ("mx_code_bytes", "mx_scale_bytes"):
+        getattr(L, f).restype = ctypes.c_size_t
+        getattr(L, f).argtypes = [D, ctypes.c_int]
+    L.mx_wgrad_workspace_bytes.restype = ctypes.c_size_t
+    L.mx_wgrad_workspace_bytes.argtypes = [D]
+    L.mx_quantize_cbf.restype = ctypes.c_int
+    L.mx_quantize_cbf.argtypes = [D, ctypes.c_int, P, Q, ctypes.c_int, ctypes.c_uint64, ctypes.c_int, P]
+    for f in ("mx_conv_fwd", "mx_conv_dgrad"):
+        getattr(L, f).restype = ctypes.c_int
+        getattr(L, f).argtypes = [D, Q, Q, P, P]
+    L.mx_conv_wgrad.restype = ctypes.c_int
+    L.mx_conv_wgrad.argtypes = [D, Q, Q, P, P, ctypes.c_size_t, P]
+    L.mx_dequantize.restype = ctypes.c_int
+    L.mx_dequantize.argtypes = [D, ctypes.c_int, Q, P, P]
+    L.mx_status_str.restype = ctypes.c_char_p
+    L.mx_status_str.argtypes = [ctypes.c_int]
+    _lib = L
+    return L
+
+
+def status_str(status: int) -> str:
+    return lib().mx_status_str(status).decode()
+
+
+def desc(n, c_in, c_out, h, w, k_h, k_w, stride_h=1, stride_w=1, pad_h=0, pad_w=0,
+         elem_fmt=MX_E2M1, block=8) -> mx_conv_desc:
+    return mx_conv_desc(n, c_in, c_out, h, w, k_h, k_w, stride_h, stride_w, pad_h, pad_w,
+                        elem_fmt, block)
+
+
+def desc_from_layer(layer, elem_fmt: int) -> mx_conv_desc:
+    return desc(layer.n, layer.c_in, layer.c_out, layer.h, layer.w, layer.k_h, layer.k_w,
+                layer.stride_h, layer.stride_w, layer.pad_h, layer.pad_w, elem_fmt)
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr() if t.numel() > 0 else None
+
+
+def _stream(stream) -> int | None:
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise MxError(status, where)
+
+
+def mx_code_bytes(d: mx_conv_desc, role: int) -> int:
+    return lib().mx_code_bytes(ctypes.byref(d), role)
+
+
+def mx_scale_bytes(d: mx_conv_desc, role: int) -> int:
+    return lib().mx_scale_bytes(ctypes.byref(d), role)
+
+
+def mx_wgrad_workspace_bytes(d: mx_conv_desc) -> int:
+    return lib().mx_wgrad_workspace_bytes(ctypes.byref(d))
+
+
+class QTensor:
+    """Device buffers of one quantized tensor (owned by torch)."""
+
+    def __init__(self, d: mx_conv_desc, role: int, device="cuda"):
+        import torch
+        self.role = role
+        self.fmt = d.elem_fmt
+        nc = mx_code_bytes(d, role)
+        ns = mx_scale_bytes(d, role)
+        # at least 16 bytes, so that an empty tensor still has valid pointers
+        self.codes = torch.empty(max(nc, 16), dtype=torch.uint8, device=device)
+        self.scales = torch.empty(max(ns, 16), dtype=torch.uint8, device=device)
+        self.tensor_scale = torch.zeros(1, dtype=torch.float32, device=device)
+        self.amax = torch.zeros(1, dtype=torch.float32, device=device)
+        self.code_bytes, self.scale_bytes = nc, ns
+
+    def c(self) -> mx_qtensor:
+        return mx_qtensor(self.codes.data_ptr(), self.scales.data_ptr(),
+                          self.tensor_scale.data_ptr(), self.amax.data_ptr())
+
+
+def _q(q) -> ctypes.POINTER(mx_qtensor):
+    if q is None:
+        return None
+    return ctypes.byref(q.c() if isinstance(q, QTensor) else q)
+
+
+def mx_quantize_cbf(d: mx_conv_desc, role: int, src, dst, rounding: int = MX_RNE, seed: int = 0,
+                    amax_given: bool = False, stream=None) -> None:
+    _check(lib().mx_quantize_cbf(ctypes.byref(d), role, _ptr(src), _q(dst), rounding,
+                                 seed & (2 ** 64 - 1), int(bool(amax_given)), _stream(stream)),
+           "mx_quantize_cbf")
+
+
+def mx_conv_fwd(d: mx_conv_desc, wq, xq, y, stream=None) -> None:
+    _check(lib().mx_conv_fwd(ctypes.byref(d), _q(wq), _q(xq), _ptr(y), _stream(stream)), "mx_conv_fwd")
+
+
+def mx_conv_dgrad(d: mx_conv_desc, wq, dyq, dx, stream=None) -> None:
+    _check(lib().mx_conv_dgrad(ctypes.byref(d), _q(wq), _q(dyq), _ptr(dx), _stream(stream)),
+           "mx_conv_dgrad")
+
+
+def mx_conv_wgrad(d: mx_conv_desc, dyq, xq, dw, workspace, ws_bytes: int | None = None,
+                  stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().mx_conv_wgrad(ctypes.byref(d), _q(dyq), _q(xq), _ptr(dw), _ptr(workspace),
+                               ws_bytes, _stream(stream)), "mx_conv_wgrad")
+
+
+def mx_dequantize(d: mx_conv_desc, role: int, q, dst, stream=None) -> None:
+    _check(lib().mx_dequantize(ctypes.byref(d), role, _q(q), _ptr(dst), _stream(stream)),
+           "mx_dequantize")

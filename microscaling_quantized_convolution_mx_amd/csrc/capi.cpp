@@ -1,0 +1,192 @@
+// C ABI of the MicroQonv hot path: host-side validation and dispatch.
+//
+// Every check below runs on the host before anything is enqueued, so the
+// error paths need no GPU.  The layouts and the meaning of each argument are
+// documented in include/mxconv.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <limits>
+
+#include "internal.h"
+
+namespace mx {
+
+Geom make_geom(const mx_conv_desc* d) {
+  Geom g;
+  g.n = d->n; g.c_in = d->c_in; g.c_out = d->c_out; g.h = d->h; g.w = d->w;
+  g.k_h = d->k_h; g.k_w = d->k_w; g.sh = d->stride_h; g.sw = d->stride_w;
+  g.ph = d->pad_h; g.pw = d->pad_w; g.fmt = d->elem_fmt;
+  g.ho = (d->h + 2 * d->pad_h - d->k_h) / d->stride_h + 1;
+  g.wo = (d->w + 2 * d->pad_w - d->k_w) / d->stride_w + 1;
+  return g;
+}
+
+int64_t role_numel(const Geom& g, mx_role role) {
+  switch (role) {
+    case MX_ROLE_ACT: return static_cast<int64_t>(g.h) * g.w * g.c_in * g.n;
+    case MX_ROLE_GRAD: return static_cast<int64_t>(g.ho) * g.wo * g.c_out * g.n;
+    default: return static_cast<int64_t>(g.c_out) * g.c_in * g.k_h * g.k_w;
+  }
+}
+
+int64_t role_nblocks(const Geom& g, mx_role role) { return role_numel(g, role) / 64; }
+
+int code_bits(int fmt) { return fmt == MX_E2M1 ? 4 : fmt == MX_E2M3 ? 6 : 8; }
+
+}  // namespace mx
+
+namespace {
+
+using mx::Geom;
+
+// Largest element count any one tensor may have (block indices are 32-bit
+// inside the conv kernels: 2^31 blocks of 64 elements).
+constexpr int64_t kMaxElems = (static_cast<int64_t>(1) << 31) * 64 - 64;
+// Geometry products fed to 32-bit kernel arithmetic must stay below this.
+constexpr int64_t kMaxIndex = std::numeric_limits<int32_t>::max();
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+mx_status check_desc(const mx_conv_desc* d) {
+  if (!d) return MX_ERR_NULL;
+  if (d->block != 8) return MX_ERR_BLOCK;
+  if (d->elem_fmt != MX_E2M1 && d->elem_fmt != MX_E2M3 && d->elem_fmt != MX_E4M3) return MX_ERR_FORMAT;
+  if (d->n < 0 || d->c_in <= 0 || d->c_out <= 0 || d->h <= 0 || d->w <= 0 || d->k_h <= 0 || d->k_w <= 0)
+    return MX_ERR_SHAPE;
+  if (d->stride_h <= 0 || d->stride_w <= 0 || d->pad_h < 0 || d->pad_w < 0) return MX_ERR_SHAPE;
+  if (d->n % 8 || d->c_in % 8 || d->c_out % 8) return MX_ERR_SHAPE;
+  if (static_cast<int64_t>(d->h) + 2 * static_cast<int64_t>(d->pad_h) < d->k_h) return MX_ERR_SHAPE;
+  if (static_cast<int64_t>(d->w) + 2 * static_cast<int64_t>(d->pad_w) < d->k_w) return MX_ERR_SHAPE;
+  const Geom g = mx::make_geom(d);
+  if (g.ho <= 0 || g.wo <= 0) return MX_ERR_SHAPE;
+  const int64_t nx = mx::role_numel(g, MX_ROLE_ACT), ny = mx::role_numel(g, MX_ROLE_GRAD),
+                nw = mx::role_numel(g, MX_ROLE_WEIGHT);
+  if (nx > kMaxElems || ny > kMaxElems || nw > kMaxElems) return MX_ERR_SHAPE;
+  // column-block and k-block counts of the three GEMMs are 32-bit
+  const int64_t kkc = static_cast<int64_t>(d->k_h) * d->k_w * d->c_in;
+  if (static_cast<int64_t>(g.h) * g.w * (d->n / 8) > kMaxIndex ||
+      static_cast<int64_t>(g.ho) * g.wo * (d->n / 8) > kMaxIndex || kkc > kMaxIndex ||
+      static_cast<int64_t>(d->c_out) * kkc > kMaxIndex)
+    return MX_ERR_SHAPE;
+  return MX_OK;
+}
+
+mx_status check_role(mx_role r) {
+  return (r == MX_ROLE_ACT || r == MX_ROLE_WEIGHT || r == MX_ROLE_GRAD) ? MX_OK : MX_ERR_ROLE;
+}
+
+mx_status check_qtensor(const mx_qtensor* q, int64_t nblocks) {
+  if (!q) return MX_ERR_NULL;
+  if (!q->tensor_scale || !q->amax) return MX_ERR_NULL;
+  if (nblocks > 0 && (!q->codes || !q->scales)) return MX_ERR_NULL;
+  if (!aligned(q->codes, 16) || !aligned(q->tensor_scale, 4) || !aligned(q->amax, 4)) return MX_ERR_ALIGN;
+  return MX_OK;
+}
+
+mx_status launched(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+size_t mx_code_bytes(const mx_conv_desc* desc, mx_role role) {
+  if (check_desc(desc) != MX_OK || check_role(role) != MX_OK) return 0;
+  const Geom g = mx::make_geom(desc);
+  return static_cast<size_t>(mx::role_numel(g, role)) * mx::code_bits(desc->elem_fmt) / 8;
+}
+
+size_t mx_scale_bytes(const mx_conv_desc* desc, mx_role role) {
+  if (check_desc(desc) != MX_OK || check_role(role) != MX_OK) return 0;
+  return static_cast<size_t>(mx::role_nblocks(mx::make_geom(desc), role));
+}
+
+size_t mx_wgrad_workspace_bytes(const mx_conv_desc* desc) {
+  if (check_desc(desc) != MX_OK) return 0;
+  return mx::wgrad_workspace_bytes(mx::make_geom(desc));
+}
+
+mx_status mx_quantize_cbf(const mx_conv_desc* desc, mx_role role, const float* src,
+                          const mx_qtensor* dst, mx_round rounding, uint64_t seed, int amax_given,
+                          hipStream_t stream) {
+  mx_status st = check_desc(desc);
+  if (st != MX_OK) return st;
+  if ((st = check_role(role)) != MX_OK) return st;
+  if (rounding != MX_RNE && rounding != MX_SR) return MX_ERR_ROUND;
+  const Geom g = mx::make_geom(desc);
+  const int64_t nb = mx::role_nblocks(g, role);
+  if ((st = check_qtensor(dst, nb)) != MX_OK) return st;
+  if (nb > 0 && !src) return MX_ERR_NULL;
+  if (!aligned(src, 16)) return MX_ERR_ALIGN;
+  return launched(mx::launch_quantize(g, role, src, dst, rounding, seed, amax_given, stream));
+}
+
+mx_status mx_dequantize(const mx_conv_desc* desc, mx_role role, const mx_qtensor* q, float* dst,
+                        hipStream_t stream) {
+  mx_status st = check_desc(desc);
+  if (st != MX_OK) return st;
+  if ((st = check_role(role)) != MX_OK) return st;
+  const Geom g = mx::make_geom(desc);
+  const int64_t nb = mx::role_nblocks(g, role);
+  if ((st = check_qtensor(q, nb)) != MX_OK) return st;
+  if (nb > 0 && !dst) return MX_ERR_NULL;
+  if (!aligned(dst, 16)) return MX_ERR_ALIGN;
+  return launched(mx::launch_dequantize(g, role, q, dst, stream));
+}
+
+mx_status mx_conv_fwd(const mx_conv_desc* desc, const mx_qtensor* wq, const mx_qtensor* xq, float* y,
+                      hipStream_t stream) {
+  mx_status st = check_desc(desc);
+  if (st != MX_OK) return st;
+  const Geom g = mx::make_geom(desc);
+  if ((st = check_qtensor(wq, mx::role_nblocks(g, MX_ROLE_WEIGHT))) != MX_OK) return st;
+  if ((st = check_qtensor(xq, mx::role_nblocks(g, MX_ROLE_ACT))) != MX_OK) return st;
+  if (mx::role_numel(g, MX_ROLE_GRAD) > 0 && !y) return MX_ERR_NULL;
+  if (!aligned(y, 16)) return MX_ERR_ALIGN;
+  return launched(mx::launch_conv_fwd(g, wq, xq, y, stream));
+}
+
+mx_status mx_conv_dgrad(const mx_conv_desc* desc, const mx_qtensor* wq, const mx_qtensor* dyq,
+                        float* dx, hipStream_t stream) {
+  mx_status st = check_desc(desc);
+  if (st != MX_OK) return st;
+  const Geom g = mx::make_geom(desc);
+  if ((st = check_qtensor(wq, mx::role_nblocks(g, MX_ROLE_WEIGHT))) != MX_OK) return st;
+  if ((st = check_qtensor(dyq, mx::role_nblocks(g, MX_ROLE_GRAD))) != MX_OK) return st;
+  if (mx::role_numel(g, MX_ROLE_ACT) > 0 && !dx) return MX_ERR_NULL;
+  if (!aligned(dx, 16)) return MX_ERR_ALIGN;
+  return launched(mx::launch_conv_dgrad(g, wq, dyq, dx, stream));
+}
+
+mx_status mx_conv_wgrad(const mx_conv_desc* desc, const mx_qtensor* dyq, const mx_qtensor* xq,
+                        float* dw, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  mx_status st = check_desc(desc);
+  if (st != MX_OK) return st;
+  const Geom g = mx::make_geom(desc);
+  if ((st = check_qtensor(dyq, mx::role_nblocks(g, MX_ROLE_GRAD))) != MX_OK) return st;
+  if ((st = check_qtensor(xq, mx::role_nblocks(g, MX_ROLE_ACT))) != MX_OK) return st;
+  if (!dw) return MX_ERR_NULL;
+  if (!aligned(dw, 16)) return MX_ERR_ALIGN;
+  const size_t need = mx::wgrad_workspace_bytes(g);
+  if (need > 0 && (!workspace || ws_bytes < need)) return MX_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return MX_ERR_ALIGN;
+  return launched(mx::launch_conv_wgrad(g, dyq, xq, dw, workspace, stream));
+}
+
+const char* mx_status_str(mx_status s) {
+  switch (s) {
+    case MX_OK: return "ok";
+    case MX_ERR_NULL: return "null pointer argument";
+    case MX_ERR_SHAPE: return "invalid shape (dimensions, stride, padding, or C_in/C_out/N not multiples of 8)";
+    case MX_ERR_FORMAT: return "unknown element format";
+    case MX_ERR_BLOCK: return "block size must be 8";
+    case MX_ERR_ALIGN: return "misaligned pointer";
+    case MX_ERR_WORKSPACE: return "workspace missing or smaller than mx_wgrad_workspace_bytes()";
+    case MX_ERR_ROLE: return "unknown tensor role";
+    case MX_ERR_LAUNCH: return "HIP launch failure";
+    case MX_ERR_ROUND: return "unknown rounding mode";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

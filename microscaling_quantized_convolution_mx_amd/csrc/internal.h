@@ -1,0 +1,37 @@
+// Internal interface between the C ABI (capi.cpp) and the HIP kernels.
+// Arguments reaching these launchers have already been validated on the host.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mxconv.h"
+
+namespace mx {
+
+// Geometry shared by all launchers, derived from an mx_conv_desc.
+struct Geom {
+  int32_t n, c_in, c_out, h, w, k_h, k_w, sh, sw, ph, pw, ho, wo, fmt;
+};
+
+Geom make_geom(const mx_conv_desc* d);
+
+// fp32 element count and 8x8 block count of the tensor of `role`.
+int64_t role_numel(const Geom& g, mx_role role);
+int64_t role_nblocks(const Geom& g, mx_role role);
+int code_bits(int fmt);
+
+hipError_t launch_quantize(const Geom& g, mx_role role, const float* src, const mx_qtensor* dst,
+                           mx_round rounding, uint64_t seed, int amax_given, hipStream_t s);
+hipError_t launch_dequantize(const Geom& g, mx_role role, const mx_qtensor* q, float* dst,
+                             hipStream_t s);
+
+hipError_t launch_conv_fwd(const Geom& g, const mx_qtensor* wq, const mx_qtensor* xq, float* y,
+                           hipStream_t s);
+hipError_t launch_conv_dgrad(const Geom& g, const mx_qtensor* wq, const mx_qtensor* dyq, float* dx,
+                             hipStream_t s);
+hipError_t launch_conv_wgrad(const Geom& g, const mx_qtensor* dyq, const mx_qtensor* xq, float* dw,
+                             void* workspace, hipStream_t s);
+size_t wgrad_workspace_bytes(const Geom& g);
+
+}  // namespace mx

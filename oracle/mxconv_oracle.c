@@ -264,12 +264,14 @@ int orc_quantize(int role, int fmt, int rounding, uint64_t seed, const float* sr
   int nonfinite = 0;
   float amax;
   if (amax_in) {
-    amax = *amax_in;
+    /* a caller-supplied statistic is used by magnitude and reported as given */
+    *amax_out = *amax_in;
+    amax = fabsf(*amax_in);
     nonfinite = !isfinite(amax);
   } else {
     amax = orc_amax(src, nel, &nonfinite);
+    *amax_out = amax;
   }
-  *amax_out = amax;
   if (nonfinite) {
     *t_out = NAN;
     memset(scales, 0x7F, (size_t)nb);

@@ -1,0 +1,95 @@
+"""GPU parity of the implicit-im2col GEMMs against the CPU oracle on shapes
+the oracle finishes in seconds: several tiles, ragged tails, stride 2, 1x1,
+rectangular kernels, padding wider than the kernel reach, empty batch.
+Every output within 2e-3 * sum|a*b| (MicroQonv, arXiv 2609.28358, §IV-B)."""
+import numpy as np
+import pytest
+import torch
+
+import microscaling_quantized_convolution_mx_amd as mx
+import oracle as O
+from microscaling_quantized_convolution_mx_amd import workloads as WL
+from gpu_util import DEV, assert_close, conv_buffers, gpu_quantize, oracle_conv, run_layer, say
+
+pytestmark = pytest.mark.gpu
+
+FMTS = [mx.MX_E2M1, mx.MX_E2M3, mx.MX_E4M3]
+
+SHAPES = [
+    # n, ci, co, h, w, kh, kw, sh, sw, ph, pw
+    (8, 16, 16, 16, 16, 3, 3, 1, 1, 0, 0),     # the single-layer workload
+    (8, 8, 16, 9, 7, 3, 3, 1, 1, 1, 1),
+    (8, 16, 8, 9, 10, 3, 3, 2, 2, 1, 1),       # stride 2, ragged
+    (16, 8, 24, 6, 6, 1, 1, 2, 2, 0, 0),       # 1x1 stride-2 shortcut
+    (8, 8, 8, 7, 8, 3, 2, 2, 1, 0, 1),         # rectangular kernel, mixed strides
+    (8, 8, 8, 5, 5, 5, 5, 1, 1, 2, 2),
+    (32, 40, 264, 11, 9, 3, 3, 1, 1, 1, 1),    # 2 row tiles (ragged), K steps straddle taps
+    (16, 136, 72, 7, 6, 3, 3, 1, 1, 1, 1),     # 128-row tile + 8-row tail in dgrad
+    (24, 64, 64, 12, 12, 3, 3, 2, 2, 1, 1),
+    (8, 8, 8, 4, 4, 3, 3, 1, 1, 3, 3),         # padding wider than the kernel reach
+    (8, 256, 256, 6, 6, 3, 3, 1, 1, 1, 1),     # 256x256 tile
+]
+
+
+def layer_inputs(shape, seed):
+    lay = WL.ConvLayer(*shape)
+    return lay, WL.gen_x(lay, "normal", seed), WL.gen_w(lay, seed + 1), WL.gen_dy(lay, 1.0, seed + 2)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("shape", SHAPES)
+def test_conv_full(fmt, shape):
+    say("conv", fmt, shape)
+    lay, x, w, dy = layer_inputs(shape, 100 + SHAPES.index(shape))
+    d = mx.desc_from_layer(lay, fmt)
+    (qx, qw, qdy), (y, dx, dw) = run_layer(d, x, w, dy, seed_sr=7)
+    ox = O.quantize(O.ACT, fmt, x.numpy())
+    ow = O.quantize(O.WEIGHT, fmt, w.numpy())
+    ody = O.quantize(O.GRAD, fmt, dy.numpy(), O.SR, 7)
+    cv = oracle_conv(d)
+    ref, s = O.conv_fwd(cv, ow.exact(), ox.exact())
+    assert_close(y.cpu().numpy(), ref, s, "fwd")
+    ref, s = O.conv_dgrad(cv, ow.exact(), ody.exact())
+    assert_close(dx.cpu().numpy(), ref, s, "dgrad")
+    ref, s = O.conv_wgrad(cv, ody.exact(), ox.exact())
+    assert_close(dw.cpu().numpy(), ref, s, "wgrad")
+
+
+def test_conv_empty_batch():
+    d = mx.desc(0, 16, 16, 6, 6, 3, 3, 1, 1, 1, 1)
+    say("conv empty batch")
+    qx, qw, qdy = (mx.QTensor(d, r, DEV) for r in (0, 1, 2))
+    w = WL.gen_w(WL.ConvLayer(8, 16, 16, 6, 6, 3, 3, 1, 1, 1, 1), 3).to(DEV)
+    mx.mx_quantize_cbf(d, mx.MX_ROLE_WEIGHT, w, qw)
+    for q, role in ((qx, 0), (qdy, 2)):
+        mx.mx_quantize_cbf(d, role, torch.empty(0, device=DEV), q)
+    y, dx, dw, ws = conv_buffers(d)
+    dw.fill_(float("nan"))
+    mx.mx_conv_fwd(d, qw, qx, y)
+    mx.mx_conv_dgrad(d, qw, qdy, dx)
+    mx.mx_conv_wgrad(d, qdy, qx, dw, ws)
+    torch.cuda.synchronize()
+    assert (dw == 0).all()   # a sum over an empty batch
+
+
+def test_conv_zero_operand():
+    # an all-zero activation (T = 0) gives exact zeros, never NaN
+    shape = (8, 16, 16, 6, 6, 3, 3, 1, 1, 1, 1)
+    lay, x, w, dy = layer_inputs(shape, 5)
+    d = mx.desc_from_layer(lay, mx.MX_E2M1)
+    say("conv zero operand")
+    (qx, qw, qdy), (y, dx, dw) = run_layer(d, torch.zeros_like(x), w, dy, 3)
+    assert (y == 0).all() and (dw == 0).all()
+    assert torch.isfinite(dx).all()
+
+
+def test_wgrad_is_deterministic():
+    shape = (64, 64, 64, 14, 14, 3, 3, 1, 1, 1, 1)
+    lay, x, w, dy = layer_inputs(shape, 9)
+    d = mx.desc_from_layer(lay, mx.MX_E2M1)
+    say("wgrad determinism")
+    (qx, qw, qdy), (_, _, dw1) = run_layer(d, x, w, dy, 3, ops=("wgrad",))
+    _, _, dw2, ws = conv_buffers(d)
+    mx.mx_conv_wgrad(d, qdy, qx, dw2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(dw1, dw2)

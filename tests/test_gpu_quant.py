@@ -1,0 +1,173 @@
+"""GPU parity of the quantizer and the dequantizer against the CPU oracle:
+codes, block scales, tensor scale and amax bit-exact (MicroQonv, arXiv
+2609.28358, §III-A, §IV-B)."""
+import numpy as np
+import pytest
+import torch
+
+import microscaling_quantized_convolution_mx_amd as mx
+import oracle as O
+from microscaling_quantized_convolution_mx_amd import workloads as WL
+from gpu_util import DEV, assert_quant_equal, gpu_quantize, oracle_quantize, say
+
+pytestmark = pytest.mark.gpu
+
+FMTS = [mx.MX_E2M1, mx.MX_E2M3, mx.MX_E4M3]
+
+# (n, c_in, c_out, h, w, k, stride, pad): ragged block rows (N/8 not a multiple
+# of the 32 blocks a wavefront covers), several workgroups, stride 2
+SHAPES = [
+    (40, 24, 16, 5, 3, 3, 1, 1),
+    (8, 16, 32, 9, 7, 3, 2, 1),
+    (264, 8, 8, 4, 4, 1, 1, 0),
+    (16, 64, 136, 6, 5, 3, 1, 0),
+]
+
+
+def src_for(d, role, seed, dist="normal", sigma=1.0):
+    lay = WL.ConvLayer(d.n, d.c_in, d.c_out, d.h, d.w, d.k_h, d.k_w, d.stride_h, d.stride_w,
+                       d.pad_h, d.pad_w)
+    if role == mx.MX_ROLE_ACT:
+        return WL.gen_x(lay, dist, seed)
+    if role == mx.MX_ROLE_WEIGHT:
+        return WL.gen_w(lay, seed)
+    return WL.gen_dy(lay, sigma, seed)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("role,rounding", [(mx.MX_ROLE_ACT, mx.MX_RNE), (mx.MX_ROLE_WEIGHT, mx.MX_RNE),
+                                           (mx.MX_ROLE_GRAD, mx.MX_SR), (mx.MX_ROLE_GRAD, mx.MX_RNE),
+                                           (mx.MX_ROLE_WEIGHT, mx.MX_SR)])
+def test_quantize_bit_exact(fmt, shape, role, rounding):
+    n, ci, co, h, w, k, s, p = shape
+    d = mx.desc(n, ci, co, h, w, k, k, s, s, p, p, elem_fmt=fmt)
+    say("quantize", fmt, shape, role, rounding)
+    src = src_for(d, role, seed=hash((fmt, shape, role)) % 1000)
+    gq = gpu_quantize(d, role, src, rounding, seed=123)
+    oq = oracle_quantize(d, role, src, rounding, seed=123)
+    assert_quant_equal(gq, oq, f"fmt {fmt} role {role}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("dist", ["halfnormal", "silu", "uniform"])
+def test_quantize_distributions(fmt, dist):
+    d = mx.desc(64, 32, 32, 7, 7, 3, 3, 1, 1, 1, 1, elem_fmt=fmt)
+    say("quantize dist", fmt, dist)
+    src = WL.gen_tensor((7, 7, 32, 64), dist, 77)
+    assert_quant_equal(gpu_quantize(d, mx.MX_ROLE_ACT, src), oracle_quantize(d, mx.MX_ROLE_ACT, src))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_quantize_extreme_magnitudes(fmt):
+    # tiny (subnormal fp32), huge, ties on the grid, signed zeros
+    d = mx.desc(16, 16, 16, 2, 2, 1, 1, elem_fmt=fmt)
+    say("quantize extremes", fmt)
+    g = torch.Generator().manual_seed(5)
+    x = torch.randn(2, 2, 16, 16, generator=g)
+    x[0, 0] *= 1e-38           # a block of fp32 subnormals next to normal blocks
+    x[0, 1] *= 1e-30
+    x[1, 0] *= 3e30
+    x[1, 1, 0, :4] = torch.tensor([0.0, -0.0, 1e-45, -1e-45])
+    for role, rnd in ((mx.MX_ROLE_ACT, mx.MX_RNE), (mx.MX_ROLE_GRAD, mx.MX_SR)):
+        assert_quant_equal(gpu_quantize(d, role, x, rnd, seed=9), oracle_quantize(d, role, x, rnd, seed=9))
+    # only tiny values: T itself subnormal
+    xs = x * 1e-8
+    assert_quant_equal(gpu_quantize(d, mx.MX_ROLE_ACT, xs), oracle_quantize(d, mx.MX_ROLE_ACT, xs))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_quantize_grid_ties(fmt):
+    # T = 1 (amax = 448 * max) and every other block holds the element
+    # maximum, so its scale is exactly 1 and the grid midpoints placed in it
+    # are exact ties after scaling: both sides must pick the even code
+    grid = O.fmt_grid(fmt)
+    mids = (grid[1:] + grid[:-1]) / 2
+    vals = np.concatenate([mids, -mids, grid[:-1]]).astype(np.float32)
+    npos = -(-vals.size // 63) + 1
+    d = mx.desc(8, 8, 8, 1, npos, 1, 1, elem_fmt=fmt)
+    x = np.zeros((1, npos, 8, 8), dtype=np.float32)
+    for p in range(npos - 1):
+        blk = x[0, p].reshape(-1)
+        chunk = vals[p * 63:(p + 1) * 63]
+        blk[0] = grid[-1]
+        blk[1:1 + chunk.size] = chunk
+    x[0, npos - 1, 7, 7] = 448.0 * grid[-1]
+    say("quantize ties", fmt)
+    xt = torch.from_numpy(x)
+    oq = oracle_quantize(d, mx.MX_ROLE_ACT, xt)
+    assert oq.t == 1.0 and np.all(oq.scales[:-1] == 0x38)
+    assert_quant_equal(gpu_quantize(d, mx.MX_ROLE_ACT, xt), oq)
+    for rnd in (mx.MX_SR,):
+        assert_quant_equal(gpu_quantize(d, mx.MX_ROLE_GRAD, xt, rnd, 11),
+                           oracle_quantize(d, mx.MX_ROLE_GRAD, xt, rnd, 11))
+
+
+@pytest.mark.parametrize("bad", [float("nan"), float("inf"), float("-inf")])
+def test_quantize_nonfinite(bad):
+    d = mx.desc(16, 16, 16, 3, 3, 1, 1, elem_fmt=mx.MX_E2M1)
+    x = WL.gen_tensor((3, 3, 16, 16), "normal", 3)
+    x[2, 1, 5, 9] = bad
+    say("quantize nonfinite", bad)
+    gq = gpu_quantize(d, mx.MX_ROLE_ACT, x)
+    assert_quant_equal(gq, oracle_quantize(d, mx.MX_ROLE_ACT, x))
+    assert np.isnan(gq.tensor_scale.item())
+    assert (gq.scales[:gq.scale_bytes] == 0x7F).all()
+
+
+def test_quantize_all_zero_and_empty():
+    d = mx.desc(16, 16, 16, 3, 3, 1, 1, elem_fmt=mx.MX_E2M3)
+    x = torch.zeros(3, 3, 16, 16)
+    say("quantize zero")
+    gq = gpu_quantize(d, mx.MX_ROLE_GRAD, x, mx.MX_SR, 1)
+    assert_quant_equal(gq, oracle_quantize(d, mx.MX_ROLE_GRAD, x, mx.MX_SR, 1))
+    assert gq.tensor_scale.item() == 0.0
+    # empty batch: nothing to quantize, T and amax still published as 0
+    de = mx.desc(0, 16, 16, 3, 3, 1, 1, elem_fmt=mx.MX_E2M1)
+    q = mx.QTensor(de, mx.MX_ROLE_ACT, DEV)
+    q.tensor_scale.fill_(5.0)
+    q.amax.fill_(5.0)
+    mx.mx_quantize_cbf(de, mx.MX_ROLE_ACT, torch.empty(0, device=DEV), q)
+    torch.cuda.synchronize()
+    assert q.tensor_scale.item() == 0.0 and q.amax.item() == 0.0
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_quantize_given_amax(fmt):
+    d = mx.desc(24, 16, 16, 4, 4, 3, 3, 1, 1, 1, 1, elem_fmt=fmt)
+    x = WL.gen_tensor((4, 4, 16, 24), "normal", 8)
+    true_amax = float(x.abs().max())
+    say("quantize given amax", fmt)
+    for a in (true_amax * 3.0, true_amax * 0.25):  # larger: coarser scales; smaller: saturation
+        gq = gpu_quantize(d, mx.MX_ROLE_ACT, x, amax=a)
+        oq = oracle_quantize(d, mx.MX_ROLE_ACT, x, amax=np.float32(a))
+        assert_quant_equal(gq, oq, f"amax {a}")
+    gq = gpu_quantize(d, mx.MX_ROLE_ACT, x, amax=float("nan"))
+    assert np.isnan(gq.tensor_scale.item())
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("role", [mx.MX_ROLE_ACT, mx.MX_ROLE_WEIGHT, mx.MX_ROLE_GRAD])
+def test_dequantize_bit_exact(fmt, role):
+    d = mx.desc(40, 24, 16, 5, 3, 3, 3, 1, 1, 1, 1, elem_fmt=fmt)
+    say("dequantize", fmt, role)
+    src = src_for(d, role, 31)
+    rnd = mx.MX_SR if role == mx.MX_ROLE_GRAD else mx.MX_RNE
+    gq = gpu_quantize(d, role, src, rnd, 3)
+    out = torch.empty(src.shape, device=DEV)
+    mx.mx_dequantize(d, role, gq, out)
+    torch.cuda.synchronize()
+    ref = O.dequantize(oracle_quantize(d, role, src, rnd, 3))
+    got = out.cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_dequantize_nonfinite_tensor():
+    d = mx.desc(8, 8, 8, 2, 2, 1, 1, elem_fmt=mx.MX_E2M1)
+    x = WL.gen_tensor((2, 2, 8, 8), "normal", 2)
+    x[0, 0, 0, 0] = float("nan")
+    gq = gpu_quantize(d, mx.MX_ROLE_ACT, x)
+    out = torch.empty(x.shape, device=DEV)
+    mx.mx_dequantize(d, mx.MX_ROLE_ACT, gq, out)
+    torch.cuda.synchronize()
+    assert torch.isnan(out).all()
