@@ -1,0 +1,376 @@
+"""Benchmark of the MicroQonv microscaling convolution hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of the workload:
+for every quantized conv layer of the stack
+  S1+S2  quantize X (activation, RNE), W (weight, RNE), dY (gradient, SR)
+  S4     forward          Y  = W . im2col(Xq)
+  S5     data gradient    dX = col2im(Wq^T . dYq)
+  S6     weight gradient  dW = dYq . im2col(Xq)^T
+  S7     dequantize Xq (fake-quantized fp32 activation)
+and, for the workload that has one, S8: the latent-replay buffer quantized
+(S1+S2) and dequantized (S7).  Inputs are seeded synthetic tensors already
+resident in device memory when the timed region starts.
+
+value = sum of the dense fwd+dgrad+wgrad flops of all layers / step time
+(quantization and dequantization time included in the step time).
+
+Prints one JSON line (see the keys below).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM = 8.0e12                    # bytes/s, MI355X HBM3E
+PEAK_MFMA = {"bf16": 2.5e15, "f16": 2.5e15}  # dense flop/s
+RIDGE = PEAK_MFMA["bf16"] / PEAK_HBM  # flop per byte
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c2", help="c1..c5 (default c2: ResNet-32 stack)")
+    ap.add_argument("--fmt", default=None, help="element format override: e2m1|e2m3|e4m3")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="approximate budget of the CPU-baseline sample")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay the step as one captured HIP graph (per-call timing then comes "
+                         "from a separate eager pass)")
+    ap.add_argument("--copy-calib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--verbose", action="store_true")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "microscaling_quantized_convolution_mx_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+class Call:
+    """One prepared C-ABI call: the function and its ctypes arguments are
+    built once, so that the timed loop only pays for the call itself."""
+
+    __slots__ = ("fn", "args", "op", "group", "flops", "bytes", "name")
+
+    def __init__(self, fn, args, op, group, flops, nbytes, name):
+        self.fn, self.args, self.op, self.group = fn, args, op, group
+        self.flops, self.bytes, self.name = flops, nbytes, name
+
+    def __call__(self):
+        rc = self.fn(*self.args)
+        if rc != 0:
+            raise RuntimeError(f"{self.name}: status {rc}")
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU: the hot path is the single-GPU "
+                                   "kernel set (multi-GPU sharding is a design note only); "
+                                   "run with --gpus 1"}))
+        sys.exit(2)
+
+    import torch
+    import microscaling_quantized_convolution_mx_amd as mx
+    from microscaling_quantized_convolution_mx_amd import workloads as WL
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if a.copy_calib:
+        n = a.copy_calib * (1 << 20) // 4
+        src = torch.ones(n, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calib_bytes_each_way": n * 4, "launches": 3}))
+        return
+
+    L = mx.lib()
+    wl = WL.workloads()[a.workload]
+    fmts = {"e2m1": mx.MX_E2M1, "e2m3": mx.MX_E2M3, "e4m3": mx.MX_E4M3}
+    fmt = fmts[a.fmt] if a.fmt else wl.elem_fmts[0]
+    ebits = {mx.MX_E2M1: 4, mx.MX_E2M3: 6, mx.MX_E4M3: 8}[fmt]
+    qb = ebits / 8 + 1 / 64          # quantized bytes per element (codes + block scales)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    D = ctypes.byref
+    calls: list[Call] = []
+    keep = []                         # keeps every buffer and ctypes struct alive
+    ws_bytes = max(mx.mx_wgrad_workspace_bytes(mx.desc_from_layer(l, fmt)) for l in wl.layers)
+    ws = torch.empty(max(ws_bytes // 4, 4), device=dev)
+    keep.append(ws)
+
+    t_gen = time.time()
+    for li, lay in enumerate(wl.layers):
+        d = mx.desc_from_layer(lay, fmt)
+        x = WL.gen_x(lay, wl.x_dist, WL.seed_for(wl.cfg_index, li, 1)).to(dev)
+        w = WL.gen_w(lay, WL.seed_for(wl.cfg_index, li, 2)).to(dev)
+        dy = WL.gen_dy(lay, wl.dy_sigma, WL.seed_for(wl.cfg_index, li, 3)).to(dev)
+        sr_seed = WL.seed_for(wl.cfg_index, li, 4)
+        qx, qw, qdy = (mx.QTensor(d, r, dev) for r in (mx.MX_ROLE_ACT, mx.MX_ROLE_WEIGHT, mx.MX_ROLE_GRAD))
+        y = torch.empty(lay.h_out, lay.w_out, lay.c_out, lay.n, device=dev)
+        dx = torch.empty(lay.h, lay.w, lay.c_in, lay.n, device=dev)
+        dw = torch.empty(lay.c_out, lay.c_in, lay.k_h, lay.k_w, device=dev)
+        xdq = torch.empty_like(x)
+        cq = [q.c() for q in (qx, qw, qdy)]
+        keep += [d, x, w, dy, qx, qw, qdy, y, dx, dw, xdq, cq]
+        shape = lay.tag()
+        nx, nw, ny = lay.numel_x(), lay.numel_w(), lay.numel_dy()
+        f = lay.flops()
+        calls += [
+            Call(L.mx_quantize_cbf, (D(d), mx.MX_ROLE_ACT, x.data_ptr(), D(cq[0]), mx.MX_RNE, 0, 0, stream),
+                 "quantize", ("quantize_act", shape), 0, nx * (8 + qb), "quantize X"),
+            Call(L.mx_quantize_cbf, (D(d), mx.MX_ROLE_WEIGHT, w.data_ptr(), D(cq[1]), mx.MX_RNE, 0, 0, stream),
+                 "quantize", ("quantize_weight", shape), 0, nw * (8 + qb), "quantize W"),
+            Call(L.mx_quantize_cbf, (D(d), mx.MX_ROLE_GRAD, dy.data_ptr(), D(cq[2]), mx.MX_SR, sr_seed, 0, stream),
+                 "quantize", ("quantize_grad", shape), 0, ny * (8 + qb), "quantize dY"),
+            Call(L.mx_conv_fwd, (D(d), D(cq[1]), D(cq[0]), y.data_ptr(), stream),
+                 "fwd", ("conv_fwd", shape), f, (nw + nx) * qb + 4 * ny, "fwd"),
+            Call(L.mx_conv_dgrad, (D(d), D(cq[1]), D(cq[2]), dx.data_ptr(), stream),
+                 "dgrad", ("conv_dgrad", shape), f, (nw + ny) * qb + 4 * nx, "dgrad"),
+            Call(L.mx_conv_wgrad, (D(d), D(cq[2]), D(cq[0]), dw.data_ptr(), ws.data_ptr(), ws_bytes, stream),
+                 "wgrad", ("conv_wgrad", shape), f, (ny + nx) * qb + 4 * nw, "wgrad"),
+            Call(L.mx_dequantize, (D(d), mx.MX_ROLE_ACT, D(cq[0]), xdq.data_ptr(), stream),
+                 "dequantize", ("dequantize_act", shape), 0, nx * (qb + 4), "dequantize X"),
+        ]
+    if wl.lr_buffer is not None:
+        nmaps, c, h, w_ = wl.lr_buffer
+        d = mx.desc(nmaps, c, c, h, w_, 1, 1, elem_fmt=mx.MX_E2M1)
+        maps = WL.gen_lr_maps(nmaps, c, h, w_, WL.seed_for(wl.cfg_index, 0, 5)).to(dev)
+        q = mx.QTensor(d, mx.MX_ROLE_ACT, dev)
+        back = torch.empty_like(maps)
+        cq = q.c()
+        keep += [d, maps, q, back, cq]
+        n_el = maps.numel()
+        qb4 = 4 / 8 + 1 / 64
+        shape = f"replay buffer {nmaps}x{c}@{h}x{w_}"
+        calls += [
+            Call(L.mx_quantize_cbf, (D(d), mx.MX_ROLE_ACT, maps.data_ptr(), D(cq), mx.MX_RNE, 0, 0, stream),
+                 "quantize", ("quantize_replay", shape), 0, n_el * (8 + qb4), "quantize replay buffer"),
+            Call(L.mx_dequantize, (D(d), mx.MX_ROLE_ACT, D(cq), back.data_ptr(), stream),
+                 "dequantize", ("dequantize_replay", shape), 0, n_el * (qb4 + 4), "dequantize replay buffer"),
+        ]
+    torch.cuda.synchronize()
+    t_gen = time.time() - t_gen
+
+    total_flops = sum(c.flops for c in calls)
+
+    def run_step(events=None):
+        if events is None:
+            for c in calls:
+                c()
+        else:
+            for i, c in enumerate(calls):
+                c()
+                events[i].record()
+
+    for _ in range(a.warmup):
+        run_step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps, an event after every call
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in calls] for _ in range(a.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    graph = None
+    if a.graph:
+        # every C-ABI call takes the stream as its last argument
+        def set_stream(h):
+            for c in calls:
+                c.args = c.args[:-1] + (h,)
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        set_stream(s.cuda_stream)
+        with torch.cuda.stream(s):
+            run_step()          # eager pass on the capture stream first
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=s):
+                run_step()
+        torch.cuda.current_stream().wait_stream(s)
+        set_stream(stream)
+        graph = g
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for k in range(a.steps):
+        if graph is not None:
+            graph.replay()
+        else:
+            run_step(ev[k])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = start.elapsed_time(end)
+    ms_step = ms_total / a.steps
+
+    if graph is not None:
+        # per-call durations from an eager pass with events (outside the timed region)
+        for k in range(a.steps):
+            run_step(ev[k])
+        torch.cuda.synchronize()
+    # per-call durations: gap between consecutive events (first call of a step
+    # measured from the previous step's last event, or from `start`)
+    per_call = [[0.0] * len(calls) for _ in range(a.steps)]
+    for k in range(a.steps):
+        for i in range(len(calls)):
+            if i == 0:
+                prev = ev[k - 1][-1] if k > 0 else None
+                if prev is None:
+                    per_call[k][i] = start.elapsed_time(ev[k][0]) if graph is None else float("nan")
+                else:
+                    per_call[k][i] = prev.elapsed_time(ev[k][0])
+            else:
+                per_call[k][i] = ev[k][i - 1].elapsed_time(ev[k][i])
+    # average over steps (skip NaN of the first call in graph mode)
+    avg_ms = []
+    for i in range(len(calls)):
+        vals = [per_call[k][i] for k in range(a.steps) if per_call[k][i] == per_call[k][i]]
+        avg_ms.append(sum(vals) / len(vals) if vals else float("nan"))
+
+    groups = {}
+    for i, c in enumerate(calls):
+        gkey = c.group
+        gi = groups.setdefault(gkey, {"ms": 0.0, "n": 0, "flops": c.flops, "bytes": c.bytes, "op": c.op})
+        gi["ms"] += avg_ms[i]
+        gi["n"] += 1
+    by_op = {}
+    for i, c in enumerate(calls):
+        o = by_op.setdefault(c.op, {"ms": 0.0, "flops": 0, "bytes": 0})
+        o["ms"] += avg_ms[i]
+        o["flops"] += c.flops
+        o["bytes"] += c.bytes
+
+    dom_key, dom = max(groups.items(), key=lambda kv: kv[1]["ms"])
+    launch_s = dom["ms"] / dom["n"] / 1e3
+    ai = dom["flops"] / dom["bytes"] if dom["bytes"] else 0.0
+    if dom["flops"] and ai >= RIDGE:
+        achieved = dom["flops"] / launch_s
+        roof = {"bound": "mfma", "achieved": achieved / 1e12, "peak": PEAK_MFMA["bf16"] / 1e12,
+                "unit": "TFLOP/s"}
+    else:
+        achieved = dom["bytes"] / launch_s
+        roof = {"bound": "hbm", "achieved": achieved / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["kernel"] = f"{dom_key[0]} [{dom_key[1]}]"
+    roof["launch_us"] = launch_s * 1e6
+    roof["algorithmic_per_launch"] = {"flops": dom["flops"], "bytes": dom["bytes"]}
+    roof["traffic"] = None
+    tfile = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(tfile):
+        try:
+            tr = json.load(open(tfile))
+            ent = tr.get("kernels", {}).get(f"{a.workload}:{dom_key[0]}:{dom_key[1]}")
+            if ent and tr.get("source_hash") == kernel_source_hash():
+                roof["traffic"] = ent["hbm_bytes_per_launch"]
+        except (ValueError, KeyError):
+            pass
+    roof["ai_flop_per_byte"] = ai
+
+    conv_ms = sum(by_op.get(o, {"ms": 0.0})["ms"] for o in ("fwd", "dgrad", "wgrad"))
+    q_ms = by_op.get("quantize", {"ms": 0.0})["ms"]
+    q_bytes = by_op.get("quantize", {"bytes": 0})["bytes"]
+
+    result = {
+        "metric": "effective TFLOP/s of MX conv fwd+dgrad+wgrad (implicit im2col); quantize GB/s",
+        "value": total_flops / (ms_step / 1e3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{a.workload}: {wl.name}", "layers": len(wl.layers),
+                   "batch": wl.layers[0].n, "elem_fmt": WL.FMT_NAMES[fmt],
+                   "block": "8x8 E4M3 scale + fp32 tensor scale",
+                   "step": "per layer: quantize X,W,dY; fwd; dgrad; wgrad; dequantize Xq"
+                           + ("; replay buffer quantize+dequantize" if wl.lr_buffer else ""),
+                   "graph": bool(graph is not None)},
+        "conv_tflops": total_flops / (conv_ms / 1e3) / 1e12 if conv_ms > 0 else None,
+        "quantize_gbps": q_bytes / (q_ms / 1e3) / 1e9 if q_ms > 0 else None,
+        "step_breakdown_ms": {k: v["ms"] for k, v in by_op.items()},
+        "roofline": roof,
+        "wall_s_timed": wall,
+        "kernel_source": kernel_source_hash(),
+    }
+    if a.verbose:
+        result["groups"] = {f"{k[0]} [{k[1]}]": {"ms_total": v["ms"], "launches": v["n"],
+                                                 "flops": v["flops"], "bytes": v["bytes"]}
+                            for k, v in sorted(groups.items(), key=lambda kv: -kv[1]["ms"])}
+
+    if not a.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, fmt, a.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(wl, fmt, budget_s):
+    """The CPU oracle, as it stands, on a bounded sample of the workload: the
+    full quantize + fwd + dgrad + wgrad of the first layers of the stack, taken
+    in order until the time budget is spent; reported in the metric's unit."""
+    import numpy as np
+    import oracle as O
+    from microscaling_quantized_convolution_mx_amd import workloads as WL
+
+    O.lib()
+    flops = 0
+    spent = 0.0
+    done = []
+    seen = set()
+    for li, lay in enumerate(wl.layers):
+        if lay.tag() in seen:
+            continue
+        seen.add(lay.tag())
+        # estimate: a few ns per multiply-add per thread; stop before the budget
+        x = WL.gen_x(lay, wl.x_dist, WL.seed_for(wl.cfg_index, li, 1)).numpy()
+        w = WL.gen_w(lay, WL.seed_for(wl.cfg_index, li, 2)).numpy()
+        dy = WL.gen_dy(lay, wl.dy_sigma, WL.seed_for(wl.cfg_index, li, 3)).numpy()
+        cv = O.conv(lay.n, lay.c_in, lay.c_out, lay.h, lay.w, lay.k_h, lay.k_w,
+                    lay.stride_h, lay.stride_w, lay.pad_h, lay.pad_w)
+        t0 = time.perf_counter()
+        qx = O.quantize(O.ACT, fmt, x)
+        qw = O.quantize(O.WEIGHT, fmt, w)
+        qdy = O.quantize(O.GRAD, fmt, dy, O.SR, WL.seed_for(wl.cfg_index, li, 4))
+        xe, we, dye = qx.exact(), qw.exact(), qdy.exact()
+        O.conv_fwd(cv, we, xe)
+        O.conv_dgrad(cv, we, dye)
+        O.conv_wgrad(cv, dye, xe)
+        dt = time.perf_counter() - t0
+        spent += dt
+        flops += 3 * lay.flops()
+        done.append(lay.tag())
+        if spent > budget_s * 0.5:
+            break
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"full quantize X/W/dY + fp64 fwd/dgrad/wgrad of {len(done)} distinct layer(s) "
+                      f"of the workload ({'; '.join(done)}), {flops / 1e9:.2f} GFLOP in {spent:.1f} s",
+            "seconds": spent}
+
+
+if __name__ == "__main__":
+    main()

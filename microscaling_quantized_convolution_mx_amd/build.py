@@ -23,7 +23,7 @@ ARCH = os.environ.get("MXCONV_ARCH", "gfx950")
 SOURCES = ["capi.cpp", "quantize.hip", "conv.hip"]
 
 FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC", "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}",
 ]

@@ -25,20 +25,32 @@
 // per stage, decodes it and writes its eight 8-value K-lines to LDS as
 // 16-byte rows [line][k] (k contiguous), which is exactly the operand layout
 // of v_mfma_f32_32x32x16_bf16 (lane l: row/col l%32, K slots 8*(l/32)..+7).
+#include <type_traits>
+#include <utility>
+
 #include "internal.h"
 #include "mx_formats.h"
 
 namespace mx {
 namespace {
 
-constexpr int kThreads = 256;
 constexpr int KT = 32;          // K per LDS stage
-constexpr int LDS_STRIDE = 40;  // bf16 per LDS line: 32 + 8 padding (80 B) against bank conflicts
+// LDS layout of a staged tile: lines of 32 K values (64 B) at a stride of
+// 80 B, and logical line L stored at physical line L ^ ((L >> 2) & 4) (the
+// two halves of every second 8-line block swapped).  With 64 LDS banks this
+// keeps both access patterns conflict-free: the 16-byte fragment reads of 16
+// consecutive lines hit 16 distinct bank quads, and the 64-byte line writes
+// of four neighbouring blocks (same line index) hit the four bank quarters.
+constexpr int LDS_STRIDE = 40;  // 16-bit elements per line
+__device__ __forceinline__ int lds_line(int line) { return (line ^ ((line >> 2) & 4)) * LDS_STRIDE; }
 
 enum { OP_FWD = 0, OP_DGRAD = 1, OP_WGRAD = 2 };
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 f16x2;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef unsigned int u32x6 __attribute__((ext_vector_type(6)));
 
 struct ConvParams {
   int32_t n, c_in, c_out, h, w, k_h, k_w, sh, sw, ph, pw, ho, wo;
@@ -57,25 +69,23 @@ struct ConvParams {
   float* out;
 };
 
-// Code of element (r, c) of a block from its 32-bit words (compile-time r, c
-// after unrolling).
-template <int FMT>
-__device__ __forceinline__ uint32_t blk_code(const uint32_t* w, int r, int c) {
-  constexpr int BITS = Fmt<FMT>::BITS;
-  const int bit = (r * 8 + c) * BITS;
-  const int wi = bit >> 5, s = bit & 31;
-  uint32_t v = w[wi] >> s;
-  if (s + BITS > 32) v |= w[wi + 1] << (32 - s);
-  return v & ((1u << BITS) - 1u);
-}
+// MFMA operand type: E2M1 and E2M3 blocks decode exactly to fp16 (g*B lies in
+// [2^-12, 3360] with at most 8 significant bits); E4M3 x E4M3 spans 2^-18 ..
+// 2*10^5, beyond fp16's normal range, and decodes exactly to bf16.
+template <int FMT> struct OperandType { static constexpr bool F16 = (FMT != FMT_E4M3); };
 
-// bf16 bit pattern of the signed value code * B (exact).
-template <int FMT>
-__device__ __forceinline__ uint32_t dq_bf16(uint32_t code, float B) {
-  using F = Fmt<FMT>;
-  const float v = code_value<F>(code & ((1u << F::SIGN) - 1u)) * B;
-  return (__float_as_uint(v) >> 16) | (((code >> F::SIGN) & 1u) << 15);
-}
+// Exponent-only scaling plus mantissa factor of an E4M3 block scale B: the
+// gfx950 scaled conversions multiply by 2^floor(log2 scale) only, so
+// convert(code, B) * mB == code * B exactly, mB = B / 2^floor(log2 B) (a
+// value 1 + m/8).  A zero scale gives mB = 0 (the block decodes to zeros).
+struct BlockScale {
+  float b;   // B itself, passed as the conversion's scale operand
+  float mb;  // mantissa factor
+  __device__ __forceinline__ explicit BlockScale(uint32_t code) {
+    b = code_value<ScaleFmt>(code);
+    mb = (code == 0u) ? 0.0f : __uint_as_float((__float_as_uint(b) & 0x007FFFFFu) | 0x3F800000u);
+  }
+};
 
 // Raw codes of one block held in registers between the global load and the
 // LDS store.
@@ -84,10 +94,13 @@ struct RawBlock {
   static constexpr int WORDS = block_bytes<FMT>() / 4;
   uint32_t w[WORDS];
   uint32_t scale;
-  bool valid;
 
   __device__ __forceinline__ void load(const uint8_t* codes, const uint8_t* scales, int64_t blk, bool ok) {
-    valid = ok;
+    // a block outside the tensor (zero padding, tails) decodes to zeros: codes
+    // 0 and scale 0 give mB = 0
+#pragma unroll
+    for (int i = 0; i < WORDS; ++i) w[i] = 0u;
+    scale = 0u;
     if (ok) {
       const uint4* p = reinterpret_cast<const uint4*>(codes + blk * block_bytes<FMT>());
 #pragma unroll
@@ -101,54 +114,173 @@ struct RawBlock {
       scale = scales[blk];
     }
   }
+};
 
-  // Write the block as eight K-lines of 8 bf16: line i is block row i
-  // (ROWS) or block column i (!ROWS), values along the other index.
-  template <bool ROWS>
-  __device__ __forceinline__ void store(uint16_t* line0) const {
+// Staging of one block into LDS, cut into units so that the units can be
+// placed between the MFMAs of a K step.  ROWS: unit u (0..7) writes line u =
+// block row u.  !ROWS: unit u (0..3) writes lines 2u and 2u+1 = block columns
+// 2u, 2u+1 (a 2x2 transpose of the row pairs).  Each unit decodes what it
+// writes (E2M3 decodes 32 elements at a time: in the first unit of a 4-row
+// group for ROWS, all 64 in unit 0 for !ROWS).
+template <int FMT, bool ROWS>
+struct Stager {
+  static constexpr int UNITS = ROWS ? 8 : 4;
+  BlockScale bs;
+  uint32_t P[8][4];  // pairs (element (r,2j), element (r,2j+1)) as two 16-bit floats
+  uint16_t* p_lo;    // lines 0-3 of the block (swizzled halves, see lds_line)
+  uint16_t* p_hi;    // lines 4-7
+
+  __device__ __forceinline__ Stager(const RawBlock<FMT>& raw, uint16_t* lo, uint16_t* hi)
+      : bs(raw.scale), p_lo(lo), p_hi(hi) {}
+
+  __device__ __forceinline__ uint16_t* line_ptr(int i) const {
+    return (i < 4) ? p_lo + i * LDS_STRIDE : p_hi + (i - 4) * LDS_STRIDE;
+  }
+
+  // pair j of row r
+  template <int R, int J>
+  __device__ __forceinline__ uint32_t pair(const RawBlock<FMT>& raw) const {
+    if constexpr (FMT == FMT_E2M1) {
+      const _Float16 m = static_cast<_Float16>(bs.mb);
+      const f16x2 m2 = {m, m};
+      return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(raw.w[R], bs.b, J) * m2);
+    } else {
+      // exact: at most 7 significant bits, so the bf16 is the high half
+      const auto f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(raw.w[2 * R + (J >> 1)], bs.b, (J & 1) != 0);
+      const float lo = f[0] * bs.mb, hi = f[1] * bs.mb;
+      return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+    }
+  }
+
+  // E2M3: rows 4G .. 4G+3 (192 consecutive bits) into P
+  template <int G>
+  __device__ __forceinline__ void fp6_group(const RawBlock<FMT>& raw) {
+    const _Float16 m = static_cast<_Float16>(bs.mb);
+    const f16x2 m2 = {m, m};
+    u32x6 src;
+    src[0] = raw.w[6 * G + 0]; src[1] = raw.w[6 * G + 1]; src[2] = raw.w[6 * G + 2];
+    src[3] = raw.w[6 * G + 3]; src[4] = raw.w[6 * G + 4]; src[5] = raw.w[6 * G + 5];
+    const auto v = __builtin_amdgcn_cvt_scalef32_pk32_f16_fp6(src, bs.b);
+    struct Words { uint32_t u[16]; };
+    const Words wv = __builtin_bit_cast(Words, v);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint4 o = make_uint4(0u, 0u, 0u, 0u);
-      if (valid) {
-        const float B = code_value<ScaleFmt>(scale);
-        uint32_t q[4];
-#pragma unroll
-        for (int k = 0; k < 8; k += 2) {
-          const uint32_t c0 = ROWS ? blk_code<FMT>(w, i, k) : blk_code<FMT>(w, k, i);
-          const uint32_t c1 = ROWS ? blk_code<FMT>(w, i, k + 1) : blk_code<FMT>(w, k + 1, i);
-          q[k / 2] = dq_bf16<FMT>(c0, B) | (dq_bf16<FMT>(c1, B) << 16);
-        }
-        o = make_uint4(q[0], q[1], q[2], q[3]);
+    for (int i = 0; i < 16; ++i)
+      P[4 * G + i / 4][i % 4] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, wv.u[i]) * m2);
+  }
+
+  template <int U>
+  __device__ __forceinline__ void unit(const RawBlock<FMT>& raw) {
+    if constexpr (ROWS) {
+      if constexpr (FMT == FMT_E2M3) {
+        if constexpr (U % 4 == 0) fp6_group<U / 4>(raw);
+      } else {
+        P[U][0] = pair<U, 0>(raw);
+        P[U][1] = pair<U, 1>(raw);
+        P[U][2] = pair<U, 2>(raw);
+        P[U][3] = pair<U, 3>(raw);
       }
-      *reinterpret_cast<uint4*>(line0 + i * LDS_STRIDE) = o;
+      *reinterpret_cast<uint4*>(line_ptr(U)) = make_uint4(P[U][0], P[U][1], P[U][2], P[U][3]);
+    } else {
+      if constexpr (FMT == FMT_E2M3) {
+        if constexpr (U == 0) {
+          fp6_group<0>(raw);
+          fp6_group<1>(raw);
+        }
+      } else {
+        P[0][U] = pair<0, U>(raw); P[1][U] = pair<1, U>(raw);
+        P[2][U] = pair<2, U>(raw); P[3][U] = pair<3, U>(raw);
+        P[4][U] = pair<4, U>(raw); P[5][U] = pair<5, U>(raw);
+        P[6][U] = pair<6, U>(raw); P[7][U] = pair<7, U>(raw);
+      }
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const uint32_t sel = e ? 0x07060302u : 0x05040100u;
+        uint4 o;
+        o.x = __builtin_amdgcn_perm(P[1][U], P[0][U], sel);
+        o.y = __builtin_amdgcn_perm(P[3][U], P[2][U], sel);
+        o.z = __builtin_amdgcn_perm(P[5][U], P[4][U], sel);
+        o.w = __builtin_amdgcn_perm(P[7][U], P[6][U], sel);
+        *reinterpret_cast<uint4*>(line_ptr(2 * U + e)) = o;
+      }
     }
   }
 };
 
-// Which operand block a thread stages for one K step, and where it goes.
-struct Slot {
-  bool is_a;      // A (rows) or B (columns) tile
-  int line;       // first LDS line (A: local row, B: MT + local column)
-  int kbl;        // k-block within the step (0..3)
-  int gblk;       // global row-block (A) or column-block (B)
+// Walks the k-blocks one thread stages, four at a time (kb, kb+4, ...),
+// keeping the decomposition of kb incrementally (no division in the loop).
+//   FWD  : kb = tap * CBin + cib,  tap = kh * Kw + kw
+//   DGRAD: kb = ti * CBout + cob,  ti over the phase's valid taps (it, jt)
+//   WGRAD: kb = pos * NB + nbk,    pos = ho * Wo + wo
+struct KWalk {
+  int a, b;    // outer index (tap / tap pair / position) split in two, inner index
+  int inner;   // fastest index (cib / cob / nbk)
+  int kb;
+  __device__ __forceinline__ void init(int kb0, int n_inner, int n_b) {
+    kb = kb0;
+    const int outer = kb0 / n_inner;
+    inner = kb0 - outer * n_inner;
+    a = outer / n_b;
+    b = outer - a * n_b;
+  }
+  __device__ __forceinline__ void advance4(int n_inner, int n_b) {
+    kb += 4;
+    inner += 4;
+    while (inner >= n_inner) {
+      inner -= n_inner;
+      if (++b == n_b) {
+        b = 0;
+        ++a;
+      }
+    }
+  }
 };
 
-template <int OP, int FMT, int MT, int NT, int WM>
-__global__ __launch_bounds__(kThreads) void k_conv(const ConvParams p) {
-  constexpr int WN = 4 / WM;
+template <bool F16>
+__device__ __forceinline__ f32x16 mfma32(const uint16_t* pa, const uint16_t* pb, f32x16 c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(*reinterpret_cast<const f16x8*>(pa),
+                                                  *reinterpret_cast<const f16x8*>(pb), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(pa),
+                                                   *reinterpret_cast<const bf16x8*>(pb), c, 0, 0, 0);
+}
+
+template <int OP, int FMT, int MT, int NT, int WM, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void k_conv(const ConvParams p) {
+  constexpr int WN = WAVES / WM;
   constexpr int WTM = MT / WM, WTN = NT / WN;
   constexpr int RM = WTM / 32, RN = WTN / 32;
   constexpr int ABLK = (MT / 8) * 4, BBLK = (NT / 8) * 4;
-  static_assert(ABLK + BBLK <= kThreads, "one block per thread per stage");
-  static_assert(RM >= 1 && RN >= 1, "wave tile at least 32x32");
+  constexpr bool F16 = OperandType<FMT>::F16;
+  static_assert(ABLK + BBLK <= WAVES * 64, "one block per thread per stage");
+  static_assert(RM >= 1 && RN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile of 32x32 MFMAs");
 
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][(MT + NT) * LDS_STRIDE];
+  // two stages of MT + NT lines, plus 8 lines that threads without a block
+  // write their zeros into (keeps the staging code branch-free)
+  constexpr int STAGE = (MT + NT + 8) * LDS_STRIDE;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2][STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave % WM, wn = wave / WM;
-  const int rb0 = blockIdx.y * (MT / 8);
-  const int cb0 = blockIdx.x * (NT / 8);
+  // Workgroups are dealt round-robin to the 8 XCDs (each with its own L2) in
+  // launch order.  Renumber them so that every XCD works on one contiguous
+  // range of tiles: neighbouring output tiles share most of their quantized
+  // input blocks (the im2col halo, and the whole weight tile).
+  int bx, by, bz;
+  {
+    const int total = gridDim.x * gridDim.y * gridDim.z;
+    const int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    const int q = total >> 3, r = total & 7, xcd = lin & 7, idx = lin >> 3;
+    const int nl = xcd < r ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+    bx = nl % gridDim.x;
+    const int t = nl / gridDim.x;
+    by = t % gridDim.y;
+    bz = t / gridDim.y;
+  }
+  const int rb0 = by * (MT / 8);
+  const int cb0 = bx * (NT / 8);
+  const int cbin = p.c_in >> 3, cbout = p.c_out >> 3;
 
   // ---- per-launch-z context: data-gradient phase or weight-gradient split
   int phh = 0, phw = 0, kh0 = 0, kw0 = 0, nkh = p.k_h, nkw = p.k_w, hp = 0, wp = 0;
@@ -156,102 +288,100 @@ __global__ __launch_bounds__(kThreads) void k_conv(const ConvParams p) {
   if constexpr (OP == OP_DGRAD) {
     // output pixels (h, w) with h = phh + sh*h', w = phw + sw*w' receive the
     // taps kh = (phh + ph) mod sh (+ sh, ...), kw likewise
-    phh = blockIdx.z / p.sw;
-    phw = blockIdx.z % p.sw;
+    phh = bz / p.sw;
+    phw = bz - phh * p.sw;
     kh0 = (phh + p.ph) % p.sh;
     kw0 = (phw + p.pw) % p.sw;
     nkh = kh0 < p.k_h ? (p.k_h - kh0 + p.sh - 1) / p.sh : 0;
     nkw = kw0 < p.k_w ? (p.k_w - kw0 + p.sw - 1) / p.sw : 0;
     hp = (p.h - phh + p.sh - 1) / p.sh;
     wp = (p.w - phw + p.sw - 1) / p.sw;
-    const int ncb_phase = hp * wp * p.nb;
-    if (cb0 >= ncb_phase) return;
-    kb_end = nkh * nkw * (p.c_out >> 3);
+    if (cb0 >= hp * wp * p.nb) return;
+    kb_end = nkh * nkw * cbout;
   } else if constexpr (OP == OP_WGRAD) {
-    kb_begin = blockIdx.z * p.ks_split * 4;
+    kb_begin = bz * p.ks_split * 4;
     kb_end = min(p.kb_total, kb_begin + p.ks_split * 4);
     if (kb_begin > kb_end) kb_begin = kb_end;
   }
   const int ncb_launch = (OP == OP_DGRAD) ? hp * wp * p.nb : p.ncb;
 
   // ---- the block this thread stages every step
-  Slot slot;
-  slot.is_a = tid < ABLK;
-  if (slot.is_a) {
-    slot.line = (tid >> 2) * 8;
-    slot.kbl = tid & 3;
-    slot.gblk = rb0 + (tid >> 2);
-  } else {
-    const int t = tid - ABLK;
-    slot.line = MT + (t >> 2) * 8;
-    slot.kbl = t & 3;
-    slot.gblk = cb0 + (t >> 2);
-  }
+  const bool is_a = tid < ABLK;
+  const int t_local = is_a ? tid : tid - ABLK;
   const bool active = tid < ABLK + BBLK;
-  const bool in_range = slot.is_a ? (slot.gblk < (p.M >> 3)) : (slot.gblk < ncb_launch);
+  const int line = !active ? MT + NT : is_a ? (t_local >> 2) * 8 : MT + (t_local >> 2) * 8;
+  const int kbl = active ? (t_local & 3) : 0;
+  const int gblk = (is_a ? rb0 : cb0) + (t_local >> 2);
+  const bool in_range = active && (is_a ? (gblk < (p.M >> 3)) : (gblk < ncb_launch));
+  // swizzled addresses of the block's two line halves (see lds_line)
+  const int rot = (line >> 2) & 4;
+  const int lo_off = (line + rot) * LDS_STRIDE + kbl * 8;
+  const int hi_off = (line + (rot ^ 4)) * LDS_STRIDE + kbl * 8;
 
   // Column-block geometry fixed over the K loop.
-  int col_ho = 0, col_wo = 0, col_nb = 0;  // FWD: output position; DGRAD: input pixel
-  int col_tap_h = 0, col_tap_w = 0, col_cib = 0;  // WGRAD: tap and channel block
-  if (!slot.is_a && in_range) {
+  int col_y = 0, col_x = 0, col_nb = 0;   // FWD: output (ho, wo); DGRAD: input pixel (h, w)
+  int col_kh = 0, col_kw = 0, col_cib = 0; // WGRAD: tap and channel block
+  if (!is_a && in_range) {
     if constexpr (OP == OP_FWD) {
-      const int pos = slot.gblk / p.nb;
-      col_nb = slot.gblk - pos * p.nb;
-      col_ho = pos / p.wo;
-      col_wo = pos - col_ho * p.wo;
+      const int pos = gblk / p.nb;
+      col_nb = gblk - pos * p.nb;
+      col_y = pos / p.wo;
+      col_x = pos - col_y * p.wo;
     } else if constexpr (OP == OP_DGRAD) {
-      const int pos = slot.gblk / p.nb;
-      col_nb = slot.gblk - pos * p.nb;
+      const int pos = gblk / p.nb;
+      col_nb = gblk - pos * p.nb;
       const int hq = pos / wp;
-      col_ho = phh + p.sh * hq;             // input row h
-      col_wo = phw + p.sw * (pos - hq * wp); // input col w
+      col_y = phh + p.sh * hq;
+      col_x = phw + p.sw * (pos - hq * wp);
     } else {
-      const int cbin = p.c_in >> 3;
-      const int tap = slot.gblk / cbin;
-      col_cib = slot.gblk - tap * cbin;
-      col_tap_h = tap / p.k_w;
-      col_tap_w = tap - col_tap_h * p.k_w;
+      const int tap = gblk / cbin;
+      col_cib = gblk - tap * cbin;
+      col_kh = tap / p.k_w;
+      col_kw = tap - col_kh * p.k_w;
     }
   }
 
-  // Locate the quantized block of this thread's slot for k-block kb; returns
-  // false when it lies in the zero padding (or outside the GEMM).
-  auto locate = [&](int kb, int64_t& blk) -> bool {
-    if (!active || !in_range || kb >= kb_end) return false;
-    const int cbin = p.c_in >> 3, cbout = p.c_out >> 3;
+  // incremental walk over this thread's k-blocks
+  int n_inner, n_b;
+  if constexpr (OP == OP_FWD) { n_inner = cbin; n_b = p.k_w; }
+  else if constexpr (OP == OP_DGRAD) { n_inner = cbout; n_b = nkw > 0 ? nkw : 1; }
+  else { n_inner = p.nb; n_b = p.wo; }
+  KWalk kw;
+  kw.init(kb_begin + kbl, n_inner, n_b);
+
+  // Locate the quantized block of this thread's slot at the walk's current
+  // k-block; false in the zero padding (or outside the GEMM).
+  auto locate = [&](int64_t& blk) -> bool {
+    if (!in_range || kw.kb >= kb_end) return false;
     if constexpr (OP == OP_FWD) {
-      const int tap = kb / cbin, cib = kb - tap * cbin;
-      if (slot.is_a) {
-        blk = (static_cast<int64_t>(tap) * cbout + slot.gblk) * cbin + cib;
+      const int kh = kw.a, kwi = kw.b, cib = kw.inner;
+      if (is_a) {
+        blk = (static_cast<int64_t>(kh * p.k_w + kwi) * cbout + gblk) * cbin + cib;
         return true;
       }
-      const int kh = tap / p.k_w, kw = tap - kh * p.k_w;
-      const int hh = col_ho * p.sh + kh - p.ph, ww = col_wo * p.sw + kw - p.pw;
+      const int hh = col_y * p.sh + kh - p.ph, ww = col_x * p.sw + kwi - p.pw;
       if (hh < 0 || hh >= p.h || ww < 0 || ww >= p.w) return false;
       blk = ((static_cast<int64_t>(hh) * p.w + ww) * cbin + cib) * p.nb + col_nb;
       return true;
     } else if constexpr (OP == OP_DGRAD) {
-      const int ti = kb / cbout, cob = kb - ti * cbout;
-      const int it = ti / nkw;
-      const int kh = kh0 + p.sh * it, kw = kw0 + p.sw * (ti - it * nkw);
-      if (slot.is_a) {
-        blk = ((static_cast<int64_t>(kh) * p.k_w + kw) * cbout + cob) * cbin + slot.gblk;
+      const int kh = kh0 + p.sh * kw.a, kwi = kw0 + p.sw * kw.b, cob = kw.inner;
+      if (is_a) {
+        blk = (static_cast<int64_t>(kh * p.k_w + kwi) * cbout + cob) * cbin + gblk;
         return true;
       }
-      const int th = col_ho + p.ph - kh, tw = col_wo + p.pw - kw;  // divisible by the strides
+      const int th = col_y + p.ph - kh, tw = col_x + p.pw - kwi;  // divisible by the strides
       if (th < 0 || tw < 0) return false;
       const int ho = th / p.sh, wo = tw / p.sw;
       if (ho >= p.ho || wo >= p.wo) return false;
       blk = ((static_cast<int64_t>(ho) * p.wo + wo) * cbout + cob) * p.nb + col_nb;
       return true;
     } else {
-      const int pos = kb / p.nb, nbk = kb - pos * p.nb;
-      if (slot.is_a) {
-        blk = (static_cast<int64_t>(pos) * cbout + slot.gblk) * p.nb + nbk;
+      const int ho = kw.a, wo = kw.b, nbk = kw.inner;
+      if (is_a) {
+        blk = ((static_cast<int64_t>(ho) * p.wo + wo) * cbout + gblk) * p.nb + nbk;
         return true;
       }
-      const int ho = pos / p.wo, wo = pos - ho * p.wo;
-      const int hh = ho * p.sh + col_tap_h - p.ph, ww = wo * p.sw + col_tap_w - p.pw;
+      const int hh = ho * p.sh + col_kh - p.ph, ww = wo * p.sw + col_kw - p.pw;
       if (hh < 0 || hh >= p.h || ww < 0 || ww >= p.w) return false;
       blk = ((static_cast<int64_t>(hh) * p.w + ww) * cbin + col_cib) * p.nb + nbk;
       return true;
@@ -265,19 +395,16 @@ __global__ __launch_bounds__(kThreads) void k_conv(const ConvParams p) {
   constexpr bool A_ROWS = (OP != OP_DGRAD);
   constexpr bool B_ROWS = (OP == OP_WGRAD);
 
-  RawBlock<FMT> raw;
-  auto fetch = [&](int step) {
-    const int kb = kb_begin + step * 4 + slot.kbl;
+  // Two register sets of raw codes: the global loads of a block are issued
+  // two K steps before its decode, so their latency hides behind two rounds
+  // of MFMAs.
+  RawBlock<FMT> raw0, raw1;
+  auto fetch = [&](RawBlock<FMT>& raw) {
     int64_t blk = 0;
-    const bool ok = locate(kb, blk);
-    if (slot.is_a) raw.load(p.a_codes, p.a_scales, blk, ok);
+    const bool ok = locate(blk);
+    if (is_a) raw.load(p.a_codes, p.a_scales, blk, ok);
     else raw.load(p.b_codes, p.b_scales, blk, ok);
-  };
-  auto stage = [&](int buf) {
-    if (!active) return;
-    uint16_t* line0 = &lds[buf][slot.line * LDS_STRIDE + slot.kbl * 8];
-    if (slot.is_a) raw.template store<A_ROWS>(line0);
-    else raw.template store<B_ROWS>(line0);
+    kw.advance4(n_inner, n_b);
   };
 
   f32x16 acc[RM][RN];
@@ -288,34 +415,101 @@ __global__ __launch_bounds__(kThreads) void k_conv(const ConvParams p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
+  // per-lane LDS offsets of the MFMA fragments (row / column lane%32 of each
+  // 32-wide sub-tile; the two K halves of a 16-wide step are 8 apart)
+  int a_off[RM], b_off[RN];
+#pragma unroll
+  for (int i = 0; i < RM; ++i) a_off[i] = lds_line(wm * WTM + i * 32 + (lane & 31)) + (lane >> 5) * 8;
+#pragma unroll
+  for (int j = 0; j < RN; ++j) b_off[j] = lds_line(MT + wn * WTN + j * 32 + (lane & 31)) + (lane >> 5) * 8;
+
+  // One K step: the MFMAs on stage `buf`, with the staging units of the next
+  // block (`nxt`, into stage buf^1) spread between them in program order, so
+  // that their VALU and LDS-write work issues while the matrix pipe is busy.
+  // An MFMA must never sit inside a branch that diverges within a wave (the
+  // wave would execute both sides).  When the A/B staging split falls on wave
+  // boundaries (ABLK a multiple of 64) the branch on is_a is wave-uniform and
+  // each side carries the MFMA sequence with its own staging units;
+  // otherwise one MFMA sequence carries both kinds of units, predicated.
+  constexpr int NMF = 2 * RM * RN;
+  using StA = Stager<FMT, A_ROWS>;
+  using StB = Stager<FMT, B_ROWS>;
+  typedef __attribute__((__vector_size__(8 * sizeof(uint16_t)))) uint16_t u16x8;
+  auto mma_seq = [&](int buf, auto&& after) {
+    const uint16_t* base = lds[buf];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      u16x8 fa[RM], fb[RN];
+#pragma unroll
+      for (int i = 0; i < RM; ++i) fa[i] = *reinterpret_cast<const u16x8*>(base + a_off[i] + kk * 16);
+#pragma unroll
+      for (int j = 0; j < RN; ++j) fb[j] = *reinterpret_cast<const u16x8*>(base + b_off[j] + kk * 16);
+#pragma unroll
+      for (int i = 0; i < RM; ++i)
+#pragma unroll
+        for (int j = 0; j < RN; ++j) {
+          acc[i][j] = mfma32<F16>(reinterpret_cast<const uint16_t*>(&fa[i]),
+                                  reinterpret_cast<const uint16_t*>(&fb[j]), acc[i][j]);
+          after((kk * RM + i) * RN + j);
+        }
+    }
+  };
+  // staging units due after MFMA m: unit u of NU follows MFMA
+  // ceil((u+1) * NMF / NU) - 1 (several per MFMA when NU > NMF)
+  auto units_after = [&](auto& st, const RawBlock<FMT>& nxt, int m, bool on) {
+    using St = std::remove_reference_t<decltype(st)>;
+    [&]<int... U>(std::integer_sequence<int, U...>) {
+      ((((U + 1) * NMF + St::UNITS - 1) / St::UNITS - 1 == m && on ? (st.template unit<U>(nxt), 0) : 0), ...);
+    }(std::make_integer_sequence<int, St::UNITS>());
+  };
+  auto run_step = [&](int buf, const RawBlock<FMT>& nxt, bool have_next) {
+    uint16_t* lo = &lds[buf ^ 1][lo_off];
+    uint16_t* hi = &lds[buf ^ 1][hi_off];
+    if constexpr (ABLK % 64 == 0) {
+      if (is_a) {
+        StA sa(nxt, lo, hi);
+        mma_seq(buf, [&](int m) { units_after(sa, nxt, m, have_next); });
+      } else {
+        StB sb(nxt, lo, hi);
+        mma_seq(buf, [&](int m) { units_after(sb, nxt, m, have_next); });
+      }
+    } else {
+      StA sa(nxt, lo, hi);
+      StB sb(nxt, lo, hi);
+      const bool do_a = have_next && is_a, do_b = have_next && !is_a;
+      mma_seq(buf, [&](int m) {
+        units_after(sa, nxt, m, do_a);
+        units_after(sb, nxt, m, do_b);
+      });
+    }
+    __syncthreads();
+  };
+
   const int nsteps = (kb_end - kb_begin + 3) / 4;
   if (nsteps > 0) {
-    fetch(0);
-    stage(0);
-    __syncthreads();
-    for (int s = 0; s < nsteps; ++s) {
-      const int buf = s & 1;
-      if (s + 1 < nsteps) fetch(s + 1);
-      const uint16_t* As = lds[buf];
-      const uint16_t* Bs = lds[buf] + MT * LDS_STRIDE;
-#pragma unroll
-      for (int kk = 0; kk < KT / 16; ++kk) {
-        const int koff = kk * 16 + (lane >> 5) * 8;
-        bf16x8 af[RM], bfr[RN];
-#pragma unroll
-        for (int i = 0; i < RM; ++i)
-          af[i] = *reinterpret_cast<const bf16x8*>(As + (wm * WTM + i * 32 + (lane & 31)) * LDS_STRIDE + koff);
-#pragma unroll
-        for (int j = 0; j < RN; ++j)
-          bfr[j] = *reinterpret_cast<const bf16x8*>(Bs + (wn * WTN + j * 32 + (lane & 31)) * LDS_STRIDE + koff);
-#pragma unroll
-        for (int i = 0; i < RM; ++i)
-#pragma unroll
-          for (int j = 0; j < RN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    fetch(raw0);
+    if (nsteps > 1) fetch(raw1);
+    {
+      // first block: stage it straight away
+      if (is_a) {
+        Stager<FMT, A_ROWS> st(raw0, &lds[0][lo_off], &lds[0][hi_off]);
+        [&]<int... U>(std::integer_sequence<int, U...>) { (st.template unit<U>(raw0), ...); }(
+            std::make_integer_sequence<int, Stager<FMT, A_ROWS>::UNITS>());
+      } else {
+        Stager<FMT, B_ROWS> st(raw0, &lds[0][lo_off], &lds[0][hi_off]);
+        [&]<int... U>(std::integer_sequence<int, U...>) { (st.template unit<U>(raw0), ...); }(
+            std::make_integer_sequence<int, Stager<FMT, B_ROWS>::UNITS>());
       }
-      if (s + 1 < nsteps) stage(buf ^ 1);
-      __syncthreads();
+    }
+    __syncthreads();
+    for (int s = 0; s < nsteps; s += 2) {
+      // step s reads stage 0; raw1 holds step s+1, raw0 is free
+      if (s + 2 < nsteps) fetch(raw0);
+      run_step(0, raw1, s + 1 < nsteps);
+      if (s + 1 >= nsteps) break;
+      // step s+1 reads stage 1; raw0 holds step s+2, raw1 is free
+      if (s + 3 < nsteps) fetch(raw1);
+      run_step(1, raw0, s + 2 < nsteps);
     }
   }
 
@@ -342,7 +536,7 @@ __global__ __launch_bounds__(kThreads) void k_conv(const ConvParams p) {
       const int hh = phh + p.sh * hq, ww = phw + p.sw * (pos - hq * wp);
       colbase = (static_cast<int64_t>(hh) * p.w + ww) * p.c_in * p.n + nbk * 8 + c;
     } else {
-      colbase = static_cast<int64_t>(blockIdx.z) * p.M * p.ncol + col;
+      colbase = static_cast<int64_t>(bz) * p.M * p.ncol + col;
     }
 #pragma unroll
     for (int i = 0; i < RM; ++i)
@@ -354,22 +548,44 @@ __global__ __launch_bounds__(kThreads) void k_conv(const ConvParams p) {
   }
 }
 
-// dW[co][ci][kh][kw] = T_dy * T_x * sum over splits (fixed order) of the
-// partial [split][co][(kh, kw, ci)].
+// dW[co][ci][kh][kw] = T_dy * T_x * (sum over splits of the partials
+// [split][co][(kh, kw, ci)]).  One workgroup owns 64 outputs; its 4 waves sum
+// interleaved quarters of the splits with 4 independent accumulators each,
+// and the 16 partial sums are combined in a fixed order: the result does not
+// depend on timing.
+constexpr int kRedOut = 64;
 __global__ __launch_bounds__(256) void k_wgrad_reduce(const float* __restrict__ ws, int splits, int M,
                                                       int ncol, int c_in, int k_h, int k_w,
                                                       const float* __restrict__ ta,
                                                       const float* __restrict__ tb, float* __restrict__ dw) {
   const int64_t total = static_cast<int64_t>(M) * ncol;
-  const float scale = (*ta) * (*tb);
-  for (int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; idx < total;
-       idx += static_cast<int64_t>(gridDim.x) * 256) {
+  const int o = threadIdx.x & (kRedOut - 1), q = threadIdx.x >> 6;  // q: wave 0..3
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * kRedOut + o;
+  float s[4] = {0.f, 0.f, 0.f, 0.f};
+  if (idx < total) {
+    int z = q;
+    for (; z + 12 < splits; z += 16) {
+      s[0] += ws[static_cast<int64_t>(z) * total + idx];
+      s[1] += ws[static_cast<int64_t>(z + 4) * total + idx];
+      s[2] += ws[static_cast<int64_t>(z + 8) * total + idx];
+      s[3] += ws[static_cast<int64_t>(z + 12) * total + idx];
+    }
+    for (int u = 0; z < splits; z += 4, ++u) s[u] += ws[static_cast<int64_t>(z) * total + idx];
+  }
+  __shared__ float part[4][4][kRedOut];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) part[q][u][o] = s[u];
+  __syncthreads();
+  if (q == 0 && idx < total) {
+    float r = 0.0f;
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) r += part[qq][u][o];
     const int co = static_cast<int>(idx / ncol), j = static_cast<int>(idx - static_cast<int64_t>(co) * ncol);
-    float s = 0.0f;
-    for (int z = 0; z < splits; ++z) s += ws[static_cast<int64_t>(z) * total + idx];
     const int tap = j / c_in, ci = j - tap * c_in;
     const int kh = tap / k_w, kw = tap - kh * k_w;
-    dw[((static_cast<int64_t>(co) * c_in + ci) * k_h + kh) * k_w + kw] = s * scale;
+    dw[((static_cast<int64_t>(co) * c_in + ci) * k_h + kh) * k_w + kw] = r * ((*ta) * (*tb));
   }
 }
 
@@ -379,24 +595,50 @@ struct Tile {
   int mt, nt, wm;
 };
 
-Tile pick_tile(int M) {
-  if (M >= 256) return {256, 256, 2};
-  if (M >= 128) return {128, 256, 2};
-  if (M >= 64) return {64, 256, 2};
-  return {32, 256, 1};
+// Candidate tiles (MT, NT, waves along M); a wave tile is a grid of 32x32
+// MFMAs, so MT = 32 uses the four waves along N.
+constexpr Tile kTiles[] = {{256, 256, 2}, {128, 256, 2}, {128, 128, 2}, {64, 256, 2},
+                           {64, 128, 2},  {64, 64, 2},   {32, 256, 1}, {32, 128, 1}};
+
+// Largest tile that still gives at least two workgroups per CU (512); if none
+// does, the one with the most useful work per workgroup among those with the
+// most workgroups.
+Tile pick_tile(int64_t M, int64_t ncols, int64_t zdim) {
+  const int mt_need = M >= 256 ? 256 : M > 64 ? 128 : M > 32 ? 64 : 32;
+  Tile best = {0, 0, 0};
+  int64_t best_wgs = -1;
+  for (const Tile& t : kTiles) {
+    if (t.mt > mt_need) continue;
+    if (t.mt < mt_need && !(t.mt * 2 == mt_need && M < mt_need)) {
+      // never split rows below what the channel count needs, except to halve
+      // a tile that would be mostly empty
+      if (t.mt != mt_need) continue;
+    }
+    const int64_t wgs = ((M + t.mt - 1) / t.mt) * ((ncols + t.nt - 1) / t.nt) * zdim;
+    if (wgs >= 512) return t;
+    if (wgs > best_wgs) {
+      best = t;
+      best_wgs = wgs;
+    }
+  }
+  return best.mt ? best : Tile{32, 128, 1};
 }
 
-template <int OP, int FMT, int MT, int NT, int WM>
+template <int OP, int FMT, int MT, int NT, int WM, int WAVES = 4>
 void launch_tile(const ConvParams& p, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((k_conv<OP, FMT, MT, NT, WM>), grid, dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL((k_conv<OP, FMT, MT, NT, WM, WAVES>), grid, dim3(WAVES * 64), 0, s, p);
 }
 
 template <int OP, int FMT>
 void launch_fmt(const ConvParams& p, const Tile& t, dim3 grid, hipStream_t s) {
   if (t.mt == 256) launch_tile<OP, FMT, 256, 256, 2>(p, grid, s);
-  else if (t.mt == 128) launch_tile<OP, FMT, 128, 256, 2>(p, grid, s);
-  else if (t.mt == 64) launch_tile<OP, FMT, 64, 256, 2>(p, grid, s);
-  else launch_tile<OP, FMT, 32, 256, 1>(p, grid, s);
+  else if (t.mt == 128 && t.nt == 256) launch_tile<OP, FMT, 128, 256, 2>(p, grid, s);
+  else if (t.mt == 128) launch_tile<OP, FMT, 128, 128, 2>(p, grid, s);
+  else if (t.mt == 64 && t.nt == 256) launch_tile<OP, FMT, 64, 256, 2>(p, grid, s);
+  else if (t.mt == 64 && t.nt == 128) launch_tile<OP, FMT, 64, 128, 2>(p, grid, s);
+  else if (t.mt == 64) launch_tile<OP, FMT, 64, 64, 2>(p, grid, s);
+  else if (t.nt == 256) launch_tile<OP, FMT, 32, 256, 1>(p, grid, s);
+  else launch_tile<OP, FMT, 32, 128, 1>(p, grid, s);
 }
 
 template <int OP>
@@ -416,19 +658,25 @@ ConvParams base_params(const Geom& g) {
   return p;
 }
 
-// Split count of the weight gradient: enough workgroups to cover the 256 CUs
-// twice, at least 8 K steps per split.
-int wgrad_splits(const Geom& g, const Tile& t) {
+// Weight gradient: tile and split count.  Enough workgroups to cover the 256
+// CUs twice, at least 8 K steps per split.
+struct WgradPlan {
+  Tile t;
+  int splits;
+};
+
+WgradPlan wgrad_plan(const Geom& g) {
   const int64_t kb_total = static_cast<int64_t>(g.ho) * g.wo * (g.n / 8);
   const int64_t ksteps = (kb_total + 3) / 4;
   const int64_t ncol = static_cast<int64_t>(g.k_h) * g.k_w * g.c_in;
+  const Tile t = pick_tile(g.c_out, ncol, 1);
   const int64_t tiles = ((g.c_out + t.mt - 1) / t.mt) * ((ncol + t.nt - 1) / t.nt);
   int64_t splits = (512 + tiles - 1) / tiles;
   const int64_t max_by_k = ksteps / 8;
   if (splits > max_by_k) splits = max_by_k;
   if (splits < 1) splits = 1;
   if (splits > 65535) splits = 65535;
-  return static_cast<int>(splits);
+  return {t, static_cast<int>(splits)};
 }
 
 }  // namespace
@@ -443,7 +691,7 @@ hipError_t launch_conv_fwd(const Geom& g, const mx_qtensor* wq, const mx_qtensor
   p.b_codes = static_cast<const uint8_t*>(xq->codes); p.b_scales = xq->scales; p.b_t = xq->tensor_scale;
   p.out = y;
   if (p.ncb == 0) return hipSuccess;
-  const Tile t = pick_tile(p.M);
+  const Tile t = pick_tile(p.M, static_cast<int64_t>(p.ncb) * 8, 1);
   dim3 grid((p.ncb * 8 + t.nt - 1) / t.nt, (p.M + t.mt - 1) / t.mt, 1);
   launch_op<OP_FWD>(p, g.fmt, t, grid, s);
   return hipGetLastError();
@@ -460,41 +708,36 @@ hipError_t launch_conv_dgrad(const Geom& g, const mx_qtensor* wq, const mx_qtens
   p.b_codes = static_cast<const uint8_t*>(dyq->codes); p.b_scales = dyq->scales; p.b_t = dyq->tensor_scale;
   p.out = dx;
   if (p.ncb == 0) return hipSuccess;
-  const Tile t = pick_tile(p.M);
+  const Tile t = pick_tile(p.M, static_cast<int64_t>(p.ncb) * 8, g.sh * g.sw);
   dim3 grid((p.ncb * 8 + t.nt - 1) / t.nt, (p.M + t.mt - 1) / t.mt, g.sh * g.sw);
   launch_op<OP_DGRAD>(p, g.fmt, t, grid, s);
   return hipGetLastError();
 }
 
 size_t wgrad_workspace_bytes(const Geom& g) {
-  const Tile t = pick_tile(g.c_out);
-  const int splits = wgrad_splits(g, t);
-  return static_cast<size_t>(splits) * g.c_out * g.k_h * g.k_w * g.c_in * sizeof(float);
+  const WgradPlan pl = wgrad_plan(g);
+  return static_cast<size_t>(pl.splits) * g.c_out * g.k_h * g.k_w * g.c_in * sizeof(float);
 }
 
 hipError_t launch_conv_wgrad(const Geom& g, const mx_qtensor* dyq, const mx_qtensor* xq, float* dw,
                              void* workspace, hipStream_t s) {
   ConvParams p = base_params(g);
-  const Tile t = pick_tile(g.c_out);
-  const int splits = wgrad_splits(g, t);
+  const WgradPlan pl = wgrad_plan(g);
   p.M = g.c_out;
   p.ncol = g.k_h * g.k_w * g.c_in;
   p.ncb = p.ncol / 8;
   p.kb_total = g.ho * g.wo * (g.n / 8);
   const int ksteps = (p.kb_total + 3) / 4;
-  p.ks_split = (ksteps + splits - 1) / splits;
+  p.ks_split = (ksteps + pl.splits - 1) / pl.splits;
   p.a_codes = static_cast<const uint8_t*>(dyq->codes); p.a_scales = dyq->scales; p.a_t = dyq->tensor_scale;
   p.b_codes = static_cast<const uint8_t*>(xq->codes); p.b_scales = xq->scales; p.b_t = xq->tensor_scale;
   p.out = static_cast<float*>(workspace);
-  dim3 grid((p.ncol + t.nt - 1) / t.nt, (p.M + t.mt - 1) / t.mt, splits);
-  launch_op<OP_WGRAD>(p, g.fmt, t, grid, s);
+  dim3 grid((p.ncol + pl.t.nt - 1) / pl.t.nt, (p.M + pl.t.mt - 1) / pl.t.mt, pl.splits);
+  launch_op<OP_WGRAD>(p, g.fmt, pl.t, grid, s);
   const int64_t total = static_cast<int64_t>(p.M) * p.ncol;
-  int64_t rg = (total + 255) / 256;
-  if (rg > 65535) rg = 65535;
-  if (rg < 1) rg = 1;
-  hipLaunchKernelGGL(k_wgrad_reduce, dim3(static_cast<unsigned>(rg)), dim3(256), 0, s,
-                     static_cast<const float*>(workspace), splits, p.M, p.ncol, g.c_in, g.k_h, g.k_w,
-                     dyq->tensor_scale, xq->tensor_scale, dw);
+  const unsigned rg = static_cast<unsigned>((total + kRedOut - 1) / kRedOut);
+  hipLaunchKernelGGL(k_wgrad_reduce, dim3(rg), dim3(256), 0, s, static_cast<const float*>(workspace),
+                     pl.splits, p.M, p.ncol, g.c_in, g.k_h, g.k_w, dyq->tensor_scale, xq->tensor_scale, dw);
   return hipGetLastError();
 }
 

@@ -59,25 +59,39 @@ __global__ __launch_bounds__(kThreads) void k_amax(const uint4* __restrict__ src
   }
 }
 
-// Linear fp32 source index of element (r, c) of block b for the role.
+// fp32 source offset of element (r, c) of a block: base + r*row + c*col.
+// The block coordinates are decoded once per lane (32-bit arithmetic: block
+// counts are below 2^31).
+struct BlockAddr {
+  int64_t base, row, col;
+};
+
 template <int ROLE>
-__device__ __forceinline__ int64_t src_index(const QDims& d, int64_t b, int r, int c) {
+__device__ __forceinline__ BlockAddr block_addr(const QDims& d, int64_t blk) {
+  const uint32_t b = static_cast<uint32_t>(blk);
+  BlockAddr a;
   if constexpr (ROLE == MX_ROLE_WEIGHT) {
-    const int cib_n = d.d1 >> 3, cob_n = d.d0 >> 3;
-    const int64_t cib = b % cib_n;
-    int64_t t = b / cib_n;
-    const int64_t cob = t % cob_n;
-    t /= cob_n;
-    const int64_t kw = t % d.d3, kh = t / d.d3;
-    const int64_t co = cob * 8 + r, ci = cib * 8 + c;
-    return ((co * d.d1 + ci) * d.d2 + kh) * d.d3 + kw;
+    const uint32_t cib_n = static_cast<uint32_t>(d.d1) >> 3, cob_n = static_cast<uint32_t>(d.d0) >> 3;
+    const uint32_t khkw = static_cast<uint32_t>(d.d2 * d.d3);
+    uint32_t t = b / cib_n;
+    const uint32_t cib = b - t * cib_n;
+    const uint32_t t2 = t / cob_n;
+    const uint32_t cob = t - t2 * cob_n;
+    const uint32_t kh = t2 / static_cast<uint32_t>(d.d3), kw = t2 - kh * static_cast<uint32_t>(d.d3);
+    a.base = (static_cast<int64_t>(cob) * 8 * d.d1 + cib * 8) * khkw + kh * d.d3 + kw;
+    a.row = static_cast<int64_t>(d.d1) * khkw;
+    a.col = khkw;
   } else {
-    const int nb_n = d.d3 >> 3, cb_n = d.d2 >> 3;
-    const int64_t nb = b % nb_n;
-    const int64_t t = b / nb_n;
-    const int64_t cb = t % cb_n, p = t / cb_n;
-    return (p * d.d2 + cb * 8 + r) * static_cast<int64_t>(d.d3) + nb * 8 + c;
+    const uint32_t nb_n = static_cast<uint32_t>(d.d3) >> 3, cb_n = static_cast<uint32_t>(d.d2) >> 3;
+    const uint32_t t = b / nb_n;
+    const uint32_t nb = b - t * nb_n;
+    const uint32_t p = t / cb_n;
+    const uint32_t cb = t - p * cb_n;
+    a.base = (static_cast<int64_t>(p) * d.d2 + cb * 8) * d.d3 + nb * 8;
+    a.row = d.d3;
+    a.col = 1;
   }
+  return a;
 }
 
 // Write this lane's half of a block whose 8 code rows are split between the
@@ -175,15 +189,16 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const float* __restrict__
   if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = T;
 
   float x[8][4];
-  const int64_t b = valid ? blk : 0;
+  const BlockAddr ad = block_addr<ROLE>(d, valid ? blk : 0);
+  const int64_t base = ad.base + half * 4 * ad.col;
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
     if constexpr (ROLE == MX_ROLE_WEIGHT) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) x[r][j] = valid ? src[src_index<ROLE>(d, b, r, half * 4 + j)] : 0.0f;
+      for (int j = 0; j < 4; ++j) x[r][j] = valid ? src[base + r * ad.row + j * ad.col] : 0.0f;
     } else {
       float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (valid) v = *reinterpret_cast<const float4*>(src + src_index<ROLE>(d, b, r, half * 4));
+      if (valid) v = *reinterpret_cast<const float4*>(src + base + r * ad.row);
       x[r][0] = v.x;
       x[r][1] = v.y;
       x[r][2] = v.z;
@@ -207,16 +222,12 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const float* __restrict__
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
     uint32_t bits = 0;
-    int64_t row_idx = 0;
-    if constexpr (SR && ROLE != MX_ROLE_WEIGHT) row_idx = src_index<ROLE>(d, b, r, half * 4);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float v = (dd == 0.0f) ? 0.0f : fabsf(x[r][j]) / dd;
       uint32_t mag;
       if constexpr (SR) {
-        int64_t idx;
-        if constexpr (ROLE == MX_ROLE_WEIGHT) idx = src_index<ROLE>(d, b, r, half * 4 + j);
-        else idx = row_idx + j;
+        const int64_t idx = base + r * ad.row + j * ad.col;
         mag = sr_code<F>(v, sr_uniform(seed, static_cast<uint64_t>(idx)));
       } else {
         mag = rne_code<F>(v);
@@ -264,6 +275,8 @@ __global__ __launch_bounds__(kThreads) void k_dequantize(const uint8_t* __restri
   const uint32_t sb = scales[blk];
   const float B = (sb == 0x7Fu) ? __uint_as_float(0x7FC00000u) : code_value<ScaleFmt>(sb);
   const float T = *tensor_scale;
+  const BlockAddr ad = block_addr<ROLE>(d, blk);
+  const int64_t base = ad.base + half * 4 * ad.col;
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
     float o[4];
@@ -278,10 +291,9 @@ __global__ __launch_bounds__(kThreads) void k_dequantize(const uint8_t* __restri
     }
     if constexpr (ROLE == MX_ROLE_WEIGHT) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dst[src_index<ROLE>(d, blk, r, half * 4 + j)] = o[j];
+      for (int j = 0; j < 4; ++j) dst[base + r * ad.row + j * ad.col] = o[j];
     } else {
-      *reinterpret_cast<float4*>(dst + src_index<ROLE>(d, blk, r, half * 4)) =
-          make_float4(o[0], o[1], o[2], o[3]);
+      *reinterpret_cast<float4*>(dst + base + r * ad.row) = make_float4(o[0], o[1], o[2], o[3]);
     }
   }
 }
