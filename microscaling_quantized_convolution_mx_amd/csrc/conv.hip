@@ -435,24 +435,27 @@ __global__ __launch_bounds__(WAVES * 64) void k_conv(const ConvParams p) {
   using StA = Stager<FMT, A_ROWS>;
   using StB = Stager<FMT, B_ROWS>;
   typedef __attribute__((__vector_size__(8 * sizeof(uint16_t)))) uint16_t u16x8;
+  // all fragments of the step are read first (one LDS wait), then the MFMAs
   auto mma_seq = [&](int buf, auto&& after) {
     const uint16_t* base = lds[buf];
+    u16x8 fa[2][RM], fb[2][RN];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      u16x8 fa[RM], fb[RN];
 #pragma unroll
-      for (int i = 0; i < RM; ++i) fa[i] = *reinterpret_cast<const u16x8*>(base + a_off[i] + kk * 16);
+      for (int i = 0; i < RM; ++i) fa[kk][i] = *reinterpret_cast<const u16x8*>(base + a_off[i] + kk * 16);
 #pragma unroll
-      for (int j = 0; j < RN; ++j) fb[j] = *reinterpret_cast<const u16x8*>(base + b_off[j] + kk * 16);
+      for (int j = 0; j < RN; ++j) fb[kk][j] = *reinterpret_cast<const u16x8*>(base + b_off[j] + kk * 16);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int i = 0; i < RM; ++i)
 #pragma unroll
         for (int j = 0; j < RN; ++j) {
-          acc[i][j] = mfma32<F16>(reinterpret_cast<const uint16_t*>(&fa[i]),
-                                  reinterpret_cast<const uint16_t*>(&fb[j]), acc[i][j]);
+          acc[i][j] = mfma32<F16>(reinterpret_cast<const uint16_t*>(&fa[kk][i]),
+                                  reinterpret_cast<const uint16_t*>(&fb[kk][j]), acc[i][j]);
           after((kk * RM + i) * RN + j);
         }
-    }
   };
   // staging units due after MFMA m: unit u of NU follows MFMA
   // ceil((u+1) * NMF / NU) - 1 (several per MFMA when NU > NMF)
