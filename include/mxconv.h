@@ -35,7 +35,10 @@
  *   codes: E2M1 2 per byte (element 2j in the low nibble), E2M3 a
  *   little-endian 6-bit stream (48 bytes per block), E4M3 1 byte each; the
  *   sign is the top bit of each code.  scales: one E4M3 byte per block, in
- *   block order.  tensor_scale: one fp32.  amax: one fp32, max |x|.
+ *   block order; the buffer continues, from the next multiple of 16 bytes,
+ *   with 2 KiB that mx_quantize_cbf uses as scratch for its amax reduction
+ *   (mx_scale_bytes() counts both).  tensor_scale: one fp32.  amax: one
+ *   fp32, max |x|.
  * - C_in, C_out and N must be multiples of 8 (zero-pad otherwise: padding
  *   changes neither the amax nor any result) and block must be 8.  N may be 0.
  */
@@ -88,13 +91,15 @@ typedef struct {
 /* A quantized tensor: device pointers owned by the caller. */
 typedef struct {
   void* codes;         /* packed element codes, mx_code_bytes() bytes */
-  uint8_t* scales;     /* E4M3 block scales, mx_scale_bytes() bytes */
+  uint8_t* scales;     /* E4M3 block scales + amax scratch, mx_scale_bytes() bytes */
   float* tensor_scale; /* one fp32: T */
   float* amax;         /* one fp32: max |x| of the source */
 } mx_qtensor;
 
-/* Bytes of packed codes / block scales of the tensor of `role` (0 on an
- * invalid descriptor or role). */
+/* Bytes of the codes / scales buffers of the tensor of `role` (0 on an
+ * invalid descriptor or role).  The scales buffer holds ceil-to-16 of the
+ * block count bytes of scales plus 2048 bytes of quantizer scratch (0 bytes
+ * in all for an empty tensor). */
 size_t mx_code_bytes(const mx_conv_desc* desc, mx_role role);
 size_t mx_scale_bytes(const mx_conv_desc* desc, mx_role role);
 
@@ -111,7 +116,10 @@ size_t mx_wgrad_workspace_bytes(const mx_conv_desc* desc);
  * SplitMix64(seed ^ 0x9E3779B97F4A7C15 * (i + 1)), i the element's linear
  * index in `src`.  Every fp32 step is one correctly rounded IEEE operation.
  *   src        fp32 tensor of `role` in the layout above
- *   dst        quantized tensor: codes, scales, tensor_scale and amax written
+ *   dst        quantized tensor: codes, scales, tensor_scale and amax written;
+ *              codes and scales 16-byte aligned.  The amax pass keeps one
+ *              partial maximum per workgroup in the scratch tail of the
+ *              scales buffer, so no atomics and no zero-fill are needed
  *   amax_given 0: *dst->amax is computed here (max |x|, two passes over src);
  *              1: *dst->amax already holds the amax to use (e.g. a
  *              statistic carried over from a previous step); not written

@@ -154,6 +154,9 @@ class QTensor:
         self.tensor_scale = torch.zeros(1, dtype=torch.float32, device=device)
         self.amax = torch.zeros(1, dtype=torch.float32, device=device)
         self.code_bytes, self.scale_bytes = nc, ns
+        # stored block scales: one byte per 8x8 block (the rest of the
+        # scales buffer is the quantizer's scratch)
+        self.nblocks = nc * 8 // (64 * {MX_E2M1: 4, MX_E2M3: 6, MX_E4M3: 8}[d.elem_fmt])
 
     def c(self) -> mx_qtensor:
         return mx_qtensor(self.codes.data_ptr(), self.scales.data_ptr(),

@@ -98,7 +98,7 @@ size_t mx_code_bytes(const mx_conv_desc* desc, mx_role role) {
 
 size_t mx_scale_bytes(const mx_conv_desc* desc, mx_role role) {
   if (check_desc(desc) != MX_OK || check_role(role) != MX_OK) return 0;
-  return static_cast<size_t>(mx::role_nblocks(mx::make_geom(desc), role));
+  return static_cast<size_t>(mx::scale_buffer_bytes(mx::role_nblocks(mx::make_geom(desc), role)));
 }
 
 size_t mx_wgrad_workspace_bytes(const mx_conv_desc* desc) {
@@ -117,7 +117,7 @@ mx_status mx_quantize_cbf(const mx_conv_desc* desc, mx_role role, const float* s
   const int64_t nb = mx::role_nblocks(g, role);
   if ((st = check_qtensor(dst, nb)) != MX_OK) return st;
   if (nb > 0 && !src) return MX_ERR_NULL;
-  if (!aligned(src, 16)) return MX_ERR_ALIGN;
+  if (!aligned(src, 16) || !aligned(dst->scales, 16)) return MX_ERR_ALIGN;
   return launched(mx::launch_quantize(g, role, src, dst, rounding, seed, amax_given, stream));
 }
 

@@ -21,6 +21,20 @@ int64_t role_numel(const Geom& g, mx_role role);
 int64_t role_nblocks(const Geom& g, mx_role role);
 int code_bits(int fmt);
 
+// The scales buffer of a quantized tensor holds the block scales (one byte
+// per block), padded to 16 bytes, then the quantizer's amax partials: one
+// 32-bit max per workgroup of the amax pass, at most kAmaxMaxPartials.
+constexpr int kAmaxMaxPartials = 512;
+inline int64_t scale_tail_offset(int64_t nblocks) { return (nblocks + 15) & ~static_cast<int64_t>(15); }
+inline int64_t amax_partials(int64_t nblocks) {
+  if (nblocks <= 0) return 0;
+  const int64_t p = (nblocks * 16 + 4095) / 4096;  // >= 4096 uint4 loads per workgroup
+  return p < kAmaxMaxPartials ? p : kAmaxMaxPartials;
+}
+inline int64_t scale_buffer_bytes(int64_t nblocks) {
+  return nblocks > 0 ? scale_tail_offset(nblocks) + 4 * kAmaxMaxPartials : 0;
+}
+
 hipError_t launch_quantize(const Geom& g, mx_role role, const float* src, const mx_qtensor* dst,
                            mx_round rounding, uint64_t seed, int amax_given, hipStream_t s);
 hipError_t launch_dequantize(const Geom& g, mx_role role, const mx_qtensor* q, float* dst,

@@ -6,12 +6,16 @@
 // §IV-B), with NVFP4-style two-level scaling: an fp32 per-tensor scale from
 // the tensor amax and an E4M3 per-block scale (§III-A).
 //
-// Work decomposition (HBM-bound): a pair of neighbouring lanes owns one 8x8
-// block; each lane holds 4 of the 8 columns of all 8 rows.  For activations
-// and gradients a block row is 8 consecutive batch elements (32 bytes), so a
-// wavefront (32 blocks) streams whole rows of the (C, N) plane with 16-byte
-// loads.  The block amax and the packed code rows are exchanged between the
-// two lanes with one DPP move each; the codes leave as 16-byte stores.
+// Two kernels per tensor, no atomics:
+//   k_amax_part  each workgroup writes the max |x| of its grid-stride share
+//                as one 32-bit partial into a scratch tail behind the block
+//                scales (the scales buffer is sized for it);
+//   k_quantize   every wave reduces the partials to the tensor amax and T,
+//                then quantizes 8 blocks per iteration, 8 lanes per block
+//                (lane = block row: 8 consecutive batch elements, 32 bytes,
+//                for activations and gradients).  The block amax is a DPP
+//                max across the 8 lanes; each lane packs and stores its own
+//                code row, so a wave writes whole contiguous runs of blocks.
 #include "internal.h"
 #include "mx_formats.h"
 
@@ -19,49 +23,49 @@ namespace mx {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBlocksPerWG = kThreads / 2;
+constexpr int kGroupsPerWG = kThreads / 64;  // 8-block groups per workgroup iteration
+constexpr int kQuantMaxWGs = 2048;
 
 struct QDims {
   int64_t nblocks;
   int32_t d0, d1, d2, d3;  // ACT/GRAD: H, W, C, N   WEIGHT: Co, Ci, Kh, Kw
 };
 
-__global__ void k_amax_zero(uint32_t* amax_bits) {
-  if (threadIdx.x == 0) *amax_bits = 0u;
+__device__ __forceinline__ uint32_t absbits(uint32_t v) { return v & 0x7FFFFFFFu; }
+__device__ __forceinline__ uint32_t max4(uint4 v) {
+  return max(max(absbits(v.x), absbits(v.y)), max(absbits(v.z), absbits(v.w)));
 }
 
-// max |x| as the unsigned max of the bit patterns with the sign cleared:
+// Max |x| as the unsigned max of the bit patterns with the sign cleared:
 // exact, order-independent, and Inf/NaN come out at or above 0x7F800000.
-__global__ __launch_bounds__(kThreads) void k_amax(const uint4* __restrict__ src, int64_t n4,
-                                                   uint32_t* amax_bits) {
+// Workgroup b writes its share's max to part[b]; every workgroup writes.
+__global__ __launch_bounds__(kThreads) void k_amax_part(const uint4* __restrict__ src, int64_t n4,
+                                                        uint32_t* __restrict__ part) {
   uint32_t m = 0;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
   int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  for (; i + 3 * stride < n4; i += 4 * stride) {
-    uint4 v0 = src[i], v1 = src[i + stride], v2 = src[i + 2 * stride], v3 = src[i + 3 * stride];
-    m = max(m, max(max(v0.x & 0x7FFFFFFFu, v0.y & 0x7FFFFFFFu), max(v0.z & 0x7FFFFFFFu, v0.w & 0x7FFFFFFFu)));
-    m = max(m, max(max(v1.x & 0x7FFFFFFFu, v1.y & 0x7FFFFFFFu), max(v1.z & 0x7FFFFFFFu, v1.w & 0x7FFFFFFFu)));
-    m = max(m, max(max(v2.x & 0x7FFFFFFFu, v2.y & 0x7FFFFFFFu), max(v2.z & 0x7FFFFFFFu, v2.w & 0x7FFFFFFFu)));
-    m = max(m, max(max(v3.x & 0x7FFFFFFFu, v3.y & 0x7FFFFFFFu), max(v3.z & 0x7FFFFFFFu, v3.w & 0x7FFFFFFFu)));
+  for (; i + 7 * stride < n4; i += 8 * stride) {
+    uint4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = src[i + k * stride];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) m = max(m, max4(v[k]));
   }
-  for (; i < n4; i += stride) {
-    uint4 v = src[i];
-    m = max(m, max(max(v.x & 0x7FFFFFFFu, v.y & 0x7FFFFFFFu), max(v.z & 0x7FFFFFFFu, v.w & 0x7FFFFFFFu)));
-  }
+  for (; i < n4; i += stride) m = max(m, max4(src[i]));
   for (int off = 32; off > 0; off >>= 1) m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), off)));
-  __shared__ uint32_t part[kThreads / 64];
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+  __shared__ uint32_t wmax[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
-    uint32_t r = part[0];
-    for (int k = 1; k < kThreads / 64; ++k) r = max(r, part[k]);
-    atomicMax(amax_bits, r);
+    uint32_t r = wmax[0];
+    for (int k = 1; k < kThreads / 64; ++k) r = max(r, wmax[k]);
+    part[blockIdx.x] = r;
   }
 }
 
 // fp32 source offset of element (r, c) of a block: base + r*row + c*col.
-// The block coordinates are decoded once per lane (32-bit arithmetic: block
-// counts are below 2^31).
+// The block coordinates are decoded with 32-bit arithmetic (block counts are
+// below 2^31).
 struct BlockAddr {
   int64_t base, row, col;
 };
@@ -94,73 +98,32 @@ __device__ __forceinline__ BlockAddr block_addr(const QDims& d, int64_t blk) {
   return a;
 }
 
-// Write this lane's half of a block whose 8 code rows are split between the
-// lane pair: row_bits[r] holds the 4 codes of this lane's column half.
+// DPP moves inside a group of 8 lanes: quad_perm [1,0,3,2], [2,3,0,1] and
+// row_half_mirror (lane i <-> 7-i).
+__device__ __forceinline__ float max8(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false)));
+  return v;
+}
+
+// Store one code row (8 codes, `lo` = bits 0..31, `hi` = bits 32..63) of
+// block `blk`; row r of a block starts at bit 8*BITS*r of the block.
 template <int FMT>
-__device__ __forceinline__ void store_block_codes(uint8_t* __restrict__ codes, int64_t blk, int half,
-                                                  const uint32_t (&rb)[8], bool valid) {
+__device__ __forceinline__ void store_row(uint8_t* __restrict__ codes, int64_t blk, int r, uint32_t lo,
+                                          uint32_t hi, bool valid) {
   if constexpr (FMT == FMT_E2M1) {
-    // row = 4 bytes: low 16 bits from the even lane, high 16 bits from the odd
-    const uint32_t s0 = half ? (rb[0] | (rb[1] << 16)) : (rb[4] | (rb[5] << 16));
-    const uint32_t s1 = half ? (rb[2] | (rb[3] << 16)) : (rb[6] | (rb[7] << 16));
-    const uint32_t r0 = swap_pair(s0), r1 = swap_pair(s1);
-    uint4 out;
-    if (half == 0) {
-      out.x = rb[0] | ((r0 & 0xFFFFu) << 16);
-      out.y = rb[1] | (r0 & 0xFFFF0000u);
-      out.z = rb[2] | ((r1 & 0xFFFFu) << 16);
-      out.w = rb[3] | (r1 & 0xFFFF0000u);
-    } else {
-      out.x = (r0 & 0xFFFFu) | (rb[4] << 16);
-      out.y = (r0 >> 16) | (rb[5] << 16);
-      out.z = (r1 & 0xFFFFu) | (rb[6] << 16);
-      out.w = (r1 >> 16) | (rb[7] << 16);
-    }
-    if (valid) *reinterpret_cast<uint4*>(codes + blk * 32 + half * 16) = out;
+    if (valid) *reinterpret_cast<uint32_t*>(codes + blk * 32 + r * 4) = lo;
   } else if constexpr (FMT == FMT_E4M3) {
-    // row = 8 bytes: first dword from the even lane, second from the odd
-    uint32_t rcv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) rcv[i] = swap_pair(half ? rb[i] : rb[4 + i]);
-    uint4 o0, o1;
-    if (half == 0) {
-      o0 = make_uint4(rb[0], rcv[0], rb[1], rcv[1]);
-      o1 = make_uint4(rb[2], rcv[2], rb[3], rcv[3]);
-    } else {
-      o0 = make_uint4(rcv[0], rb[4], rcv[1], rb[5]);
-      o1 = make_uint4(rcv[2], rb[6], rcv[3], rb[7]);
-    }
-    if (valid) {
-      uint4* p = reinterpret_cast<uint4*>(codes + blk * 64 + half * 32);
-      p[0] = o0;
-      p[1] = o1;
-    }
+    if (valid) *reinterpret_cast<uint2*>(codes + blk * 64 + r * 8) = make_uint2(lo, hi);
   } else {
-    // E2M3: row = 48 bits (6 bytes), low 24 bits from the even lane
-    const int base = half ? 0 : 4;
-    const uint32_t a0 = rb[base], a1 = rb[base + 1], a2 = rb[base + 2], a3 = rb[base + 3];
-    const uint32_t w0 = a0 | (a1 << 24), w1 = (a1 >> 8) | (a2 << 16), w2 = (a2 >> 16) | (a3 << 8);
-    const uint32_t v0 = swap_pair(w0), v1 = swap_pair(w1), v2 = swap_pair(w2);
-    uint32_t o[4];  // partner's four 24-bit row halves
-    o[0] = v0 & 0xFFFFFFu;
-    o[1] = (v0 >> 24) | ((v1 & 0xFFFFu) << 8);
-    o[2] = (v1 >> 16) | ((v2 & 0xFFu) << 16);
-    o[3] = v2 >> 8;
-    uint64_t row[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint64_t lo = half ? o[i] : rb[i];
-      const uint64_t hi = half ? rb[4 + i] : o[i];
-      row[i] = lo | (hi << 24);
-    }
-    const uint64_t q0 = row[0] | (row[1] << 48);
-    const uint64_t q1 = (row[1] >> 16) | (row[2] << 32);
-    const uint64_t q2 = (row[2] >> 32) | (row[3] << 16);
-    if (valid) {
-      uint2* p = reinterpret_cast<uint2*>(codes + blk * 48 + half * 24);
-      p[0] = make_uint2(static_cast<uint32_t>(q0), static_cast<uint32_t>(q0 >> 32));
-      p[1] = make_uint2(static_cast<uint32_t>(q1), static_cast<uint32_t>(q1 >> 32));
-      p[2] = make_uint2(static_cast<uint32_t>(q2), static_cast<uint32_t>(q2 >> 32));
+    // 48-bit rows: the even lane of each pair writes both rows (12 bytes)
+    const uint32_t plo = swap_pair(lo), phi = swap_pair(hi);
+    if (valid && (r & 1) == 0) {
+      uint32_t* q = reinterpret_cast<uint32_t*>(codes + blk * 48 + (r >> 1) * 12);
+      q[0] = lo;
+      q[1] = (hi & 0xFFFFu) | (plo << 16);
+      q[2] = (plo >> 16) | (phi << 16);
     }
   }
 }
@@ -170,131 +133,133 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const float* __restrict__
                                                        uint8_t* __restrict__ codes,
                                                        uint8_t* __restrict__ scales,
                                                        float* __restrict__ tensor_scale,
-                                                       const float* __restrict__ amax, QDims d,
-                                                       uint64_t seed) {
+                                                       float* __restrict__ amax, const uint32_t* __restrict__ part,
+                                                       int nparts, QDims d, uint64_t seed) {
   using F = Fmt<FMT>;
-  const int half = threadIdx.x & 1;
-  const int64_t blk = static_cast<int64_t>(blockIdx.x) * kBlocksPerWG + (threadIdx.x >> 1);
-  const bool valid = blk < d.nblocks;
-  const uint32_t ab = __float_as_uint(*amax) & 0x7FFFFFFFu;
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 7;
 
-  if (ab >= NONFINITE_BITS) {  // non-finite input: T = NaN, scales 0x7F, codes 0
-    if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = __uint_as_float(0x7FC00000u);
-    const uint32_t zero[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    store_block_codes<FMT>(codes, blk, half, zero, valid);
-    if (valid && half == 0) scales[blk] = 0x7F;
-    return;
+  // tensor amax: the partials of k_amax_part, or the caller's value
+  uint32_t ab;
+  if (nparts >= 0) {
+    uint32_t m = 0;
+    for (int i = lane; i < nparts; i += 64) m = max(m, part[i]);
+    for (int off = 32; off > 0; off >>= 1) m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), off)));
+    ab = m;
+  } else {
+    ab = __float_as_uint(*amax) & 0x7FFFFFFFu;
   }
-  const float T = __uint_as_float(ab) / (448.0f * F::MAXV);
-  if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = T;
+  const bool nonfinite = ab >= NONFINITE_BITS;
+  const float T = nonfinite ? __uint_as_float(0x7FC00000u) : __uint_as_float(ab) / (448.0f * F::MAXV);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    *tensor_scale = T;
+    if (nparts >= 0) *amax = __uint_as_float(ab);
+  }
 
-  float x[8][4];
-  const BlockAddr ad = block_addr<ROLE>(d, valid ? blk : 0);
-  const int64_t base = ad.base + half * 4 * ad.col;
-#pragma unroll
-  for (int r = 0; r < 8; ++r) {
+  const int64_t ngroups = (d.nblocks + 7) >> 3;
+  const int64_t gstride = static_cast<int64_t>(gridDim.x) * kGroupsPerWG;
+  for (int64_t grp = static_cast<int64_t>(blockIdx.x) * kGroupsPerWG + (threadIdx.x >> 6); grp < ngroups;
+       grp += gstride) {
+    const int64_t blk = grp * 8 + (lane >> 3);
+    const bool valid = blk < d.nblocks;
+    if (nonfinite) {  // T = NaN, scales 0x7F, codes 0
+      store_row<FMT>(codes, blk, r, 0u, 0u, valid);
+      if (valid && r == 0) scales[blk] = 0x7F;
+      continue;
+    }
+    float x[8];
+    const BlockAddr ad = block_addr<ROLE>(d, valid ? blk : 0);
+    const int64_t rowbase = ad.base + r * ad.row;
     if constexpr (ROLE == MX_ROLE_WEIGHT) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) x[r][j] = valid ? src[base + r * ad.row + j * ad.col] : 0.0f;
+      for (int j = 0; j < 8; ++j) x[j] = valid ? src[rowbase + j * ad.col] : 0.0f;
     } else {
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (valid) v = *reinterpret_cast<const float4*>(src + base + r * ad.row);
-      x[r][0] = v.x;
-      x[r][1] = v.y;
-      x[r][2] = v.z;
-      x[r][3] = v.w;
+      float4 v0 = make_float4(0.f, 0.f, 0.f, 0.f), v1 = v0;
+      if (valid) {
+        v0 = *reinterpret_cast<const float4*>(src + rowbase);
+        v1 = *reinterpret_cast<const float4*>(src + rowbase + 4);
+      }
+      x[0] = v0.x; x[1] = v0.y; x[2] = v0.z; x[3] = v0.w;
+      x[4] = v1.x; x[5] = v1.y; x[6] = v1.z; x[7] = v1.w;
     }
-  }
-  float am = 0.0f;
+    float am = 0.0f;
 #pragma unroll
-  for (int r = 0; r < 8; ++r)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) am = fmaxf(am, fabsf(x[r][j]));
-  am = fmaxf(am, swap_pair(am));
+    for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(x[j]));
+    am = max8(am);
 
-  const float den = F::MAXV * T;
-  const float braw = (T == 0.0f) ? 0.0f : am / den;
-  const uint32_t bcode = rne_code<ScaleFmt>(braw);
-  const float B = code_value<ScaleFmt>(bcode);
-  const float dd = B * T;
+    const float den = F::MAXV * T;
+    const float braw = (T == 0.0f) ? 0.0f : am / den;
+    const uint32_t bcode = rne_code<ScaleFmt>(braw);
+    const float B = code_value<ScaleFmt>(bcode);
+    const float dd = B * T;
 
-  uint32_t rb[8];
+    uint64_t bits = 0;
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    uint32_t bits = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float v = (dd == 0.0f) ? 0.0f : fabsf(x[r][j]) / dd;
+    for (int j = 0; j < 8; ++j) {
+      const float v = (dd == 0.0f) ? 0.0f : fabsf(x[j]) / dd;
       uint32_t mag;
       if constexpr (SR) {
-        const int64_t idx = base + r * ad.row + j * ad.col;
-        mag = sr_code<F>(v, sr_uniform(seed, static_cast<uint64_t>(idx)));
+        mag = sr_code<F>(v, sr_uniform(seed, static_cast<uint64_t>(rowbase + j * ad.col)));
       } else {
         mag = rne_code<F>(v);
       }
-      const uint32_t code = mag | ((__float_as_uint(x[r][j]) >> 31) << F::SIGN);
-      bits |= code << (F::BITS * j);
+      const uint32_t code = mag | ((__float_as_uint(x[j]) >> 31) << F::SIGN);
+      bits |= static_cast<uint64_t>(code) << (F::BITS * j);
     }
-    rb[r] = bits;
+    store_row<FMT>(codes, blk, r, static_cast<uint32_t>(bits), static_cast<uint32_t>(bits >> 32), valid);
+    if (valid && r == 0) scales[blk] = static_cast<uint8_t>(bcode);
   }
-  store_block_codes<FMT>(codes, blk, half, rb, valid);
-  if (valid && half == 0) scales[blk] = static_cast<uint8_t>(bcode);
 }
 
-// Code of element (r, c) from the 32-bit words of one block.
+// One code row of a block as a 64-bit value (8 codes, BITS each).
 template <int FMT>
-__device__ __forceinline__ uint32_t get_code(const uint32_t* w, int r, int c) {
-  constexpr int BITS = Fmt<FMT>::BITS;
-  const int bit = (r * 8 + c) * BITS;
-  const int wi = bit >> 5, sh = bit & 31;
-  uint32_t v = w[wi] >> sh;
-  if (sh + BITS > 32) v |= w[wi + 1] << (32 - sh);
-  return v & ((1u << BITS) - 1u);
+__device__ __forceinline__ uint64_t load_row(const uint8_t* __restrict__ codes, int64_t blk, int r) {
+  if constexpr (FMT == FMT_E2M1) {
+    return *reinterpret_cast<const uint32_t*>(codes + blk * 32 + r * 4);
+  } else if constexpr (FMT == FMT_E4M3) {
+    const uint2 v = *reinterpret_cast<const uint2*>(codes + blk * 64 + r * 8);
+    return static_cast<uint64_t>(v.x) | (static_cast<uint64_t>(v.y) << 32);
+  } else {
+    // bytes 6r .. 6r+5 lie inside the two dwords starting at floor(6r/4)
+    const int off = 6 * r;
+    const uint32_t* q = reinterpret_cast<const uint32_t*>(codes + blk * 48) + (off >> 2);
+    const uint64_t v = static_cast<uint64_t>(q[0]) | (static_cast<uint64_t>(q[1]) << 32);
+    return (v >> ((off & 3) * 8)) & 0xFFFFFFFFFFFFull;
+  }
 }
 
+// 8 lanes per block, lane = block row, as in k_quantize.
 template <int FMT, int ROLE>
 __global__ __launch_bounds__(kThreads) void k_dequantize(const uint8_t* __restrict__ codes,
                                                          const uint8_t* __restrict__ scales,
                                                          const float* __restrict__ tensor_scale,
                                                          float* __restrict__ dst, QDims d) {
   using F = Fmt<FMT>;
-  constexpr int BYTES = block_bytes<FMT>();
-  const int half = threadIdx.x & 1;
-  const int64_t blk = static_cast<int64_t>(blockIdx.x) * kBlocksPerWG + (threadIdx.x >> 1);
+  const int r = threadIdx.x & 7;
+  const int64_t blk = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) >> 3;
   if (blk >= d.nblocks) return;
-  uint32_t w[BYTES / 4];
-  const uint4* p = reinterpret_cast<const uint4*>(codes + blk * BYTES);
-#pragma unroll
-  for (int i = 0; i < BYTES / 16; ++i) {
-    const uint4 v = p[i];
-    w[4 * i] = v.x;
-    w[4 * i + 1] = v.y;
-    w[4 * i + 2] = v.z;
-    w[4 * i + 3] = v.w;
-  }
+  const uint64_t row = load_row<FMT>(codes, blk, r);
   const uint32_t sb = scales[blk];
   const float B = (sb == 0x7Fu) ? __uint_as_float(0x7FC00000u) : code_value<ScaleFmt>(sb);
   const float T = *tensor_scale;
   const BlockAddr ad = block_addr<ROLE>(d, blk);
-  const int64_t base = ad.base + half * 4 * ad.col;
+  const int64_t rowbase = ad.base + r * ad.row;
+  float o[8];
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    float o[4];
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t code = static_cast<uint32_t>(row >> (F::BITS * j)) & ((1u << F::BITS) - 1u);
+    const float g = code_value<F>(code & ((1u << F::SIGN) - 1u));
+    const float gb = g * B;
+    float v = gb * T;
+    if ((code >> F::SIGN) & 1u) v = -v;
+    o[j] = v;
+  }
+  if constexpr (ROLE == MX_ROLE_WEIGHT) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t code = get_code<FMT>(w, r, half * 4 + j);
-      const float g = code_value<F>(code & ((1u << F::SIGN) - 1u));
-      const float gb = g * B;
-      float v = gb * T;
-      if ((code >> F::SIGN) & 1u) v = -v;
-      o[j] = v;
-    }
-    if constexpr (ROLE == MX_ROLE_WEIGHT) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) dst[base + r * ad.row + j * ad.col] = o[j];
-    } else {
-      *reinterpret_cast<float4*>(dst + base + r * ad.row) = make_float4(o[0], o[1], o[2], o[3]);
-    }
+    for (int j = 0; j < 8; ++j) dst[rowbase + j * ad.col] = o[j];
+  } else {
+    *reinterpret_cast<float4*>(dst + rowbase) = make_float4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<float4*>(dst + rowbase + 4) = make_float4(o[4], o[5], o[6], o[7]);
   }
 }
 
@@ -313,32 +278,34 @@ QDims make_qdims(const Geom& g, mx_role role) {
 
 template <int FMT, int ROLE>
 void launch_q(const QDims& d, const float* src, const mx_qtensor* q, bool sr, uint64_t seed,
-              hipStream_t s) {
+              const uint32_t* part, int nparts, hipStream_t s) {
   // at least one workgroup, so that an empty tensor still publishes T
-  unsigned grid = static_cast<unsigned>((d.nblocks + kBlocksPerWG - 1) / kBlocksPerWG);
-  if (grid == 0) grid = 1;
+  int64_t wgs = (d.nblocks + 8 * kGroupsPerWG - 1) / (8 * kGroupsPerWG);
+  if (wgs > kQuantMaxWGs) wgs = kQuantMaxWGs;
+  if (wgs < 1) wgs = 1;
+  const dim3 grid(static_cast<unsigned>(wgs));
   auto* codes = static_cast<uint8_t*>(q->codes);
   if (sr)
-    hipLaunchKernelGGL((k_quantize<FMT, ROLE, true>), dim3(grid), dim3(kThreads), 0, s, src, codes,
-                       q->scales, q->tensor_scale, q->amax, d, seed);
+    hipLaunchKernelGGL((k_quantize<FMT, ROLE, true>), grid, dim3(kThreads), 0, s, src, codes, q->scales,
+                       q->tensor_scale, q->amax, part, nparts, d, seed);
   else
-    hipLaunchKernelGGL((k_quantize<FMT, ROLE, false>), dim3(grid), dim3(kThreads), 0, s, src, codes,
-                       q->scales, q->tensor_scale, q->amax, d, seed);
+    hipLaunchKernelGGL((k_quantize<FMT, ROLE, false>), grid, dim3(kThreads), 0, s, src, codes, q->scales,
+                       q->tensor_scale, q->amax, part, nparts, d, seed);
 }
 
 template <int FMT>
 void launch_q_role(mx_role role, const QDims& d, const float* src, const mx_qtensor* q, bool sr,
-                   uint64_t seed, hipStream_t s) {
-  if (role == MX_ROLE_ACT) launch_q<FMT, MX_ROLE_ACT>(d, src, q, sr, seed, s);
-  else if (role == MX_ROLE_GRAD) launch_q<FMT, MX_ROLE_GRAD>(d, src, q, sr, seed, s);
-  else launch_q<FMT, MX_ROLE_WEIGHT>(d, src, q, sr, seed, s);
+                   uint64_t seed, const uint32_t* part, int nparts, hipStream_t s) {
+  if (role == MX_ROLE_ACT) launch_q<FMT, MX_ROLE_ACT>(d, src, q, sr, seed, part, nparts, s);
+  else if (role == MX_ROLE_GRAD) launch_q<FMT, MX_ROLE_GRAD>(d, src, q, sr, seed, part, nparts, s);
+  else launch_q<FMT, MX_ROLE_WEIGHT>(d, src, q, sr, seed, part, nparts, s);
 }
 
 template <int FMT, int ROLE>
 void launch_dq(const QDims& d, const mx_qtensor* q, float* dst, hipStream_t s) {
-  const unsigned grid = static_cast<unsigned>((d.nblocks + kBlocksPerWG - 1) / kBlocksPerWG);
-  if (grid == 0) return;
-  hipLaunchKernelGGL((k_dequantize<FMT, ROLE>), dim3(grid), dim3(kThreads), 0, s,
+  const int64_t wgs = (d.nblocks * 8 + kThreads - 1) / kThreads;
+  if (wgs == 0) return;
+  hipLaunchKernelGGL((k_dequantize<FMT, ROLE>), dim3(static_cast<unsigned>(wgs)), dim3(kThreads), 0, s,
                      static_cast<const uint8_t*>(q->codes), q->scales, q->tensor_scale, dst, d);
 }
 
@@ -354,23 +321,23 @@ void launch_dq_role(mx_role role, const QDims& d, const mx_qtensor* q, float* ds
 hipError_t launch_quantize(const Geom& g, mx_role role, const float* src, const mx_qtensor* dst,
                            mx_round rounding, uint64_t seed, int amax_given, hipStream_t s) {
   const QDims d = make_qdims(g, role);
-  const int64_t numel = role_numel(g, role);
-  auto* amax_bits = reinterpret_cast<uint32_t*>(dst->amax);
+  // partials of the amax pass: in the scales buffer, behind the block scales
+  uint32_t* part = nullptr;
+  int nparts = -1;  // -1: the caller's amax
   if (!amax_given) {
-    hipLaunchKernelGGL(k_amax_zero, dim3(1), dim3(64), 0, s, amax_bits);
-    const int64_t n4 = numel / 4;
-    if (n4 > 0) {
-      int64_t wgs = (n4 + kThreads * 4 - 1) / (kThreads * 4);
-      if (wgs > 4096) wgs = 4096;
-      hipLaunchKernelGGL(k_amax, dim3(static_cast<unsigned>(wgs)), dim3(kThreads), 0, s,
-                         reinterpret_cast<const uint4*>(src), n4, amax_bits);
+    const int64_t n4 = d.nblocks * 16;
+    nparts = static_cast<int>(amax_partials(d.nblocks));
+    if (nparts > 0) {
+      part = reinterpret_cast<uint32_t*>(dst->scales + scale_tail_offset(d.nblocks));
+      hipLaunchKernelGGL(k_amax_part, dim3(static_cast<unsigned>(nparts)), dim3(kThreads), 0, s,
+                         reinterpret_cast<const uint4*>(src), n4, part);
     }
   }
   const bool sr = rounding == MX_SR;
   switch (g.fmt) {
-    case FMT_E2M1: launch_q_role<FMT_E2M1>(role, d, src, dst, sr, seed, s); break;
-    case FMT_E2M3: launch_q_role<FMT_E2M3>(role, d, src, dst, sr, seed, s); break;
-    default: launch_q_role<FMT_E4M3>(role, d, src, dst, sr, seed, s); break;
+    case FMT_E2M1: launch_q_role<FMT_E2M1>(role, d, src, dst, sr, seed, part, nparts, s); break;
+    case FMT_E2M3: launch_q_role<FMT_E2M3>(role, d, src, dst, sr, seed, part, nparts, s); break;
+    default: launch_q_role<FMT_E4M3>(role, d, src, dst, sr, seed, part, nparts, s); break;
   }
   return hipGetLastError();
 }

@@ -43,7 +43,7 @@ def f32_bits(v: float) -> int:
 def assert_quant_equal(gq: mx.QTensor, oq, what=""):
     torch.cuda.synchronize()
     codes = gq.codes[:gq.code_bytes].cpu().numpy()
-    scales = gq.scales[:gq.scale_bytes].cpu().numpy()
+    scales = gq.scales[:gq.nblocks].cpu().numpy()
     t = gq.tensor_scale.item()
     amax = gq.amax.item()
     if np.isnan(oq.t):

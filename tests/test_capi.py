@@ -39,8 +39,11 @@ def test_buffer_sizes(fmt, bits):
     assert mx.mx_code_bytes(d, mx.MX_ROLE_ACT) == 9 * 7 * 24 * 16 * bits // 8
     assert mx.mx_code_bytes(d, mx.MX_ROLE_GRAD) == ho * wo * 40 * 16 * bits // 8
     assert mx.mx_code_bytes(d, mx.MX_ROLE_WEIGHT) == 40 * 24 * 9 * bits // 8
-    assert mx.mx_scale_bytes(d, mx.MX_ROLE_ACT) == 9 * 7 * 24 * 16 // 64
-    assert mx.mx_scale_bytes(d, mx.MX_ROLE_WEIGHT) == 40 * 24 * 9 // 64
+    # one byte per block, padded to 16, then 2 KiB of amax-reduction scratch
+    pad16 = lambda v: (v + 15) // 16 * 16
+    assert mx.mx_scale_bytes(d, mx.MX_ROLE_ACT) == pad16(9 * 7 * 24 * 16 // 64) + 2048
+    assert mx.mx_scale_bytes(d, mx.MX_ROLE_WEIGHT) == pad16(40 * 24 * 9 // 64) + 2048
+    assert mx.mx_scale_bytes(mx.desc(0, 16, 16, 3, 3, 1, 1), mx.MX_ROLE_ACT) == 0
     ws = mx.mx_wgrad_workspace_bytes(d)
     assert ws > 0 and ws % (40 * 9 * 24 * 4) == 0
 
@@ -102,6 +105,7 @@ def test_null_and_role_and_rounding():
 def test_alignment():
     d = mx.desc(**GOOD)
     assert quant(d, dst=q(codes=MIS)) == -5
+    assert quant(d, dst=q(scales=A16 + 4)) == -5   # the amax scratch tail needs 16-byte alignment
     assert quant(d, dst=q(t=A16 + 2)) == -5
     assert quant(d, src=A16 + 4) == -5
 

@@ -112,7 +112,7 @@ def test_quantize_nonfinite(bad):
     gq = gpu_quantize(d, mx.MX_ROLE_ACT, x)
     assert_quant_equal(gq, oracle_quantize(d, mx.MX_ROLE_ACT, x))
     assert np.isnan(gq.tensor_scale.item())
-    assert (gq.scales[:gq.scale_bytes] == 0x7F).all()
+    assert (gq.scales[:gq.nblocks] == 0x7F).all()
 
 
 def test_quantize_all_zero_and_empty():

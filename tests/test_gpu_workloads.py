@@ -104,4 +104,4 @@ def test_replay_buffer_codec():
     ref = O.dequantize(oq)
     assert np.array_equal(back.cpu().numpy().view(np.uint32), ref.view(np.uint32))
     # stored size: 4 bits per element + one byte per 64 elements
-    assert q.code_bytes + q.scale_bytes == maps.numel() * 4 // 8 + maps.numel() // 64
+    assert q.code_bytes + q.nblocks == maps.numel() * 4 // 8 + maps.numel() // 64
