@@ -20,11 +20,14 @@
 // in the epilogue.  Block scales change every 8 elements along K, which the
 // E8M0-per-32 scaled MFMA of gfx950 cannot express, hence bf16 MFMA.
 //
-// Kernel shape: 256 threads (4 wave64), tile MT x NT, K step 32 (four 8-wide
-// k-blocks), two LDS stages.  Each thread fetches at most one quantized block
-// per stage, decodes it and writes its eight 8-value K-lines to LDS as
-// 16-byte rows [line][k] (k contiguous), which is exactly the operand layout
-// of v_mfma_f32_32x32x16_bf16 (lane l: row/col l%32, K slots 8*(l/32)..+7).
+// Kernel shape: 2 or 4 wave64, tile MT x NT, K stage of KB k-blocks (8 K
+// values each) sized so that every thread stages one quantized block per
+// stage: small tiles take long stages, so the latency-bound K loop of a
+// small layer has few steps.  Two LDS stages.  Each thread fetches its
+// block two stages ahead, decodes it and writes its eight 8-value K-lines
+// to LDS as 16-byte rows [line][k] (k contiguous), which is exactly the
+// operand layout of v_mfma_f32_32x32x16_{f16,bf16} (lane l: row/col l%32,
+// K slots 8*(l/32)..+7).
 #include <type_traits>
 #include <utility>
 
@@ -34,15 +37,18 @@
 namespace mx {
 namespace {
 
-constexpr int KT = 32;          // K per LDS stage
-// LDS layout of a staged tile: lines of 32 K values (64 B) at a stride of
-// 80 B, and logical line L stored at physical line L ^ ((L >> 2) & 4) (the
-// two halves of every second 8-line block swapped).  With 64 LDS banks this
-// keeps both access patterns conflict-free: the 16-byte fragment reads of 16
-// consecutive lines hit 16 distinct bank quads, and the 64-byte line writes
-// of four neighbouring blocks (same line index) hit the four bank quarters.
-constexpr int LDS_STRIDE = 40;  // 16-bit elements per line
-__device__ __forceinline__ int lds_line(int line) { return (line ^ ((line >> 2) & 4)) * LDS_STRIDE; }
+// LDS layout of a staged tile: lines of KT = 8*KB K values, KB the k-blocks
+// of one stage, at a stride of KT + 8 16-bit elements (LS), and logical line
+// L stored at physical line L ^ ((L >> 2) & 4) (the two halves of every
+// second 8-line block swapped).  The stride is an odd number of 16-byte bank
+// quads modulo the 64 banks, so the 16-byte fragment reads of 16 consecutive
+// lines hit 16 distinct quads; the swizzle spreads the line writes of
+// neighbouring blocks (with KB = 4 they hit the four bank quarters).
+template <int KB> struct Lds {
+  static constexpr int KT = 8 * KB;
+  static constexpr int LS = KT + 8;
+  static __device__ __forceinline__ int line(int l) { return (l ^ ((l >> 2) & 4)) * LS; }
+};
 
 enum { OP_FWD = 0, OP_DGRAD = 1, OP_WGRAD = 2 };
 
@@ -58,7 +64,7 @@ struct ConvParams {
   int32_t M;          // GEMM rows
   int32_t ncb;        // column blocks (8 columns each) of the launch's column space
   int32_t kb_total;   // k-blocks (8 each) along K
-  int32_t ks_split;   // K steps per split (wgrad)
+  int32_t ks_split;   // K steps (of the kernel's KB k-blocks) per split (wgrad)
   int32_t ncol;       // wgrad: columns of one partial (Kh*Kw*Cin)
   const uint8_t* a_codes;
   const uint8_t* a_scales;
@@ -122,7 +128,7 @@ struct RawBlock {
 // 2u, 2u+1 (a 2x2 transpose of the row pairs).  Each unit decodes what it
 // writes (E2M3 decodes 32 elements at a time: in the first unit of a 4-row
 // group for ROWS, all 64 in unit 0 for !ROWS).
-template <int FMT, bool ROWS>
+template <int FMT, bool ROWS, int LS>
 struct Stager {
   static constexpr int UNITS = ROWS ? 8 : 4;
   BlockScale bs;
@@ -134,7 +140,7 @@ struct Stager {
       : bs(raw.scale), p_lo(lo), p_hi(hi) {}
 
   __device__ __forceinline__ uint16_t* line_ptr(int i) const {
-    return (i < 4) ? p_lo + i * LDS_STRIDE : p_hi + (i - 4) * LDS_STRIDE;
+    return (i < 4) ? p_lo + i * LS : p_hi + (i - 4) * LS;
   }
 
   // pair j of row r
@@ -206,7 +212,7 @@ struct Stager {
   }
 };
 
-// Walks the k-blocks one thread stages, four at a time (kb, kb+4, ...),
+// Walks the k-blocks one thread stages, KB at a time (kb, kb+KB, ...),
 // keeping the decomposition of kb incrementally (no division in the loop).
 //   FWD  : kb = tap * CBin + cib,  tap = kh * Kw + kw
 //   DGRAD: kb = ti * CBout + cob,  ti over the phase's valid taps (it, jt)
@@ -222,9 +228,9 @@ struct KWalk {
     a = outer / n_b;
     b = outer - a * n_b;
   }
-  __device__ __forceinline__ void advance4(int n_inner, int n_b) {
-    kb += 4;
-    inner += 4;
+  __device__ __forceinline__ void advance(int step, int n_inner, int n_b) {
+    kb += step;
+    inner += step;
     while (inner >= n_inner) {
       inner -= n_inner;
       if (++b == n_b) {
@@ -245,19 +251,22 @@ __device__ __forceinline__ f32x16 mfma32(const uint16_t* pa, const uint16_t* pb,
                                                    *reinterpret_cast<const bf16x8*>(pb), c, 0, 0, 0);
 }
 
-template <int OP, int FMT, int MT, int NT, int WM, int WAVES>
+template <int OP, int FMT, int MT, int NT, int WM, int WAVES, int KB>
 __global__ __launch_bounds__(WAVES * 64) void k_conv(const ConvParams p) {
   constexpr int WN = WAVES / WM;
   constexpr int WTM = MT / WM, WTN = NT / WN;
   constexpr int RM = WTM / 32, RN = WTN / 32;
-  constexpr int ABLK = (MT / 8) * 4, BBLK = (NT / 8) * 4;
+  constexpr int ABLK = (MT / 8) * KB, BBLK = (NT / 8) * KB;
+  constexpr int NK = KB / 2;  // 16-wide MFMA K slices per stage
+  constexpr int LS = Lds<KB>::LS;
+  static_assert(KB % 2 == 0, "a stage is a whole number of 16-wide K slices");
   constexpr bool F16 = OperandType<FMT>::F16;
   static_assert(ABLK + BBLK <= WAVES * 64, "one block per thread per stage");
   static_assert(RM >= 1 && RN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile of 32x32 MFMAs");
 
   // two stages of MT + NT lines, plus 8 lines that threads without a block
   // write their zeros into (keeps the staging code branch-free)
-  constexpr int STAGE = (MT + NT + 8) * LDS_STRIDE;
+  constexpr int STAGE = (MT + NT + 8) * LS;
   __shared__ __attribute__((aligned(16))) uint16_t lds[2][STAGE];
 
   const int tid = threadIdx.x;
@@ -299,8 +308,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_conv(const ConvParams p) {
     if (cb0 >= hp * wp * p.nb) return;
     kb_end = nkh * nkw * cbout;
   } else if constexpr (OP == OP_WGRAD) {
-    kb_begin = bz * p.ks_split * 4;
-    kb_end = min(p.kb_total, kb_begin + p.ks_split * 4);
+    kb_begin = bz * p.ks_split * KB;
+    kb_end = min(p.kb_total, kb_begin + p.ks_split * KB);
     if (kb_begin > kb_end) kb_begin = kb_end;
   }
   const int ncb_launch = (OP == OP_DGRAD) ? hp * wp * p.nb : p.ncb;
@@ -309,14 +318,15 @@ __global__ __launch_bounds__(WAVES * 64) void k_conv(const ConvParams p) {
   const bool is_a = tid < ABLK;
   const int t_local = is_a ? tid : tid - ABLK;
   const bool active = tid < ABLK + BBLK;
-  const int line = !active ? MT + NT : is_a ? (t_local >> 2) * 8 : MT + (t_local >> 2) * 8;
-  const int kbl = active ? (t_local & 3) : 0;
-  const int gblk = (is_a ? rb0 : cb0) + (t_local >> 2);
+  const int lblk = t_local / KB;  // line block (8 lines) within the tile
+  const int line = !active ? MT + NT : is_a ? lblk * 8 : MT + lblk * 8;
+  const int kbl = active ? t_local - lblk * KB : 0;
+  const int gblk = (is_a ? rb0 : cb0) + lblk;
   const bool in_range = active && (is_a ? (gblk < (p.M >> 3)) : (gblk < ncb_launch));
   // swizzled addresses of the block's two line halves (see lds_line)
   const int rot = (line >> 2) & 4;
-  const int lo_off = (line + rot) * LDS_STRIDE + kbl * 8;
-  const int hi_off = (line + (rot ^ 4)) * LDS_STRIDE + kbl * 8;
+  const int lo_off = (line + rot) * LS + kbl * 8;
+  const int hi_off = (line + (rot ^ 4)) * LS + kbl * 8;
 
   // Column-block geometry fixed over the K loop.
   int col_y = 0, col_x = 0, col_nb = 0;   // FWD: output (ho, wo); DGRAD: input pixel (h, w)
@@ -404,7 +414,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_conv(const ConvParams p) {
     const bool ok = locate(blk);
     if (is_a) raw.load(p.a_codes, p.a_scales, blk, ok);
     else raw.load(p.b_codes, p.b_scales, blk, ok);
-    kw.advance4(n_inner, n_b);
+    kw.advance(KB, n_inner, n_b);
   };
 
   f32x16 acc[RM][RN];
@@ -419,9 +429,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_conv(const ConvParams p) {
   // 32-wide sub-tile; the two K halves of a 16-wide step are 8 apart)
   int a_off[RM], b_off[RN];
 #pragma unroll
-  for (int i = 0; i < RM; ++i) a_off[i] = lds_line(wm * WTM + i * 32 + (lane & 31)) + (lane >> 5) * 8;
+  for (int i = 0; i < RM; ++i) a_off[i] = Lds<KB>::line(wm * WTM + i * 32 + (lane & 31)) + (lane >> 5) * 8;
 #pragma unroll
-  for (int j = 0; j < RN; ++j) b_off[j] = lds_line(MT + wn * WTN + j * 32 + (lane & 31)) + (lane >> 5) * 8;
+  for (int j = 0; j < RN; ++j) b_off[j] = Lds<KB>::line(MT + wn * WTN + j * 32 + (lane & 31)) + (lane >> 5) * 8;
 
   // One K step: the MFMAs on stage `buf`, with the staging units of the next
   // block (`nxt`, into stage buf^1) spread between them in program order, so
@@ -431,23 +441,23 @@ __global__ __launch_bounds__(WAVES * 64) void k_conv(const ConvParams p) {
   // boundaries (ABLK a multiple of 64) the branch on is_a is wave-uniform and
   // each side carries the MFMA sequence with its own staging units;
   // otherwise one MFMA sequence carries both kinds of units, predicated.
-  constexpr int NMF = 2 * RM * RN;
-  using StA = Stager<FMT, A_ROWS>;
-  using StB = Stager<FMT, B_ROWS>;
+  constexpr int NMF = NK * RM * RN;
+  using StA = Stager<FMT, A_ROWS, LS>;
+  using StB = Stager<FMT, B_ROWS, LS>;
   typedef __attribute__((__vector_size__(8 * sizeof(uint16_t)))) uint16_t u16x8;
   // all fragments of the step are read first (one LDS wait), then the MFMAs
   auto mma_seq = [&](int buf, auto&& after) {
     const uint16_t* base = lds[buf];
-    u16x8 fa[2][RM], fb[2][RN];
+    u16x8 fa[NK][RM], fb[NK][RN];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < NK; ++kk) {
 #pragma unroll
       for (int i = 0; i < RM; ++i) fa[kk][i] = *reinterpret_cast<const u16x8*>(base + a_off[i] + kk * 16);
 #pragma unroll
       for (int j = 0; j < RN; ++j) fb[kk][j] = *reinterpret_cast<const u16x8*>(base + b_off[j] + kk * 16);
     }
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
+    for (int kk = 0; kk < NK; ++kk)
 #pragma unroll
       for (int i = 0; i < RM; ++i)
 #pragma unroll
@@ -488,20 +498,20 @@ __global__ __launch_bounds__(WAVES * 64) void k_conv(const ConvParams p) {
     __syncthreads();
   };
 
-  const int nsteps = (kb_end - kb_begin + 3) / 4;
+  const int nsteps = (kb_end - kb_begin + KB - 1) / KB;
   if (nsteps > 0) {
     fetch(raw0);
     if (nsteps > 1) fetch(raw1);
     {
       // first block: stage it straight away
       if (is_a) {
-        Stager<FMT, A_ROWS> st(raw0, &lds[0][lo_off], &lds[0][hi_off]);
+        StA st(raw0, &lds[0][lo_off], &lds[0][hi_off]);
         [&]<int... U>(std::integer_sequence<int, U...>) { (st.template unit<U>(raw0), ...); }(
-            std::make_integer_sequence<int, Stager<FMT, A_ROWS>::UNITS>());
+            std::make_integer_sequence<int, StA::UNITS>());
       } else {
-        Stager<FMT, B_ROWS> st(raw0, &lds[0][lo_off], &lds[0][hi_off]);
+        StB st(raw0, &lds[0][lo_off], &lds[0][hi_off]);
         [&]<int... U>(std::integer_sequence<int, U...>) { (st.template unit<U>(raw0), ...); }(
-            std::make_integer_sequence<int, Stager<FMT, B_ROWS>::UNITS>());
+            std::make_integer_sequence<int, StB::UNITS>());
       }
     }
     __syncthreads();
@@ -552,39 +562,39 @@ __global__ __launch_bounds__(WAVES * 64) void k_conv(const ConvParams p) {
 }
 
 // dW[co][ci][kh][kw] = T_dy * T_x * (sum over splits of the partials
-// [split][co][(kh, kw, ci)]).  One workgroup owns 64 outputs; its 4 waves sum
-// interleaved quarters of the splits with 4 independent accumulators each,
-// and the 16 partial sums are combined in a fixed order: the result does not
-// depend on timing.
-constexpr int kRedOut = 64;
+// [split][co][(kh, kw, ci)]).  One workgroup owns 16 consecutive outputs;
+// its 256 threads are 16 split groups x 16 outputs (a group reads 64
+// contiguous bytes of one partial), each summing every 16th split with 4
+// independent accumulators; the 64 partial sums of an output are combined in
+// a fixed order, so the result does not depend on timing.
+constexpr int kRedOut = 16;
 __global__ __launch_bounds__(256) void k_wgrad_reduce(const float* __restrict__ ws, int splits, int M,
                                                       int ncol, int c_in, int k_h, int k_w,
                                                       const float* __restrict__ ta,
                                                       const float* __restrict__ tb, float* __restrict__ dw) {
   const int64_t total = static_cast<int64_t>(M) * ncol;
-  const int o = threadIdx.x & (kRedOut - 1), q = threadIdx.x >> 6;  // q: wave 0..3
+  const int o = threadIdx.x & (kRedOut - 1), g = threadIdx.x / kRedOut;  // g: split group 0..15
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * kRedOut + o;
   float s[4] = {0.f, 0.f, 0.f, 0.f};
   if (idx < total) {
-    int z = q;
-    for (; z + 12 < splits; z += 16) {
+    int z = g;
+    for (; z + 48 < splits; z += 64) {
       s[0] += ws[static_cast<int64_t>(z) * total + idx];
-      s[1] += ws[static_cast<int64_t>(z + 4) * total + idx];
-      s[2] += ws[static_cast<int64_t>(z + 8) * total + idx];
-      s[3] += ws[static_cast<int64_t>(z + 12) * total + idx];
+      s[1] += ws[static_cast<int64_t>(z + 16) * total + idx];
+      s[2] += ws[static_cast<int64_t>(z + 32) * total + idx];
+      s[3] += ws[static_cast<int64_t>(z + 48) * total + idx];
     }
-    for (int u = 0; z < splits; z += 4, ++u) s[u] += ws[static_cast<int64_t>(z) * total + idx];
+    for (int u = 0; z < splits; z += 16, ++u) s[u] += ws[static_cast<int64_t>(z) * total + idx];
   }
-  __shared__ float part[4][4][kRedOut];
+  __shared__ float part[16][4][kRedOut];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) part[q][u][o] = s[u];
+  for (int u = 0; u < 4; ++u) part[g][u][o] = s[u];
   __syncthreads();
-  if (q == 0 && idx < total) {
+  if (g == 0 && idx < total) {
     float r = 0.0f;
+    for (int gg = 0; gg < 16; ++gg)
 #pragma unroll
-    for (int qq = 0; qq < 4; ++qq)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) r += part[qq][u][o];
+      for (int u = 0; u < 4; ++u) r += part[gg][u][o];
     const int co = static_cast<int>(idx / ncol), j = static_cast<int>(idx - static_cast<int64_t>(co) * ncol);
     const int tap = j / c_in, ci = j - tap * c_in;
     const int kh = tap / k_w, kw = tap - kh * k_w;
@@ -595,53 +605,79 @@ __global__ __launch_bounds__(256) void k_wgrad_reduce(const float* __restrict__ 
 // ---- tile selection and launch -------------------------------------------
 
 struct Tile {
-  int mt, nt, wm;
+  int mt, nt, wm, waves, kb;
 };
 
-// Candidate tiles (MT, NT, waves along M); a wave tile is a grid of 32x32
-// MFMAs, so MT = 32 uses the four waves along N.
-constexpr Tile kTiles[] = {{256, 256, 2}, {128, 256, 2}, {128, 128, 2}, {64, 256, 2},
-                           {64, 128, 2},  {64, 64, 2},   {32, 256, 1}, {32, 128, 1}};
+// Candidate tiles (MT, NT, waves along M, waves, k-blocks per stage), largest
+// first.  A wave tile is a grid of 32x32 MFMAs; KB is the largest even count
+// with (MT/8 + NT/8) * KB <= threads.
+constexpr Tile kTiles[] = {{256, 256, 2, 4, 4}, {128, 256, 2, 4, 4}, {128, 128, 2, 4, 8},
+                           {64, 256, 2, 4, 6},  {64, 128, 2, 4, 10}, {64, 64, 2, 4, 16},
+                           {32, 256, 1, 4, 6},  {32, 128, 1, 4, 12}, {64, 32, 2, 2, 10},
+                           {32, 64, 1, 2, 10}};
 
-// Largest tile that still gives at least two workgroups per CU (512); if none
-// does, the one with the most useful work per workgroup among those with the
-// most workgroups.
+// Tile heights never exceed the GEMM's rows rounded up to a tile height.
+// fwd / dgrad: the largest tile that still gives 2048 waves (two 4-wave
+// workgroups per CU); else the one reaching the most CUs, preferring the
+// larger tile.  The K loop of a small layer is latency-bound, so spreading
+// it over more CUs beats operand reuse inside a workgroup.
+int mt_cap(int64_t M) { return M > 128 ? 256 : M > 64 ? 128 : M > 32 ? 64 : 32; }
+
 Tile pick_tile(int64_t M, int64_t ncols, int64_t zdim) {
-  const int mt_need = M >= 256 ? 256 : M > 64 ? 128 : M > 32 ? 64 : 32;
-  Tile best = {0, 0, 0};
-  int64_t best_wgs = -1;
+  const int cap = mt_cap(M);
+  Tile best = {0, 0, 0, 0, 0};
+  int64_t best_reach = -1;
   for (const Tile& t : kTiles) {
-    if (t.mt > mt_need) continue;
-    if (t.mt < mt_need && !(t.mt * 2 == mt_need && M < mt_need)) {
-      // never split rows below what the channel count needs, except to halve
-      // a tile that would be mostly empty
-      if (t.mt != mt_need) continue;
-    }
+    if (t.mt > cap) continue;
     const int64_t wgs = ((M + t.mt - 1) / t.mt) * ((ncols + t.nt - 1) / t.nt) * zdim;
-    if (wgs >= 512) return t;
-    if (wgs > best_wgs) {
+    if (wgs * t.waves >= 2048) return t;
+    const int64_t reach = wgs < 256 ? wgs : 256;
+    if (reach > best_reach) {
       best = t;
-      best_wgs = wgs;
+      best_reach = reach;
     }
   }
-  return best.mt ? best : Tile{32, 128, 1};
+  return best;
 }
 
-template <int OP, int FMT, int MT, int NT, int WM, int WAVES = 4>
+// wgrad: split K supplies the parallelism, so the tile is chosen for operand
+// reuse: the largest one whose share of useful (unpadded) outputs is within
+// 3/4 of the best share any tile reaches.
+Tile pick_wgrad_tile(int64_t M, int64_t ncols) {
+  const int cap = mt_cap(M);
+  double best_eff = 0.0;
+  for (const Tile& t : kTiles) {
+    if (t.mt > cap) continue;
+    const double eff = static_cast<double>(M * ncols) /
+                       (static_cast<double>((M + t.mt - 1) / t.mt * t.mt) * ((ncols + t.nt - 1) / t.nt * t.nt));
+    if (eff > best_eff) best_eff = eff;
+  }
+  for (const Tile& t : kTiles) {
+    if (t.mt > cap) continue;
+    const double eff = static_cast<double>(M * ncols) /
+                       (static_cast<double>((M + t.mt - 1) / t.mt * t.mt) * ((ncols + t.nt - 1) / t.nt * t.nt));
+    if (eff * 4.0 >= best_eff * 3.0) return t;
+  }
+  return kTiles[0];
+}
+
+template <int OP, int FMT, int MT, int NT, int WM, int WAVES, int KB>
 void launch_tile(const ConvParams& p, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((k_conv<OP, FMT, MT, NT, WM, WAVES>), grid, dim3(WAVES * 64), 0, s, p);
+  hipLaunchKernelGGL((k_conv<OP, FMT, MT, NT, WM, WAVES, KB>), grid, dim3(WAVES * 64), 0, s, p);
 }
 
 template <int OP, int FMT>
 void launch_fmt(const ConvParams& p, const Tile& t, dim3 grid, hipStream_t s) {
-  if (t.mt == 256) launch_tile<OP, FMT, 256, 256, 2>(p, grid, s);
-  else if (t.mt == 128 && t.nt == 256) launch_tile<OP, FMT, 128, 256, 2>(p, grid, s);
-  else if (t.mt == 128) launch_tile<OP, FMT, 128, 128, 2>(p, grid, s);
-  else if (t.mt == 64 && t.nt == 256) launch_tile<OP, FMT, 64, 256, 2>(p, grid, s);
-  else if (t.mt == 64 && t.nt == 128) launch_tile<OP, FMT, 64, 128, 2>(p, grid, s);
-  else if (t.mt == 64) launch_tile<OP, FMT, 64, 64, 2>(p, grid, s);
-  else if (t.nt == 256) launch_tile<OP, FMT, 32, 256, 1>(p, grid, s);
-  else launch_tile<OP, FMT, 32, 128, 1>(p, grid, s);
+  if (t.mt == 256) launch_tile<OP, FMT, 256, 256, 2, 4, 4>(p, grid, s);
+  else if (t.mt == 128 && t.nt == 256) launch_tile<OP, FMT, 128, 256, 2, 4, 4>(p, grid, s);
+  else if (t.mt == 128) launch_tile<OP, FMT, 128, 128, 2, 4, 8>(p, grid, s);
+  else if (t.mt == 64 && t.nt == 256) launch_tile<OP, FMT, 64, 256, 2, 4, 6>(p, grid, s);
+  else if (t.mt == 64 && t.nt == 128) launch_tile<OP, FMT, 64, 128, 2, 4, 10>(p, grid, s);
+  else if (t.mt == 64 && t.nt == 64) launch_tile<OP, FMT, 64, 64, 2, 4, 16>(p, grid, s);
+  else if (t.mt == 64) launch_tile<OP, FMT, 64, 32, 2, 2, 10>(p, grid, s);
+  else if (t.nt == 256) launch_tile<OP, FMT, 32, 256, 1, 4, 6>(p, grid, s);
+  else if (t.nt == 128) launch_tile<OP, FMT, 32, 128, 1, 4, 12>(p, grid, s);
+  else launch_tile<OP, FMT, 32, 64, 1, 2, 10>(p, grid, s);
 }
 
 template <int OP>
@@ -661,8 +697,8 @@ ConvParams base_params(const Geom& g) {
   return p;
 }
 
-// Weight gradient: tile and split count.  Enough workgroups to cover the 256
-// CUs twice, at least 8 K steps per split.
+// Weight gradient: tile and split count.  Up to 2048 waves, at least 4 K
+// steps per split.
 struct WgradPlan {
   Tile t;
   int splits;
@@ -670,12 +706,13 @@ struct WgradPlan {
 
 WgradPlan wgrad_plan(const Geom& g) {
   const int64_t kb_total = static_cast<int64_t>(g.ho) * g.wo * (g.n / 8);
-  const int64_t ksteps = (kb_total + 3) / 4;
   const int64_t ncol = static_cast<int64_t>(g.k_h) * g.k_w * g.c_in;
-  const Tile t = pick_tile(g.c_out, ncol, 1);
+  const Tile t = pick_wgrad_tile(g.c_out, ncol);
+  const int64_t ksteps = (kb_total + t.kb - 1) / t.kb;
   const int64_t tiles = ((g.c_out + t.mt - 1) / t.mt) * ((ncol + t.nt - 1) / t.nt);
-  int64_t splits = (512 + tiles - 1) / tiles;
-  const int64_t max_by_k = ksteps / 8;
+  // rounded down: a last, nearly empty round of workgroups costs a full one
+  int64_t splits = (2048 / t.waves) / tiles;
+  const int64_t max_by_k = ksteps / 4;
   if (splits > max_by_k) splits = max_by_k;
   if (splits < 1) splits = 1;
   if (splits > 65535) splits = 65535;
@@ -730,7 +767,7 @@ hipError_t launch_conv_wgrad(const Geom& g, const mx_qtensor* dyq, const mx_qten
   p.ncol = g.k_h * g.k_w * g.c_in;
   p.ncb = p.ncol / 8;
   p.kb_total = g.ho * g.wo * (g.n / 8);
-  const int ksteps = (p.kb_total + 3) / 4;
+  const int ksteps = (p.kb_total + pl.t.kb - 1) / pl.t.kb;
   p.ks_split = (ksteps + pl.splits - 1) / pl.splits;
   p.a_codes = static_cast<const uint8_t*>(dyq->codes); p.a_scales = dyq->scales; p.a_t = dyq->tensor_scale;
   p.b_codes = static_cast<const uint8_t*>(xq->codes); p.b_scales = xq->scales; p.b_t = xq->tensor_scale;

@@ -28,6 +28,9 @@ SHAPES = [
     (24, 64, 64, 12, 12, 3, 3, 2, 2, 1, 1),
     (8, 8, 8, 4, 4, 3, 3, 1, 1, 3, 3),         # padding wider than the kernel reach
     (8, 256, 256, 6, 6, 3, 3, 1, 1, 1, 1),     # 256x256 tile
+    (64, 8, 128, 32, 32, 1, 1, 1, 1, 0, 0),    # fwd on a 128x128 tile (65536 columns)
+    (128, 8, 128, 32, 32, 1, 1, 1, 1, 0, 0),   # fwd on a 128x256 tile (131072 columns)
+    (16, 24, 64, 6, 6, 1, 1, 1, 1, 0, 0),      # wgrad on the 2-wave 64x32 tile (24 columns)
 ]
 
 
