@@ -94,31 +94,31 @@ struct BlockScale {
 };
 
 // Raw codes of one block held in registers between the global load and the
-// LDS store.
+// LDS store.  The loads are unconditional: a block outside the tensor (zero
+// padding, tails) reads block 0 of the tensor instead and carries mask 0,
+// which the decode applies to codes and scale (giving zeros).  Branch-free
+// loads keep the wait counts exact, so a fetch stays in flight while the
+// intervening K steps compute.
 template <int FMT>
 struct RawBlock {
   static constexpr int WORDS = block_bytes<FMT>() / 4;
   uint32_t w[WORDS];
   uint32_t scale;
+  uint32_t mask;  // ~0 for a block of the tensor, 0 for padding
 
-  __device__ __forceinline__ void load(const uint8_t* codes, const uint8_t* scales, int64_t blk, bool ok) {
-    // a block outside the tensor (zero padding, tails) decodes to zeros: codes
-    // 0 and scale 0 give mB = 0
+  __device__ __forceinline__ void load(const uint8_t* codes, const uint8_t* scales, uint32_t blk, bool ok) {
+    const uint64_t b = ok ? blk : 0u;
+    const uint4* p = reinterpret_cast<const uint4*>(codes + b * block_bytes<FMT>());
 #pragma unroll
-    for (int i = 0; i < WORDS; ++i) w[i] = 0u;
-    scale = 0u;
-    if (ok) {
-      const uint4* p = reinterpret_cast<const uint4*>(codes + blk * block_bytes<FMT>());
-#pragma unroll
-      for (int i = 0; i < WORDS / 4; ++i) {
-        const uint4 v = p[i];
-        w[4 * i] = v.x;
-        w[4 * i + 1] = v.y;
-        w[4 * i + 2] = v.z;
-        w[4 * i + 3] = v.w;
-      }
-      scale = scales[blk];
+    for (int i = 0; i < WORDS / 4; ++i) {
+      const uint4 v = p[i];
+      w[4 * i] = v.x;
+      w[4 * i + 1] = v.y;
+      w[4 * i + 2] = v.z;
+      w[4 * i + 3] = v.w;
     }
+    scale = scales[b];
+    mask = ok ? ~0u : 0u;
   }
 };
 
@@ -132,12 +132,13 @@ template <int FMT, bool ROWS, int LS>
 struct Stager {
   static constexpr int UNITS = ROWS ? 8 : 4;
   BlockScale bs;
+  uint32_t mask;
   uint32_t P[8][4];  // pairs (element (r,2j), element (r,2j+1)) as two 16-bit floats
   uint16_t* p_lo;    // lines 0-3 of the block (swizzled halves, see lds_line)
   uint16_t* p_hi;    // lines 4-7
 
   __device__ __forceinline__ Stager(const RawBlock<FMT>& raw, uint16_t* lo, uint16_t* hi)
-      : bs(raw.scale), p_lo(lo), p_hi(hi) {}
+      : bs(raw.scale & raw.mask), mask(raw.mask), p_lo(lo), p_hi(hi) {}
 
   __device__ __forceinline__ uint16_t* line_ptr(int i) const {
     return (i < 4) ? p_lo + i * LS : p_hi + (i - 4) * LS;
@@ -149,10 +150,10 @@ struct Stager {
     if constexpr (FMT == FMT_E2M1) {
       const _Float16 m = static_cast<_Float16>(bs.mb);
       const f16x2 m2 = {m, m};
-      return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(raw.w[R], bs.b, J) * m2);
+      return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(raw.w[R] & mask, bs.b, J) * m2);
     } else {
       // exact: at most 7 significant bits, so the bf16 is the high half
-      const auto f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(raw.w[2 * R + (J >> 1)], bs.b, (J & 1) != 0);
+      const auto f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(raw.w[2 * R + (J >> 1)] & mask, bs.b, (J & 1) != 0);
       const float lo = f[0] * bs.mb, hi = f[1] * bs.mb;
       return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
     }
@@ -164,8 +165,8 @@ struct Stager {
     const _Float16 m = static_cast<_Float16>(bs.mb);
     const f16x2 m2 = {m, m};
     u32x6 src;
-    src[0] = raw.w[6 * G + 0]; src[1] = raw.w[6 * G + 1]; src[2] = raw.w[6 * G + 2];
-    src[3] = raw.w[6 * G + 3]; src[4] = raw.w[6 * G + 4]; src[5] = raw.w[6 * G + 5];
+    src[0] = raw.w[6 * G + 0] & mask; src[1] = raw.w[6 * G + 1] & mask; src[2] = raw.w[6 * G + 2] & mask;
+    src[3] = raw.w[6 * G + 3] & mask; src[4] = raw.w[6 * G + 4] & mask; src[5] = raw.w[6 * G + 5] & mask;
     const auto v = __builtin_amdgcn_cvt_scalef32_pk32_f16_fp6(src, bs.b);
     struct Words { uint32_t u[16]; };
     const Words wv = __builtin_bit_cast(Words, v);
@@ -212,32 +213,22 @@ struct Stager {
   }
 };
 
-// Walks the k-blocks one thread stages, KB at a time (kb, kb+KB, ...),
-// keeping the decomposition of kb incrementally (no division in the loop).
-//   FWD  : kb = tap * CBin + cib,  tap = kh * Kw + kw
-//   DGRAD: kb = ti * CBout + cob,  ti over the phase's valid taps (it, jt)
-//   WGRAD: kb = pos * NB + nbk,    pos = ho * Wo + wo
-struct KWalk {
-  int a, b;    // outer index (tap / tap pair / position) split in two, inner index
-  int inner;   // fastest index (cib / cob / nbk)
-  int kb;
-  __device__ __forceinline__ void init(int kb0, int n_inner, int n_b) {
-    kb = kb0;
-    const int outer = kb0 / n_inner;
-    inner = kb0 - outer * n_inner;
-    a = outer / n_b;
-    b = outer - a * n_b;
+// Division by a runtime constant d >= 1 for dividends below 2^31 (block
+// and k-block indices): q = floor(x * m / 2^sh) with sh = 31 + ceil(log2 d)
+// and m = ceil(2^sh / d) < 2^32.  The product overshoots x/d by less than
+// x / 2^sh < 1/d, which never crosses the next integer, so q is exact.
+// Branch-free, so the k-block walk can be scheduled between MFMAs.
+struct FastDiv {
+  uint32_t m, d;
+  int sh;
+  __device__ __forceinline__ void init(uint32_t dv) {
+    d = dv;
+    const int l = dv > 1 ? 32 - __builtin_clz(dv - 1) : 0;
+    sh = 31 + l;
+    m = static_cast<uint32_t>(((static_cast<uint64_t>(1) << sh) + dv - 1) / dv);
   }
-  __device__ __forceinline__ void advance(int step, int n_inner, int n_b) {
-    kb += step;
-    inner += step;
-    while (inner >= n_inner) {
-      inner -= n_inner;
-      if (++b == n_b) {
-        b = 0;
-        ++a;
-      }
-    }
+  __device__ __forceinline__ uint32_t div(uint32_t x) const {
+    return static_cast<uint32_t>((static_cast<uint64_t>(x) * m) >> sh);
   }
 };
 
@@ -351,51 +342,56 @@ __global__ __launch_bounds__(WAVES * 64) void k_conv(const ConvParams p) {
     }
   }
 
-  // incremental walk over this thread's k-blocks
-  int n_inner, n_b;
-  if constexpr (OP == OP_FWD) { n_inner = cbin; n_b = p.k_w; }
-  else if constexpr (OP == OP_DGRAD) { n_inner = cbout; n_b = nkw > 0 ? nkw : 1; }
-  else { n_inner = p.nb; n_b = p.wo; }
-  KWalk kw;
-  kw.init(kb_begin + kbl, n_inner, n_b);
+  // The k-blocks one thread stages are kb, kb+KB, ...; each is split as
+  //   FWD  : kb = tap * CBin + cib,  tap = kh * Kw + kw          (a = kh, b = kw)
+  //   DGRAD: kb = ti * CBout + cob,  ti over the phase's valid taps (a, b)
+  //   WGRAD: kb = pos * NB + nbk,    pos = ho * Wo + wo          (a = ho, b = wo)
+  FastDiv div_inner, div_b;
+  if constexpr (OP == OP_FWD) { div_inner.init(cbin); div_b.init(p.k_w); }
+  else if constexpr (OP == OP_DGRAD) { div_inner.init(cbout); div_b.init(nkw > 0 ? nkw : 1); }
+  else { div_inner.init(p.nb); div_b.init(p.wo); }
+  uint32_t kb = static_cast<uint32_t>(kb_begin + kbl);
+  // per-thread offsets of the spatial gather: the source position of a tap
+  // (a, b) is (sp_y + a * st_y, sp_x + b * st_x)
+  int sp_y = 0, sp_x = 0, st_y = 1, st_x = 1;
+  if constexpr (OP == OP_FWD) {
+    sp_y = col_y * p.sh - p.ph; sp_x = col_x * p.sw - p.pw;
+  } else if constexpr (OP == OP_DGRAD) {
+    // dY row of the tap: (col_y + ph - kh) / sh with kh = kh0 + sh * a, an
+    // exact division by construction of the phase
+    sp_y = (col_y + p.ph - kh0) / p.sh; sp_x = (col_x + p.pw - kw0) / p.sw;
+    st_y = -1; st_x = -1;
+  } else {
+    sp_y = col_kh - p.ph; sp_x = col_kw - p.pw; st_y = p.sh; st_x = p.sw;
+  }
 
-  // Locate the quantized block of this thread's slot at the walk's current
-  // k-block; false in the zero padding (or outside the GEMM).
-  auto locate = [&](int64_t& blk) -> bool {
-    if (!in_range || kw.kb >= kb_end) return false;
+  // The quantized block of this thread's slot at k-block kb, and whether it
+  // exists (false in the zero padding or outside the GEMM).  Straight-line
+  // 32-bit arithmetic: indices past the tensor are computed but never used.
+  auto locate = [&](uint32_t& blk) -> bool {
+    const uint32_t outer = div_inner.div(kb);
+    const uint32_t inner = kb - outer * div_inner.d;
+    const uint32_t a = div_b.div(outer);
+    const uint32_t b = outer - a * div_b.d;
+    const int y = sp_y + static_cast<int>(a) * st_y, x = sp_x + static_cast<int>(b) * st_x;
+    uint32_t ba, bb;
+    bool inb;
     if constexpr (OP == OP_FWD) {
-      const int kh = kw.a, kwi = kw.b, cib = kw.inner;
-      if (is_a) {
-        blk = (static_cast<int64_t>(kh * p.k_w + kwi) * cbout + gblk) * cbin + cib;
-        return true;
-      }
-      const int hh = col_y * p.sh + kh - p.ph, ww = col_x * p.sw + kwi - p.pw;
-      if (hh < 0 || hh >= p.h || ww < 0 || ww >= p.w) return false;
-      blk = ((static_cast<int64_t>(hh) * p.w + ww) * cbin + cib) * p.nb + col_nb;
-      return true;
+      ba = ((a * p.k_w + b) * cbout + gblk) * cbin + inner;
+      inb = static_cast<uint32_t>(y) < static_cast<uint32_t>(p.h) && static_cast<uint32_t>(x) < static_cast<uint32_t>(p.w);
+      bb = ((static_cast<uint32_t>(y) * p.w + x) * cbin + inner) * p.nb + col_nb;
     } else if constexpr (OP == OP_DGRAD) {
-      const int kh = kh0 + p.sh * kw.a, kwi = kw0 + p.sw * kw.b, cob = kw.inner;
-      if (is_a) {
-        blk = (static_cast<int64_t>(kh * p.k_w + kwi) * cbout + cob) * cbin + gblk;
-        return true;
-      }
-      const int th = col_y + p.ph - kh, tw = col_x + p.pw - kwi;  // divisible by the strides
-      if (th < 0 || tw < 0) return false;
-      const int ho = th / p.sh, wo = tw / p.sw;
-      if (ho >= p.ho || wo >= p.wo) return false;
-      blk = ((static_cast<int64_t>(ho) * p.wo + wo) * cbout + cob) * p.nb + col_nb;
-      return true;
+      const uint32_t kh = kh0 + p.sh * a, kwi = kw0 + p.sw * b;
+      ba = ((kh * p.k_w + kwi) * cbout + inner) * cbin + gblk;
+      inb = static_cast<uint32_t>(y) < static_cast<uint32_t>(p.ho) && static_cast<uint32_t>(x) < static_cast<uint32_t>(p.wo);
+      bb = ((static_cast<uint32_t>(y) * p.wo + x) * cbout + inner) * p.nb + col_nb;
     } else {
-      const int ho = kw.a, wo = kw.b, nbk = kw.inner;
-      if (is_a) {
-        blk = ((static_cast<int64_t>(ho) * p.wo + wo) * cbout + gblk) * p.nb + nbk;
-        return true;
-      }
-      const int hh = ho * p.sh + col_kh - p.ph, ww = wo * p.sw + col_kw - p.pw;
-      if (hh < 0 || hh >= p.h || ww < 0 || ww >= p.w) return false;
-      blk = ((static_cast<int64_t>(hh) * p.w + ww) * cbin + col_cib) * p.nb + nbk;
-      return true;
+      ba = ((a * p.wo + b) * cbout + gblk) * p.nb + inner;
+      inb = static_cast<uint32_t>(y) < static_cast<uint32_t>(p.h) && static_cast<uint32_t>(x) < static_cast<uint32_t>(p.w);
+      bb = ((static_cast<uint32_t>(y) * p.w + x) * cbin + col_cib) * p.nb + inner;
     }
+    blk = is_a ? ba : bb;
+    return in_range && kb < static_cast<uint32_t>(kb_end) && (is_a || inb);
   };
 
   // A lines are block rows for FWD (co rows, ci along K) and WGRAD (co rows,
@@ -409,12 +405,13 @@ __global__ __launch_bounds__(WAVES * 64) void k_conv(const ConvParams p) {
   // two K steps before its decode, so their latency hides behind two rounds
   // of MFMAs.
   RawBlock<FMT> raw0, raw1;
+  const uint8_t* my_codes = is_a ? p.a_codes : p.b_codes;
+  const uint8_t* my_scales = is_a ? p.a_scales : p.b_scales;
   auto fetch = [&](RawBlock<FMT>& raw) {
-    int64_t blk = 0;
+    uint32_t blk = 0;
     const bool ok = locate(blk);
-    if (is_a) raw.load(p.a_codes, p.a_scales, blk, ok);
-    else raw.load(p.b_codes, p.b_scales, blk, ok);
-    kw.advance(KB, n_inner, n_b);
+    raw.load(my_codes, my_scales, blk, ok);
+    kb += KB;
   };
 
   f32x16 acc[RM][RN];
@@ -426,82 +423,113 @@ __global__ __launch_bounds__(WAVES * 64) void k_conv(const ConvParams p) {
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
   // per-lane LDS offsets of the MFMA fragments (row / column lane%32 of each
-  // 32-wide sub-tile; the two K halves of a 16-wide step are 8 apart)
+  // 32-wide sub-tile; the two K halves of a 16-wide slice are 8 apart)
   int a_off[RM], b_off[RN];
 #pragma unroll
   for (int i = 0; i < RM; ++i) a_off[i] = Lds<KB>::line(wm * WTM + i * 32 + (lane & 31)) + (lane >> 5) * 8;
 #pragma unroll
   for (int j = 0; j < RN; ++j) b_off[j] = Lds<KB>::line(MT + wn * WTN + j * 32 + (lane & 31)) + (lane >> 5) * 8;
 
-  // One K step: the MFMAs on stage `buf`, with the staging units of the next
-  // block (`nxt`, into stage buf^1) spread between them in program order, so
-  // that their VALU and LDS-write work issues while the matrix pipe is busy.
+  // One K step on stage `buf` is NK slices of 16 K values.  Fragments are
+  // double-buffered in registers: the LDS reads of slice k+1 are issued
+  // before the MFMAs of slice k.  The staging units of the next block
+  // (`nxt`, into stage buf^1) are spread between the MFMAs of slices
+  // 0..NK-2; then the workgroup barrier, after which the first slice of stage
+  // buf^1 is read while the last slice's MFMAs run.  So the only LDS latency
+  // left exposed per step is the barrier itself.
   // An MFMA must never sit inside a branch that diverges within a wave (the
   // wave would execute both sides).  When the A/B staging split falls on wave
   // boundaries (ABLK a multiple of 64) the branch on is_a is wave-uniform and
   // each side carries the MFMA sequence with its own staging units;
   // otherwise one MFMA sequence carries both kinds of units, predicated.
-  constexpr int NMF = NK * RM * RN;
+  // MFMAs that carry staging units: the first three quarters of slices
+  // 0..NK-2, so that the LDS writes have landed when the barrier comes
+  constexpr int NMF = ((NK - 1) * RM * RN * 3 + 3) / 4;
   using StA = Stager<FMT, A_ROWS, LS>;
   using StB = Stager<FMT, B_ROWS, LS>;
   typedef __attribute__((__vector_size__(8 * sizeof(uint16_t)))) uint16_t u16x8;
-  // all fragments of the step are read first (one LDS wait), then the MFMAs
-  auto mma_seq = [&](int buf, auto&& after) {
-    const uint16_t* base = lds[buf];
-    u16x8 fa[NK][RM], fb[NK][RN];
+  u16x8 fa0[RM], fb0[RN], fa1[RM], fb1[RN];
+  auto read_slice = [&](int buf, int kk, u16x8 (&fa)[RM], u16x8 (&fb)[RN]) {
+    const uint16_t* base = lds[buf] + kk * 16;
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
+    for (int i = 0; i < RM; ++i) fa[i] = *reinterpret_cast<const u16x8*>(base + a_off[i]);
 #pragma unroll
-      for (int i = 0; i < RM; ++i) fa[kk][i] = *reinterpret_cast<const u16x8*>(base + a_off[i] + kk * 16);
-#pragma unroll
-      for (int j = 0; j < RN; ++j) fb[kk][j] = *reinterpret_cast<const u16x8*>(base + b_off[j] + kk * 16);
-    }
-#pragma unroll
-    for (int kk = 0; kk < NK; ++kk)
-#pragma unroll
-      for (int i = 0; i < RM; ++i)
-#pragma unroll
-        for (int j = 0; j < RN; ++j) {
-          acc[i][j] = mfma32<F16>(reinterpret_cast<const uint16_t*>(&fa[kk][i]),
-                                  reinterpret_cast<const uint16_t*>(&fb[kk][j]), acc[i][j]);
-          after((kk * RM + i) * RN + j);
-        }
+    for (int j = 0; j < RN; ++j) fb[j] = *reinterpret_cast<const u16x8*>(base + b_off[j]);
   };
-  // staging units due after MFMA m: unit u of NU follows MFMA
-  // ceil((u+1) * NMF / NU) - 1 (several per MFMA when NU > NMF)
+  // staging units due after MFMA m (m < NMF): unit u of NU follows MFMA
+  // ceil((u+1) * NMF / NU) - 1 (several per MFMA when NU > NMF).  Each MFMA
+  // with the work placed after it is closed by a scheduling barrier, so the
+  // compiler keeps this interleave instead of clumping the VALU work.
   auto units_after = [&](auto& st, const RawBlock<FMT>& nxt, int m, bool on) {
     using St = std::remove_reference_t<decltype(st)>;
     [&]<int... U>(std::integer_sequence<int, U...>) {
       ((((U + 1) * NMF + St::UNITS - 1) / St::UNITS - 1 == m && on ? (st.template unit<U>(nxt), 0) : 0), ...);
     }(std::make_integer_sequence<int, St::UNITS>());
   };
-  auto run_step = [&](int buf, const RawBlock<FMT>& nxt, bool have_next) {
+  // slice KK of a step whose slice 0 sits in fragment set PAR
+  auto slice = [&]<int PAR, int KK>(int buf, auto&& after) {
+    constexpr int CUR = (PAR + KK) & 1;
+    auto& fa_c = CUR ? fa1 : fa0;
+    auto& fb_c = CUR ? fb1 : fb0;
+    auto& fa_n = CUR ? fa0 : fa1;
+    auto& fb_n = CUR ? fb0 : fb1;
+    if constexpr (KK + 1 < NK) {
+      read_slice(buf, KK + 1, fa_n, fb_n);
+    } else {
+      __syncthreads();  // stage buf^1 complete; stage buf no longer read
+      read_slice(buf ^ 1, 0, fa_n, fb_n);
+    }
+#pragma unroll
+    for (int i = 0; i < RM; ++i)
+#pragma unroll
+      for (int j = 0; j < RN; ++j) {
+        acc[i][j] = mfma32<F16>(reinterpret_cast<const uint16_t*>(&fa_c[i]),
+                                reinterpret_cast<const uint16_t*>(&fb_c[j]), acc[i][j]);
+        if constexpr (KK + 1 < NK) after((KK * RM + i) * RN + j);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  };
+  auto mma_step = [&]<int PAR>(int buf, auto&& after) {
+    [&]<int... KK>(std::integer_sequence<int, KK...>) {
+      (slice.template operator()<PAR, KK>(buf, after), ...);
+    }(std::make_integer_sequence<int, NK>());
+  };
+  // One step: MFMAs on stage buf; stage `nxt` into buf^1; the global loads
+  // of the step after next go into `fut` right after the first MFMA.
+  auto run_step = [&]<int PAR>(int buf, const RawBlock<FMT>& nxt, RawBlock<FMT>& fut) {
     uint16_t* lo = &lds[buf ^ 1][lo_off];
     uint16_t* hi = &lds[buf ^ 1][hi_off];
     if constexpr (ABLK % 64 == 0) {
       if (is_a) {
         StA sa(nxt, lo, hi);
-        mma_seq(buf, [&](int m) { units_after(sa, nxt, m, have_next); });
+        mma_step.template operator()<PAR>(buf, [&](int m) {
+          if (m == 0) fetch(fut);
+          units_after(sa, nxt, m, true);
+        });
       } else {
         StB sb(nxt, lo, hi);
-        mma_seq(buf, [&](int m) { units_after(sb, nxt, m, have_next); });
+        mma_step.template operator()<PAR>(buf, [&](int m) {
+          if (m == 0) fetch(fut);
+          units_after(sb, nxt, m, true);
+        });
       }
     } else {
       StA sa(nxt, lo, hi);
       StB sb(nxt, lo, hi);
-      const bool do_a = have_next && is_a, do_b = have_next && !is_a;
-      mma_seq(buf, [&](int m) {
-        units_after(sa, nxt, m, do_a);
-        units_after(sb, nxt, m, do_b);
+      mma_step.template operator()<PAR>(buf, [&](int m) {
+        if (m == 0) fetch(fut);
+        units_after(sa, nxt, m, is_a);
+        units_after(sb, nxt, m, !is_a);
       });
     }
-    __syncthreads();
   };
 
+  // Steps past the end fetch padding (mask 0) and stage into the stage that
+  // is never read again: no branch around a fetch or a staging unit.
   const int nsteps = (kb_end - kb_begin + KB - 1) / KB;
   if (nsteps > 0) {
     fetch(raw0);
-    if (nsteps > 1) fetch(raw1);
+    fetch(raw1);
     {
       // first block: stage it straight away
       if (is_a) {
@@ -515,14 +543,14 @@ __global__ __launch_bounds__(WAVES * 64) void k_conv(const ConvParams p) {
       }
     }
     __syncthreads();
+    read_slice(0, 0, fa0, fb0);
+    constexpr int PAR1 = NK & 1;  // fragment set of slice 0 in odd steps
     for (int s = 0; s < nsteps; s += 2) {
       // step s reads stage 0; raw1 holds step s+1, raw0 is free
-      if (s + 2 < nsteps) fetch(raw0);
-      run_step(0, raw1, s + 1 < nsteps);
+      run_step.template operator()<0>(0, raw1, raw0);
       if (s + 1 >= nsteps) break;
       // step s+1 reads stage 1; raw0 holds step s+2, raw1 is free
-      if (s + 3 < nsteps) fetch(raw1);
-      run_step(1, raw0, s + 2 < nsteps);
+      run_step.template operator()<PAR1>(1, raw0, raw1);
     }
   }
 
