@@ -242,133 +242,131 @@ __device__ __forceinline__ f32x16 mfma32(const uint16_t* pa, const uint16_t* pb,
                                                    *reinterpret_cast<const bf16x8*>(pb), c, 0, 0, 0);
 }
 
-template <int OP, int FMT, int MT, int NT, int WM, int WAVES, int KB>
-__global__ __launch_bounds__(WAVES * 64) void k_conv(const ConvParams p) {
-  constexpr int WN = WAVES / WM;
-  constexpr int WTM = MT / WM, WTN = NT / WN;
-  constexpr int RM = WTM / 32, RN = WTN / 32;
-  constexpr int ABLK = (MT / 8) * KB, BBLK = (NT / 8) * KB;
-  constexpr int NK = KB / 2;  // 16-wide MFMA K slices per stage
-  constexpr int LS = Lds<KB>::LS;
-  static_assert(KB % 2 == 0, "a stage is a whole number of 16-wide K slices");
-  constexpr bool F16 = OperandType<FMT>::F16;
-  static_assert(ABLK + BBLK <= WAVES * 64, "one block per thread per stage");
-  static_assert(RM >= 1 && RN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile of 32x32 MFMAs");
-
-  // two stages of MT + NT lines, plus 8 lines that threads without a block
-  // write their zeros into (keeps the staging code branch-free)
-  constexpr int STAGE = (MT + NT + 8) * LS;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][STAGE];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave % WM, wn = wave / WM;
-  // Workgroups are dealt round-robin to the 8 XCDs (each with its own L2) in
-  // launch order.  Renumber them so that every XCD works on one contiguous
-  // range of tiles: neighbouring output tiles share most of their quantized
-  // input blocks (the im2col halo, and the whole weight tile).
-  int bx, by, bz;
-  {
-    const int total = gridDim.x * gridDim.y * gridDim.z;
-    const int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
-    const int q = total >> 3, r = total & 7, xcd = lin & 7, idx = lin >> 3;
-    const int nl = xcd < r ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
-    bx = nl % gridDim.x;
-    const int t = nl / gridDim.x;
-    by = t % gridDim.y;
-    bz = t / gridDim.y;
-  }
-  const int rb0 = by * (MT / 8);
-  const int cb0 = bx * (NT / 8);
-  const int cbin = p.c_in >> 3, cbout = p.c_out >> 3;
-
-  // ---- per-launch-z context: data-gradient phase or weight-gradient split
-  int phh = 0, phw = 0, kh0 = 0, kw0 = 0, nkh = p.k_h, nkw = p.k_w, hp = 0, wp = 0;
-  int kb_begin = 0, kb_end = p.kb_total;
-  if constexpr (OP == OP_DGRAD) {
-    // output pixels (h, w) with h = phh + sh*h', w = phw + sw*w' receive the
-    // taps kh = (phh + ph) mod sh (+ sh, ...), kw likewise
-    phh = bz / p.sw;
-    phw = bz - phh * p.sw;
-    kh0 = (phh + p.ph) % p.sh;
-    kw0 = (phw + p.pw) % p.sw;
-    nkh = kh0 < p.k_h ? (p.k_h - kh0 + p.sh - 1) / p.sh : 0;
-    nkw = kw0 < p.k_w ? (p.k_w - kw0 + p.sw - 1) / p.sw : 0;
-    hp = (p.h - phh + p.sh - 1) / p.sh;
-    wp = (p.w - phw + p.sw - 1) / p.sw;
-    if (cb0 >= hp * wp * p.nb) return;
-    kb_end = nkh * nkw * cbout;
-  } else if constexpr (OP == OP_WGRAD) {
-    kb_begin = bz * p.ks_split * KB;
-    kb_end = min(p.kb_total, kb_begin + p.ks_split * KB);
-    if (kb_begin > kb_end) kb_begin = kb_end;
-  }
-  const int ncb_launch = (OP == OP_DGRAD) ? hp * wp * p.nb : p.ncb;
-
-  // ---- the block this thread stages every step
-  const bool is_a = tid < ABLK;
-  const int t_local = is_a ? tid : tid - ABLK;
-  const bool active = tid < ABLK + BBLK;
-  const int lblk = t_local / KB;  // line block (8 lines) within the tile
-  const int line = !active ? MT + NT : is_a ? lblk * 8 : MT + lblk * 8;
-  const int kbl = active ? t_local - lblk * KB : 0;
-  const int gblk = (is_a ? rb0 : cb0) + lblk;
-  const bool in_range = active && (is_a ? (gblk < (p.M >> 3)) : (gblk < ncb_launch));
-  // swizzled addresses of the block's two line halves (see lds_line)
-  const int rot = (line >> 2) & 4;
-  const int lo_off = (line + rot) * LS + kbl * 8;
-  const int hi_off = (line + (rot ^ 4)) * LS + kbl * 8;
-
-  // Column-block geometry fixed over the K loop.
-  int col_y = 0, col_x = 0, col_nb = 0;   // FWD: output (ho, wo); DGRAD: input pixel (h, w)
-  int col_kh = 0, col_kw = 0, col_cib = 0; // WGRAD: tap and channel block
-  if (!is_a && in_range) {
-    if constexpr (OP == OP_FWD) {
-      const int pos = gblk / p.nb;
-      col_nb = gblk - pos * p.nb;
-      col_y = pos / p.wo;
-      col_x = pos - col_y * p.wo;
-    } else if constexpr (OP == OP_DGRAD) {
-      const int pos = gblk / p.nb;
-      col_nb = gblk - pos * p.nb;
-      const int hq = pos / wp;
-      col_y = phh + p.sh * hq;
-      col_x = phw + p.sw * (pos - hq * wp);
-    } else {
-      const int tap = gblk / cbin;
-      col_cib = gblk - tap * cbin;
-      col_kh = tap / p.k_w;
-      col_kw = tap - col_kh * p.k_w;
-    }
-  }
-
-  // The k-blocks one thread stages are kb, kb+KB, ...; each is split as
-  //   FWD  : kb = tap * CBin + cib,  tap = kh * Kw + kw          (a = kh, b = kw)
-  //   DGRAD: kb = ti * CBout + cob,  ti over the phase's valid taps (a, b)
-  //   WGRAD: kb = pos * NB + nbk,    pos = ho * Wo + wo          (a = ho, b = wo)
+// Per-workgroup context shared by the conv kernels: the tile this
+// workgroup computes, the data-gradient phase or weight-gradient split of
+// the launch's z index, and the quantized block one thread stages per K
+// step (thread t < ABLK stages A blocks, the next BBLK threads B blocks).
+template <int OP, int MT, int NT, int KB>
+struct TileCtx {
+  static constexpr int ABLK = (MT / 8) * KB, BBLK = (NT / 8) * KB;
+  int bx, by, bz, rb0, cb0, cbin, cbout;
+  int phh, phw, kh0, kw0, nkh, nkw, hp, wp;
+  int kb_begin, kb_end, ncb_launch;
+  bool is_a, active, in_range;
+  int lblk, kbl, gblk;
+  int col_nb, col_cib;
+  int sp_y, sp_x, st_y, st_x;
   FastDiv div_inner, div_b;
-  if constexpr (OP == OP_FWD) { div_inner.init(cbin); div_b.init(p.k_w); }
-  else if constexpr (OP == OP_DGRAD) { div_inner.init(cbout); div_b.init(nkw > 0 ? nkw : 1); }
-  else { div_inner.init(p.nb); div_b.init(p.wo); }
-  uint32_t kb = static_cast<uint32_t>(kb_begin + kbl);
-  // per-thread offsets of the spatial gather: the source position of a tap
-  // (a, b) is (sp_y + a * st_y, sp_x + b * st_x)
-  int sp_y = 0, sp_x = 0, st_y = 1, st_x = 1;
-  if constexpr (OP == OP_FWD) {
-    sp_y = col_y * p.sh - p.ph; sp_x = col_x * p.sw - p.pw;
-  } else if constexpr (OP == OP_DGRAD) {
-    // dY row of the tap: (col_y + ph - kh) / sh with kh = kh0 + sh * a, an
-    // exact division by construction of the phase
-    sp_y = (col_y + p.ph - kh0) / p.sh; sp_x = (col_x + p.pw - kw0) / p.sw;
-    st_y = -1; st_x = -1;
-  } else {
-    sp_y = col_kh - p.ph; sp_x = col_kw - p.pw; st_y = p.sh; st_x = p.sw;
+  uint32_t kb;  // the k-block this thread stages next
+
+  // false: the workgroup has no output (a data-gradient phase smaller than
+  // the grid)
+  __device__ __forceinline__ bool init(const ConvParams& p, int tid) {
+    // Workgroups are dealt round-robin to the 8 XCDs (each with its own L2)
+    // in launch order.  Renumber them so that every XCD works on one
+    // contiguous range of tiles: neighbouring output tiles share most of
+    // their quantized input blocks (the im2col halo, and the weight tile).
+    {
+      const int total = gridDim.x * gridDim.y * gridDim.z;
+      const int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+      const int q = total >> 3, r = total & 7, xcd = lin & 7, idx = lin >> 3;
+      const int nl = xcd < r ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+      bx = nl % gridDim.x;
+      const int t = nl / gridDim.x;
+      by = t % gridDim.y;
+      bz = t / gridDim.y;
+    }
+    rb0 = by * (MT / 8);
+    cb0 = bx * (NT / 8);
+    cbin = p.c_in >> 3;
+    cbout = p.c_out >> 3;
+
+    // per-launch-z context: data-gradient phase or weight-gradient split
+    phh = 0; phw = 0; kh0 = 0; kw0 = 0; nkh = p.k_h; nkw = p.k_w; hp = 0; wp = 0;
+    kb_begin = 0;
+    kb_end = p.kb_total;
+    if constexpr (OP == OP_DGRAD) {
+      // output pixels (h, w) with h = phh + sh*h', w = phw + sw*w' receive
+      // the taps kh = (phh + ph) mod sh (+ sh, ...), kw likewise
+      phh = bz / p.sw;
+      phw = bz - phh * p.sw;
+      kh0 = (phh + p.ph) % p.sh;
+      kw0 = (phw + p.pw) % p.sw;
+      nkh = kh0 < p.k_h ? (p.k_h - kh0 + p.sh - 1) / p.sh : 0;
+      nkw = kw0 < p.k_w ? (p.k_w - kw0 + p.sw - 1) / p.sw : 0;
+      hp = (p.h - phh + p.sh - 1) / p.sh;
+      wp = (p.w - phw + p.sw - 1) / p.sw;
+      if (cb0 >= hp * wp * p.nb) return false;
+      kb_end = nkh * nkw * cbout;
+    } else if constexpr (OP == OP_WGRAD) {
+      kb_begin = bz * p.ks_split * KB;
+      kb_end = min(p.kb_total, kb_begin + p.ks_split * KB);
+      if (kb_begin > kb_end) kb_begin = kb_end;
+    }
+    ncb_launch = (OP == OP_DGRAD) ? hp * wp * p.nb : p.ncb;
+
+    // the block this thread stages every step
+    is_a = tid < ABLK;
+    const int t_local = is_a ? tid : tid - ABLK;
+    active = tid < ABLK + BBLK;
+    lblk = t_local / KB;  // line block (8 lines) within the tile
+    kbl = active ? t_local - lblk * KB : 0;
+    gblk = (is_a ? rb0 : cb0) + lblk;
+    in_range = active && (is_a ? (gblk < (p.M >> 3)) : (gblk < ncb_launch));
+
+    // column-block geometry fixed over the K loop
+    int col_y = 0, col_x = 0;            // FWD: output (ho, wo); DGRAD: input pixel (h, w)
+    int col_kh = 0, col_kw = 0;          // WGRAD: tap
+    col_nb = 0;
+    col_cib = 0;
+    if (!is_a && in_range) {
+      if constexpr (OP == OP_FWD) {
+        const int pos = gblk / p.nb;
+        col_nb = gblk - pos * p.nb;
+        col_y = pos / p.wo;
+        col_x = pos - col_y * p.wo;
+      } else if constexpr (OP == OP_DGRAD) {
+        const int pos = gblk / p.nb;
+        col_nb = gblk - pos * p.nb;
+        const int hq = pos / wp;
+        col_y = phh + p.sh * hq;
+        col_x = phw + p.sw * (pos - hq * wp);
+      } else {
+        const int tap = gblk / cbin;
+        col_cib = gblk - tap * cbin;
+        col_kh = tap / p.k_w;
+        col_kw = tap - col_kh * p.k_w;
+      }
+    }
+
+    // The k-blocks one thread stages are kb, kb+KB, ...; each is split as
+    //   FWD  : kb = tap * CBin + cib,  tap = kh * Kw + kw          (a = kh, b = kw)
+    //   DGRAD: kb = ti * CBout + cob,  ti over the phase's valid taps (a, b)
+    //   WGRAD: kb = pos * NB + nbk,    pos = ho * Wo + wo          (a = ho, b = wo)
+    if constexpr (OP == OP_FWD) { div_inner.init(cbin); div_b.init(p.k_w); }
+    else if constexpr (OP == OP_DGRAD) { div_inner.init(cbout); div_b.init(nkw > 0 ? nkw : 1); }
+    else { div_inner.init(p.nb); div_b.init(p.wo); }
+    kb = static_cast<uint32_t>(kb_begin + kbl);
+    // offsets of the spatial gather: the source position of a tap (a, b) is
+    // (sp_y + a * st_y, sp_x + b * st_x)
+    sp_y = 0; sp_x = 0; st_y = 1; st_x = 1;
+    if constexpr (OP == OP_FWD) {
+      sp_y = col_y * p.sh - p.ph; sp_x = col_x * p.sw - p.pw;
+    } else if constexpr (OP == OP_DGRAD) {
+      // dY row of the tap: (col_y + ph - kh) / sh with kh = kh0 + sh * a,
+      // an exact division by construction of the phase
+      sp_y = (col_y + p.ph - kh0) / p.sh; sp_x = (col_x + p.pw - kw0) / p.sw;
+      st_y = -1; st_x = -1;
+    } else {
+      sp_y = col_kh - p.ph; sp_x = col_kw - p.pw; st_y = p.sh; st_x = p.sw;
+    }
+    return true;
   }
 
   // The quantized block of this thread's slot at k-block kb, and whether it
   // exists (false in the zero padding or outside the GEMM).  Straight-line
   // 32-bit arithmetic: indices past the tensor are computed but never used.
-  auto locate = [&](uint32_t& blk) -> bool {
+  __device__ __forceinline__ bool locate(const ConvParams& p, uint32_t& blk) const {
     const uint32_t outer = div_inner.div(kb);
     const uint32_t inner = kb - outer * div_inner.d;
     const uint32_t a = div_b.div(outer);
@@ -392,7 +390,92 @@ __global__ __launch_bounds__(WAVES * 64) void k_conv(const ConvParams p) {
     }
     blk = is_a ? ba : bb;
     return in_range && kb < static_cast<uint32_t>(kb_end) && (is_a || inb);
-  };
+  }
+};
+
+// Epilogue: D lane layout of the 32x32 MFMA: column lane%32, rows
+// 8*(v/4) + 4*(lane/32) + v%4 for accumulator element v.  fwd / dgrad write
+// the scaled outputs in place; wgrad writes unscaled split partials.
+template <int OP, int MT, int NT, int KB, int WTM, int WTN, int RM, int RN>
+__device__ __forceinline__ void store_tile(const ConvParams& p, const TileCtx<OP, MT, NT, KB>& t,
+                                           const f32x16 (&acc)[RM][RN], int lane, int wm, int wn) {
+  float scale = 1.0f;
+  if constexpr (OP != OP_WGRAD) scale = (*p.a_t) * (*p.b_t);
+  int64_t row_stride;
+  if constexpr (OP == OP_WGRAD) row_stride = p.ncol;
+  else row_stride = p.n;
+
+#pragma unroll
+  for (int j = 0; j < RN; ++j) {
+    const int col = t.cb0 * 8 + wn * WTN + j * 32 + (lane & 31);  // column in the launch space
+    const int cbk = col >> 3, c = col & 7;
+    if (cbk >= t.ncb_launch) continue;
+    int64_t colbase;
+    if constexpr (OP == OP_FWD) {
+      const int pos = cbk / p.nb, nbk = cbk - pos * p.nb;
+      colbase = static_cast<int64_t>(pos) * p.c_out * p.n + nbk * 8 + c;
+    } else if constexpr (OP == OP_DGRAD) {
+      const int pos = cbk / p.nb, nbk = cbk - pos * p.nb;
+      const int hq = pos / t.wp;
+      const int hh = t.phh + p.sh * hq, ww = t.phw + p.sw * (pos - hq * t.wp);
+      colbase = (static_cast<int64_t>(hh) * p.w + ww) * p.c_in * p.n + nbk * 8 + c;
+    } else {
+      colbase = static_cast<int64_t>(t.bz) * p.M * p.ncol + col;
+    }
+    float* out = p.out + colbase;
+    const int row0 = t.rb0 * 8 + wm * WTM + 4 * (lane >> 5);
+    if (t.rb0 * 8 + wm * WTM + WTM <= p.M) {
+      // the wave's rows all exist (uniform test): no per-element branch
+#pragma unroll
+      for (int i = 0; i < RM; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          out[static_cast<int64_t>(row0 + i * 32 + 8 * (v >> 2) + (v & 3)) * row_stride] = acc[i][j][v] * scale;
+    } else {
+#pragma unroll
+      for (int i = 0; i < RM; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = row0 + i * 32 + 8 * (v >> 2) + (v & 3);
+          if (row < p.M) out[static_cast<int64_t>(row) * row_stride] = acc[i][j][v] * scale;
+        }
+    }
+  }
+}
+
+template <int OP, int FMT, int MT, int NT, int WM, int WAVES, int KB>
+__global__ __launch_bounds__(WAVES * 64) void k_conv(const ConvParams p) {
+  constexpr int WN = WAVES / WM;
+  constexpr int WTM = MT / WM, WTN = NT / WN;
+  constexpr int RM = WTM / 32, RN = WTN / 32;
+  constexpr int ABLK = (MT / 8) * KB, BBLK = (NT / 8) * KB;
+  constexpr int NK = KB / 2;  // 16-wide MFMA K slices per stage
+  constexpr int LS = Lds<KB>::LS;
+  static_assert(KB % 2 == 0, "a stage is a whole number of 16-wide K slices");
+  constexpr bool F16 = OperandType<FMT>::F16;
+  static_assert(ABLK + BBLK <= WAVES * 64, "one block per thread per stage");
+  static_assert(RM >= 1 && RN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile of 32x32 MFMAs");
+
+  // NSTAGE stages of MT + NT lines, plus 8 lines that threads without a
+  // block write their zeros into (keeps the staging code branch-free).  The
+  // 256x256 tile runs one workgroup per CU and takes three stages; the
+  // smaller tiles keep two, so that two workgroups fit on a CU.
+  constexpr int NSTAGE = (MT == 256) ? 3 : 2;
+  constexpr int STAGE = (MT + NT + 8) * LS;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[NSTAGE][STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % WM, wn = wave / WM;
+  TileCtx<OP, MT, NT, KB> t;
+  if (!t.init(p, tid)) return;
+  const bool is_a = t.is_a;
+  const int line = !t.active ? MT + NT : is_a ? t.lblk * 8 : MT + t.lblk * 8;
+  // swizzled addresses of the block's two line halves (see Lds)
+  const int rot = (line >> 2) & 4;
+  const int lo_off = (line + rot) * LS + t.kbl * 8;
+  const int hi_off = (line + (rot ^ 4)) * LS + t.kbl * 8;
+  const int kb_begin = t.kb_begin, kb_end = t.kb_end;
 
   // A lines are block rows for FWD (co rows, ci along K) and WGRAD (co rows,
   // n along K), block columns for DGRAD (ci lines, co along K).  B lines are
@@ -409,9 +492,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_conv(const ConvParams p) {
   const uint8_t* my_scales = is_a ? p.a_scales : p.b_scales;
   auto fetch = [&](RawBlock<FMT>& raw) {
     uint32_t blk = 0;
-    const bool ok = locate(blk);
+    const bool ok = t.locate(p, blk);
     raw.load(my_codes, my_scales, blk, ok);
-    kb += KB;
+    t.kb += KB;
   };
 
   f32x16 acc[RM][RN];
@@ -430,27 +513,34 @@ __global__ __launch_bounds__(WAVES * 64) void k_conv(const ConvParams p) {
 #pragma unroll
   for (int j = 0; j < RN; ++j) b_off[j] = Lds<KB>::line(MT + wn * WTN + j * 32 + (lane & 31)) + (lane >> 5) * 8;
 
-  // One K step on stage `buf` is NK slices of 16 K values.  Fragments are
+  // One K step on stage `cur` is NK slices of 16 K values.  Fragments are
   // double-buffered in registers: the LDS reads of slice k+1 are issued
-  // before the MFMAs of slice k.  The staging units of the next block
-  // (`nxt`, into stage buf^1) are spread between the MFMAs of slices
-  // 0..NK-2; then the workgroup barrier, after which the first slice of stage
-  // buf^1 is read while the last slice's MFMAs run.  So the only LDS latency
-  // left exposed per step is the barrier itself.
+  // before the MFMAs of slice k.  The staging units of a future block (`nxt`,
+  // into stage `dst`) are spread between the MFMAs.
+  //   2 stages: dst is the next step's stage; the staging units sit in
+  //     slices 0..NK-2, then the workgroup barrier, after which the first
+  //     slice of the next stage is read while the last slice's MFMAs run.
+  //   3 stages: dst is the stage two steps ahead, so the next stage is
+  //     already complete: its first slice is read during the last slice and
+  //     the barrier closes the step; the staging units spread over (nearly)
+  //     all MFMAs of the step, keeping the VALU work per MFMA within what
+  //     one wave hides behind a 32-cycle MFMA.
   // An MFMA must never sit inside a branch that diverges within a wave (the
   // wave would execute both sides).  When the A/B staging split falls on wave
   // boundaries (ABLK a multiple of 64) the branch on is_a is wave-uniform and
   // each side carries the MFMA sequence with its own staging units;
   // otherwise one MFMA sequence carries both kinds of units, predicated.
-  // MFMAs that carry staging units: the first three quarters of slices
-  // 0..NK-2, so that the LDS writes have landed when the barrier comes
-  constexpr int NMF = ((NK - 1) * RM * RN * 3 + 3) / 4;
+  constexpr int NMF_ALL = (NSTAGE == 3 ? NK : NK - 1) * RM * RN;
+  // MFMAs that carry staging units: the first 7/8 (3 stages) or 3/4 (2
+  // stages) of those, so that the LDS writes have landed when the barrier
+  // comes
+  constexpr int NMF = NSTAGE == 3 ? (NMF_ALL * 7 + 7) / 8 : (NMF_ALL * 3 + 3) / 4;
   using StA = Stager<FMT, A_ROWS, LS>;
   using StB = Stager<FMT, B_ROWS, LS>;
   typedef __attribute__((__vector_size__(8 * sizeof(uint16_t)))) uint16_t u16x8;
   u16x8 fa0[RM], fb0[RN], fa1[RM], fb1[RN];
-  auto read_slice = [&](int buf, int kk, u16x8 (&fa)[RM], u16x8 (&fb)[RN]) {
-    const uint16_t* base = lds[buf] + kk * 16;
+  auto read_slice = [&](int stage, int kk, u16x8 (&fa)[RM], u16x8 (&fb)[RN]) {
+    const uint16_t* base = lds[stage] + kk * 16;
 #pragma unroll
     for (int i = 0; i < RM; ++i) fa[i] = *reinterpret_cast<const u16x8*>(base + a_off[i]);
 #pragma unroll
@@ -466,18 +556,20 @@ __global__ __launch_bounds__(WAVES * 64) void k_conv(const ConvParams p) {
       ((((U + 1) * NMF + St::UNITS - 1) / St::UNITS - 1 == m && on ? (st.template unit<U>(nxt), 0) : 0), ...);
     }(std::make_integer_sequence<int, St::UNITS>());
   };
-  // slice KK of a step whose slice 0 sits in fragment set PAR
-  auto slice = [&]<int PAR, int KK>(int buf, auto&& after) {
+  // slice KK of a step on stage cur whose slice 0 sits in fragment set PAR;
+  // `nstage` is the stage of the next step
+  auto slice = [&]<int PAR, int KK>(int cur, int nstage, auto&& after) {
     constexpr int CUR = (PAR + KK) & 1;
     auto& fa_c = CUR ? fa1 : fa0;
     auto& fb_c = CUR ? fb1 : fb0;
     auto& fa_n = CUR ? fa0 : fa1;
     auto& fb_n = CUR ? fb0 : fb1;
+    constexpr bool CARRIES = NSTAGE == 3 || KK + 1 < NK;  // staging units in this slice
     if constexpr (KK + 1 < NK) {
-      read_slice(buf, KK + 1, fa_n, fb_n);
+      read_slice(cur, KK + 1, fa_n, fb_n);
     } else {
-      __syncthreads();  // stage buf^1 complete; stage buf no longer read
-      read_slice(buf ^ 1, 0, fa_n, fb_n);
+      if constexpr (NSTAGE == 2) __syncthreads();  // next stage complete; cur no longer read
+      read_slice(nstage, 0, fa_n, fb_n);
     }
 #pragma unroll
     for (int i = 0; i < RM; ++i)
@@ -485,30 +577,31 @@ __global__ __launch_bounds__(WAVES * 64) void k_conv(const ConvParams p) {
       for (int j = 0; j < RN; ++j) {
         acc[i][j] = mfma32<F16>(reinterpret_cast<const uint16_t*>(&fa_c[i]),
                                 reinterpret_cast<const uint16_t*>(&fb_c[j]), acc[i][j]);
-        if constexpr (KK + 1 < NK) after((KK * RM + i) * RN + j);
+        if constexpr (CARRIES) after((KK * RM + i) * RN + j);
         __builtin_amdgcn_sched_barrier(0);
       }
+    if constexpr (NSTAGE == 3 && KK + 1 == NK) __syncthreads();  // dst complete; cur free
   };
-  auto mma_step = [&]<int PAR>(int buf, auto&& after) {
+  auto mma_step = [&]<int PAR>(int cur, int nstage, auto&& after) {
     [&]<int... KK>(std::integer_sequence<int, KK...>) {
-      (slice.template operator()<PAR, KK>(buf, after), ...);
+      (slice.template operator()<PAR, KK>(cur, nstage, after), ...);
     }(std::make_integer_sequence<int, NK>());
   };
-  // One step: MFMAs on stage buf; stage `nxt` into buf^1; the global loads
-  // of the step after next go into `fut` right after the first MFMA.
-  auto run_step = [&]<int PAR>(int buf, const RawBlock<FMT>& nxt, RawBlock<FMT>& fut) {
-    uint16_t* lo = &lds[buf ^ 1][lo_off];
-    uint16_t* hi = &lds[buf ^ 1][hi_off];
+  // One step: MFMAs on stage cur; stage `nxt` into stage dst; the global
+  // loads of a later step go into `fut` right after the first MFMA.
+  auto run_step = [&]<int PAR>(int cur, int nstage, int dst, const RawBlock<FMT>& nxt, RawBlock<FMT>& fut) {
+    uint16_t* lo = &lds[dst][lo_off];
+    uint16_t* hi = &lds[dst][hi_off];
     if constexpr (ABLK % 64 == 0) {
       if (is_a) {
         StA sa(nxt, lo, hi);
-        mma_step.template operator()<PAR>(buf, [&](int m) {
+        mma_step.template operator()<PAR>(cur, nstage, [&](int m) {
           if (m == 0) fetch(fut);
           units_after(sa, nxt, m, true);
         });
       } else {
         StB sb(nxt, lo, hi);
-        mma_step.template operator()<PAR>(buf, [&](int m) {
+        mma_step.template operator()<PAR>(cur, nstage, [&](int m) {
           if (m == 0) fetch(fut);
           units_after(sb, nxt, m, true);
         });
@@ -516,77 +609,437 @@ __global__ __launch_bounds__(WAVES * 64) void k_conv(const ConvParams p) {
     } else {
       StA sa(nxt, lo, hi);
       StB sb(nxt, lo, hi);
-      mma_step.template operator()<PAR>(buf, [&](int m) {
+      mma_step.template operator()<PAR>(cur, nstage, [&](int m) {
         if (m == 0) fetch(fut);
         units_after(sa, nxt, m, is_a);
         units_after(sb, nxt, m, !is_a);
       });
     }
   };
+  auto stage_all = [&](const RawBlock<FMT>& raw, int stage) {
+    if (is_a) {
+      StA st(raw, &lds[stage][lo_off], &lds[stage][hi_off]);
+      [&]<int... U>(std::integer_sequence<int, U...>) { (st.template unit<U>(raw), ...); }(
+          std::make_integer_sequence<int, StA::UNITS>());
+    } else {
+      StB st(raw, &lds[stage][lo_off], &lds[stage][hi_off]);
+      [&]<int... U>(std::integer_sequence<int, U...>) { (st.template unit<U>(raw), ...); }(
+          std::make_integer_sequence<int, StB::UNITS>());
+    }
+  };
 
-  // Steps past the end fetch padding (mask 0) and stage into the stage that
+  // Steps past the end fetch padding (mask 0) and stage into a stage that
   // is never read again: no branch around a fetch or a staging unit.
   const int nsteps = (kb_end - kb_begin + KB - 1) / KB;
+  constexpr int PAR1 = NK & 1;  // fragment set of slice 0 in odd steps
   if (nsteps > 0) {
-    fetch(raw0);
-    fetch(raw1);
-    {
-      // first block: stage it straight away
-      if (is_a) {
-        StA st(raw0, &lds[0][lo_off], &lds[0][hi_off]);
-        [&]<int... U>(std::integer_sequence<int, U...>) { (st.template unit<U>(raw0), ...); }(
-            std::make_integer_sequence<int, StA::UNITS>());
-      } else {
-        StB st(raw0, &lds[0][lo_off], &lds[0][hi_off]);
-        [&]<int... U>(std::integer_sequence<int, U...>) { (st.template unit<U>(raw0), ...); }(
-            std::make_integer_sequence<int, StB::UNITS>());
+    if constexpr (NSTAGE == 2) {
+      fetch(raw0);
+      fetch(raw1);
+      stage_all(raw0, 0);
+      __syncthreads();
+      read_slice(0, 0, fa0, fb0);
+      for (int s = 0; s < nsteps; s += 2) {
+        // step s reads stage 0; raw1 holds step s+1, raw0 is free
+        run_step.template operator()<0>(0, 1, 1, raw1, raw0);
+        if (s + 1 >= nsteps) break;
+        // step s+1 reads stage 1; raw0 holds step s+2, raw1 is free
+        run_step.template operator()<PAR1>(1, 0, 0, raw0, raw1);
       }
-    }
-    __syncthreads();
-    read_slice(0, 0, fa0, fb0);
-    constexpr int PAR1 = NK & 1;  // fragment set of slice 0 in odd steps
-    for (int s = 0; s < nsteps; s += 2) {
-      // step s reads stage 0; raw1 holds step s+1, raw0 is free
-      run_step.template operator()<0>(0, raw1, raw0);
-      if (s + 1 >= nsteps) break;
-      // step s+1 reads stage 1; raw0 holds step s+2, raw1 is free
-      run_step.template operator()<PAR1>(1, raw0, raw1);
+    } else {
+      // step s computes stage s%3, stages step s+2 (held in raw[s%2]) into
+      // stage (s+2)%3 and fetches step s+3 into raw[(s+1)%2]
+      fetch(raw0);
+      fetch(raw1);
+      stage_all(raw0, 0);
+      stage_all(raw1, 1);
+      fetch(raw0);  // step 2
+      __syncthreads();
+      read_slice(0, 0, fa0, fb0);
+      int cur = 0;
+      for (int s = 0; s < nsteps; s += 2) {
+        const int c1 = cur == 2 ? 0 : cur + 1, c2 = c1 == 2 ? 0 : c1 + 1;
+        run_step.template operator()<0>(cur, c1, c2, raw0, raw1);
+        if (s + 1 >= nsteps) break;
+        const int c3 = c2 == 2 ? 0 : c2 + 1;
+        run_step.template operator()<PAR1>(c1, c2, c3, raw1, raw0);
+        cur = c2;
+      }
     }
   }
 
-  // ---- epilogue: D lane layout of the 32x32 MFMA: column lane%32, rows
-  // 8*(v/4) + 4*(lane/32) + v%4 for accumulator element v
-  float scale = 1.0f;
-  if constexpr (OP != OP_WGRAD) scale = (*p.a_t) * (*p.b_t);
-  int64_t row_stride;
-  if constexpr (OP == OP_WGRAD) row_stride = p.ncol;
-  else row_stride = p.n;
+  store_tile<OP, MT, NT, KB, WTM, WTN, RM, RN>(p, t, acc, lane, wm, wn);
+}
 
+// ---- E2M1 operands: decode at fragment read ------------------------------
+//
+// An fp16 stage of the kernel above costs the LDS one 16-byte write and two
+// 16-byte reads per 8 K values of a line, which is as much LDS time as the
+// MFMAs take on the 256-wide tiles.  For E2M1 the LDS holds the raw 4-bit
+// codes instead (4 bytes per line per k-block) and every wave decodes its
+// own fragments in registers, between its MFMAs.
+//
+// Stage layout (KB = 4, one k-quad = two 16-wide K slices):
+//   codes  [line][16 B]: the 4 k-blocks of a line in the order 0, 2, 1, 3,
+//          so that lane half h reads k-blocks h and 2+h (its K slots in
+//          slice 0 and slice 1) with one 8-byte read; the 8 lines of a line
+//          block are XOR-permuted by the block index, which keeps the
+//          staging writes (one row of 8 codes = 4 bytes each) to at most two
+//          per bank while the fragment reads still cover 512 contiguous
+//          bytes;
+//   scales [line block][16 B]: one word per k-block, same order: the fp32
+//          exponent field of B with the fp16 mantissa factor mB in the low
+//          16 bits.  The hardware conversion takes only the exponent of its
+//          scale operand, so the word serves as the scale directly.
+
+// Transpose an 8x8 matrix of 4-bit codes held as 8 rows of 8 nibbles
+// (nibble c of w[r] = element (r, c)): 4x4 blocks, then 2x2, then single
+// nibbles.
+__device__ __forceinline__ void transpose_nibbles(uint32_t (&w)[8]) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t a = w[r], b = w[r + 4];
+    w[r] = __builtin_amdgcn_perm(b, a, 0x05040100u);
+    w[r + 4] = __builtin_amdgcn_perm(b, a, 0x07060302u);
+  }
+#pragma unroll
+  for (int r = 0; r < 8; r += (r & 1) ? 3 : 1) {  // r = 0, 1, 4, 5
+    const uint32_t a = w[r], b = w[r + 2];
+    w[r] = __builtin_amdgcn_perm(b, a, 0x06020400u);
+    w[r + 2] = __builtin_amdgcn_perm(b, a, 0x07030501u);
+  }
+#pragma unroll
+  for (int r = 0; r < 8; r += 2) {
+    const uint32_t a = w[r], b = w[r + 1];
+    w[r] = (a & 0x0F0F0F0Fu) | ((b << 4) & 0xF0F0F0F0u);
+    w[r + 1] = ((a >> 4) & 0x0F0F0F0Fu) | (b & 0xF0F0F0F0u);
+  }
+}
+
+// Scale word of an E4M3 block scale code (0 for a zero scale).
+__device__ __forceinline__ uint32_t scale_word(uint32_t code) {
+  const float b = code_value<ScaleFmt>(code);
+  const uint32_t bits = __float_as_uint(b);
+  const _Float16 mb = static_cast<_Float16>(__uint_as_float((bits & 0x007FFFFFu) | 0x3F800000u));
+  return code == 0u ? 0u : (bits & 0x7F800000u) | __builtin_bit_cast(uint16_t, mb);
+}
+
+// Eight exact fp16 values code * B of one fragment: the conversion applies
+// 2^exponent(B), the packed multiply the mantissa factor mB.
+__device__ __forceinline__ f16x8 decode_frag(uint32_t codes, uint32_t sw) {
+  const float sc = __uint_as_float(sw);
+  const _Float16 m = __builtin_bit_cast(_Float16, static_cast<uint16_t>(sw & 0xFFFFu));
+  const f16x2 m2 = {m, m};
+  const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, sc, 0) * m2;
+  const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, sc, 1) * m2;
+  const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, sc, 2) * m2;
+  const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, sc, 3) * m2;
+  return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// two workgroups per CU: at most 256 registers per wave
+template <int OP, int MT, int NT, int WM, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_conv4(const ConvParams p) {
+  constexpr int KB = 4;
+  constexpr int WN = WAVES / WM;
+  constexpr int WTM = MT / WM, WTN = NT / WN;
+  constexpr int RM = WTM / 32, RN = WTN / 32;
+  constexpr int ABLK = (MT / 8) * KB, BBLK = (NT / 8) * KB;
+  static_assert(ABLK + BBLK <= WAVES * 64, "one block per thread per stage");
+  static_assert(ABLK % 64 == 0, "the A/B staging split falls on wave boundaries");
+  static_assert(RM >= 1 && RN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile of 32x32 MFMAs");
+  constexpr int LINES = MT + NT + 8;  // + 8 spare lines for threads without a block
+  constexpr int CODE_B = LINES * 16;
+  constexpr int STAGE_B = CODE_B + (LINES / 8) * 16;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][STAGE_B];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % WM, wn = wave / WM;
+  TileCtx<OP, MT, NT, KB> t;
+  if (!t.init(p, tid)) return;
+  const bool is_a = t.is_a;
+  constexpr bool A_ROWS = (OP != OP_DGRAD);
+  constexpr bool B_ROWS = (OP == OP_WGRAD);
+  const bool rows = is_a ? A_ROWS : B_ROWS;  // uniform per wave
+
+  // staging addresses of this thread's block: row r goes to physical line
+  // lb*8 + (r ^ (lb & 7)) at the k-block's slot
+  const int lb = !t.active ? (MT + NT) / 8 : is_a ? t.lblk : MT / 8 + t.lblk;
+  const int slot = ((t.kbl & 1) << 1) | ((t.kbl >> 1) & 1);
+  const int st_code = lb * 8 * 16 + slot * 4;
+  const int st_perm = lb & 7;
+  const int st_scale = CODE_B + lb * 16 + slot * 4;
+
+  const uint8_t* my_codes = is_a ? p.a_codes : p.b_codes;
+  const uint8_t* my_scales = is_a ? p.a_scales : p.b_scales;
+  RawBlock<FMT_E2M1> g;
+  auto fetch = [&]() {
+    uint32_t blk = 0;
+    const bool ok = t.locate(p, blk);
+    g.load(my_codes, my_scales, blk, ok);
+    t.kb += KB;
+  };
+  // stage the fetched block: its 8 code lines (transposed first when K runs
+  // along the block's rows) and its scale word
+  auto stage_block = [&](int stg) {
+    uint32_t w[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) w[r] = g.w[r] & g.mask;
+    if (!rows) transpose_nibbles(w);
+    const uint32_t sw = scale_word(g.scale & g.mask);
+    uint8_t* base = lds[stg];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) *reinterpret_cast<uint32_t*>(base + st_code + ((r ^ st_perm) * 16)) = w[r];
+    *reinterpret_cast<uint32_t*>(base + st_scale) = sw;
+  };
+
+  f32x16 acc[RM][RN];
+#pragma unroll
+  for (int i = 0; i < RM; ++i)
+#pragma unroll
+    for (int j = 0; j < RN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  // fragment read offsets (physical line of logical line L, lane half h)
+  auto pline = [](int L) { return L ^ ((L >> 3) & 7); };
+  int a_code[RM], a_scale[RM], b_code[RN], b_scale[RN];
+#pragma unroll
+  for (int i = 0; i < RM; ++i) {
+    const int L = wm * WTM + i * 32 + (lane & 31);
+    a_code[i] = pline(L) * 16 + (lane >> 5) * 8;
+    a_scale[i] = CODE_B + (L >> 3) * 16 + (lane >> 5) * 8;
+  }
 #pragma unroll
   for (int j = 0; j < RN; ++j) {
-    const int col = cb0 * 8 + wn * WTN + j * 32 + (lane & 31);  // column in the launch space
-    const int cbk = col >> 3, c = col & 7;
-    if (cbk >= ncb_launch) continue;
-    int64_t colbase;
-    if constexpr (OP == OP_FWD) {
-      const int pos = cbk / p.nb, nbk = cbk - pos * p.nb;
-      colbase = static_cast<int64_t>(pos) * p.c_out * p.n + nbk * 8 + c;
-    } else if constexpr (OP == OP_DGRAD) {
-      const int pos = cbk / p.nb, nbk = cbk - pos * p.nb;
-      const int hq = pos / wp;
-      const int hh = phh + p.sh * hq, ww = phw + p.sw * (pos - hq * wp);
-      colbase = (static_cast<int64_t>(hh) * p.w + ww) * p.c_in * p.n + nbk * 8 + c;
-    } else {
-      colbase = static_cast<int64_t>(bz) * p.M * p.ncol + col;
+    const int L = MT + wn * WTN + j * 32 + (lane & 31);
+    b_code[j] = pline(L) * 16 + (lane >> 5) * 8;
+    b_scale[j] = CODE_B + (L >> 3) * 16 + (lane >> 5) * 8;
+  }
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  // raw fragments of one stage (.x slice 0, .y slice 1)
+  u32x2 ra[RM], sa[RM], rb[RN], sbv[RN];
+  auto read_raw = [&](int stg) {
+    const uint8_t* base = lds[stg];
+#pragma unroll
+    for (int i = 0; i < RM; ++i) {
+      ra[i] = *reinterpret_cast<const u32x2*>(base + a_code[i]);
+      sa[i] = *reinterpret_cast<const u32x2*>(base + a_scale[i]);
     }
 #pragma unroll
-    for (int i = 0; i < RM; ++i)
+    for (int j = 0; j < RN; ++j) {
+      rb[j] = *reinterpret_cast<const u32x2*>(base + b_code[j]);
+      sbv[j] = *reinterpret_cast<const u32x2*>(base + b_scale[j]);
+    }
+  };
+  // one slice: the A fragments are decoded up front, each B fragment just
+  // before its column of MFMAs.  The scheduling barriers keep this order:
+  // left free, the scheduler hoists all decodes to the top and spills.
+  auto slice = [&](bool second) {
+    f16x8 fa[RM];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = rb0 * 8 + wm * WTM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (row < p.M) p.out[colbase + row * row_stride] = acc[i][j][v] * scale;
-      }
+    for (int i = 0; i < RM; ++i) fa[i] = decode_frag(second ? ra[i].y : ra[i].x, second ? sa[i].y : sa[i].x);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < RN; ++j) {
+      const f16x8 fb = decode_frag(second ? rb[j].y : rb[j].x, second ? sbv[j].y : sbv[j].x);
+#pragma unroll
+      for (int i = 0; i < RM; ++i)
+        acc[i][j] = mfma32<true>(reinterpret_cast<const uint16_t*>(&fa[i]),
+                                 reinterpret_cast<const uint16_t*>(&fb), acc[i][j]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Step s (stage s%2): stage the block fetched during step s-1 (K step
+  // s+1) into stage (s+1)%2, which nobody reads since the last barrier;
+  // fetch the block of step s+2; multiply slices 0 and 1; barrier; read the
+  // raw fragments of stage (s+1)%2.  A fetch thus has one whole step to
+  // arrive.  Two workgroups share a CU, so one workgroup's decode and LDS
+  // phases overlap the other's MFMAs.  Steps past the end fetch padding and
+  // stage it into a stage that is never read again.
+  const int nsteps = (t.kb_end - t.kb_begin + KB - 1) / KB;
+  if (nsteps > 0) {
+    fetch();
+    stage_block(0);
+    fetch();
+    __syncthreads();
+    read_raw(0);
+    for (int s = 0; s < nsteps; ++s) {
+      const int nxt = (s + 1) & 1;
+      stage_block(nxt);
+      fetch();
+      __builtin_amdgcn_sched_barrier(0);
+      slice(false);
+      slice(true);
+      __syncthreads();
+      read_raw(nxt);
+    }
   }
+  store_tile<OP, MT, NT, KB, WTM, WTN, RM, RN>(p, t, acc, lane, wm, wn);
+}
+
+// E2M1 on the 256x256 tile: four waves of 128x128 (one wave per SIMD, 256
+// accumulator registers), the same LDS stage layout as k_conv4.  Each wave
+// decodes 8 fragments per 16-wide slice for 16 MFMAs (4 VALU operations per
+// MFMA, within what one wave issues in an MFMA's shadow), so the decode is
+// spread between the MFMAs: every B fragment right before its column of
+// MFMAs, the A fragments of the next slice between the columns of this one.
+template <int OP>
+__global__ __launch_bounds__(256) void k_conv4w(const ConvParams p) {
+  constexpr int MT = 256, NT = 256, WM = 2, KB = 4;
+  constexpr int WTM = 128, WTN = 128, RM = 4, RN = 4;
+  constexpr int LINES = MT + NT + 8;
+  constexpr int CODE_B = LINES * 16;
+  constexpr int STAGE_B = CODE_B + (LINES / 8) * 16;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][STAGE_B];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % WM, wn = wave / WM;
+  TileCtx<OP, MT, NT, KB> t;
+  if (!t.init(p, tid)) return;
+  const bool is_a = t.is_a;
+  constexpr bool A_ROWS = (OP != OP_DGRAD);
+  constexpr bool B_ROWS = (OP == OP_WGRAD);
+  const bool rows = is_a ? A_ROWS : B_ROWS;  // uniform per wave
+
+  const int lb = !t.active ? (MT + NT) / 8 : is_a ? t.lblk : MT / 8 + t.lblk;
+  const int slot = ((t.kbl & 1) << 1) | ((t.kbl >> 1) & 1);
+  const int st_code = lb * 8 * 16 + slot * 4;
+  const int st_perm = lb & 7;
+  const int st_scale = CODE_B + lb * 16 + slot * 4;
+
+  const uint8_t* my_codes = is_a ? p.a_codes : p.b_codes;
+  const uint8_t* my_scales = is_a ? p.a_scales : p.b_scales;
+  RawBlock<FMT_E2M1> g;
+  auto fetch = [&]() {
+    uint32_t blk = 0;
+    const bool ok = t.locate(p, blk);
+    g.load(my_codes, my_scales, blk, ok);
+    t.kb += KB;
+  };
+  uint32_t sw_[8];  // the block being staged: its code lines
+  uint32_t sws;     // and its scale word
+  auto prepare_a = [&]() {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) sw_[r] = g.w[r] & g.mask;
+    sws = scale_word(g.scale & g.mask);
+  };
+  auto prepare_b = [&]() {
+    if (!rows) transpose_nibbles(sw_);
+  };
+  auto write_staged = [&](int stg) {
+    uint8_t* base = lds[stg];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) *reinterpret_cast<uint32_t*>(base + st_code + ((r ^ st_perm) * 16)) = sw_[r];
+    *reinterpret_cast<uint32_t*>(base + st_scale) = sws;
+  };
+
+  f32x16 acc[RM][RN];
+#pragma unroll
+  for (int i = 0; i < RM; ++i)
+#pragma unroll
+    for (int j = 0; j < RN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  auto pline = [](int L) { return L ^ ((L >> 3) & 7); };
+  int a_code[RM], a_scale[RM], b_code[RN], b_scale[RN];
+#pragma unroll
+  for (int i = 0; i < RM; ++i) {
+    const int L = wm * WTM + i * 32 + (lane & 31);
+    a_code[i] = pline(L) * 16 + (lane >> 5) * 8;
+    a_scale[i] = CODE_B + (L >> 3) * 16 + (lane >> 5) * 8;
+  }
+#pragma unroll
+  for (int j = 0; j < RN; ++j) {
+    const int L = MT + wn * WTN + j * 32 + (lane & 31);
+    b_code[j] = pline(L) * 16 + (lane >> 5) * 8;
+    b_scale[j] = CODE_B + (L >> 3) * 16 + (lane >> 5) * 8;
+  }
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  u32x2 ra[RM], sa[RM], rb[RN], sbv[RN];  // raw fragments of a stage (.x slice 0, .y slice 1)
+  auto read_raw = [&](int stg) {
+    const uint8_t* base = lds[stg];
+#pragma unroll
+    for (int i = 0; i < RM; ++i) {
+      ra[i] = *reinterpret_cast<const u32x2*>(base + a_code[i]);
+      sa[i] = *reinterpret_cast<const u32x2*>(base + a_scale[i]);
+    }
+#pragma unroll
+    for (int j = 0; j < RN; ++j) {
+      rb[j] = *reinterpret_cast<const u32x2*>(base + b_code[j]);
+      sbv[j] = *reinterpret_cast<const u32x2*>(base + b_scale[j]);
+    }
+  };
+  f16x8 fa0[RM], fa1[RM];  // A fragments of slice 0 and slice 1
+
+  // One column j of a slice: decode its B fragment, 4 MFMAs, then the work
+  // item placed after it; a scheduling barrier closes the group.
+  auto column_dec = [&](const f16x8 (&fa)[RM], const f16x8& fb, int j, auto&& work) {
+#pragma unroll
+    for (int i = 0; i < RM; ++i)
+      acc[i][j] = mfma32<true>(reinterpret_cast<const uint16_t*>(&fa[i]),
+                               reinterpret_cast<const uint16_t*>(&fb), acc[i][j]);
+    work();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto column = [&](const f16x8 (&fa)[RM], uint32_t bcodes, uint32_t bsw, int j, auto&& work) {
+    column_dec(fa, decode_frag(bcodes, bsw), j, work);
+  };
+
+  // Step s on stage s%2 (raw fragments in registers, slice-0 A fragments
+  // decoded):
+  //   slice 0, columns 0..3: the A fragments of slice 1; the fetch of step
+  //            s+2 after column 0
+  //   slice 1, column 0: mask and scale word of the block fetched during
+  //            step s-1 (step s+1); column 1: its transpose and LDS writes
+  //            into stage (s+1)%2, read by nobody since the last barrier,
+  //            and the next fetch; columns 0 and 1 also decode the B
+  //            fragments of columns 2 and 3, whose raw fragments the
+  //            barrier and the reads of stage (s+1)%2 after column 2
+  //            replace; column 3: the slice-0 A fragments of step s+1.
+  const int nsteps = (t.kb_end - t.kb_begin + KB - 1) / KB;
+  if (nsteps > 0) {
+    fetch();
+    prepare_a();
+    prepare_b();
+    write_staged(0);
+    fetch();
+    __syncthreads();
+    read_raw(0);
+#pragma unroll
+    for (int i = 0; i < RM; ++i) fa0[i] = decode_frag(ra[i].x, sa[i].x);
+    for (int s = 0; s < nsteps; ++s) {
+      const int nxt = (s + 1) & 1;
+      column(fa0, rb[0].x, sbv[0].x, 0, [&] { fa1[0] = decode_frag(ra[0].y, sa[0].y); });
+      column(fa0, rb[1].x, sbv[1].x, 1, [&] { fa1[1] = decode_frag(ra[1].y, sa[1].y); });
+      column(fa0, rb[2].x, sbv[2].x, 2, [&] { fa1[2] = decode_frag(ra[2].y, sa[2].y); });
+      column(fa0, rb[3].x, sbv[3].x, 3, [&] { fa1[3] = decode_frag(ra[3].y, sa[3].y); });
+      f16x8 fb2, fb3;
+      column(fa1, rb[0].y, sbv[0].y, 0, [&] {
+        prepare_a();
+        fb2 = decode_frag(rb[2].y, sbv[2].y);
+      });
+      column(fa1, rb[1].y, sbv[1].y, 1, [&] {
+        prepare_b();
+        write_staged(nxt);
+        fetch();
+        fb3 = decode_frag(rb[3].y, sbv[3].y);
+      });
+      column_dec(fa1, fb2, 2, [&] {
+        __syncthreads();
+        read_raw(nxt);
+      });
+      column_dec(fa1, fb3, 3, [&] {
+#pragma unroll
+        for (int i = 0; i < RM; ++i) fa0[i] = decode_frag(ra[i].x, sa[i].x);
+      });
+    }
+  }
+  store_tile<OP, MT, NT, KB, WTM, WTN, RM, RN>(p, t, acc, lane, wm, wn);
 }
 
 // dW[co][ci][kh][kw] = T_dy * T_x * (sum over splits of the partials
@@ -651,12 +1104,14 @@ constexpr Tile kTiles[] = {{256, 256, 2, 4, 4}, {128, 256, 2, 4, 4}, {128, 128, 
 // it over more CUs beats operand reuse inside a workgroup.
 int mt_cap(int64_t M) { return M > 128 ? 256 : M > 64 ? 128 : M > 32 ? 64 : 32; }
 
-Tile pick_tile(int64_t M, int64_t ncols, int64_t zdim) {
+bool tile_ok(const Tile&, int) { return true; }
+
+Tile pick_tile(int64_t M, int64_t ncols, int64_t zdim, int fmt) {
   const int cap = mt_cap(M);
   Tile best = {0, 0, 0, 0, 0};
   int64_t best_reach = -1;
   for (const Tile& t : kTiles) {
-    if (t.mt > cap) continue;
+    if (t.mt > cap || !tile_ok(t, fmt)) continue;
     const int64_t wgs = ((M + t.mt - 1) / t.mt) * ((ncols + t.nt - 1) / t.nt) * zdim;
     if (wgs * t.waves >= 2048) return t;
     const int64_t reach = wgs < 256 ? wgs : 256;
@@ -671,22 +1126,22 @@ Tile pick_tile(int64_t M, int64_t ncols, int64_t zdim) {
 // wgrad: split K supplies the parallelism, so the tile is chosen for operand
 // reuse: the largest one whose share of useful (unpadded) outputs is within
 // 3/4 of the best share any tile reaches.
-Tile pick_wgrad_tile(int64_t M, int64_t ncols) {
+Tile pick_wgrad_tile(int64_t M, int64_t ncols, int fmt) {
   const int cap = mt_cap(M);
   double best_eff = 0.0;
   for (const Tile& t : kTiles) {
-    if (t.mt > cap) continue;
+    if (t.mt > cap || !tile_ok(t, fmt)) continue;
     const double eff = static_cast<double>(M * ncols) /
                        (static_cast<double>((M + t.mt - 1) / t.mt * t.mt) * ((ncols + t.nt - 1) / t.nt * t.nt));
     if (eff > best_eff) best_eff = eff;
   }
   for (const Tile& t : kTiles) {
-    if (t.mt > cap) continue;
+    if (t.mt > cap || !tile_ok(t, fmt)) continue;
     const double eff = static_cast<double>(M * ncols) /
                        (static_cast<double>((M + t.mt - 1) / t.mt * t.mt) * ((ncols + t.nt - 1) / t.nt * t.nt));
     if (eff * 4.0 >= best_eff * 3.0) return t;
   }
-  return kTiles[0];
+  return kTiles[1];
 }
 
 template <int OP, int FMT, int MT, int NT, int WM, int WAVES, int KB>
@@ -694,8 +1149,21 @@ void launch_tile(const ConvParams& p, dim3 grid, hipStream_t s) {
   hipLaunchKernelGGL((k_conv<OP, FMT, MT, NT, WM, WAVES, KB>), grid, dim3(WAVES * 64), 0, s, p);
 }
 
+template <int OP, int MT, int NT, int WM, int WAVES>
+void launch_tile4(const ConvParams& p, dim3 grid, hipStream_t s) {
+  hipLaunchKernelGGL((k_conv4<OP, MT, NT, WM, WAVES>), grid, dim3(WAVES * 64), 0, s, p);
+}
+
 template <int OP, int FMT>
 void launch_fmt(const ConvParams& p, const Tile& t, dim3 grid, hipStream_t s) {
+  // E2M1 on the 4-k-block tiles: codes in LDS, decoded at fragment read
+  if constexpr (FMT == FMT_E2M1) {
+    if (t.mt == 256) {
+      hipLaunchKernelGGL((k_conv4w<OP>), grid, dim3(256), 0, s, p);
+      return;
+    }
+    if (t.mt == 128 && t.nt == 256) return launch_tile4<OP, 128, 256, 2, 4>(p, grid, s);
+  }
   if (t.mt == 256) launch_tile<OP, FMT, 256, 256, 2, 4, 4>(p, grid, s);
   else if (t.mt == 128 && t.nt == 256) launch_tile<OP, FMT, 128, 256, 2, 4, 4>(p, grid, s);
   else if (t.mt == 128) launch_tile<OP, FMT, 128, 128, 2, 4, 8>(p, grid, s);
@@ -735,7 +1203,7 @@ struct WgradPlan {
 WgradPlan wgrad_plan(const Geom& g) {
   const int64_t kb_total = static_cast<int64_t>(g.ho) * g.wo * (g.n / 8);
   const int64_t ncol = static_cast<int64_t>(g.k_h) * g.k_w * g.c_in;
-  const Tile t = pick_wgrad_tile(g.c_out, ncol);
+  const Tile t = pick_wgrad_tile(g.c_out, ncol, g.fmt);
   const int64_t ksteps = (kb_total + t.kb - 1) / t.kb;
   const int64_t tiles = ((g.c_out + t.mt - 1) / t.mt) * ((ncol + t.nt - 1) / t.nt);
   // rounded down: a last, nearly empty round of workgroups costs a full one
@@ -759,7 +1227,7 @@ hipError_t launch_conv_fwd(const Geom& g, const mx_qtensor* wq, const mx_qtensor
   p.b_codes = static_cast<const uint8_t*>(xq->codes); p.b_scales = xq->scales; p.b_t = xq->tensor_scale;
   p.out = y;
   if (p.ncb == 0) return hipSuccess;
-  const Tile t = pick_tile(p.M, static_cast<int64_t>(p.ncb) * 8, 1);
+  const Tile t = pick_tile(p.M, static_cast<int64_t>(p.ncb) * 8, 1, g.fmt);
   dim3 grid((p.ncb * 8 + t.nt - 1) / t.nt, (p.M + t.mt - 1) / t.mt, 1);
   launch_op<OP_FWD>(p, g.fmt, t, grid, s);
   return hipGetLastError();
@@ -776,7 +1244,7 @@ hipError_t launch_conv_dgrad(const Geom& g, const mx_qtensor* wq, const mx_qtens
   p.b_codes = static_cast<const uint8_t*>(dyq->codes); p.b_scales = dyq->scales; p.b_t = dyq->tensor_scale;
   p.out = dx;
   if (p.ncb == 0) return hipSuccess;
-  const Tile t = pick_tile(p.M, static_cast<int64_t>(p.ncb) * 8, g.sh * g.sw);
+  const Tile t = pick_tile(p.M, static_cast<int64_t>(p.ncb) * 8, g.sh * g.sw, g.fmt);
   dim3 grid((p.ncb * 8 + t.nt - 1) / t.nt, (p.M + t.mt - 1) / t.mt, g.sh * g.sw);
   launch_op<OP_DGRAD>(p, g.fmt, t, grid, s);
   return hipGetLastError();

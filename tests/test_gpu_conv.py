@@ -31,6 +31,9 @@ SHAPES = [
     (64, 8, 128, 32, 32, 1, 1, 1, 1, 0, 0),    # fwd on a 128x128 tile (65536 columns)
     (128, 8, 128, 32, 32, 1, 1, 1, 1, 0, 0),   # fwd on a 128x256 tile (131072 columns)
     (16, 24, 64, 6, 6, 1, 1, 1, 1, 0, 0),      # wgrad on the 2-wave 64x32 tile (24 columns)
+    (128, 128, 8, 32, 32, 1, 1, 1, 1, 0, 0),   # dgrad on the 128x256 tile (E2M1: decode at read)
+    (128, 8, 256, 32, 32, 1, 1, 1, 1, 0, 0),   # fwd on the 256x256 tile
+    (128, 256, 8, 32, 32, 1, 1, 1, 1, 0, 0),   # dgrad on the 256x256 tile
 ]
 
 
