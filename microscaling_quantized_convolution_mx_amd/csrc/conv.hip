@@ -880,20 +880,140 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
   store_tile<OP, MT, NT, KB, WTM, WTN, RM, RN>(p, t, acc, lane, wm, wn);
 }
 
-// E2M1 on the 256x256 tile: four waves of 128x128 (one wave per SIMD, 256
-// accumulator registers), the same LDS stage layout as k_conv4.  Each wave
-// decodes 8 fragments per 16-wide slice for 16 MFMAs (4 VALU operations per
-// MFMA, within what one wave issues in an MFMA's shadow), so the decode is
-// spread between the MFMAs: every B fragment right before its column of
-// MFMAs, the A fragments of the next slice between the columns of this one.
+// The k-blocks kb0, kb0 + KB, kb0 + 2 KB, ... of one staging thread, walked
+// with additions only.  kb splits into (outer, mid, inner) as in
+// TileCtx::locate; the block index and the source position are affine in the
+// three, and when inner's extent is at least KB a step carries at most once
+// into mid and once into outer.
+template <int OP, int MT, int NT, int KB>
+struct KWalk {
+  uint32_t lim;            // k-blocks of this thread's range left at step 0 (kb_end - kb0)
+  uint32_t inner, mid, blk;
+  uint32_t d_in, d_mid;
+  uint32_t s_step, s_c1, s_c2;  // block increments: per step, carry into mid, carry into outer
+  int y, x, x_c1, y_c2, x_c2;   // source position and its increments on carries
+  uint32_t hlim, wlim;          // position bounds (all ones: no spatial gather)
+
+  __device__ __forceinline__ void init(const ConvParams& p, const TileCtx<OP, MT, NT, KB>& t) {
+    const uint32_t kb0 = static_cast<uint32_t>(t.kb_begin + t.kbl);
+    lim = (t.in_range && static_cast<int>(kb0) < t.kb_end) ? static_cast<uint32_t>(t.kb_end) - kb0 : 0u;
+    const int cbin = p.c_in >> 3, cbout = p.c_out >> 3;
+    int e_in, e_mid, s_in, s_mid, s_out, base;
+    int sx1 = 0, sy2 = 0, sx2 = 0;
+    hlim = ~0u; wlim = ~0u;
+    if constexpr (OP == OP_FWD) {
+      e_in = cbin; e_mid = p.k_w;
+      if (t.is_a) { s_in = 1; s_mid = cbout * cbin; s_out = p.k_w * s_mid; base = t.gblk * cbin; }
+      else {
+        s_in = p.nb; s_mid = cbin * p.nb; s_out = p.w * s_mid;
+        base = (t.sp_y * p.w + t.sp_x) * s_mid + t.col_nb;
+        sx1 = 1; sy2 = 1; sx2 = -p.k_w;
+        hlim = p.h; wlim = p.w;
+      }
+    } else if constexpr (OP == OP_DGRAD) {
+      e_in = cbout; e_mid = t.nkw;
+      if (t.is_a) {
+        s_in = cbin; s_mid = p.sw * cbout * cbin; s_out = p.sh * p.k_w * cbout * cbin;
+        base = (t.kh0 * p.k_w + t.kw0) * cbout * cbin + t.gblk;
+      } else {
+        s_in = p.nb; s_mid = -cbout * p.nb; s_out = -p.wo * cbout * p.nb;
+        base = (t.sp_y * p.wo + t.sp_x) * cbout * p.nb + t.col_nb;
+        sx1 = -1; sy2 = -1; sx2 = t.nkw;
+        hlim = p.ho; wlim = p.wo;
+      }
+    } else {
+      e_in = p.nb; e_mid = p.wo;
+      if (t.is_a) { s_in = 1; s_mid = cbout * p.nb; s_out = p.wo * s_mid; base = t.gblk * p.nb; }
+      else {
+        s_in = 1; s_mid = p.sw * cbin * p.nb; s_out = p.sh * p.w * cbin * p.nb;
+        base = (t.sp_y * p.w + t.sp_x) * cbin * p.nb + t.col_cib * p.nb;
+        sx1 = p.sw; sy2 = p.sh; sx2 = -p.wo * p.sw;
+        hlim = p.h; wlim = p.w;
+      }
+    }
+    d_in = static_cast<uint32_t>(e_in);
+    d_mid = static_cast<uint32_t>(e_mid > 0 ? e_mid : 1);
+    const uint32_t outer_all = kb0 / d_in;
+    inner = kb0 - outer_all * d_in;
+    const uint32_t outer = outer_all / d_mid;
+    mid = outer_all - outer * d_mid;
+    blk = static_cast<uint32_t>(base) + outer * static_cast<uint32_t>(s_out) + mid * static_cast<uint32_t>(s_mid) +
+          inner * static_cast<uint32_t>(s_in);
+    // operands without a spatial gather stay at (0, 0)
+    const bool gather = hlim != ~0u;
+    y = (gather ? t.sp_y : 0) + static_cast<int>(outer) * sy2;
+    x = (gather ? t.sp_x : 0) + static_cast<int>(mid) * sx1;
+    s_step = static_cast<uint32_t>(KB * s_in);
+    s_c1 = static_cast<uint32_t>(s_mid - e_in * s_in);
+    s_c2 = static_cast<uint32_t>(s_out - e_mid * s_mid);
+    x_c1 = sx1; y_c2 = sy2; x_c2 = sx2;
+  }
+
+  // the block of step s (s * KB < lim and inside the source) and advance
+  __device__ __forceinline__ bool next(uint32_t s_kb, uint32_t& b) {
+    const bool ok = (s_kb < lim) & (static_cast<uint32_t>(y) < hlim) & (static_cast<uint32_t>(x) < wlim);
+    b = blk;
+    inner += KB;
+    blk += s_step;
+    const bool c1 = inner >= d_in;
+    inner = c1 ? inner - d_in : inner;
+    mid = c1 ? mid + 1u : mid;
+    blk = c1 ? blk + s_c1 : blk;
+    x = c1 ? x + x_c1 : x;
+    const bool c2 = mid >= d_mid;
+    mid = c2 ? 0u : mid;
+    blk = c2 ? blk + s_c2 : blk;
+    y = c2 ? y + y_c2 : y;
+    x = c2 ? x + x_c2 : x;
+    return ok;
+  }
+};
+
+// True when every step of KWalk carries at most once: the innermost extent
+// of the K split (input channel blocks, output channel blocks, batch blocks)
+// is at least the K step.
+inline bool kwalk_ok(int op, const ConvParams& p, int kb) {
+  const int e_in = op == OP_FWD ? p.c_in / 8 : op == OP_DGRAD ? p.c_out / 8 : p.nb;
+  return e_in >= kb;
+}
+
+template <int V>
+struct IC {
+  static constexpr int value = V;
+};
+
+// E2M1, 256x256 tile, 4 waves of 128x128, one workgroup per CU (the 256
+// accumulator registers of a wave fill the AGPR file).  LDS holds the raw
+// 4-bit codes of two K steps; each wave decodes its MFMA fragments from
+// them (conversion with the block scale's exponent, then a packed multiply
+// by its mantissa factor: exact in fp16).
+//
+// Per stage and operand, 32 pitches of 136 bytes (the 8-byte pad staggers
+// the banks):
+//   block rows along M/N (fwd A, wgrad A and B): 32 line blocks of 8 lines;
+//     a line is 16 bytes, the 4 k-blocks of one row in the order 0, 2, 1, 3,
+//     so that an 8-byte read gives k-block (lane/32) of both MFMA k-slices;
+//   block rows along K (fwd B, dgrad A and B): 32 k rows of 256 codes, the
+//     rows of k-block kb at pitches 8 * slot(kb); the transposing LDS read
+//     (16x16 4-bit transpose within each group of 16 lanes) turns the rows
+//     of 16 lanes into the k-runs of 16 columns.
+// Scale words (fp32 exponent of the block scale | fp16 mantissa factor) come
+// from a 256-entry table; padding blocks take entry 0, whose word is 0, so
+// that their codes, whatever they are, decode to zero.
+//
+// Block fetches run two steps ahead in two register sets; the loop is
+// unrolled twice so that sets and stages are static.
 template <int OP>
 __global__ __launch_bounds__(256) void k_conv4w(const ConvParams p) {
   constexpr int MT = 256, NT = 256, WM = 2, KB = 4;
   constexpr int WTM = 128, WTN = 128, RM = 4, RN = 4;
-  constexpr int LINES = MT + NT + 8;
-  constexpr int CODE_B = LINES * 16;
-  constexpr int STAGE_B = CODE_B + (LINES / 8) * 16;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][STAGE_B];
+  constexpr bool A_ROWS = (OP != OP_DGRAD);
+  constexpr bool B_ROWS = (OP == OP_WGRAD);
+  constexpr int PITCH = 136, OPND = 32 * PITCH, SCL = 32 * 16;
+  constexpr int A_C = 0, B_C = OPND, A_S = 2 * OPND, B_S = 2 * OPND + SCL;
+  constexpr int STAGE = 2 * OPND + 2 * SCL;
+  constexpr int LUT = 2 * STAGE;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE + 1024];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -901,40 +1021,44 @@ __global__ __launch_bounds__(256) void k_conv4w(const ConvParams p) {
   TileCtx<OP, MT, NT, KB> t;
   if (!t.init(p, tid)) return;
   const bool is_a = t.is_a;
-  constexpr bool A_ROWS = (OP != OP_DGRAD);
-  constexpr bool B_ROWS = (OP == OP_WGRAD);
-  const bool rows = is_a ? A_ROWS : B_ROWS;  // uniform per wave
 
-  const int lb = !t.active ? (MT + NT) / 8 : is_a ? t.lblk : MT / 8 + t.lblk;
+  *reinterpret_cast<uint32_t*>(lds + LUT + tid * 4) = scale_word(static_cast<uint32_t>(tid));
+
+  // this thread's staging addresses (every thread stages one block a step)
   const int slot = ((t.kbl & 1) << 1) | ((t.kbl >> 1) & 1);
-  const int st_code = lb * 8 * 16 + slot * 4;
-  const int st_perm = lb & 7;
-  const int st_scale = CODE_B + lb * 16 + slot * 4;
+  const bool rows = is_a ? A_ROWS : B_ROWS;  // uniform per wave
+  const int st_code = (is_a ? A_C : B_C) + (rows ? t.lblk * PITCH + slot * 4 : slot * 8 * PITCH + t.lblk * 4);
+  const int st_scale = (is_a ? A_S : B_S) + t.lblk * 16 + slot * 4;
 
   const uint8_t* my_codes = is_a ? p.a_codes : p.b_codes;
   const uint8_t* my_scales = is_a ? p.a_scales : p.b_scales;
-  RawBlock<FMT_E2M1> g;
-  auto fetch = [&]() {
-    uint32_t blk = 0;
-    const bool ok = t.locate(p, blk);
+  KWalk<OP, MT, NT, KB> walk;
+  walk.init(p, t);
+  uint32_t s_fetch = 0;  // k offset (s * KB) of the next fetch
+  auto fetch = [&](RawBlock<FMT_E2M1>& g) {
+    uint32_t blk;
+    const bool ok = walk.next(s_fetch, blk);
     g.load(my_codes, my_scales, blk, ok);
-    t.kb += KB;
+    s_fetch += KB;
   };
-  uint32_t sw_[8];  // the block being staged: its code lines
-  uint32_t sws;     // and its scale word
-  auto prepare_a = [&]() {
+  uint32_t sws;  // scale word of the block being staged
+  auto lookup_scale = [&](const RawBlock<FMT_E2M1>& g) {
+    sws = *reinterpret_cast<const uint32_t*>(lds + LUT + ((g.scale & g.mask) << 2));
+  };
+  auto write_rows = [&](const RawBlock<FMT_E2M1>& g, uint8_t* base, int r0) {
+    if constexpr (A_ROWS == B_ROWS) {
 #pragma unroll
-    for (int r = 0; r < 8; ++r) sw_[r] = g.w[r] & g.mask;
-    sws = scale_word(g.scale & g.mask);
-  };
-  auto prepare_b = [&]() {
-    if (!rows) transpose_nibbles(sw_);
-  };
-  auto write_staged = [&](int stg) {
-    uint8_t* base = lds[stg];
+      for (int r = r0; r < r0 + 4; ++r)
+        *reinterpret_cast<uint32_t*>(base + st_code + r * (A_ROWS ? 16 : PITCH)) = g.w[r];
+    } else {
+      if (__builtin_amdgcn_readfirstlane(static_cast<int>(rows))) {
 #pragma unroll
-    for (int r = 0; r < 8; ++r) *reinterpret_cast<uint32_t*>(base + st_code + ((r ^ st_perm) * 16)) = sw_[r];
-    *reinterpret_cast<uint32_t*>(base + st_scale) = sws;
+        for (int r = r0; r < r0 + 4; ++r) *reinterpret_cast<uint32_t*>(base + st_code + r * 16) = g.w[r];
+      } else {
+#pragma unroll
+        for (int r = r0; r < r0 + 4; ++r) *reinterpret_cast<uint32_t*>(base + st_code + r * PITCH) = g.w[r];
+      }
+    }
   };
 
   f32x16 acc[RM][RN];
@@ -945,40 +1069,40 @@ __global__ __launch_bounds__(256) void k_conv4w(const ConvParams p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  auto pline = [](int L) { return L ^ ((L >> 3) & 7); };
-  int a_code[RM], a_scale[RM], b_code[RN], b_scale[RN];
-#pragma unroll
-  for (int i = 0; i < RM; ++i) {
-    const int L = wm * WTM + i * 32 + (lane & 31);
-    a_code[i] = pline(L) * 16 + (lane >> 5) * 8;
-    a_scale[i] = CODE_B + (L >> 3) * 16 + (lane >> 5) * 8;
-  }
-#pragma unroll
-  for (int j = 0; j < RN; ++j) {
-    const int L = MT + wn * WTN + j * 32 + (lane & 31);
-    b_code[j] = pline(L) * 16 + (lane >> 5) * 8;
-    b_scale[j] = CODE_B + (L >> 3) * 16 + (lane >> 5) * 8;
-  }
+  // fragment read addresses (fragment i adds i * 4 pitches in the line
+  // layout, i * 16 bytes in the k-row layout, i * 64 bytes of scale words)
+  const int l32 = lane & 31, half = lane >> 5;
+  const int line_off = (l32 >> 3) * PITCH + (l32 & 7) * 16 + half * 8;
+  const int krow_off = (((lane >> 5) * 16) + (lane & 15)) * PITCH + ((lane >> 4) & 1) * 8;
+  const int a_code = A_C + (A_ROWS ? wm * 16 * PITCH + line_off : krow_off + wm * 64);
+  const int b_code = B_C + (B_ROWS ? wn * 16 * PITCH + line_off : krow_off + wn * 64);
+  const int a_scale = A_S + (wm * 16 + (l32 >> 3)) * 16 + half * 8;
+  const int b_scale = B_S + (wn * 16 + (l32 >> 3)) * 16 + half * 8;
   typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  typedef int i32x2 __attribute__((ext_vector_type(2)));
+  typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
   u32x2 ra[RM], sa[RM], rb[RN], sbv[RN];  // raw fragments of a stage (.x slice 0, .y slice 1)
-  auto read_raw = [&](int stg) {
-    const uint8_t* base = lds[stg];
+  auto read_code = [&](const uint8_t* q, bool line) -> u32x2 {
+    if (line) return *reinterpret_cast<const u32x2*>(q);
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr4_b64_v2i32((lds_i32x2*)(q)));
+  };
+  auto read_raw = [&](const uint8_t* base) {
 #pragma unroll
     for (int i = 0; i < RM; ++i) {
-      ra[i] = *reinterpret_cast<const u32x2*>(base + a_code[i]);
-      sa[i] = *reinterpret_cast<const u32x2*>(base + a_scale[i]);
+      ra[i] = read_code(base + a_code + i * (A_ROWS ? 4 * PITCH : 16), A_ROWS);
+      sa[i] = *reinterpret_cast<const u32x2*>(base + a_scale + i * 64);
     }
 #pragma unroll
     for (int j = 0; j < RN; ++j) {
-      rb[j] = *reinterpret_cast<const u32x2*>(base + b_code[j]);
-      sbv[j] = *reinterpret_cast<const u32x2*>(base + b_scale[j]);
+      rb[j] = read_code(base + b_code + j * (B_ROWS ? 4 * PITCH : 16), B_ROWS);
+      sbv[j] = *reinterpret_cast<const u32x2*>(base + b_scale + j * 64);
     }
   };
   f16x8 fa0[RM], fa1[RM];  // A fragments of slice 0 and slice 1
 
-  // One column j of a slice: decode its B fragment, 4 MFMAs, then the work
-  // item placed after it; a scheduling barrier closes the group.
-  auto column_dec = [&](const f16x8 (&fa)[RM], const f16x8& fb, int j, auto&& work) {
+  // One column j of a slice: 4 MFMAs with the B fragment fb, then the work
+  // item placed after them; a scheduling barrier closes the group.
+  auto column = [&](const f16x8 (&fa)[RM], const f16x8& fb, int j, auto&& work) {
 #pragma unroll
     for (int i = 0; i < RM; ++i)
       acc[i][j] = mfma32<true>(reinterpret_cast<const uint16_t*>(&fa[i]),
@@ -986,57 +1110,74 @@ __global__ __launch_bounds__(256) void k_conv4w(const ConvParams p) {
     work();
     __builtin_amdgcn_sched_barrier(0);
   };
-  auto column = [&](const f16x8 (&fa)[RM], uint32_t bcodes, uint32_t bsw, int j, auto&& work) {
-    column_dec(fa, decode_frag(bcodes, bsw), j, work);
+
+  // Step s (fragments of stage s%2 in registers, slice-0 A decoded; set G
+  // holds the block of step s+1):
+  //   slice 0: decode the slice-1 A fragments and each column's B fragment;
+  //            stage G into stage (s+1)%2 (free since the barrier of step
+  //            s-1), then refill G with the block of step s+3
+  //   slice 1: decode the B fragments, barrier, read stage (s+1)%2, decode
+  //            its slice-0 A fragments
+  auto step = [&](auto nxt_c, RawBlock<FMT_E2M1>& G) {
+    constexpr int NXT = decltype(nxt_c)::value;
+    uint8_t* nbase = lds + NXT * STAGE;
+    column(fa0, decode_frag(rb[0].x, sbv[0].x), 0, [&] {
+      fa1[0] = decode_frag(ra[0].y, sa[0].y);
+      lookup_scale(G);
+      write_rows(G, nbase, 0);
+    });
+    column(fa0, decode_frag(rb[1].x, sbv[1].x), 1, [&] {
+      fa1[1] = decode_frag(ra[1].y, sa[1].y);
+      write_rows(G, nbase, 4);
+    });
+    column(fa0, decode_frag(rb[2].x, sbv[2].x), 2, [&] {
+      fa1[2] = decode_frag(ra[2].y, sa[2].y);
+      fetch(G);
+    });
+    column(fa0, decode_frag(rb[3].x, sbv[3].x), 3, [&] {
+      fa1[3] = decode_frag(ra[3].y, sa[3].y);
+      *reinterpret_cast<uint32_t*>(nbase + st_scale) = sws;
+    });
+    f16x8 fb1, fb2, fb3;
+    column(fa1, decode_frag(rb[0].y, sbv[0].y), 0, [&] {
+      fb1 = decode_frag(rb[1].y, sbv[1].y);
+      fb2 = decode_frag(rb[2].y, sbv[2].y);
+    });
+    column(fa1, fb1, 1, [&] {
+      fb3 = decode_frag(rb[3].y, sbv[3].y);
+      __syncthreads();
+      read_raw(nbase);
+    });
+    column(fa1, fb2, 2, [&] {
+      fa0[0] = decode_frag(ra[0].x, sa[0].x);
+      fa0[1] = decode_frag(ra[1].x, sa[1].x);
+    });
+    column(fa1, fb3, 3, [&] {
+      fa0[2] = decode_frag(ra[2].x, sa[2].x);
+      fa0[3] = decode_frag(ra[3].x, sa[3].x);
+    });
   };
 
-  // Step s on stage s%2 (raw fragments in registers, slice-0 A fragments
-  // decoded):
-  //   slice 0, columns 0..3: the A fragments of slice 1; the fetch of step
-  //            s+2 after column 0
-  //   slice 1, column 0: mask and scale word of the block fetched during
-  //            step s-1 (step s+1); column 1: its transpose and LDS writes
-  //            into stage (s+1)%2, read by nobody since the last barrier,
-  //            and the next fetch; columns 0 and 1 also decode the B
-  //            fragments of columns 2 and 3, whose raw fragments the
-  //            barrier and the reads of stage (s+1)%2 after column 2
-  //            replace; column 3: the slice-0 A fragments of step s+1.
   const int nsteps = (t.kb_end - t.kb_begin + KB - 1) / KB;
   if (nsteps > 0) {
-    fetch();
-    prepare_a();
-    prepare_b();
-    write_staged(0);
-    fetch();
+    RawBlock<FMT_E2M1> g0, g1;  // blocks of even and odd steps
+    fetch(g0);
+    fetch(g1);
+    __syncthreads();  // scale-word table
+    lookup_scale(g0);
+    write_rows(g0, lds, 0);
+    write_rows(g0, lds, 4);
+    *reinterpret_cast<uint32_t*>(lds + st_scale) = sws;
+    fetch(g0);
     __syncthreads();
-    read_raw(0);
+    read_raw(lds);
 #pragma unroll
     for (int i = 0; i < RM; ++i) fa0[i] = decode_frag(ra[i].x, sa[i].x);
-    for (int s = 0; s < nsteps; ++s) {
-      const int nxt = (s + 1) & 1;
-      column(fa0, rb[0].x, sbv[0].x, 0, [&] { fa1[0] = decode_frag(ra[0].y, sa[0].y); });
-      column(fa0, rb[1].x, sbv[1].x, 1, [&] { fa1[1] = decode_frag(ra[1].y, sa[1].y); });
-      column(fa0, rb[2].x, sbv[2].x, 2, [&] { fa1[2] = decode_frag(ra[2].y, sa[2].y); });
-      column(fa0, rb[3].x, sbv[3].x, 3, [&] { fa1[3] = decode_frag(ra[3].y, sa[3].y); });
-      f16x8 fb2, fb3;
-      column(fa1, rb[0].y, sbv[0].y, 0, [&] {
-        prepare_a();
-        fb2 = decode_frag(rb[2].y, sbv[2].y);
-      });
-      column(fa1, rb[1].y, sbv[1].y, 1, [&] {
-        prepare_b();
-        write_staged(nxt);
-        fetch();
-        fb3 = decode_frag(rb[3].y, sbv[3].y);
-      });
-      column_dec(fa1, fb2, 2, [&] {
-        __syncthreads();
-        read_raw(nxt);
-      });
-      column_dec(fa1, fb3, 3, [&] {
-#pragma unroll
-        for (int i = 0; i < RM; ++i) fa0[i] = decode_frag(ra[i].x, sa[i].x);
-      });
+    // an odd step count runs one more step, on padding blocks only (zero
+    // scale words: it adds exact zeros)
+    for (int s = 0; s < nsteps; s += 2) {
+      step(IC<1>{}, g1);
+      step(IC<0>{}, g0);
     }
   }
   store_tile<OP, MT, NT, KB, WTM, WTN, RM, RN>(p, t, acc, lane, wm, wn);
@@ -1158,7 +1299,7 @@ template <int OP, int FMT>
 void launch_fmt(const ConvParams& p, const Tile& t, dim3 grid, hipStream_t s) {
   // E2M1 on the 4-k-block tiles: codes in LDS, decoded at fragment read
   if constexpr (FMT == FMT_E2M1) {
-    if (t.mt == 256) {
+    if (t.mt == 256 && kwalk_ok(OP, p, 4)) {
       hipLaunchKernelGGL((k_conv4w<OP>), grid, dim3(256), 0, s, p);
       return;
     }

@@ -34,6 +34,11 @@ SHAPES = [
     (128, 128, 8, 32, 32, 1, 1, 1, 1, 0, 0),   # dgrad on the 128x256 tile (E2M1: decode at read)
     (128, 8, 256, 32, 32, 1, 1, 1, 1, 0, 0),   # fwd on the 256x256 tile
     (128, 256, 8, 32, 32, 1, 1, 1, 1, 0, 0),   # dgrad on the 256x256 tile
+    # E2M1 256x256 tiles with the incremental K walk (channel blocks >= 4)
+    (128, 32, 256, 32, 32, 1, 1, 1, 1, 0, 0),  # fwd: one K step (odd step count)
+    (128, 32, 256, 32, 32, 3, 3, 1, 1, 1, 1),  # fwd: 9 K steps across taps and padding
+    (32, 256, 32, 64, 64, 3, 3, 2, 2, 1, 1),   # dgrad: 4 phases of 4, 2, 2 and 1 taps
+    (32, 256, 256, 12, 12, 3, 3, 1, 1, 1, 1),  # wgrad: 2304 columns, split K
 ]
 
 
