@@ -39,46 +39,46 @@ __host__ __device__ constexpr float pow2(int k) {
   return k >= 0 ? float(1ull << k) : 1.0f / float(1ull << -k);
 }
 
-// Round-to-nearest-even magnitude code of v >= 0 (v may be +inf).
+// Round-to-nearest-even magnitude code of v >= 0 (v may be +inf).  Both
+// the subnormal and the normal candidate are computed and one is selected
+// (no divergent branch).
 template <class F>
 __device__ __forceinline__ uint32_t rne_code(float v) {
-  if (!(v < F::MAXV)) return F::MAXCODE;
   constexpr float MIN_NORMAL = pow2(1 - F::BIAS);
-  if (v < MIN_NORMAL) {
-    // subnormal grid step 2^(1-BIAS-MB): code = nearest integer of v / step
-    return static_cast<uint32_t>(__builtin_rintf(v * pow2(F::MB + F::BIAS - 1)));
-  }
+  // subnormal grid step 2^(1-BIAS-MB): code = nearest integer of v / step
+  const uint32_t sub = static_cast<uint32_t>(__builtin_rintf(fminf(v, MIN_NORMAL) * pow2(F::MB + F::BIAS - 1)));
   constexpr int SH = 23 - F::MB;
   uint32_t b = __float_as_uint(v);
   b += ((1u << (SH - 1)) - 1u) + ((b >> SH) & 1u);
-  return (b >> SH) - static_cast<uint32_t>((127 - F::BIAS) << F::MB);
+  const uint32_t nor = (b >> SH) - static_cast<uint32_t>((127 - F::BIAS) << F::MB);
+  const uint32_t c = v < MIN_NORMAL ? sub : nor;
+  return v < F::MAXV ? c : static_cast<uint32_t>(F::MAXCODE);
 }
 
 // Stochastic rounding: with lo <= v < hi the neighbouring grid points, round
-// up iff u * (hi - lo) < v - lo (both fp32 operations exact).
+// up iff u * (hi - lo) < v - lo (both fp32 operations exact).  Branch-free
+// like rne_code.
 template <class F>
 __device__ __forceinline__ uint32_t sr_code(float v, float u) {
-  if (!(v < F::MAXV)) return F::MAXCODE;
   constexpr float MIN_NORMAL = pow2(1 - F::BIAS);
-  uint32_t lo;
-  float lov, delta;
-  if (v < MIN_NORMAL) {
-    constexpr float STEP = pow2(1 - F::BIAS - F::MB);
-    float q = __builtin_floorf(v * pow2(F::MB + F::BIAS - 1));
-    lo = static_cast<uint32_t>(q);
-    lov = q * STEP;
-    delta = STEP;
-  } else {
-    constexpr int SH = 23 - F::MB;
-    uint32_t b = __float_as_uint(v);
-    uint32_t t = b & ~((1u << SH) - 1u);
-    lov = __uint_as_float(t);
-    lo = (t >> SH) - static_cast<uint32_t>((127 - F::BIAS) << F::MB);
-    delta = __uint_as_float((b & 0x7F800000u) - (static_cast<uint32_t>(F::MB) << 23));
-  }
-  float diff = v - lov;
-  float thr = u * delta;
-  return lo + (thr < diff ? 1u : 0u);
+  constexpr float STEP = pow2(1 - F::BIAS - F::MB);
+  // subnormal range: lo = floor(v / step)
+  const float qs = __builtin_floorf(fminf(v, MIN_NORMAL) * pow2(F::MB + F::BIAS - 1));
+  const uint32_t lo_s = static_cast<uint32_t>(qs);
+  const float lov_s = qs * STEP;
+  // normal range: truncate the mantissa to MB bits
+  constexpr int SH = 23 - F::MB;
+  const uint32_t b = __float_as_uint(v);
+  const uint32_t t = b & ~((1u << SH) - 1u);
+  const uint32_t lo_n = (t >> SH) - static_cast<uint32_t>((127 - F::BIAS) << F::MB);
+  const float lov_n = __uint_as_float(t);
+  const float delta_n = __uint_as_float((b & 0x7F800000u) - (static_cast<uint32_t>(F::MB) << 23));
+  const bool sub = v < MIN_NORMAL;
+  const uint32_t lo = sub ? lo_s : lo_n;
+  const float diff = v - (sub ? lov_s : lov_n);
+  const float thr = u * (sub ? STEP : delta_n);
+  const uint32_t c = lo + (thr < diff ? 1u : 0u);
+  return v < F::MAXV ? c : static_cast<uint32_t>(F::MAXCODE);
 }
 
 // Value of a magnitude code as fp32 (exact).
@@ -91,16 +91,28 @@ __device__ __forceinline__ float code_value(uint32_t mag) {
   return e ? normal : sub;
 }
 
-// SplitMix64 output function (Steele, Lea & Flood, OOPSLA 2014) and the
-// 24-bit uniform drawn for element `idx`.
+// SplitMix64 output function (Steele, Lea & Flood, OOPSLA 2014).  The
+// stochastic-rounding uniform of element idx takes 24 bits of the output for
+// counter idx / 2: bits 40..63 for an even idx, bits 16..39 for an odd one.
 __device__ __forceinline__ uint64_t splitmix64(uint64_t z) {
   z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
   z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
   return z ^ (z >> 31);
 }
+constexpr uint64_t kGolden64 = 0x9E3779B97F4A7C15ull;
+__device__ __forceinline__ float u24(uint32_t bits) {
+  return static_cast<float>(bits) * (1.0f / 16777216.0f);
+}
+// the two uniforms of elements 2k, 2k+1 from gk = kGolden64 * (k + 1)
+__device__ __forceinline__ void sr_uniform_pair(uint64_t seed, uint64_t gk, float& u_even, float& u_odd) {
+  const uint64_t h = splitmix64(seed ^ gk);
+  u_even = u24(static_cast<uint32_t>(h >> 40));
+  u_odd = u24(static_cast<uint32_t>(h >> 16) & 0xFFFFFFu);
+}
 __device__ __forceinline__ float sr_uniform(uint64_t seed, uint64_t idx) {
-  uint64_t h = splitmix64(seed ^ (0x9E3779B97F4A7C15ull * (idx + 1ull)));
-  return static_cast<float>(static_cast<uint32_t>(h >> 40)) * (1.0f / 16777216.0f);
+  float ue, uo;
+  sr_uniform_pair(seed, kGolden64 * ((idx >> 1) + 1ull), ue, uo);
+  return (idx & 1ull) ? uo : ue;
 }
 
 // Exchange a 32-bit value with the neighbouring lane (lane ^ 1) through DPP

@@ -11,7 +11,8 @@
 //                as one 32-bit partial into a scratch tail behind the block
 //                scales (the scales buffer is sized for it);
 //   k_quantize   every wave reduces the partials to the tensor amax and T,
-//                then quantizes 8 blocks per iteration, 8 lanes per block
+//                then quantizes 8 blocks per iteration (the next 8 already
+//                in flight), 8 lanes per block
 //                (lane = block row: 8 consecutive batch elements, 32 bytes,
 //                for activations and gradients).  The block amax is a DPP
 //                max across the 8 lanes; each lane packs and stores its own
@@ -29,7 +30,24 @@ constexpr int kQuantMaxWGs = 2048;
 struct QDims {
   int64_t nblocks;
   int32_t d0, d1, d2, d3;  // ACT/GRAD: H, W, C, N   WEIGHT: Co, Ci, Kh, Kw
+  // ACT/GRAD: division by the batch-block and channel-block counts as
+  // mulhi(x, m) >> s (m = 0: divisor 1)
+  uint32_t m_nb, m_cb;
+  int32_t s_nb, s_cb;
 };
+
+// Magic multiplier for x / d with x < 2^31: m = ceil(2^(31+l) / d),
+// l = ceil(log2 d), so that floor(x / d) = floor(x m / 2^(31+l)).
+inline void magic_div(uint32_t d, uint32_t& m, int32_t& sh) {
+  if (d <= 1) { m = 0; sh = 0; return; }
+  int l = 0;
+  while ((1ull << l) < d) ++l;
+  m = static_cast<uint32_t>(((1ull << (31 + l)) + d - 1) / d);
+  sh = l - 1;  // applied to the high 32 bits of the 64-bit product
+}
+__device__ __forceinline__ uint32_t magic_quot(uint32_t x, uint32_t m, int32_t sh) {
+  return m == 0u ? x : (__umulhi(x, m) >> sh);
+}
 
 __device__ __forceinline__ uint32_t absbits(uint32_t v) { return v & 0x7FFFFFFFu; }
 __device__ __forceinline__ uint32_t max4(uint4 v) {
@@ -39,11 +57,14 @@ __device__ __forceinline__ uint32_t max4(uint4 v) {
 // Max |x| as the unsigned max of the bit patterns with the sign cleared:
 // exact, order-independent, and Inf/NaN come out at or above 0x7F800000.
 // Workgroup b writes its share's max to part[b]; every workgroup writes.
-__global__ __launch_bounds__(kThreads) void k_amax_part(const uint4* __restrict__ src, int64_t n4,
-                                                        uint32_t* __restrict__ part) {
+// 16 waves per workgroup: with at most kAmaxMaxPartials workgroups, 8 loads
+// of 16 bytes in flight per lane still make 128 KiB per CU.
+constexpr int kAmaxThreads = 1024;
+__global__ __launch_bounds__(kAmaxThreads) void k_amax_part(const uint4* __restrict__ src, int64_t n4,
+                                                            uint32_t* __restrict__ part) {
   uint32_t m = 0;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
-  int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kAmaxThreads;
+  int64_t i = static_cast<int64_t>(blockIdx.x) * kAmaxThreads + threadIdx.x;
   for (; i + 7 * stride < n4; i += 8 * stride) {
     uint4 v[8];
 #pragma unroll
@@ -53,12 +74,12 @@ __global__ __launch_bounds__(kThreads) void k_amax_part(const uint4* __restrict_
   }
   for (; i < n4; i += stride) m = max(m, max4(src[i]));
   for (int off = 32; off > 0; off >>= 1) m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), off)));
-  __shared__ uint32_t wmax[kThreads / 64];
+  __shared__ uint32_t wmax[kAmaxThreads / 64];
   if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
     uint32_t r = wmax[0];
-    for (int k = 1; k < kThreads / 64; ++k) r = max(r, wmax[k]);
+    for (int k = 1; k < kAmaxThreads / 64; ++k) r = max(r, wmax[k]);
     part[blockIdx.x] = r;
   }
 }
@@ -87,9 +108,9 @@ __device__ __forceinline__ BlockAddr block_addr(const QDims& d, int64_t blk) {
     a.col = khkw;
   } else {
     const uint32_t nb_n = static_cast<uint32_t>(d.d3) >> 3, cb_n = static_cast<uint32_t>(d.d2) >> 3;
-    const uint32_t t = b / nb_n;
+    const uint32_t t = magic_quot(b, d.m_nb, d.s_nb);
     const uint32_t nb = b - t * nb_n;
-    const uint32_t p = t / cb_n;
+    const uint32_t p = magic_quot(t, d.m_cb, d.s_cb);
     const uint32_t cb = t - p * cb_n;
     a.base = (static_cast<int64_t>(p) * d.d2 + cb * 8) * d.d3 + nb * 8;
     a.row = d.d3;
@@ -128,6 +149,54 @@ __device__ __forceinline__ void store_row(uint8_t* __restrict__ codes, int64_t b
   }
 }
 
+typedef short short2v __attribute__((ext_vector_type(2)));
+
+// RN(a / b) from y = RN(1 / b) with two fused multiply-adds: the residual
+// a - b q of q = RN(a y) is exact and RN(q + (a - b q) y) = RN(a / b)
+// (Markstein, IBM J. Res. Dev. 34(1), 1990) as long as nothing under- or
+// overflows.  That holds when b is in [2^-125, 2^125], a is 0 or at least
+// max(2^-100, b 2^-98) (so that q >= 2^-100 and the residual is not
+// subnormal) and a / b is below 2^100; callers check the first two and
+// divide otherwise, the third holds by construction at every call.
+__device__ __forceinline__ float div_by_recip(float a, float b, float y) {
+  const float q = a * y;
+  return __builtin_fmaf(__builtin_fmaf(-q, b, a), y, q);
+}
+
+// E4M3 round-to-nearest-even code of b >= 0 through the hardware packed
+// conversion (identical to rne_code<ScaleFmt> once b is clamped to 448).
+__device__ __forceinline__ uint32_t rne_e4m3_hw(float b) {
+  const short2v w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(short2v{0, 0}, fminf(b, 448.0f), 0.0f, 1.0f, false);
+  return static_cast<uint32_t>(static_cast<uint16_t>(w.x)) & 0xFFu;
+}
+
+// The 8 source values of code row r of block blk (blk clamped to block 0
+// when past the tensor: always loaded, never stored).
+template <int ROLE>
+struct RowIn {
+  float x[8];
+  int64_t rowbase, col;
+  __device__ __forceinline__ void load(const float* __restrict__ src, const QDims& d, int64_t blk, int r) {
+    const BlockAddr ad = block_addr<ROLE>(d, blk);
+    rowbase = ad.base + r * ad.row;
+    col = ad.col;
+    if (d.nblocks == 0) {  // an empty tensor: nothing to read
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = 0.0f;
+      return;
+    }
+    if constexpr (ROLE == MX_ROLE_WEIGHT) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = src[rowbase + j * ad.col];
+    } else {
+      const float4 v0 = *reinterpret_cast<const float4*>(src + rowbase);
+      const float4 v1 = *reinterpret_cast<const float4*>(src + rowbase + 4);
+      x[0] = v0.x; x[1] = v0.y; x[2] = v0.z; x[3] = v0.w;
+      x[4] = v1.x; x[5] = v1.y; x[6] = v1.z; x[7] = v1.w;
+    }
+  }
+};
+
 template <int FMT, int ROLE, bool SR>
 __global__ __launch_bounds__(kThreads) void k_quantize(const float* __restrict__ src,
                                                        uint8_t* __restrict__ codes,
@@ -138,6 +207,17 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const float* __restrict__
   using F = Fmt<FMT>;
   const int lane = threadIdx.x & 63;
   const int r = lane & 7;
+  const int64_t ngroups = (d.nblocks + 7) >> 3;
+  const int64_t gstride = static_cast<int64_t>(gridDim.x) * kGroupsPerWG;
+  int64_t grp = static_cast<int64_t>(blockIdx.x) * kGroupsPerWG + (threadIdx.x >> 6);
+  auto group_blk = [&](int64_t g) {
+    const int64_t b = g * 8 + (lane >> 3);
+    return b < d.nblocks ? b : int64_t{0};
+  };
+
+  // the first rows are requested before the partials: the two loads overlap
+  RowIn<ROLE> cur;
+  cur.load(src, d, group_blk(grp), r);
 
   // tensor amax: the partials of k_amax_part, or the caller's value
   uint32_t ab;
@@ -155,59 +235,115 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const float* __restrict__
     *tensor_scale = T;
     if (nparts >= 0) *amax = __uint_as_float(ab);
   }
+  const float den = F::MAXV * T;
+  const float y_den = 1.0f / den;
+  const bool den_ok = (den >= 0x1p-125f) & (den <= 0x1p125f);
+  const float thr_den = fmaxf(0x1p-100f, den * 0x1p-98f);
 
-  const int64_t ngroups = (d.nblocks + 7) >> 3;
-  const int64_t gstride = static_cast<int64_t>(gridDim.x) * kGroupsPerWG;
-  for (int64_t grp = static_cast<int64_t>(blockIdx.x) * kGroupsPerWG + (threadIdx.x >> 6); grp < ngroups;
-       grp += gstride) {
+  // two stages: the next group's rows are in flight while this one is coded
+  for (; grp < ngroups; grp += gstride) {
     const int64_t blk = grp * 8 + (lane >> 3);
     const bool valid = blk < d.nblocks;
+    RowIn<ROLE> nxt;
+    nxt.load(src, d, group_blk(grp + gstride), r);
     if (nonfinite) {  // T = NaN, scales 0x7F, codes 0
       store_row<FMT>(codes, blk, r, 0u, 0u, valid);
       if (valid && r == 0) scales[blk] = 0x7F;
+      cur = nxt;
       continue;
-    }
-    float x[8];
-    const BlockAddr ad = block_addr<ROLE>(d, valid ? blk : 0);
-    const int64_t rowbase = ad.base + r * ad.row;
-    if constexpr (ROLE == MX_ROLE_WEIGHT) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = valid ? src[rowbase + j * ad.col] : 0.0f;
-    } else {
-      float4 v0 = make_float4(0.f, 0.f, 0.f, 0.f), v1 = v0;
-      if (valid) {
-        v0 = *reinterpret_cast<const float4*>(src + rowbase);
-        v1 = *reinterpret_cast<const float4*>(src + rowbase + 4);
-      }
-      x[0] = v0.x; x[1] = v0.y; x[2] = v0.z; x[3] = v0.w;
-      x[4] = v1.x; x[5] = v1.y; x[6] = v1.z; x[7] = v1.w;
     }
     float am = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(x[j]));
+    for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(cur.x[j]));
     am = max8(am);
 
-    const float den = F::MAXV * T;
-    const float braw = (T == 0.0f) ? 0.0f : am / den;
-    const uint32_t bcode = rne_code<ScaleFmt>(braw);
+    // Quotients a / b are computed as RN(a / b) from y = RN(1/b) without a
+    // division (div_by_recip); the guards send everything else through the
+    // division.  Block scale: the quotient is at most 448 (1 + 2^-23).
+    float braw = div_by_recip(am, den, y_den);
+    if (!((T == 0.0f) | (den_ok & ((am == 0.0f) | (am >= thr_den))))) braw = am / den;
+    braw = (T == 0.0f) ? 0.0f : braw;
+    const uint32_t bcode = rne_e4m3_hw(braw);
     const float B = code_value<ScaleFmt>(bcode);
     const float dd = B * T;
-
-    uint64_t bits = 0;
+    // Elements: |x| / dd is at most 8 * MAXV because dd is the block amax
+    // over MAXV rounded to an E4M3 block scale; a zero block scale gives 0.
+    const float y = 1.0f / dd;
+    const bool dd_ok = (dd >= 0x1p-125f) & (dd <= 0x1p125f);
+    const float thr = fmaxf(0x1p-100f, dd * 0x1p-98f);
+    float v[8];
+    bool any_slow = false;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float v = (dd == 0.0f) ? 0.0f : fabsf(x[j]) / dd;
-      uint32_t mag;
-      if constexpr (SR) {
-        mag = sr_code<F>(v, sr_uniform(seed, static_cast<uint64_t>(rowbase + j * ad.col)));
-      } else {
-        mag = rne_code<F>(v);
+      const float ax = fabsf(cur.x[j]);
+      v[j] = div_by_recip(ax, dd, y);
+      any_slow |= (ax != 0.0f) & (ax < thr);
+    }
+    any_slow = (any_slow | !dd_ok) & (dd != 0.0f);
+    if (any_slow) {  // rare: tiny elements or an extreme block scale
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float ax = fabsf(cur.x[j]);
+        if (!dd_ok | ((ax != 0.0f) & (ax < thr))) v[j] = ax / dd;
       }
-      const uint32_t code = mag | ((__float_as_uint(x[j]) >> 31) << F::SIGN);
-      bits |= static_cast<uint64_t>(code) << (F::BITS * j);
+    }
+
+    uint64_t bits = 0;
+    if constexpr (!SR && (FMT == FMT_E2M1 || FMT == FMT_E4M3)) {
+      // the hardware conversion rounds to nearest even like rne_code and
+      // takes the sign of its input (also of -0); v is clamped to the format
+      // maximum first
+      float sv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sv[j] = __builtin_copysignf(fminf((dd == 0.0f) ? 0.0f : v[j], F::MAXV), cur.x[j]);
+      if constexpr (FMT == FMT_E2M1) {
+        uint32_t w = 0;
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, sv[0], sv[1], 1.0f, 0);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, sv[2], sv[3], 1.0f, 1);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, sv[4], sv[5], 1.0f, 2);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, sv[6], sv[7], 1.0f, 3);
+        bits = w;
+      } else {
+        short2v lo = {0, 0}, hi = {0, 0};
+        lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, sv[0], sv[1], 1.0f, false);
+        lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, sv[2], sv[3], 1.0f, true);
+        hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(hi, sv[4], sv[5], 1.0f, false);
+        hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(hi, sv[6], sv[7], 1.0f, true);
+        bits = static_cast<uint64_t>(__builtin_bit_cast(uint32_t, lo)) |
+               (static_cast<uint64_t>(__builtin_bit_cast(uint32_t, hi)) << 32);
+      }
+    } else {
+      float u[8];
+      if constexpr (SR) {
+        if constexpr (ROLE == MX_ROLE_WEIGHT) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) u[j] = sr_uniform(seed, static_cast<uint64_t>(cur.rowbase + j * cur.col));
+        } else {
+          // a row is 8 consecutive elements from an even index: 4 draws
+          uint64_t gk = kGolden64 * (static_cast<uint64_t>(cur.rowbase >> 1) + 1ull);
+#pragma unroll
+          for (int j = 0; j < 8; j += 2) {
+            sr_uniform_pair(seed, gk, u[j], u[j + 1]);
+            gk += kGolden64;
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float vj = (dd == 0.0f) ? 0.0f : v[j];
+        uint32_t mag;
+        if constexpr (SR) {
+          mag = sr_code<F>(vj, u[j]);
+        } else {
+          mag = rne_code<F>(vj);
+        }
+        const uint32_t code = mag | ((__float_as_uint(cur.x[j]) >> 31) << F::SIGN);
+        bits |= static_cast<uint64_t>(code) << (F::BITS * j);
+      }
     }
     store_row<FMT>(codes, blk, r, static_cast<uint32_t>(bits), static_cast<uint32_t>(bits >> 32), valid);
     if (valid && r == 0) scales[blk] = static_cast<uint8_t>(bcode);
+    cur = nxt;
   }
 }
 
@@ -273,6 +409,12 @@ QDims make_qdims(const Geom& g, mx_role role) {
   } else {
     d.d0 = g.ho; d.d1 = g.wo; d.d2 = g.c_out; d.d3 = g.n;
   }
+  d.m_nb = d.m_cb = 0;
+  d.s_nb = d.s_cb = 0;
+  if (role != MX_ROLE_WEIGHT) {
+    magic_div(static_cast<uint32_t>(d.d3 >> 3), d.m_nb, d.s_nb);
+    magic_div(static_cast<uint32_t>(d.d2 >> 3), d.m_cb, d.s_cb);
+  }
   return d;
 }
 
@@ -329,7 +471,7 @@ hipError_t launch_quantize(const Geom& g, mx_role role, const float* src, const 
     nparts = static_cast<int>(amax_partials(d.nblocks));
     if (nparts > 0) {
       part = reinterpret_cast<uint32_t*>(dst->scales + scale_tail_offset(d.nblocks));
-      hipLaunchKernelGGL(k_amax_part, dim3(static_cast<unsigned>(nparts)), dim3(kThreads), 0, s,
+      hipLaunchKernelGGL(k_amax_part, dim3(static_cast<unsigned>(nparts)), dim3(kAmaxThreads), 0, s,
                          reinterpret_cast<const uint4*>(src), n4, part);
     }
   }

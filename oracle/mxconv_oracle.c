@@ -32,9 +32,10 @@
  *   code  = element grid round-to-nearest-even (ties to the even code),
  *           saturating; sign bit = signbit(x)
  *   stochastic rounding: lo <= v < hi adjacent grid points, round up iff
- *           u * (hi - lo) < v - lo, u = top 24 bits of SplitMix64 (Steele,
- *           Lea & Flood, OOPSLA 2014) of seed ^ (0x9E3779B97F4A7C15*(idx+1)),
- *           idx the element's linear index in the fp32 source
+ *           u * (hi - lo) < v - lo, u = 24 bits of h = SplitMix64 (Steele,
+ *           Lea & Flood, OOPSLA 2014) of seed ^ (0x9E3779B97F4A7C15*(idx/2+1))
+ *           (bits 40..63 of h for even idx, bits 16..39 for odd idx), idx the
+ *           element's linear index in the fp32 source
  *   non-finite input: T = NaN, every block scale 0x7F (E4M3 NaN), codes 0
  *
  * All fp32 steps are single IEEE operations (build with -ffp-contract=off, no
@@ -163,10 +164,13 @@ uint64_t orc_splitmix64(uint64_t z) {
   return z ^ (z >> 31);
 }
 
-/* Uniform in [0,1) with 24 random bits, for element index idx. */
+/* Uniform in [0,1) with 24 random bits, for element index idx: elements
+ * 2k and 2k+1 share the SplitMix64 output of counter k, the even one taking
+ * its bits 40..63, the odd one its bits 16..39. */
 float orc_sr_uniform(uint64_t seed, uint64_t idx) {
-  uint64_t h = orc_splitmix64(seed ^ (0x9E3779B97F4A7C15ULL * (idx + 1ULL)));
-  return (float)(h >> 40) * (1.0f / 16777216.0f);
+  uint64_t h = orc_splitmix64(seed ^ (0x9E3779B97F4A7C15ULL * ((idx >> 1) + 1ULL)));
+  uint64_t bits = (idx & 1ULL) ? ((h >> 16) & 0xFFFFFFULL) : (h >> 40);
+  return (float)bits * (1.0f / 16777216.0f);
 }
 
 /* ------------------------------------------------------------------------ */

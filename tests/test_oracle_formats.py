@@ -145,5 +145,10 @@ def test_splitmix64_published_sequence(orc):
     gamma = 0x9E3779B97F4A7C15
     for i, e in enumerate(expect, start=1):
         assert O.splitmix64((gamma * i) % (1 << 64)) == e
-    # u for (seed 0, element 0) is the top 24 bits of the first output
+    # elements 2k and 2k+1 take bits 40..63 and 16..39 of output k+1: for
+    # seed 0 these are fields of the published outputs above
     assert O.sr_uniform(0, 0) == 0xE220A8 / 2.0 ** 24
+    assert O.sr_uniform(0, 1) == 0x397B1D / 2.0 ** 24
+    assert O.sr_uniform(0, 2) == 0x6E789E / 2.0 ** 24
+    assert O.sr_uniform(0, 3) == 0x6AA1B9 / 2.0 ** 24
+    assert O.sr_uniform(0, 7) == ((0xF88BB8A8724C81EC >> 16) & 0xFFFFFF) / 2.0 ** 24
