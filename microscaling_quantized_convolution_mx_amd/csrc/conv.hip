@@ -1184,44 +1184,61 @@ __global__ __launch_bounds__(256) void k_conv4w(const ConvParams p) {
 }
 
 // dW[co][ci][kh][kw] = T_dy * T_x * (sum over splits of the partials
-// [split][co][(kh, kw, ci)]).  One workgroup owns 16 consecutive outputs;
-// its 256 threads are 16 split groups x 16 outputs (a group reads 64
-// contiguous bytes of one partial), each summing every 16th split with 4
-// independent accumulators; the 64 partial sums of an output are combined in
-// a fixed order, so the result does not depend on timing.
-constexpr int kRedOut = 16;
-__global__ __launch_bounds__(256) void k_wgrad_reduce(const float* __restrict__ ws, int splits, int M,
+// [split][co][(kh, kw, ci)]).  A thread owns 4 consecutive outputs (16-byte
+// loads, whole 1 KiB rows per wave) and one of G split groups: group g sums
+// splits g, g+G, g+2G, ... in that order; the G group sums are combined in
+// LDS in group order.  The summation order depends only on the shape, so
+// the result does not depend on timing.  G (1..64) is chosen so that small
+// outputs still spread over enough threads.
+template <int G>
+__global__ __launch_bounds__(256) void k_wgrad_reduce(const float4* __restrict__ ws, int splits, int64_t quads,
                                                       int ncol, int c_in, int k_h, int k_w,
                                                       const float* __restrict__ ta,
                                                       const float* __restrict__ tb, float* __restrict__ dw) {
-  const int64_t total = static_cast<int64_t>(M) * ncol;
-  const int o = threadIdx.x & (kRedOut - 1), g = threadIdx.x / kRedOut;  // g: split group 0..15
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * kRedOut + o;
-  float s[4] = {0.f, 0.f, 0.f, 0.f};
-  if (idx < total) {
+  constexpr int QPW = 256 / G;  // output quads per workgroup
+  const int g = threadIdx.x / QPW, qi = threadIdx.x - g * QPW;
+  const int64_t q = static_cast<int64_t>(blockIdx.x) * QPW + qi;
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (q < quads) {
     int z = g;
-    for (; z + 48 < splits; z += 64) {
-      s[0] += ws[static_cast<int64_t>(z) * total + idx];
-      s[1] += ws[static_cast<int64_t>(z + 16) * total + idx];
-      s[2] += ws[static_cast<int64_t>(z + 32) * total + idx];
-      s[3] += ws[static_cast<int64_t>(z + 48) * total + idx];
+    for (; z + 3 * G < splits; z += 4 * G) {  // 4 loads in flight, summed in split order
+      const float4 a = ws[static_cast<int64_t>(z) * quads + q];
+      const float4 b = ws[static_cast<int64_t>(z + G) * quads + q];
+      const float4 c = ws[static_cast<int64_t>(z + 2 * G) * quads + q];
+      const float4 d = ws[static_cast<int64_t>(z + 3 * G) * quads + q];
+      s.x += a.x; s.y += a.y; s.z += a.z; s.w += a.w;
+      s.x += b.x; s.y += b.y; s.z += b.z; s.w += b.w;
+      s.x += c.x; s.y += c.y; s.z += c.z; s.w += c.w;
+      s.x += d.x; s.y += d.y; s.z += d.z; s.w += d.w;
     }
-    for (int u = 0; z < splits; z += 16, ++u) s[u] += ws[static_cast<int64_t>(z) * total + idx];
+    for (; z < splits; z += G) {
+      const float4 a = ws[static_cast<int64_t>(z) * quads + q];
+      s.x += a.x; s.y += a.y; s.z += a.z; s.w += a.w;
+    }
   }
-  __shared__ float part[16][4][kRedOut];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) part[g][u][o] = s[u];
-  __syncthreads();
-  if (g == 0 && idx < total) {
-    float r = 0.0f;
-    for (int gg = 0; gg < 16; ++gg)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) r += part[gg][u][o];
-    const int co = static_cast<int>(idx / ncol), j = static_cast<int>(idx - static_cast<int64_t>(co) * ncol);
-    const int tap = j / c_in, ci = j - tap * c_in;
-    const int kh = tap / k_w, kw = tap - kh * k_w;
-    dw[((static_cast<int64_t>(co) * c_in + ci) * k_h + kh) * k_w + kw] = r * ((*ta) * (*tb));
+  if constexpr (G > 1) {
+    __shared__ float4 part[G][QPW];
+    part[g][qi] = s;
+    __syncthreads();
+    if (g != 0) return;
+#pragma unroll 4
+    for (int k = 1; k < G; ++k) {
+      const float4 a = part[k][qi];
+      s.x += a.x; s.y += a.y; s.z += a.z; s.w += a.w;
+    }
   }
+  if (q >= quads) return;
+  const float scale = (*ta) * (*tb);
+  // columns 4r..4r+3 of output row co: one tap, 4 consecutive input channels
+  const int64_t idx = q * 4;
+  const int co = static_cast<int>(idx / ncol), j = static_cast<int>(idx - static_cast<int64_t>(co) * ncol);
+  const int tap = j / c_in, ci = j - tap * c_in;
+  const int taps = k_h * k_w;
+  float* out = dw + (static_cast<int64_t>(co) * c_in + ci) * taps + tap;
+  out[0] = s.x * scale;
+  out[taps] = s.y * scale;
+  out[2 * taps] = s.z * scale;
+  out[3 * taps] = s.w * scale;
 }
 
 // ---- tile selection and launch -------------------------------------------
@@ -1411,10 +1428,25 @@ hipError_t launch_conv_wgrad(const Geom& g, const mx_qtensor* dyq, const mx_qten
   p.out = static_cast<float*>(workspace);
   dim3 grid((p.ncol + pl.t.nt - 1) / pl.t.nt, (p.M + pl.t.mt - 1) / pl.t.mt, pl.splits);
   launch_op<OP_WGRAD>(p, g.fmt, pl.t, grid, s);
-  const int64_t total = static_cast<int64_t>(p.M) * p.ncol;
-  const unsigned rg = static_cast<unsigned>((total + kRedOut - 1) / kRedOut);
-  hipLaunchKernelGGL(k_wgrad_reduce, dim3(rg), dim3(256), 0, s, static_cast<const float*>(workspace),
-                     pl.splits, p.M, p.ncol, g.c_in, g.k_h, g.k_w, dyq->tensor_scale, xq->tensor_scale, dw);
+  // ncol = Kh*Kw*C_in is a multiple of 8: whole quads of outputs
+  const int64_t quads = static_cast<int64_t>(p.M) * p.ncol / 4;
+  int gsplit = 1;  // split groups: at least 2^18 threads where the splits allow
+  while (gsplit < 64 && gsplit < pl.splits && quads * gsplit < (int64_t{1} << 18)) gsplit *= 2;
+  const unsigned rg = static_cast<unsigned>((quads + 256 / gsplit - 1) / (256 / gsplit));
+  const float4* wsq = static_cast<const float4*>(workspace);
+  auto red = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(rg), dim3(256), 0, s, wsq, pl.splits, quads, p.ncol, g.c_in, g.k_h, g.k_w,
+                       dyq->tensor_scale, xq->tensor_scale, dw);
+  };
+  switch (gsplit) {
+    case 1: red(k_wgrad_reduce<1>); break;
+    case 2: red(k_wgrad_reduce<2>); break;
+    case 4: red(k_wgrad_reduce<4>); break;
+    case 8: red(k_wgrad_reduce<8>); break;
+    case 16: red(k_wgrad_reduce<16>); break;
+    case 32: red(k_wgrad_reduce<32>); break;
+    default: red(k_wgrad_reduce<64>); break;
+  }
   return hipGetLastError();
 }
 
