@@ -1351,8 +1351,7 @@ ConvParams base_params(const Geom& g) {
   return p;
 }
 
-// Weight gradient: tile and split count.  Up to 2048 waves, at least 4 K
-// steps per split.
+// Weight gradient: tile and split count.  At least 4 K steps per split.
 struct WgradPlan {
   Tile t;
   int splits;
@@ -1364,8 +1363,13 @@ WgradPlan wgrad_plan(const Geom& g) {
   const Tile t = pick_wgrad_tile(g.c_out, ncol, g.fmt);
   const int64_t ksteps = (kb_total + t.kb - 1) / t.kb;
   const int64_t tiles = ((g.c_out + t.mt - 1) / t.mt) * ((ncol + t.nt - 1) / t.nt);
-  // rounded down: a last, nearly empty round of workgroups costs a full one
-  int64_t splits = (2048 / t.waves) / tiles;
+  // About one round of workgroups: 1024 waves, or 2048 for the 128x256 E2M1
+  // tile, which runs two workgroups per CU.  More splits shorten each K loop
+  // but add partials to write and reduce (a sweep over the ResNet stacks put
+  // the optimum there).  Rounded down: a last, nearly empty round of
+  // workgroups costs a full one.
+  const int64_t target_waves = (g.fmt == FMT_E2M1 && t.mt == 128 && t.nt == 256) ? 2048 : 1024;
+  int64_t splits = (target_waves / t.waves) / tiles;
   const int64_t max_by_k = ksteps / 4;
   if (splits > max_by_k) splits = max_by_k;
   if (splits < 1) splits = 1;
