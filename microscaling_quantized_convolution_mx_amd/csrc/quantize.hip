@@ -197,8 +197,13 @@ struct RowIn {
   }
 };
 
-template <int FMT, int ROLE, bool SR>
-__global__ __launch_bounds__(kThreads) void k_quantize(const float* __restrict__ src,
+// ONE: a single 1024-thread workgroup that also computes the amax (nparts
+// >= 0) over the whole tensor first, for tensors of at most kOneBlocks
+// blocks (up to 4 loads of 16 bytes per thread): one launch instead of two.
+constexpr int kOneThreads = 1024;
+constexpr int64_t kOneBlocks = 256;  // at most 2 groups per wave
+template <int FMT, int ROLE, bool SR, bool ONE>
+__global__ __launch_bounds__(ONE ? kOneThreads : kThreads) void k_quantize(const float* __restrict__ src,
                                                        uint8_t* __restrict__ codes,
                                                        uint8_t* __restrict__ scales,
                                                        float* __restrict__ tensor_scale,
@@ -208,8 +213,8 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const float* __restrict__
   const int lane = threadIdx.x & 63;
   const int r = lane & 7;
   const int64_t ngroups = (d.nblocks + 7) >> 3;
-  const int64_t gstride = static_cast<int64_t>(gridDim.x) * kGroupsPerWG;
-  int64_t grp = static_cast<int64_t>(blockIdx.x) * kGroupsPerWG + (threadIdx.x >> 6);
+  const int64_t gstride = ONE ? kOneThreads / 64 : static_cast<int64_t>(gridDim.x) * kGroupsPerWG;
+  int64_t grp = (ONE ? 0 : static_cast<int64_t>(blockIdx.x) * kGroupsPerWG) + (threadIdx.x >> 6);
   auto group_blk = [&](int64_t g) {
     const int64_t b = g * 8 + (lane >> 3);
     return b < d.nblocks ? b : int64_t{0};
@@ -223,8 +228,29 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const float* __restrict__
   uint32_t ab;
   if (nparts >= 0) {
     uint32_t m = 0;
-    for (int i = lane; i < nparts; i += 64) m = max(m, part[i]);
+    if constexpr (ONE) {
+      const uint4* s4 = reinterpret_cast<const uint4*>(src);
+      const int64_t n4 = d.nblocks * 16;
+      int64_t i = threadIdx.x;
+      for (; i + 3 * kOneThreads < n4; i += 4 * kOneThreads) {  // 4 loads in flight
+        uint4 v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = s4[i + k * kOneThreads];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) m = max(m, max4(v[k]));
+      }
+      for (; i < n4; i += kOneThreads) m = max(m, max4(s4[i]));
+    } else {
+      for (int i = lane; i < nparts; i += 64) m = max(m, part[i]);
+    }
     for (int off = 32; off > 0; off >>= 1) m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), off)));
+    if constexpr (ONE) {
+      __shared__ uint32_t wmax[kOneThreads / 64];
+      if (lane == 0) wmax[threadIdx.x >> 6] = m;
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < kOneThreads / 64; ++k) m = max(m, wmax[k]);
+    }
     ab = m;
   } else {
     ab = __float_as_uint(*amax) & 0x7FFFFFFFu;
@@ -420,27 +446,36 @@ QDims make_qdims(const Geom& g, mx_role role) {
 
 template <int FMT, int ROLE>
 void launch_q(const QDims& d, const float* src, const mx_qtensor* q, bool sr, uint64_t seed,
-              const uint32_t* part, int nparts, hipStream_t s) {
+              const uint32_t* part, int nparts, bool one, hipStream_t s) {
+  auto* codes = static_cast<uint8_t*>(q->codes);
+  if (one) {  // nparts >= 0: the kernel computes the amax itself
+    if (sr)
+      hipLaunchKernelGGL((k_quantize<FMT, ROLE, true, true>), dim3(1), dim3(kOneThreads), 0, s, src, codes,
+                         q->scales, q->tensor_scale, q->amax, part, nparts, d, seed);
+    else
+      hipLaunchKernelGGL((k_quantize<FMT, ROLE, false, true>), dim3(1), dim3(kOneThreads), 0, s, src, codes,
+                         q->scales, q->tensor_scale, q->amax, part, nparts, d, seed);
+    return;
+  }
   // at least one workgroup, so that an empty tensor still publishes T
   int64_t wgs = (d.nblocks + 8 * kGroupsPerWG - 1) / (8 * kGroupsPerWG);
   if (wgs > kQuantMaxWGs) wgs = kQuantMaxWGs;
   if (wgs < 1) wgs = 1;
   const dim3 grid(static_cast<unsigned>(wgs));
-  auto* codes = static_cast<uint8_t*>(q->codes);
   if (sr)
-    hipLaunchKernelGGL((k_quantize<FMT, ROLE, true>), grid, dim3(kThreads), 0, s, src, codes, q->scales,
+    hipLaunchKernelGGL((k_quantize<FMT, ROLE, true, false>), grid, dim3(kThreads), 0, s, src, codes, q->scales,
                        q->tensor_scale, q->amax, part, nparts, d, seed);
   else
-    hipLaunchKernelGGL((k_quantize<FMT, ROLE, false>), grid, dim3(kThreads), 0, s, src, codes, q->scales,
+    hipLaunchKernelGGL((k_quantize<FMT, ROLE, false, false>), grid, dim3(kThreads), 0, s, src, codes, q->scales,
                        q->tensor_scale, q->amax, part, nparts, d, seed);
 }
 
 template <int FMT>
 void launch_q_role(mx_role role, const QDims& d, const float* src, const mx_qtensor* q, bool sr,
-                   uint64_t seed, const uint32_t* part, int nparts, hipStream_t s) {
-  if (role == MX_ROLE_ACT) launch_q<FMT, MX_ROLE_ACT>(d, src, q, sr, seed, part, nparts, s);
-  else if (role == MX_ROLE_GRAD) launch_q<FMT, MX_ROLE_GRAD>(d, src, q, sr, seed, part, nparts, s);
-  else launch_q<FMT, MX_ROLE_WEIGHT>(d, src, q, sr, seed, part, nparts, s);
+                   uint64_t seed, const uint32_t* part, int nparts, bool one, hipStream_t s) {
+  if (role == MX_ROLE_ACT) launch_q<FMT, MX_ROLE_ACT>(d, src, q, sr, seed, part, nparts, one, s);
+  else if (role == MX_ROLE_GRAD) launch_q<FMT, MX_ROLE_GRAD>(d, src, q, sr, seed, part, nparts, one, s);
+  else launch_q<FMT, MX_ROLE_WEIGHT>(d, src, q, sr, seed, part, nparts, one, s);
 }
 
 template <int FMT, int ROLE>
@@ -463,10 +498,13 @@ void launch_dq_role(mx_role role, const QDims& d, const mx_qtensor* q, float* ds
 hipError_t launch_quantize(const Geom& g, mx_role role, const float* src, const mx_qtensor* dst,
                            mx_round rounding, uint64_t seed, int amax_given, hipStream_t s) {
   const QDims d = make_qdims(g, role);
-  // partials of the amax pass: in the scales buffer, behind the block scales
+  const bool sr = rounding == MX_SR;
+  // small tensors: one workgroup, amax included; otherwise the partials of
+  // the amax pass go into the scales buffer, behind the block scales
+  const bool one = d.nblocks <= kOneBlocks;
   uint32_t* part = nullptr;
-  int nparts = -1;  // -1: the caller's amax
-  if (!amax_given) {
+  int nparts = amax_given ? -1 : 0;  // -1: the caller's amax
+  if (!amax_given && !one) {
     const int64_t n4 = d.nblocks * 16;
     nparts = static_cast<int>(amax_partials(d.nblocks));
     if (nparts > 0) {
@@ -475,11 +513,10 @@ hipError_t launch_quantize(const Geom& g, mx_role role, const float* src, const 
                          reinterpret_cast<const uint4*>(src), n4, part);
     }
   }
-  const bool sr = rounding == MX_SR;
   switch (g.fmt) {
-    case FMT_E2M1: launch_q_role<FMT_E2M1>(role, d, src, dst, sr, seed, part, nparts, s); break;
-    case FMT_E2M3: launch_q_role<FMT_E2M3>(role, d, src, dst, sr, seed, part, nparts, s); break;
-    default: launch_q_role<FMT_E4M3>(role, d, src, dst, sr, seed, part, nparts, s); break;
+    case FMT_E2M1: launch_q_role<FMT_E2M1>(role, d, src, dst, sr, seed, part, nparts, one, s); break;
+    case FMT_E2M3: launch_q_role<FMT_E2M3>(role, d, src, dst, sr, seed, part, nparts, one, s); break;
+    default: launch_q_role<FMT_E4M3>(role, d, src, dst, sr, seed, part, nparts, one, s); break;
   }
   return hipGetLastError();
 }
