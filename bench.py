@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate budget of the CPU-baseline sample")
+    ap.add_argument("--producer-amax", action="store_true",
+                    help="chain the stack: where a layer's input has the previous layer's output shape, X is that "
+                         "output, quantized in one pass with the amax its fwd produced (mx_conv_fwd_amax)")
     ap.add_argument("--graph", action="store_true",
                     help="replay the step as one captured HIP graph (per-call timing then comes "
                          "from a separate eager pass)")
@@ -118,6 +121,8 @@ def main():
     keep.append(ws)
 
     t_gen = time.time()
+    prev = None  # --producer-amax: (layer, y, its fwd Call) of the previous layer
+    n_chained = 0
     for li, lay in enumerate(wl.layers):
         d = mx.desc_from_layer(lay, fmt)
         x = WL.gen_x(lay, wl.x_dist, WL.seed_for(wl.cfg_index, li, 1)).to(dev)
@@ -134,9 +139,28 @@ def main():
         shape = lay.tag()
         nx, nw, ny = lay.numel_x(), lay.numel_w(), lay.numel_dy()
         f = lay.flops()
+        # --producer-amax: where the previous layer's output has this layer's
+        # input shape, X is that output, its fwd writes max|y| into qx.amax
+        # and X is quantized in one pass (amax given)
+        chained = (a.producer_amax and prev is not None and (prev[0].h_out, prev[0].w_out, prev[0].c_out, prev[0].n)
+                   == (lay.h, lay.w, lay.c_in, lay.n))  # prev[0] is the previous layer's descriptor
+        if chained:
+            pd, py, pcall = prev
+            # the previous fwd's amax buffer: word 0 is the amax this layer's X is quantized with
+            abuf = torch.empty(mx.mx_fwd_amax_bytes(pd) // 4, device=dev)
+            keep.append(abuf)
+            qx.amax = abuf[:1]
+            cq[0] = qx.c()
+            pcall.fn = L.mx_conv_fwd_amax
+            pcall.args = pcall.args[:-1] + (abuf.data_ptr(), stream)
+            pcall.name = "fwd (+amax)"
+            x_src, x_given, x_bytes = py.data_ptr(), 1, nx * (4 + qb)
+            n_chained += 1
+        else:
+            x_src, x_given, x_bytes = x.data_ptr(), 0, nx * (8 + qb)
         calls += [
-            Call(L.mx_quantize_cbf, (D(d), mx.MX_ROLE_ACT, x.data_ptr(), D(cq[0]), mx.MX_RNE, 0, 0, stream),
-                 "quantize", ("quantize_act", shape), 0, nx * (8 + qb), "quantize X"),
+            Call(L.mx_quantize_cbf, (D(d), mx.MX_ROLE_ACT, x_src, D(cq[0]), mx.MX_RNE, 0, x_given, stream),
+                 "quantize", ("quantize_act", shape), 0, x_bytes, "quantize X"),
             Call(L.mx_quantize_cbf, (D(d), mx.MX_ROLE_WEIGHT, w.data_ptr(), D(cq[1]), mx.MX_RNE, 0, 0, stream),
                  "quantize", ("quantize_weight", shape), 0, nw * (8 + qb), "quantize W"),
             Call(L.mx_quantize_cbf, (D(d), mx.MX_ROLE_GRAD, dy.data_ptr(), D(cq[2]), mx.MX_SR, sr_seed, 0, stream),
@@ -150,6 +174,7 @@ def main():
             Call(L.mx_dequantize, (D(d), mx.MX_ROLE_ACT, D(cq[0]), xdq.data_ptr(), stream),
                  "dequantize", ("dequantize_act", shape), 0, nx * (qb + 4), "dequantize X"),
         ]
+        prev = (d, y, calls[-4])
     if wl.lr_buffer is not None:
         nmaps, c, h, w_ = wl.lr_buffer
         d = mx.desc(nmaps, c, c, h, w_, 1, 1, elem_fmt=mx.MX_E2M1)
@@ -310,7 +335,8 @@ def main():
                    "block": "8x8 E4M3 scale + fp32 tensor scale",
                    "step": "per layer: quantize X,W,dY; fwd; dgrad; wgrad; dequantize Xq"
                            + ("; replay buffer quantize+dequantize" if wl.lr_buffer else ""),
-                   "graph": bool(graph is not None)},
+                   "graph": bool(graph is not None),
+                   "producer_amax": {"chained_layers": n_chained} if a.producer_amax else False},
         "conv_tflops": total_flops / (conv_ms / 1e3) / 1e12 if conv_ms > 0 else None,
         "quantize_gbps": q_bytes / (q_ms / 1e3) / 1e9 if q_ms > 0 else None,
         "step_breakdown_ms": {k: v["ms"] for k, v in by_op.items()},

@@ -112,9 +112,10 @@ size_t mx_wgrad_workspace_bytes(const mx_conv_desc* desc);
  *   B     = E4M3_RNE_sat(blockamax / (max_elem * T))      one per 8x8 block
  *   code  = Round(|x| / (B * T)) on the element grid, sign = sign of x
  * Round is nearest-even (MX_RNE) or stochastic (MX_SR): round up iff
- * u * (hi - lo) < v - lo with u the top 24 bits of
- * SplitMix64(seed ^ 0x9E3779B97F4A7C15 * (i + 1)), i the element's linear
- * index in `src`.  Every fp32 step is one correctly rounded IEEE operation.
+ * u * (hi - lo) < v - lo, where u takes 24 bits of
+ * h = SplitMix64(seed ^ 0x9E3779B97F4A7C15 * (i/2 + 1)): bits 40..63 of h for
+ * an even i, bits 16..39 for an odd i, with i the element's linear index in
+ * `src`.  Every fp32 step is one correctly rounded IEEE operation.
  *   src        fp32 tensor of `role` in the layout above
  *   dst        quantized tensor: codes, scales, tensor_scale and amax written;
  *              codes and scales 16-byte aligned.  The amax pass keeps one
@@ -136,6 +137,22 @@ mx_status mx_quantize_cbf(const mx_conv_desc* desc, mx_role role, const float* s
  * Products of dequantized elements are exact; sums are fp32. */
 mx_status mx_conv_fwd(const mx_conv_desc* desc, const mx_qtensor* wq, const mx_qtensor* xq,
                       float* y, hipStream_t stream);
+
+/* mx_conv_fwd that also produces max |y| over every output element (§VII
+ * loads each tensor once with its statistic estimated ahead of time; here
+ * the producer supplies the exact statistic instead).  Passing y_amax as the
+ * amax of the next quantization of y (amax_given = 1) then skips that
+ * call's amax pass: one read of y instead of two, with the same codes.
+ *   y_amax device buffer of mx_fwd_amax_bytes(desc) bytes, 4-byte aligned;
+ *          y_amax[0] is overwritten with max |y| (the comparison is the
+ *          unsigned order of the sign-cleared bits, so a NaN in y gives a
+ *          NaN amax, which quantizes as non-finite input); the rest of the
+ *          buffer receives one partial maximum per wave of the GEMM (no
+ *          atomics), so its contents are unspecified
+ * Errors as mx_conv_fwd, plus MX_ERR_NULL / MX_ERR_ALIGN for y_amax. */
+size_t mx_fwd_amax_bytes(const mx_conv_desc* desc);
+mx_status mx_conv_fwd_amax(const mx_conv_desc* desc, const mx_qtensor* wq, const mx_qtensor* xq,
+                           float* y, float* y_amax, hipStream_t stream);
 
 /* Data gradient dX = col2im(W_f^T . dY) (§II-A "transposed kernels",
  * §IV-B), evaluated in gather form: each dX element sums exactly the

@@ -28,8 +28,8 @@ STATUS = {0: "MX_OK", -1: "MX_ERR_NULL", -2: "MX_ERR_SHAPE", -3: "MX_ERR_FORMAT"
           -4: "MX_ERR_BLOCK", -5: "MX_ERR_ALIGN", -6: "MX_ERR_WORKSPACE", -7: "MX_ERR_ROLE",
           -8: "MX_ERR_LAUNCH", -9: "MX_ERR_ROUND"}
 
-EXPORTS = ("mx_code_bytes", "mx_scale_bytes", "mx_wgrad_workspace_bytes", "mx_quantize_cbf",
-           "mx_conv_fwd", "mx_conv_dgrad", "mx_conv_wgrad", "mx_dequantize", "mx_status_str")
+EXPORTS = ("mx_code_bytes", "mx_scale_bytes", "mx_wgrad_workspace_bytes", "mx_fwd_amax_bytes", "mx_quantize_cbf",
+           "mx_conv_fwd", "mx_conv_fwd_amax", "mx_conv_dgrad", "mx_conv_wgrad", "mx_dequantize", "mx_status_str")
 
 
 class MxError(RuntimeError):
@@ -82,6 +82,10 @@ def lib() -> ctypes.CDLL:
     for f in ("mx_conv_fwd", "mx_conv_dgrad"):
         getattr(L, f).restype = ctypes.c_int
         getattr(L, f).argtypes = [D, Q, Q, P, P]
+    L.mx_fwd_amax_bytes.restype = ctypes.c_size_t
+    L.mx_fwd_amax_bytes.argtypes = [D]
+    L.mx_conv_fwd_amax.restype = ctypes.c_int
+    L.mx_conv_fwd_amax.argtypes = [D, Q, Q, P, P, P]
     L.mx_conv_wgrad.restype = ctypes.c_int
     L.mx_conv_wgrad.argtypes = [D, Q, Q, P, P, ctypes.c_size_t, P]
     L.mx_dequantize.restype = ctypes.c_int
@@ -178,6 +182,15 @@ def mx_quantize_cbf(d: mx_conv_desc, role: int, src, dst, rounding: int = MX_RNE
 
 def mx_conv_fwd(d: mx_conv_desc, wq, xq, y, stream=None) -> None:
     _check(lib().mx_conv_fwd(ctypes.byref(d), _q(wq), _q(xq), _ptr(y), _stream(stream)), "mx_conv_fwd")
+
+
+def mx_fwd_amax_bytes(d: mx_conv_desc) -> int:
+    return lib().mx_fwd_amax_bytes(ctypes.byref(d))
+
+
+def mx_conv_fwd_amax(d: mx_conv_desc, wq, xq, y, y_amax, stream=None) -> None:
+    _check(lib().mx_conv_fwd_amax(ctypes.byref(d), _q(wq), _q(xq), _ptr(y), _ptr(y_amax), _stream(stream)),
+           "mx_conv_fwd_amax")
 
 
 def mx_conv_dgrad(d: mx_conv_desc, wq, dyq, dx, stream=None) -> None:

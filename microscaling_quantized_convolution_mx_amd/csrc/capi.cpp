@@ -143,7 +143,25 @@ mx_status mx_conv_fwd(const mx_conv_desc* desc, const mx_qtensor* wq, const mx_q
   if ((st = check_qtensor(xq, mx::role_nblocks(g, MX_ROLE_ACT))) != MX_OK) return st;
   if (mx::role_numel(g, MX_ROLE_GRAD) > 0 && !y) return MX_ERR_NULL;
   if (!aligned(y, 16)) return MX_ERR_ALIGN;
-  return launched(mx::launch_conv_fwd(g, wq, xq, y, stream));
+  return launched(mx::launch_conv_fwd(g, wq, xq, y, nullptr, stream));
+}
+
+size_t mx_fwd_amax_bytes(const mx_conv_desc* desc) {
+  if (check_desc(desc) != MX_OK) return 0;
+  return mx::fwd_amax_bytes(mx::make_geom(desc));
+}
+
+mx_status mx_conv_fwd_amax(const mx_conv_desc* desc, const mx_qtensor* wq, const mx_qtensor* xq, float* y,
+                           float* y_amax, hipStream_t stream) {
+  mx_status st = check_desc(desc);
+  if (st != MX_OK) return st;
+  const Geom g = mx::make_geom(desc);
+  if ((st = check_qtensor(wq, mx::role_nblocks(g, MX_ROLE_WEIGHT))) != MX_OK) return st;
+  if ((st = check_qtensor(xq, mx::role_nblocks(g, MX_ROLE_ACT))) != MX_OK) return st;
+  if (mx::role_numel(g, MX_ROLE_GRAD) > 0 && !y) return MX_ERR_NULL;
+  if (!y_amax) return MX_ERR_NULL;
+  if (!aligned(y, 16) || !aligned(y_amax, 4)) return MX_ERR_ALIGN;
+  return launched(mx::launch_conv_fwd(g, wq, xq, y, y_amax, stream));
 }
 
 mx_status mx_conv_dgrad(const mx_conv_desc* desc, const mx_qtensor* wq, const mx_qtensor* dyq,

@@ -73,6 +73,7 @@ struct ConvParams {
   const uint8_t* b_scales;
   const float* b_t;
   float* out;
+  uint32_t* amax_out;  // fwd: per-wave max |y| slots (slot 1 + global wave index; nullptr: not wanted)
 };
 
 // MFMA operand type: E2M1 and E2M3 blocks decode exactly to fp16 (g*B lies in
@@ -405,6 +406,11 @@ __device__ __forceinline__ void store_tile(const ConvParams& p, const TileCtx<OP
   if constexpr (OP == OP_WGRAD) row_stride = p.ncol;
   else row_stride = p.n;
 
+  uint32_t ymax = 0;  // fwd: max over the written outputs of their sign-cleared bits
+  auto put = [&](float* q, float v) {
+    *q = v;
+    if constexpr (OP == OP_FWD) ymax = max(ymax, __float_as_uint(v) & 0x7FFFFFFFu);
+  };
 #pragma unroll
   for (int j = 0; j < RN; ++j) {
     const int col = t.cb0 * 8 + wn * WTN + j * 32 + (lane & 31);  // column in the launch space
@@ -430,15 +436,27 @@ __device__ __forceinline__ void store_tile(const ConvParams& p, const TileCtx<OP
       for (int i = 0; i < RM; ++i)
 #pragma unroll
         for (int v = 0; v < 16; ++v)
-          out[static_cast<int64_t>(row0 + i * 32 + 8 * (v >> 2) + (v & 3)) * row_stride] = acc[i][j][v] * scale;
+          put(out + static_cast<int64_t>(row0 + i * 32 + 8 * (v >> 2) + (v & 3)) * row_stride, acc[i][j][v] * scale);
     } else {
 #pragma unroll
       for (int i = 0; i < RM; ++i)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int row = row0 + i * 32 + 8 * (v >> 2) + (v & 3);
-          if (row < p.M) out[static_cast<int64_t>(row) * row_stride] = acc[i][j][v] * scale;
+          if (row < p.M) put(out + static_cast<int64_t>(row) * row_stride, acc[i][j][v] * scale);
         }
+    }
+  }
+  if constexpr (OP == OP_FWD) {
+    // producer-fused amax: every wave stores the max of its outputs in its
+    // own slot (no atomics); k_amax_finish reduces the slots.  The uint order
+    // of sign-cleared bits is the order of |y|, NaN above everything, as in
+    // the quantizer's amax pass.
+    if (p.amax_out != nullptr) {
+      for (int off = 32; off > 0; off >>= 1)
+        ymax = max(ymax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(ymax), off)));
+      const int64_t wg = blockIdx.x + static_cast<int64_t>(gridDim.x) * (blockIdx.y + static_cast<int64_t>(gridDim.y) * blockIdx.z);
+      if (lane == 0) p.amax_out[1 + wg * (blockDim.x >> 6) + (threadIdx.x >> 6)] = ymax;
     }
   }
 }
@@ -1302,6 +1320,22 @@ Tile pick_wgrad_tile(int64_t M, int64_t ncols, int fmt) {
   return kTiles[1];
 }
 
+// Reduces the per-wave slots of a producer-fused fwd into slot 0 (one
+// workgroup; 0 when there are no slots).
+__global__ __launch_bounds__(1024) void k_amax_finish(uint32_t* __restrict__ w, int64_t nslots) {
+  uint32_t m = 0;
+  for (int64_t i = threadIdx.x; i < nslots; i += 1024) m = max(m, w[1 + i]);
+  for (int off = 32; off > 0; off >>= 1) m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), off)));
+  __shared__ uint32_t wmax[16];
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int k = 1; k < 16; ++k) m = max(m, wmax[k]);
+    w[0] = m;
+  }
+}
+
 template <int OP, int FMT, int MT, int NT, int WM, int WAVES, int KB>
 void launch_tile(const ConvParams& p, dim3 grid, hipStream_t s) {
   hipLaunchKernelGGL((k_conv<OP, FMT, MT, NT, WM, WAVES, KB>), grid, dim3(WAVES * 64), 0, s, p);
@@ -1377,21 +1411,48 @@ WgradPlan wgrad_plan(const Geom& g) {
   return {t, static_cast<int>(splits)};
 }
 
-}  // namespace
+// Forward launch geometry: tile, grid and waves per workgroup.
+struct FwdPlan {
+  Tile t;
+  dim3 grid;
+};
+FwdPlan fwd_plan(const Geom& g, const ConvParams& p) {
+  const Tile t = pick_tile(p.M, static_cast<int64_t>(p.ncb) * 8, 1, g.fmt);
+  return {t, dim3((p.ncb * 8 + t.nt - 1) / t.nt, (p.M + t.mt - 1) / t.mt, 1)};
+}
 
-hipError_t launch_conv_fwd(const Geom& g, const mx_qtensor* wq, const mx_qtensor* xq, float* y,
-                           hipStream_t s) {
+ConvParams fwd_params(const Geom& g) {
   ConvParams p = base_params(g);
   p.M = g.c_out;
   p.ncb = g.ho * g.wo * (g.n / 8);
   p.kb_total = g.k_h * g.k_w * (g.c_in / 8);
+  return p;
+}
+
+}  // namespace
+
+size_t fwd_amax_bytes(const Geom& g) {
+  const ConvParams p = fwd_params(g);
+  if (p.ncb == 0) return 4;
+  const FwdPlan pl = fwd_plan(g, p);
+  return 4 * (1 + static_cast<size_t>(pl.grid.x) * pl.grid.y * pl.grid.z * pl.t.waves);
+}
+
+hipError_t launch_conv_fwd(const Geom& g, const mx_qtensor* wq, const mx_qtensor* xq, float* y,
+                           float* y_amax, hipStream_t s) {
+  ConvParams p = fwd_params(g);
   p.a_codes = static_cast<const uint8_t*>(wq->codes); p.a_scales = wq->scales; p.a_t = wq->tensor_scale;
   p.b_codes = static_cast<const uint8_t*>(xq->codes); p.b_scales = xq->scales; p.b_t = xq->tensor_scale;
   p.out = y;
-  if (p.ncb == 0) return hipSuccess;
-  const Tile t = pick_tile(p.M, static_cast<int64_t>(p.ncb) * 8, 1, g.fmt);
-  dim3 grid((p.ncb * 8 + t.nt - 1) / t.nt, (p.M + t.mt - 1) / t.mt, 1);
-  launch_op<OP_FWD>(p, g.fmt, t, grid, s);
+  p.amax_out = reinterpret_cast<uint32_t*>(y_amax);
+  int64_t nslots = 0;
+  if (p.ncb > 0) {
+    const FwdPlan pl = fwd_plan(g, p);
+    nslots = static_cast<int64_t>(pl.grid.x) * pl.grid.y * pl.grid.z * pl.t.waves;
+    launch_op<OP_FWD>(p, g.fmt, pl.t, pl.grid, s);
+  }
+  if (y_amax != nullptr)
+    hipLaunchKernelGGL(k_amax_finish, dim3(1), dim3(1024), 0, s, p.amax_out, nslots);
   return hipGetLastError();
 }
 

@@ -40,8 +40,11 @@ hipError_t launch_quantize(const Geom& g, mx_role role, const float* src, const 
 hipError_t launch_dequantize(const Geom& g, mx_role role, const mx_qtensor* q, float* dst,
                              hipStream_t s);
 
+// y_amax: nullptr, or a device buffer of fwd_amax_bytes(g) bytes whose first
+// word receives max |y| (exact); the rest holds the per-wave partial maxima
 hipError_t launch_conv_fwd(const Geom& g, const mx_qtensor* wq, const mx_qtensor* xq, float* y,
-                           hipStream_t s);
+                           float* y_amax, hipStream_t s);
+size_t fwd_amax_bytes(const Geom& g);
 hipError_t launch_conv_dgrad(const Geom& g, const mx_qtensor* wq, const mx_qtensor* dyq, float* dx,
                              hipStream_t s);
 hipError_t launch_conv_wgrad(const Geom& g, const mx_qtensor* dyq, const mx_qtensor* xq, float* dw,

@@ -127,6 +127,14 @@ def test_conv_argument_checks():
     assert L.mx_dequantize(ctypes.byref(d), 0, ctypes.byref(good), MIS, None) == -5
     bad = mx.desc(**dict(GOOD, n=4))
     assert L.mx_conv_fwd(ctypes.byref(bad), ctypes.byref(good), ctypes.byref(good), A16, None) == -2
+    # fwd with the producer-fused amax: one word plus one per GEMM wave
+    assert mx.mx_fwd_amax_bytes(d) >= 8 and mx.mx_fwd_amax_bytes(d) % 4 == 0
+    assert mx.mx_fwd_amax_bytes(bad) == 0
+    # fwd with the producer-fused amax: the amax word is checked too
+    assert L.mx_conv_fwd_amax(ctypes.byref(d), ctypes.byref(good), ctypes.byref(good), A16, None, None) == -1
+    assert L.mx_conv_fwd_amax(ctypes.byref(d), ctypes.byref(good), ctypes.byref(good), A16, A16 + 2, None) == -5
+    assert L.mx_conv_fwd_amax(ctypes.byref(d), ctypes.byref(good), ctypes.byref(good), MIS, A16, None) == -5
+    assert L.mx_conv_fwd_amax(ctypes.byref(bad), ctypes.byref(good), ctypes.byref(good), A16, A16, None) == -2
 
 
 def test_binding_raises_on_error():

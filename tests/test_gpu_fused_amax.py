@@ -1,0 +1,89 @@
+"""Forward convolution with the producer-fused amax (mx_conv_fwd_amax).
+
+The paper loads each tensor once and estimates its statistics ahead of time
+(MicroQonv, arXiv 2609.28358, §VII, with Hindsight).  Here the forward GEMM
+that produces Y also returns max |y| exactly, so the next quantization of Y
+can skip its amax pass.  Checked through the C ABI:
+  - Y is bit-identical to mx_conv_fwd's (the same kernels);
+  - the returned amax equals max |y| over every output, computed on the host
+    from Y's bits (the order of the sign-cleared bit patterns);
+  - quantizing Y as the next layer's activation with that amax given gives
+    the same codes, block scales and tensor scale as the two-pass quantizer.
+Y itself is held to the oracle by test_gpu_conv.py on the same kernels."""
+import numpy as np
+import pytest
+import torch
+
+import microscaling_quantized_convolution_mx_amd as mx
+from microscaling_quantized_convolution_mx_amd import workloads as WL
+from gpu_util import DEV, gpu_quantize, say
+
+pytestmark = pytest.mark.gpu
+
+# every forward kernel family: generic tiles, the 128x256 and the 256x256
+# decode-at-read tiles (E2M1), stride 2, ragged tiles
+CASES = [
+    ((8, 16, 16, 16, 16, 3, 3, 1, 1, 0, 0), mx.MX_E2M1),
+    ((8, 16, 8, 9, 10, 3, 3, 2, 2, 1, 1), mx.MX_E2M3),
+    ((32, 40, 264, 11, 9, 3, 3, 1, 1, 1, 1), mx.MX_E4M3),
+    ((128, 8, 128, 32, 32, 1, 1, 1, 1, 0, 0), mx.MX_E2M1),
+    ((128, 32, 256, 32, 32, 3, 3, 1, 1, 1, 1), mx.MX_E2M1),
+]
+
+
+def amax_bits(t: torch.Tensor) -> int:
+    b = t.detach().cpu().contiguous().view(torch.int32).numpy().view(np.uint32) & np.uint32(0x7FFFFFFF)
+    return int(b.max()) if b.size else 0
+
+
+@pytest.mark.parametrize("shape,fmt", CASES)
+def test_fused_amax_matches_output_and_two_pass_quantize(shape, fmt):
+    say("fused amax", shape, fmt)
+    lay = WL.ConvLayer(*shape)
+    d = mx.desc_from_layer(lay, fmt)
+    x, w = WL.gen_x(lay, "normal", 11), WL.gen_w(lay, 12)
+    qx = gpu_quantize(d, mx.MX_ROLE_ACT, x)
+    qw = gpu_quantize(d, mx.MX_ROLE_WEIGHT, w)
+    y0 = torch.full((d.h_out, d.w_out, d.c_out, d.n), float("nan"), device=DEV)
+    y1 = torch.full_like(y0, float("nan"))
+    # first word: the amax; the rest: per-wave partials
+    ya = torch.full((mx.mx_fwd_amax_bytes(d) // 4,), float("nan"), device=DEV)
+    mx.mx_conv_fwd(d, qw, qx, y0)
+    mx.mx_conv_fwd_amax(d, qw, qx, y1, ya)
+    torch.cuda.synchronize()
+    assert torch.equal(y0.view(torch.int32), y1.view(torch.int32))
+    got = int(ya[:1].cpu().view(torch.int32).numpy().view(np.uint32)[0])
+    assert got == amax_bits(y1)
+
+    # Y as the activation of a next layer with C_in = C_out, same image
+    nd = mx.desc(d.n, d.c_out, 8, d.h_out, d.w_out, 1, 1, elem_fmt=fmt)
+    src = y1.contiguous()
+    two = mx.QTensor(nd, mx.MX_ROLE_ACT, DEV)
+    mx.mx_quantize_cbf(nd, mx.MX_ROLE_ACT, src, two)
+    one = mx.QTensor(nd, mx.MX_ROLE_ACT, DEV)
+    one.amax.copy_(ya[:1])
+    mx.mx_quantize_cbf(nd, mx.MX_ROLE_ACT, src, one, amax_given=True)
+    torch.cuda.synchronize()
+    assert torch.equal(two.codes[:two.code_bytes], one.codes[:one.code_bytes])
+    assert torch.equal(two.scales[:two.nblocks], one.scales[:one.nblocks])
+    assert torch.equal(two.tensor_scale.view(torch.int32), one.tensor_scale.view(torch.int32))
+    assert torch.equal(two.amax.view(torch.int32), ya[:1].view(torch.int32))
+
+
+def test_fused_amax_repeated_calls_reset_the_word():
+    # a second call on a smaller output must not keep the first call's maximum
+    # (every partial slot is rewritten by every call)
+    lay = WL.ConvLayer(8, 16, 16, 16, 16, 3, 3, 1, 1, 0, 0)
+    d = mx.desc_from_layer(lay, mx.MX_E2M1)
+    x, w = WL.gen_x(lay, "normal", 21), WL.gen_w(lay, 22)
+    qx = gpu_quantize(d, mx.MX_ROLE_ACT, x)
+    qw = gpu_quantize(d, mx.MX_ROLE_WEIGHT, w)
+    big = gpu_quantize(d, mx.MX_ROLE_WEIGHT, w * 1000.0)
+    y = torch.empty(d.h_out, d.w_out, d.c_out, d.n, device=DEV)
+    ya = torch.zeros(mx.mx_fwd_amax_bytes(d) // 4, device=DEV)
+    mx.mx_conv_fwd_amax(d, big, qx, y, ya)
+    first = float(ya[0].item())
+    mx.mx_conv_fwd_amax(d, qw, qx, y, ya)
+    torch.cuda.synchronize()
+    assert float(ya[0].item()) < first
+    assert int(ya[:1].cpu().view(torch.int32).numpy().view(np.uint32)[0]) == amax_bits(y)
