@@ -47,6 +47,10 @@ def parse():
     ap.add_argument("--producer-amax", action="store_true",
                     help="chain the stack: where a layer's input has the previous layer's output shape, X is that "
                          "output, quantized in one pass with the amax its fwd produced (mx_conv_fwd_amax)")
+    ap.add_argument("--flow", default=None, choices=["microqonv", "im2col-square", "dacapo"],
+                    help="time only the activation path (fwd + wgrad) of one flow: MicroQonv's single quantization, "
+                         "quantize-after-im2col (X' written and square-quantized once), or DaCapo-style "
+                         "(X' formed and quantized again for the backward)")
     ap.add_argument("--graph", action="store_true",
                     help="replay the step as one captured HIP graph (per-call timing then comes "
                          "from a separate eager pass)")
@@ -78,6 +82,49 @@ class Call:
         rc = self.fn(*self.args)
         if rc != 0:
             raise RuntimeError(f"{self.name}: status {rc}")
+
+
+def flow_calls(flow, L, mx, torch, D, d, lay, x, w, dy, sr_seed, fmt, qb, ws, ws_bytes, stream, keep, dev):
+    """The activation path (fwd + wgrad) of one layer under one flow.  W and dY
+    are quantized here, outside the timed step (they are the same in every
+    flow).  The baseline flows run the GEMMs as 1x1 convolutions over X'
+    [Ho][Wo][(Kh, Kw, C)][N] (mx_im2col_cbf)."""
+    shape = lay.tag()
+    nx, nw, ny = lay.numel_x(), lay.numel_w(), lay.numel_dy()
+    f = lay.flops()
+    if flow == "microqonv":
+        g, xs = d, x
+    else:
+        g = mx.desc(d.n, d.k_h * d.k_w * d.c_in, d.c_out, d.h_out, d.w_out, 1, 1, elem_fmt=fmt)
+        w = w.permute(0, 2, 3, 1).reshape(d.c_out, g.c_in, 1, 1).contiguous()
+        xs = torch.empty(d.h_out, d.w_out, d.k_h, d.k_w, d.c_in, d.n, device=dev)
+    qx, qw, qdy = (mx.QTensor(g, r, dev) for r in (mx.MX_ROLE_ACT, mx.MX_ROLE_WEIGHT, mx.MX_ROLE_GRAD))
+    mx.mx_quantize_cbf(g, mx.MX_ROLE_WEIGHT, w, qw)
+    mx.mx_quantize_cbf(g, mx.MX_ROLE_GRAD, dy, qdy, mx.MX_SR, sr_seed)
+    y = torch.empty(lay.h_out, lay.w_out, lay.c_out, lay.n, device=dev)
+    dw = torch.empty(g.c_out, g.c_in, g.k_h, g.k_w, device=dev)
+    wsb = mx.mx_wgrad_workspace_bytes(g)
+    wsf = torch.empty(max(wsb // 4, 4), device=dev)
+    cq = [q.c() for q in (qx, qw, qdy)]
+    keep += [g, w, xs, qx, qw, qdy, y, dw, wsf, cq]
+    nxc = xs.numel() if flow != "microqonv" else nx
+    q_x = Call(L.mx_quantize_cbf, (D(g), mx.MX_ROLE_ACT, xs.data_ptr(), D(cq[0]), mx.MX_RNE, 0, 0, stream),
+               "quantize", ("quantize_act", shape), 0, nxc * (8 + qb), "quantize X" if flow == "microqonv" else "quantize X'")
+    fwd = Call(L.mx_conv_fwd, (D(g), D(cq[1]), D(cq[0]), y.data_ptr(), stream),
+               "fwd", ("conv_fwd", shape), f, (nw + nxc) * qb + 4 * ny, "fwd")
+    wgrad = Call(L.mx_conv_wgrad, (D(g), D(cq[2]), D(cq[0]), dw.data_ptr(), wsf.data_ptr(), wsb, stream),
+                 "wgrad", ("conv_wgrad", shape), f, (ny + nxc) * qb + 4 * nw, "wgrad")
+    if flow == "microqonv":
+        return [q_x, fwd, wgrad]
+
+    def im2col():
+        return Call(L.mx_im2col_cbf, (D(d), x.data_ptr(), xs.data_ptr(), stream),
+                    "im2col", ("im2col", shape), 0, 4 * (nx + nxc), "im2col")
+    if flow == "im2col-square":
+        return [im2col(), q_x, fwd, wgrad]
+    # dacapo: X kept in fp32; X' formed and quantized in the forward and again in the backward
+    q_x2 = Call(q_x.fn, q_x.args, "quantize", ("quantize_act", shape), 0, nxc * (8 + qb), "quantize X' (backward)")
+    return [im2col(), q_x, fwd, im2col(), q_x2, wgrad]
 
 
 def main():
@@ -122,6 +169,7 @@ def main():
 
     t_gen = time.time()
     prev = None  # --producer-amax: (layer, y, its fwd Call) of the previous layer
+    flow_stats = {"activation_elements": 0, "quantized_elements": 0, "stored_activation_bytes": 0.0}
     n_chained = 0
     for li, lay in enumerate(wl.layers):
         d = mx.desc_from_layer(lay, fmt)
@@ -139,6 +187,16 @@ def main():
         shape = lay.tag()
         nx, nw, ny = lay.numel_x(), lay.numel_w(), lay.numel_dy()
         f = lay.flops()
+        if a.flow:
+            calls += flow_calls(a.flow, L, mx, torch, D, d, lay, x, w, dy, sr_seed, fmt, qb, ws, ws_bytes, stream, keep,
+                                dev)
+            nx = lay.numel_x()
+            nxc = lay.h_out * lay.w_out * lay.k_h * lay.k_w * lay.c_in * lay.n
+            flow_stats["activation_elements"] += nx
+            flow_stats["quantized_elements"] += {"microqonv": nx, "im2col-square": nxc, "dacapo": 2 * nxc}[a.flow]
+            flow_stats["stored_activation_bytes"] += {"microqonv": nx * qb, "im2col-square": nxc * qb,
+                                                      "dacapo": nx * 4.0}[a.flow]
+            continue
         # --producer-amax: where the previous layer's output has this layer's
         # input shape, X is that output, its fwd writes max|y| into qx.amax
         # and X is quantized in one pass (amax given)
@@ -175,7 +233,7 @@ def main():
                  "dequantize", ("dequantize_act", shape), 0, nx * (qb + 4), "dequantize X"),
         ]
         prev = (d, y, calls[-4])
-    if wl.lr_buffer is not None:
+    if wl.lr_buffer is not None and not a.flow:
         nmaps, c, h, w_ = wl.lr_buffer
         d = mx.desc(nmaps, c, c, h, w_, 1, 1, elem_fmt=mx.MX_E2M1)
         maps = WL.gen_lr_maps(nmaps, c, h, w_, WL.seed_for(wl.cfg_index, 0, 5)).to(dev)
@@ -340,6 +398,12 @@ def main():
         "conv_tflops": total_flops / (conv_ms / 1e3) / 1e12 if conv_ms > 0 else None,
         "quantize_gbps": q_bytes / (q_ms / 1e3) / 1e9 if q_ms > 0 else None,
         "step_breakdown_ms": {k: v["ms"] for k, v in by_op.items()},
+        **({"flow": {"name": a.flow,
+                     "quantizations_per_activation_element": flow_stats["quantized_elements"]
+                     / max(flow_stats["activation_elements"], 1),
+                     "stored_activation_bytes_for_backward": flow_stats["stored_activation_bytes"],
+                     "note": "value and conv_tflops count fwd + wgrad only (the activation path)"}}
+           if a.flow else {}),
         "roofline": roof,
         "wall_s_timed": wall,
         "kernel_source": kernel_source_hash(),

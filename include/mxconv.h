@@ -172,6 +172,18 @@ mx_status mx_conv_dgrad(const mx_conv_desc* desc, const mx_qtensor* wq, const mx
 mx_status mx_conv_wgrad(const mx_conv_desc* desc, const mx_qtensor* dyq, const mx_qtensor* xq,
                         float* dw, void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/* Explicit channel-batch-first im2col: the expanded activation X' that the
+ * quantize-after-im2col flow (§III-C, the extrapolation of Cuyckens et al.
+ * to convolutions; Table I) writes to memory and MicroQonv never forms.
+ *   x     fp32 [H][W][C_in][N]
+ *   xcol  fp32 [Ho][Wo][Kh][Kw][C_in][N], overwritten; zero where a tap falls
+ *         in the padding.  As an activation it is a 1x1 convolution input
+ *         with C_in' = Kh*Kw*C_in channels on an Ho x Wo image, so the
+ *         baseline flow is mx_im2col_cbf + mx_quantize_cbf + the GEMM calls
+ *         on that 1x1 descriptor.
+ * Pointers 16-byte aligned; errors as the other calls. */
+mx_status mx_im2col_cbf(const mx_conv_desc* desc, const float* x, float* xcol, hipStream_t stream);
+
 /* Fake-quantized fp32 values (-1)^s * fl32(fl32(g * B) * T) (§III-A), written
  * in the fp32 layout of `role`. */
 mx_status mx_dequantize(const mx_conv_desc* desc, mx_role role, const mx_qtensor* q, float* dst,

@@ -29,7 +29,8 @@ STATUS = {0: "MX_OK", -1: "MX_ERR_NULL", -2: "MX_ERR_SHAPE", -3: "MX_ERR_FORMAT"
           -8: "MX_ERR_LAUNCH", -9: "MX_ERR_ROUND"}
 
 EXPORTS = ("mx_code_bytes", "mx_scale_bytes", "mx_wgrad_workspace_bytes", "mx_fwd_amax_bytes", "mx_quantize_cbf",
-           "mx_conv_fwd", "mx_conv_fwd_amax", "mx_conv_dgrad", "mx_conv_wgrad", "mx_dequantize", "mx_status_str")
+           "mx_conv_fwd", "mx_conv_fwd_amax", "mx_conv_dgrad", "mx_conv_wgrad", "mx_dequantize",
+           "mx_im2col_cbf", "mx_status_str")
 
 
 class MxError(RuntimeError):
@@ -90,6 +91,8 @@ def lib() -> ctypes.CDLL:
     L.mx_conv_wgrad.argtypes = [D, Q, Q, P, P, ctypes.c_size_t, P]
     L.mx_dequantize.restype = ctypes.c_int
     L.mx_dequantize.argtypes = [D, ctypes.c_int, Q, P, P]
+    L.mx_im2col_cbf.restype = ctypes.c_int
+    L.mx_im2col_cbf.argtypes = [D, P, P, P]
     L.mx_status_str.restype = ctypes.c_char_p
     L.mx_status_str.argtypes = [ctypes.c_int]
     _lib = L
@@ -204,6 +207,10 @@ def mx_conv_wgrad(d: mx_conv_desc, dyq, xq, dw, workspace, ws_bytes: int | None 
         ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().mx_conv_wgrad(ctypes.byref(d), _q(dyq), _q(xq), _ptr(dw), _ptr(workspace),
                                ws_bytes, _stream(stream)), "mx_conv_wgrad")
+
+
+def mx_im2col_cbf(d: mx_conv_desc, x, xcol, stream=None) -> None:
+    _check(lib().mx_im2col_cbf(ctypes.byref(d), _ptr(x), _ptr(xcol), _stream(stream)), "mx_im2col_cbf")
 
 
 def mx_dequantize(d: mx_conv_desc, role: int, q, dst, stream=None) -> None:

@@ -146,6 +146,17 @@ mx_status mx_conv_fwd(const mx_conv_desc* desc, const mx_qtensor* wq, const mx_q
   return launched(mx::launch_conv_fwd(g, wq, xq, y, nullptr, stream));
 }
 
+mx_status mx_im2col_cbf(const mx_conv_desc* desc, const float* x, float* xcol, hipStream_t stream) {
+  mx_status st = check_desc(desc);
+  if (st != MX_OK) return st;
+  const Geom g = mx::make_geom(desc);
+  const int64_t nx = mx::role_numel(g, MX_ROLE_ACT);
+  const int64_t nc = static_cast<int64_t>(g.ho) * g.wo * g.k_h * g.k_w * g.c_in * g.n;
+  if ((nx > 0 && !x) || (nc > 0 && !xcol)) return MX_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(xcol, 16)) return MX_ERR_ALIGN;
+  return launched(mx::launch_im2col(g, x, xcol, stream));
+}
+
 size_t mx_fwd_amax_bytes(const mx_conv_desc* desc) {
   if (check_desc(desc) != MX_OK) return 0;
   return mx::fwd_amax_bytes(mx::make_geom(desc));

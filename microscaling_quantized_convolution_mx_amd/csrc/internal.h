@@ -39,6 +39,7 @@ hipError_t launch_quantize(const Geom& g, mx_role role, const float* src, const 
                            mx_round rounding, uint64_t seed, int amax_given, hipStream_t s);
 hipError_t launch_dequantize(const Geom& g, mx_role role, const mx_qtensor* q, float* dst,
                              hipStream_t s);
+hipError_t launch_im2col(const Geom& g, const float* x, float* xcol, hipStream_t s);
 
 // y_amax: nullptr, or a device buffer of fwd_amax_bytes(g) bytes whose first
 // word receives max |y| (exact); the rest holds the per-wave partial maxima

@@ -425,6 +425,32 @@ __global__ __launch_bounds__(kThreads) void k_dequantize(const uint8_t* __restri
   }
 }
 
+// Explicit channel-batch-first im2col, the baseline the paper compares
+// against (quantize after im2col, §III-C): X' [Ho][Wo][Kh][Kw][C][N] from X
+// [H][W][C][N], zero where a tap falls in the padding.  Each (ho, wo, kh, kw)
+// row is C*N contiguous floats of X at one position, copied with 16-byte
+// loads and stores; a workgroup copies whole rows.
+__global__ __launch_bounds__(256) void k_im2col_cbf(const float4* __restrict__ x, float4* __restrict__ xc,
+                                                    int h, int w, int k_h, int k_w, int sh, int sw, int ph,
+                                                    int pw, int wo, int64_t row4, int64_t rows) {
+  for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+    int64_t t = row;
+    const int kw = static_cast<int>(t % k_w); t /= k_w;
+    const int kh = static_cast<int>(t % k_h); t /= k_h;
+    const int ox = static_cast<int>(t % wo);
+    const int oy = static_cast<int>(t / wo);
+    const int iy = oy * sh - ph + kh, ix = ox * sw - pw + kw;
+    const bool in = iy >= 0 && iy < h && ix >= 0 && ix < w;
+    float4* dst = xc + row * row4;
+    if (in) {
+      const float4* src = x + (static_cast<int64_t>(iy) * w + ix) * row4;
+      for (int64_t i = threadIdx.x; i < row4; i += 256) dst[i] = src[i];
+    } else {
+      for (int64_t i = threadIdx.x; i < row4; i += 256) dst[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+}
+
 QDims make_qdims(const Geom& g, mx_role role) {
   QDims d;
   d.nblocks = role_nblocks(g, role);
@@ -518,6 +544,17 @@ hipError_t launch_quantize(const Geom& g, mx_role role, const float* src, const 
     case FMT_E2M3: launch_q_role<FMT_E2M3>(role, d, src, dst, sr, seed, part, nparts, one, s); break;
     default: launch_q_role<FMT_E4M3>(role, d, src, dst, sr, seed, part, nparts, one, s); break;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_im2col(const Geom& g, const float* x, float* xcol, hipStream_t s) {
+  const int64_t rows = static_cast<int64_t>(g.ho) * g.wo * g.k_h * g.k_w;
+  const int64_t row4 = static_cast<int64_t>(g.c_in) * g.n / 4;  // C*N is a multiple of 64
+  if (rows == 0 || row4 == 0) return hipSuccess;
+  const unsigned wgs = static_cast<unsigned>(rows < 65536 ? rows : 65536);
+  hipLaunchKernelGGL(k_im2col_cbf, dim3(wgs), dim3(256), 0, s, reinterpret_cast<const float4*>(x),
+                     reinterpret_cast<float4*>(xcol), g.h, g.w, g.k_h, g.k_w, g.sh, g.sw, g.ph, g.pw, g.wo,
+                     row4, rows);
   return hipGetLastError();
 }
 

@@ -127,6 +127,10 @@ def test_conv_argument_checks():
     assert L.mx_dequantize(ctypes.byref(d), 0, ctypes.byref(good), MIS, None) == -5
     bad = mx.desc(**dict(GOOD, n=4))
     assert L.mx_conv_fwd(ctypes.byref(bad), ctypes.byref(good), ctypes.byref(good), A16, None) == -2
+    # explicit im2col of the baseline flow
+    assert L.mx_im2col_cbf(ctypes.byref(d), None, A16, None) == -1
+    assert L.mx_im2col_cbf(ctypes.byref(d), A16, MIS, None) == -5
+    assert L.mx_im2col_cbf(ctypes.byref(bad), A16, A16, None) == -2
     # fwd with the producer-fused amax: one word plus one per GEMM wave
     assert mx.mx_fwd_amax_bytes(d) >= 8 and mx.mx_fwd_amax_bytes(d) % 4 == 0
     assert mx.mx_fwd_amax_bytes(bad) == 0
