@@ -28,6 +28,7 @@ SRC = os.path.join(HERE, "mxconv_oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
 E2M1, E2M3, E4M3, E3M2 = 1, 2, 3, 4
+UE2M1 = 5  # E2M1 magnitude without sign: 3-bit post-ReLU activation codes
 ACT, WEIGHT, GRAD = 0, 1, 2
 RNE, SR = 0, 1
 

@@ -51,6 +51,12 @@
 #define ORC_E2M3 2
 #define ORC_E4M3 3
 #define ORC_E3M2 4
+/* E2M1 magnitude without the sign bit: the 3-bit activation codes of a
+ * post-ReLU tensor (§V-B: the sign bit "simply removed", 3 + 8/64 = 3.125
+ * bits per element with the block scale), used by the compact latent-replay
+ * buffer (§VII).  Quantized like E2M1; a negative element keeps only its
+ * magnitude. */
+#define ORC_UE2M1 5
 
 #define ORC_ACT 0
 #define ORC_WEIGHT 1
@@ -68,15 +74,17 @@
 
 typedef struct {
   int ebits, mbits, bias;
-  int nmag; /* number of finite magnitude codes */
+  int nmag;   /* number of finite magnitude codes */
+  int signed_; /* 1: a sign bit above the magnitude; 0: magnitude only */
 } orc_fmt_t;
 
 static int fmt_desc(int fmt, orc_fmt_t* f) {
   switch (fmt) {
-    case ORC_E2M1: f->ebits = 2; f->mbits = 1; f->bias = 1; f->nmag = 8; return 0;
-    case ORC_E2M3: f->ebits = 2; f->mbits = 3; f->bias = 1; f->nmag = 32; return 0;
-    case ORC_E3M2: f->ebits = 3; f->mbits = 2; f->bias = 3; f->nmag = 32; return 0;
-    case ORC_E4M3: f->ebits = 4; f->mbits = 3; f->bias = 7; f->nmag = 127; return 0;
+    case ORC_E2M1: f->ebits = 2; f->mbits = 1; f->bias = 1; f->nmag = 8; f->signed_ = 1; return 0;
+    case ORC_E2M3: f->ebits = 2; f->mbits = 3; f->bias = 1; f->nmag = 32; f->signed_ = 1; return 0;
+    case ORC_E3M2: f->ebits = 3; f->mbits = 2; f->bias = 3; f->nmag = 32; f->signed_ = 1; return 0;
+    case ORC_E4M3: f->ebits = 4; f->mbits = 3; f->bias = 7; f->nmag = 127; f->signed_ = 1; return 0;
+    case ORC_UE2M1: f->ebits = 2; f->mbits = 1; f->bias = 1; f->nmag = 8; f->signed_ = 0; return 0;
     default: return -1;
   }
 }
@@ -104,7 +112,7 @@ int orc_fmt_sign_shift(int fmt) {
 
 int orc_fmt_bits(int fmt) {
   orc_fmt_t f;
-  return fmt_desc(fmt, &f) ? -1 : 1 + f.ebits + f.mbits;
+  return fmt_desc(fmt, &f) ? -1 : f.signed_ + f.ebits + f.mbits;
 }
 
 double orc_fmt_max(int fmt) {
@@ -311,7 +319,7 @@ int orc_quantize(int role, int fmt, int rounding, uint64_t seed, const float* sr
         int mag;
         if (rounding == ORC_SR) mag = orc_round_sr(fmt, v, orc_sr_uniform(seed, (uint64_t)si));
         else mag = orc_round_rne(fmt, v);
-        int s = signbit(x) ? 1 : 0;
+        int s = (f.signed_ && signbit(x)) ? 1 : 0; /* an unsigned format drops the sign */
         codes[b * 64 + r * 8 + c] = (uint8_t)(mag | (s << sign_shift));
       }
   }
@@ -361,7 +369,7 @@ int orc_quantize_blocks(int role, int fmt, int rounding, uint64_t seed, const fl
         float v = (dd == 0.0f) ? 0.0f : fabsf(x) / dd;
         int mag = (rounding == ORC_SR) ? orc_round_sr(fmt, v, orc_sr_uniform(seed, (uint64_t)si))
                                        : orc_round_rne(fmt, v);
-        codes[i * 64 + r * 8 + c] = (uint8_t)(mag | ((signbit(x) ? 1 : 0) << sign_shift));
+        codes[i * 64 + r * 8 + c] = (uint8_t)(mag | (((f.signed_ && signbit(x)) ? 1 : 0) << sign_shift));
       }
   }
   return 0;
@@ -420,19 +428,22 @@ int orc_dequantize64(int role, int fmt, int64_t d0, int64_t d1, int64_t d2, int6
 }
 
 /* Pack codes (O6): E2M1 two per byte, element 2j in the low nibble; E2M3 and
- * E3M2 as a little-endian 6-bit stream (48 bytes per 64-element block);
- * E4M3 one byte each. */
+ * E3M2 as a little-endian 6-bit stream (48 bytes per 64-element block), the
+ * unsigned 3-bit E2M1 as a 3-bit stream (24 bytes per block); E4M3 one byte
+ * each. */
 int orc_pack(int fmt, const uint8_t* codes, int64_t nel, uint8_t* out) {
   int bits = orc_fmt_bits(fmt);
   if (bits == 4) {
     for (int64_t j = 0; j < nel / 2; ++j)
       out[j] = (uint8_t)((codes[2 * j] & 0xF) | ((codes[2 * j + 1] & 0xF) << 4));
-  } else if (bits == 6) {
-    memset(out, 0, (size_t)(nel * 6 / 8));
+  } else if (bits == 6 || bits == 3) {
+    /* little-endian bit stream per 64-element block: element e of a block at
+     * bits e*bits .. e*bits + bits - 1 */
+    memset(out, 0, (size_t)(nel * bits / 8));
     for (int64_t i = 0; i < nel; ++i) {
       int64_t blk = i / 64, e = i % 64;
-      for (int k = 0; k < 6; ++k) {
-        int64_t bit = blk * 384 + e * 6 + k;
+      for (int k = 0; k < bits; ++k) {
+        int64_t bit = blk * 64 * bits + e * bits + k;
         if ((codes[i] >> k) & 1) out[bit / 8] |= (uint8_t)(1u << (bit % 8));
       }
     }
