@@ -51,6 +51,8 @@ def parse():
                     help="time only the activation path (fwd + wgrad) of one flow: MicroQonv's single quantization, "
                          "quantize-after-im2col (X' written and square-quantized once), or DaCapo-style "
                          "(X' formed and quantized again for the backward)")
+    ap.add_argument("--replay-compact", action="store_true",
+                    help="store the latent-replay buffer in the compact 3-bit codes (MX_UE2M1, 3.125 b/element)")
     ap.add_argument("--graph", action="store_true",
                     help="replay the step as one captured HIP graph (per-call timing then comes "
                          "from a separate eager pass)")
@@ -235,14 +237,15 @@ def main():
         prev = (d, y, calls[-4])
     if wl.lr_buffer is not None and not a.flow:
         nmaps, c, h, w_ = wl.lr_buffer
-        d = mx.desc(nmaps, c, c, h, w_, 1, 1, elem_fmt=mx.MX_E2M1)
+        lr_fmt = mx.MX_UE2M1 if a.replay_compact else mx.MX_E2M1
+        d = mx.desc(nmaps, c, c, h, w_, 1, 1, elem_fmt=lr_fmt)
         maps = WL.gen_lr_maps(nmaps, c, h, w_, WL.seed_for(wl.cfg_index, 0, 5)).to(dev)
         q = mx.QTensor(d, mx.MX_ROLE_ACT, dev)
         back = torch.empty_like(maps)
         cq = q.c()
         keep += [d, maps, q, back, cq]
         n_el = maps.numel()
-        qb4 = 4 / 8 + 1 / 64
+        qb4 = (3 if a.replay_compact else 4) / 8 + 1 / 64
         shape = f"replay buffer {nmaps}x{c}@{h}x{w_}"
         calls += [
             Call(L.mx_quantize_cbf, (D(d), mx.MX_ROLE_ACT, maps.data_ptr(), D(cq), mx.MX_RNE, 0, 0, stream),
@@ -394,7 +397,8 @@ def main():
                    "step": "per layer: quantize X,W,dY; fwd; dgrad; wgrad; dequantize Xq"
                            + ("; replay buffer quantize+dequantize" if wl.lr_buffer else ""),
                    "graph": bool(graph is not None),
-                   "producer_amax": {"chained_layers": n_chained} if a.producer_amax else False},
+                   "producer_amax": {"chained_layers": n_chained} if a.producer_amax else False,
+                   **({"replay_buffer_fmt": "ue2m1" if a.replay_compact else "e2m1"} if wl.lr_buffer else {})},
         "conv_tflops": total_flops / (conv_ms / 1e3) / 1e12 if conv_ms > 0 else None,
         "quantize_gbps": q_bytes / (q_ms / 1e3) / 1e9 if q_ms > 0 else None,
         "step_breakdown_ms": {k: v["ms"] for k, v in by_op.items()},

@@ -69,8 +69,15 @@ typedef enum {
 
 /* Element formats; the block scale is always E4M3 and the tensor scale fp32
  * (the NVFP4-style two-level scaling of §II-D / §III-A, with FP6 and FP8
- * element variants of §IV-D, §IV-E and §VI-B). */
-typedef enum { MX_E2M1 = 1, MX_E2M3 = 2, MX_E4M3 = 3 } mx_elem_fmt;
+ * element variants of §IV-D, §IV-E and §VI-B).
+ * MX_UE2M1 is the compact storage format of post-ReLU activations (§V-B: the
+ * sign bit removed, 3 bits per element + 8/64 for the block scale = 3.125;
+ * §VII stores the latent-replay buffer so): quantized exactly like E2M1 with
+ * the sign dropped (a negative element keeps its magnitude), packed as a
+ * little-endian 3-bit stream, 24 bytes per block.  Only mx_quantize_cbf and
+ * mx_dequantize with MX_ROLE_ACT accept it; every GEMM call and the other
+ * roles return MX_ERR_FORMAT. */
+typedef enum { MX_E2M1 = 1, MX_E2M3 = 2, MX_E4M3 = 3, MX_UE2M1 = 4 } mx_elem_fmt;
 
 /* Which tensor of the layer a quantization applies to (§IV-B: activations
  * blocked over (C_in, N), weights over (C_out, C_in), output gradients over

@@ -21,6 +21,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmxconv.so")
 
 MX_E2M1, MX_E2M3, MX_E4M3 = 1, 2, 3
+MX_UE2M1 = 4  # compact 3-bit post-ReLU activation codes (quantize / dequantize only)
 MX_ROLE_ACT, MX_ROLE_WEIGHT, MX_ROLE_GRAD = 0, 1, 2
 MX_RNE, MX_SR = 0, 1
 
@@ -163,7 +164,7 @@ class QTensor:
         self.code_bytes, self.scale_bytes = nc, ns
         # stored block scales: one byte per 8x8 block (the rest of the
         # scales buffer is the quantizer's scratch)
-        self.nblocks = nc * 8 // (64 * {MX_E2M1: 4, MX_E2M3: 6, MX_E4M3: 8}[d.elem_fmt])
+        self.nblocks = nc * 8 // (64 * {MX_E2M1: 4, MX_E2M3: 6, MX_E4M3: 8, MX_UE2M1: 3}[d.elem_fmt])
 
     def c(self) -> mx_qtensor:
         return mx_qtensor(self.codes.data_ptr(), self.scales.data_ptr(),

@@ -32,7 +32,7 @@ int64_t role_numel(const Geom& g, mx_role role) {
 
 int64_t role_nblocks(const Geom& g, mx_role role) { return role_numel(g, role) / 64; }
 
-int code_bits(int fmt) { return fmt == MX_E2M1 ? 4 : fmt == MX_E2M3 ? 6 : 8; }
+int code_bits(int fmt) { return fmt == MX_E2M1 ? 4 : fmt == MX_E2M3 ? 6 : fmt == MX_UE2M1 ? 3 : 8; }
 
 }  // namespace mx
 
@@ -51,7 +51,8 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 mx_status check_desc(const mx_conv_desc* d) {
   if (!d) return MX_ERR_NULL;
   if (d->block != 8) return MX_ERR_BLOCK;
-  if (d->elem_fmt != MX_E2M1 && d->elem_fmt != MX_E2M3 && d->elem_fmt != MX_E4M3) return MX_ERR_FORMAT;
+  if (d->elem_fmt != MX_E2M1 && d->elem_fmt != MX_E2M3 && d->elem_fmt != MX_E4M3 && d->elem_fmt != MX_UE2M1)
+    return MX_ERR_FORMAT;
   if (d->n < 0 || d->c_in <= 0 || d->c_out <= 0 || d->h <= 0 || d->w <= 0 || d->k_h <= 0 || d->k_w <= 0)
     return MX_ERR_SHAPE;
   if (d->stride_h <= 0 || d->stride_w <= 0 || d->pad_h < 0 || d->pad_w < 0) return MX_ERR_SHAPE;
@@ -71,6 +72,18 @@ mx_status check_desc(const mx_conv_desc* d) {
     return MX_ERR_SHAPE;
   return MX_OK;
 }
+
+// The compact 3-bit activation codes are a storage format (the replay
+// buffer): activations only, and no GEMM reads them.
+mx_status check_gemm_desc(const mx_conv_desc* d) {
+  const mx_status st = check_desc(d);
+  if (st != MX_OK) return st;
+  return d->elem_fmt == MX_UE2M1 ? MX_ERR_FORMAT : MX_OK;
+}
+mx_status check_role_fmt(const mx_conv_desc* d, mx_role role) {
+  return (d->elem_fmt == MX_UE2M1 && role != MX_ROLE_ACT) ? MX_ERR_FORMAT : MX_OK;
+}
+
 
 mx_status check_role(mx_role r) {
   return (r == MX_ROLE_ACT || r == MX_ROLE_WEIGHT || r == MX_ROLE_GRAD) ? MX_OK : MX_ERR_ROLE;
@@ -102,7 +115,7 @@ size_t mx_scale_bytes(const mx_conv_desc* desc, mx_role role) {
 }
 
 size_t mx_wgrad_workspace_bytes(const mx_conv_desc* desc) {
-  if (check_desc(desc) != MX_OK) return 0;
+  if (check_gemm_desc(desc) != MX_OK) return 0;
   return mx::wgrad_workspace_bytes(mx::make_geom(desc));
 }
 
@@ -112,6 +125,7 @@ mx_status mx_quantize_cbf(const mx_conv_desc* desc, mx_role role, const float* s
   mx_status st = check_desc(desc);
   if (st != MX_OK) return st;
   if ((st = check_role(role)) != MX_OK) return st;
+  if ((st = check_role_fmt(desc, role)) != MX_OK) return st;
   if (rounding != MX_RNE && rounding != MX_SR) return MX_ERR_ROUND;
   const Geom g = mx::make_geom(desc);
   const int64_t nb = mx::role_nblocks(g, role);
@@ -126,6 +140,7 @@ mx_status mx_dequantize(const mx_conv_desc* desc, mx_role role, const mx_qtensor
   mx_status st = check_desc(desc);
   if (st != MX_OK) return st;
   if ((st = check_role(role)) != MX_OK) return st;
+  if ((st = check_role_fmt(desc, role)) != MX_OK) return st;
   const Geom g = mx::make_geom(desc);
   const int64_t nb = mx::role_nblocks(g, role);
   if ((st = check_qtensor(q, nb)) != MX_OK) return st;
@@ -136,7 +151,7 @@ mx_status mx_dequantize(const mx_conv_desc* desc, mx_role role, const mx_qtensor
 
 mx_status mx_conv_fwd(const mx_conv_desc* desc, const mx_qtensor* wq, const mx_qtensor* xq, float* y,
                       hipStream_t stream) {
-  mx_status st = check_desc(desc);
+  mx_status st = check_gemm_desc(desc);
   if (st != MX_OK) return st;
   const Geom g = mx::make_geom(desc);
   if ((st = check_qtensor(wq, mx::role_nblocks(g, MX_ROLE_WEIGHT))) != MX_OK) return st;
@@ -158,13 +173,13 @@ mx_status mx_im2col_cbf(const mx_conv_desc* desc, const float* x, float* xcol, h
 }
 
 size_t mx_fwd_amax_bytes(const mx_conv_desc* desc) {
-  if (check_desc(desc) != MX_OK) return 0;
+  if (check_gemm_desc(desc) != MX_OK) return 0;
   return mx::fwd_amax_bytes(mx::make_geom(desc));
 }
 
 mx_status mx_conv_fwd_amax(const mx_conv_desc* desc, const mx_qtensor* wq, const mx_qtensor* xq, float* y,
                            float* y_amax, hipStream_t stream) {
-  mx_status st = check_desc(desc);
+  mx_status st = check_gemm_desc(desc);
   if (st != MX_OK) return st;
   const Geom g = mx::make_geom(desc);
   if ((st = check_qtensor(wq, mx::role_nblocks(g, MX_ROLE_WEIGHT))) != MX_OK) return st;
@@ -177,7 +192,7 @@ mx_status mx_conv_fwd_amax(const mx_conv_desc* desc, const mx_qtensor* wq, const
 
 mx_status mx_conv_dgrad(const mx_conv_desc* desc, const mx_qtensor* wq, const mx_qtensor* dyq,
                         float* dx, hipStream_t stream) {
-  mx_status st = check_desc(desc);
+  mx_status st = check_gemm_desc(desc);
   if (st != MX_OK) return st;
   const Geom g = mx::make_geom(desc);
   if ((st = check_qtensor(wq, mx::role_nblocks(g, MX_ROLE_WEIGHT))) != MX_OK) return st;
@@ -189,7 +204,7 @@ mx_status mx_conv_dgrad(const mx_conv_desc* desc, const mx_qtensor* wq, const mx
 
 mx_status mx_conv_wgrad(const mx_conv_desc* desc, const mx_qtensor* dyq, const mx_qtensor* xq,
                         float* dw, void* workspace, size_t ws_bytes, hipStream_t stream) {
-  mx_status st = check_desc(desc);
+  mx_status st = check_gemm_desc(desc);
   if (st != MX_OK) return st;
   const Geom g = mx::make_geom(desc);
   if ((st = check_qtensor(dyq, mx::role_nblocks(g, MX_ROLE_GRAD))) != MX_OK) return st;

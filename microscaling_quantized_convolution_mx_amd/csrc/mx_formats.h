@@ -14,20 +14,30 @@
 
 namespace mx {
 
-enum { FMT_E2M1 = 1, FMT_E2M3 = 2, FMT_E4M3 = 3 };
+enum { FMT_E2M1 = 1, FMT_E2M3 = 2, FMT_E4M3 = 3, FMT_UE2M1 = 4 };
 
 template <int FMT> struct Fmt;
 template <> struct Fmt<FMT_E2M1> {
   static constexpr int MB = 1, BIAS = 1, SIGN = 3, BITS = 4, MAXCODE = 7;
   static constexpr float MAXV = 6.0f;
+  static constexpr bool SIGNED = true;
+};
+// E2M1 magnitude without the sign bit (3-bit codes of post-ReLU activations,
+// §V-B): quantized like E2M1, a negative element keeps only its magnitude
+template <> struct Fmt<FMT_UE2M1> {
+  static constexpr int MB = 1, BIAS = 1, SIGN = 3, BITS = 3, MAXCODE = 7;
+  static constexpr float MAXV = 6.0f;
+  static constexpr bool SIGNED = false;
 };
 template <> struct Fmt<FMT_E2M3> {
   static constexpr int MB = 3, BIAS = 1, SIGN = 5, BITS = 6, MAXCODE = 31;
   static constexpr float MAXV = 7.5f;
+  static constexpr bool SIGNED = true;
 };
 template <> struct Fmt<FMT_E4M3> {
   static constexpr int MB = 3, BIAS = 7, SIGN = 7, BITS = 8, MAXCODE = 126;
   static constexpr float MAXV = 448.0f;
+  static constexpr bool SIGNED = true;
 };
 using ScaleFmt = Fmt<FMT_E4M3>;
 

@@ -137,6 +137,19 @@ __device__ __forceinline__ void store_row(uint8_t* __restrict__ codes, int64_t b
     if (valid) *reinterpret_cast<uint32_t*>(codes + blk * 32 + r * 4) = lo;
   } else if constexpr (FMT == FMT_E4M3) {
     if (valid) *reinterpret_cast<uint2*>(codes + blk * 64 + r * 8) = make_uint2(lo, hi);
+  } else if constexpr (FMT == FMT_UE2M1) {
+    // 24-bit rows: the first lane of each quad (rows 4q..4q+3) writes them as
+    // three words at byte 12q of the 24-byte block
+    const int lane = threadIdx.x & 63;
+    const uint32_t r1 = static_cast<uint32_t>(__shfl(static_cast<int>(lo), lane + 1));
+    const uint32_t r2 = static_cast<uint32_t>(__shfl(static_cast<int>(lo), lane + 2));
+    const uint32_t r3 = static_cast<uint32_t>(__shfl(static_cast<int>(lo), lane + 3));
+    if (valid && (r & 3) == 0) {
+      uint32_t* q = reinterpret_cast<uint32_t*>(codes + blk * 24 + (r >> 2) * 12);
+      q[0] = lo | (r1 << 24);
+      q[1] = (r1 >> 8) | (r2 << 16);
+      q[2] = (r2 >> 16) | (r3 << 8);
+    }
   } else {
     // 48-bit rows: the even lane of each pair writes both rows (12 bytes)
     const uint32_t plo = swap_pair(lo), phi = swap_pair(hi);
@@ -363,7 +376,7 @@ __global__ __launch_bounds__(ONE ? kOneThreads : kThreads) void k_quantize(const
         } else {
           mag = rne_code<F>(vj);
         }
-        const uint32_t code = mag | ((__float_as_uint(cur.x[j]) >> 31) << F::SIGN);
+        const uint32_t code = F::SIGNED ? (mag | ((__float_as_uint(cur.x[j]) >> 31) << F::SIGN)) : mag;
         bits |= static_cast<uint64_t>(code) << (F::BITS * j);
       }
     }
@@ -381,6 +394,14 @@ __device__ __forceinline__ uint64_t load_row(const uint8_t* __restrict__ codes, 
   } else if constexpr (FMT == FMT_E4M3) {
     const uint2 v = *reinterpret_cast<const uint2*>(codes + blk * 64 + r * 8);
     return static_cast<uint64_t>(v.x) | (static_cast<uint64_t>(v.y) << 32);
+  } else if constexpr (FMT == FMT_UE2M1) {
+    // bytes 3r .. 3r+2 of the 24-byte block: in word 3r/4 and the next one,
+    // except for row 7, whose bytes all lie in word 5 (the last of the block)
+    const int off = 3 * r;
+    const uint32_t* q = reinterpret_cast<const uint32_t*>(codes + blk * 24);
+    const int w0 = off >> 2, w1 = w0 + 1 < 6 ? w0 + 1 : 5;
+    const uint64_t v = static_cast<uint64_t>(q[w0]) | (static_cast<uint64_t>(q[w1]) << 32);
+    return (v >> ((off & 3) * 8)) & 0xFFFFFFull;
   } else {
     // bytes 6r .. 6r+5 lie inside the two dwords starting at floor(6r/4)
     const int off = 6 * r;
@@ -413,7 +434,7 @@ __global__ __launch_bounds__(kThreads) void k_dequantize(const uint8_t* __restri
     const float g = code_value<F>(code & ((1u << F::SIGN) - 1u));
     const float gb = g * B;
     float v = gb * T;
-    if ((code >> F::SIGN) & 1u) v = -v;
+    if (F::SIGNED && ((code >> F::SIGN) & 1u)) v = -v;
     o[j] = v;
   }
   if constexpr (ROLE == MX_ROLE_WEIGHT) {
@@ -542,6 +563,7 @@ hipError_t launch_quantize(const Geom& g, mx_role role, const float* src, const 
   switch (g.fmt) {
     case FMT_E2M1: launch_q_role<FMT_E2M1>(role, d, src, dst, sr, seed, part, nparts, one, s); break;
     case FMT_E2M3: launch_q_role<FMT_E2M3>(role, d, src, dst, sr, seed, part, nparts, one, s); break;
+    case FMT_UE2M1: launch_q<FMT_UE2M1, MX_ROLE_ACT>(d, src, dst, sr, seed, part, nparts, one, s); break;
     default: launch_q_role<FMT_E4M3>(role, d, src, dst, sr, seed, part, nparts, one, s); break;
   }
   return hipGetLastError();
@@ -564,6 +586,7 @@ hipError_t launch_dequantize(const Geom& g, mx_role role, const mx_qtensor* q, f
   switch (g.fmt) {
     case FMT_E2M1: launch_dq_role<FMT_E2M1>(role, d, q, dst, s); break;
     case FMT_E2M3: launch_dq_role<FMT_E2M3>(role, d, q, dst, s); break;
+    case FMT_UE2M1: launch_dq<FMT_UE2M1, MX_ROLE_ACT>(d, q, dst, s); break;
     default: launch_dq_role<FMT_E4M3>(role, d, q, dst, s); break;
   }
   return hipGetLastError();

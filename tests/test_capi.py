@@ -76,7 +76,7 @@ GOOD = dict(n=8, c_in=16, c_out=16, h=8, w=8, k_h=3, k_w=3)
 
 @pytest.mark.parametrize("change,status", [
     (dict(block=4), -4), (dict(block=16), -4),
-    (dict(elem_fmt=0), -3), (dict(elem_fmt=4), -3),
+    (dict(elem_fmt=0), -3), (dict(elem_fmt=5), -3),
     (dict(c_in=12), -2), (dict(c_out=20), -2), (dict(n=12), -2), (dict(n=-8), -2),
     (dict(stride_h=0), -2), (dict(stride_w=-1), -2), (dict(pad_h=-1), -2),
     (dict(k_h=11), -2), (dict(h=0), -2), (dict(k_w=0), -2), (dict(c_in=0), -2),
@@ -156,3 +156,20 @@ def test_product_path_does_not_use_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "liboracle" not in text and "mxconv_oracle" not in text, f
+
+
+def test_compact_activation_format_is_storage_only():
+    # 3-bit codes: 3/8 byte per element, activations only, no GEMM
+    d = mx.desc(16, 24, 40, 9, 7, 3, 3, 2, 2, 1, 1, elem_fmt=mx.MX_UE2M1)
+    assert mx.mx_code_bytes(d, mx.MX_ROLE_ACT) == 9 * 7 * 24 * 16 * 3 // 8
+    assert mx.mx_wgrad_workspace_bytes(d) == 0
+    assert mx.mx_fwd_amax_bytes(d) == 0
+    L = mx.lib()
+    good = q()
+    assert quant(d, role=mx.MX_ROLE_WEIGHT) == -3
+    assert quant(d, role=mx.MX_ROLE_GRAD) == -3
+    assert L.mx_dequantize(ctypes.byref(d), mx.MX_ROLE_GRAD, ctypes.byref(good), A16, None) == -3
+    assert L.mx_conv_fwd(ctypes.byref(d), ctypes.byref(good), ctypes.byref(good), A16, None) == -3
+    assert L.mx_conv_dgrad(ctypes.byref(d), ctypes.byref(good), ctypes.byref(good), A16, None) == -3
+    assert L.mx_conv_wgrad(ctypes.byref(d), ctypes.byref(good), ctypes.byref(good), A16, A16, 1 << 20, None) == -3
+    assert L.mx_conv_fwd_amax(ctypes.byref(d), ctypes.byref(good), ctypes.byref(good), A16, A16, None) == -3
