@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c2", help="c1..c5 (default c2: ResNet-32 stack)")
     ap.add_argument("--fmt", default=None, help="element format override: e2m1|e2m3|e4m3")
+    ap.add_argument("--act-fmt", default=None, choices=["e3m2", "e2m3"],
+                    help="MicroQonv+: activations in this FP6 format, weights and gradients in the "
+                         "element format (E2M1)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate budget of the CPU-baseline sample")
@@ -156,16 +159,19 @@ def main():
 
     L = mx.lib()
     wl = WL.workloads()[a.workload]
-    fmts = {"e2m1": mx.MX_E2M1, "e2m3": mx.MX_E2M3, "e4m3": mx.MX_E4M3}
+    fmts = {"e2m1": mx.MX_E2M1, "e2m3": mx.MX_E2M3, "e4m3": mx.MX_E4M3, "e3m2": mx.MX_E3M2}
     fmt = fmts[a.fmt] if a.fmt else wl.elem_fmts[0]
-    ebits = {mx.MX_E2M1: 4, mx.MX_E2M3: 6, mx.MX_E4M3: 8}[fmt]
-    qb = ebits / 8 + 1 / 64          # quantized bytes per element (codes + block scales)
+    afmt = fmts[a.act_fmt] if a.act_fmt else 0   # 0: activations in fmt too
+    if afmt and a.flow:
+        raise SystemExit("--act-fmt applies to the MicroQonv step, not to --flow")
+    qb = mx.CODE_BITS[fmt] / 8 + 1 / 64          # quantized bytes per element (codes + block scales)
+    qbx = mx.CODE_BITS[afmt or fmt] / 8 + 1 / 64  # the same for the activation X
     stream = torch.cuda.current_stream().cuda_stream
 
     D = ctypes.byref
     calls: list[Call] = []
     keep = []                         # keeps every buffer and ctypes struct alive
-    ws_bytes = max(mx.mx_wgrad_workspace_bytes(mx.desc_from_layer(l, fmt)) for l in wl.layers)
+    ws_bytes = max(mx.mx_wgrad_workspace_bytes(mx.desc_from_layer(l, fmt, afmt)) for l in wl.layers)
     ws = torch.empty(max(ws_bytes // 4, 4), device=dev)
     keep.append(ws)
 
@@ -174,7 +180,7 @@ def main():
     flow_stats = {"activation_elements": 0, "quantized_elements": 0, "stored_activation_bytes": 0.0}
     n_chained = 0
     for li, lay in enumerate(wl.layers):
-        d = mx.desc_from_layer(lay, fmt)
+        d = mx.desc_from_layer(lay, fmt, afmt)
         x = WL.gen_x(lay, wl.x_dist, WL.seed_for(wl.cfg_index, li, 1)).to(dev)
         w = WL.gen_w(lay, WL.seed_for(wl.cfg_index, li, 2)).to(dev)
         dy = WL.gen_dy(lay, wl.dy_sigma, WL.seed_for(wl.cfg_index, li, 3)).to(dev)
@@ -214,10 +220,10 @@ def main():
             pcall.fn = L.mx_conv_fwd_amax
             pcall.args = pcall.args[:-1] + (abuf.data_ptr(), stream)
             pcall.name = "fwd (+amax)"
-            x_src, x_given, x_bytes = py.data_ptr(), 1, nx * (4 + qb)
+            x_src, x_given, x_bytes = py.data_ptr(), 1, nx * (4 + qbx)
             n_chained += 1
         else:
-            x_src, x_given, x_bytes = x.data_ptr(), 0, nx * (8 + qb)
+            x_src, x_given, x_bytes = x.data_ptr(), 0, nx * (8 + qbx)
         calls += [
             Call(L.mx_quantize_cbf, (D(d), mx.MX_ROLE_ACT, x_src, D(cq[0]), mx.MX_RNE, 0, x_given, stream),
                  "quantize", ("quantize_act", shape), 0, x_bytes, "quantize X"),
@@ -226,13 +232,13 @@ def main():
             Call(L.mx_quantize_cbf, (D(d), mx.MX_ROLE_GRAD, dy.data_ptr(), D(cq[2]), mx.MX_SR, sr_seed, 0, stream),
                  "quantize", ("quantize_grad", shape), 0, ny * (8 + qb), "quantize dY"),
             Call(L.mx_conv_fwd, (D(d), D(cq[1]), D(cq[0]), y.data_ptr(), stream),
-                 "fwd", ("conv_fwd", shape), f, (nw + nx) * qb + 4 * ny, "fwd"),
+                 "fwd", ("conv_fwd", shape), f, nw * qb + nx * qbx + 4 * ny, "fwd"),
             Call(L.mx_conv_dgrad, (D(d), D(cq[1]), D(cq[2]), dx.data_ptr(), stream),
                  "dgrad", ("conv_dgrad", shape), f, (nw + ny) * qb + 4 * nx, "dgrad"),
             Call(L.mx_conv_wgrad, (D(d), D(cq[2]), D(cq[0]), dw.data_ptr(), ws.data_ptr(), ws_bytes, stream),
-                 "wgrad", ("conv_wgrad", shape), f, (ny + nx) * qb + 4 * nw, "wgrad"),
+                 "wgrad", ("conv_wgrad", shape), f, ny * qb + nx * qbx + 4 * nw, "wgrad"),
             Call(L.mx_dequantize, (D(d), mx.MX_ROLE_ACT, D(cq[0]), xdq.data_ptr(), stream),
-                 "dequantize", ("dequantize_act", shape), 0, nx * (qb + 4), "dequantize X"),
+                 "dequantize", ("dequantize_act", shape), 0, nx * (qbx + 4), "dequantize X"),
         ]
         prev = (d, y, calls[-4])
     if wl.lr_buffer is not None and not a.flow:
@@ -393,6 +399,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{a.workload}: {wl.name}", "layers": len(wl.layers),
                    "batch": wl.layers[0].n, "elem_fmt": WL.FMT_NAMES[fmt],
+                   **({"act_fmt": a.act_fmt, "variant": "MicroQonv+ (FP6 activations)"} if afmt else {}),
                    "block": "8x8 E4M3 scale + fp32 tensor scale",
                    "step": "per layer: quantize X,W,dY; fwd; dgrad; wgrad; dequantize Xq"
                            + ("; replay buffer quantize+dequantize" if wl.lr_buffer else ""),
@@ -418,11 +425,11 @@ def main():
                             for k, v in sorted(groups.items(), key=lambda kv: -kv[1]["ms"])}
 
     if not a.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, fmt, a.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(wl, fmt, afmt, a.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(wl, fmt, budget_s):
+def cpu_baseline(wl, fmt, afmt, budget_s):
     """The CPU oracle, as it stands, on a bounded sample of the workload: the
     full quantize X/W/dY + fp64 fwd/dgrad/wgrad of the stack's layers, taken in
     stack order (repeated layers included, wrapping round to the first) until
@@ -432,6 +439,9 @@ def cpu_baseline(wl, fmt, budget_s):
     from microscaling_quantized_convolution_mx_amd import workloads as WL
 
     O.lib()
+    import microscaling_quantized_convolution_mx_amd as mx
+    ofmt = {mx.MX_E2M1: O.E2M1, mx.MX_E2M3: O.E2M3, mx.MX_E4M3: O.E4M3, mx.MX_E3M2: O.E3M2}
+    fmt_w, fmt_x = ofmt[fmt], ofmt[afmt or fmt]
     flops = 0
     spent = 0.0
     done = 0
@@ -444,9 +454,9 @@ def cpu_baseline(wl, fmt, budget_s):
         cv = O.conv(lay.n, lay.c_in, lay.c_out, lay.h, lay.w, lay.k_h, lay.k_w,
                     lay.stride_h, lay.stride_w, lay.pad_h, lay.pad_w)
         t0 = time.perf_counter()
-        qx = O.quantize(O.ACT, fmt, x)
-        qw = O.quantize(O.WEIGHT, fmt, w)
-        qdy = O.quantize(O.GRAD, fmt, dy, O.SR, WL.seed_for(wl.cfg_index, li % len(wl.layers), 4))
+        qx = O.quantize(O.ACT, fmt_x, x)
+        qw = O.quantize(O.WEIGHT, fmt_w, w)
+        qdy = O.quantize(O.GRAD, fmt_w, dy, O.SR, WL.seed_for(wl.cfg_index, li % len(wl.layers), 4))
         xe, we, dye = qx.exact(), qw.exact(), qdy.exact()
         O.conv_fwd(cv, we, xe)
         O.conv_dgrad(cv, we, dye)

@@ -32,7 +32,7 @@
  *     ACT    blocks [H][W][C_in/8][N/8],    in-block order [c][n]
  *     GRAD   blocks [Ho][Wo][C_out/8][N/8], in-block order [c][n]
  *     WEIGHT blocks [K_h][K_w][C_out/8][C_in/8], in-block order [co][ci]
- *   codes: E2M1 2 per byte (element 2j in the low nibble), E2M3 a
+ *   codes: E2M1 2 per byte (element 2j in the low nibble), E2M3 and E3M2 a
  *   little-endian 6-bit stream (48 bytes per block), E4M3 1 byte each; the
  *   sign is the top bit of each code.  scales: one E4M3 byte per block, in
  *   block order; the buffer continues, from the next multiple of 16 bytes,
@@ -58,7 +58,7 @@ typedef enum {
   MX_OK = 0,
   MX_ERR_NULL = -1,      /* a required pointer is NULL */
   MX_ERR_SHAPE = -2,     /* bad dimension, stride, padding, or not a multiple of 8 */
-  MX_ERR_FORMAT = -3,    /* unknown element format */
+  MX_ERR_FORMAT = -3,    /* unknown element format, or one this call does not take */
   MX_ERR_BLOCK = -4,     /* block size other than 8 */
   MX_ERR_ALIGN = -5,     /* misaligned pointer */
   MX_ERR_WORKSPACE = -6, /* workspace missing or too small */
@@ -69,15 +69,19 @@ typedef enum {
 
 /* Element formats; the block scale is always E4M3 and the tensor scale fp32
  * (the NVFP4-style two-level scaling of §II-D / §III-A, with FP6 and FP8
- * element variants of §IV-D, §IV-E and §VI-B).
- * MX_UE2M1 is the compact storage format of post-ReLU activations (§V-B: the
+ * element variants of §IV-D, §IV-E and §VI-B).  MX_E3M2 is the FP6 with the
+ * wider range (max 28, subnormal step 1/16): MicroQonv+ (§IV-D, Table VI)
+ * keeps activations in it while weights and gradients stay E2M1 (see
+ * mx_conv_desc.act_fmt).
+ * MX_UE2M1 is the compact storage format of post-ReLU activations (§VI-A: the
  * sign bit removed, 3 bits per element + 8/64 for the block scale = 3.125;
  * §VII stores the latent-replay buffer so): quantized exactly like E2M1 with
  * the sign dropped (a negative element keeps its magnitude), packed as a
- * little-endian 3-bit stream, 24 bytes per block.  Only mx_quantize_cbf and
- * mx_dequantize with MX_ROLE_ACT accept it; every GEMM call and the other
- * roles return MX_ERR_FORMAT. */
-typedef enum { MX_E2M1 = 1, MX_E2M3 = 2, MX_E4M3 = 3, MX_UE2M1 = 4 } mx_elem_fmt;
+ * little-endian 3-bit stream, 24 bytes per block.  It is an activation
+ * format only: mx_quantize_cbf and mx_dequantize take it for MX_ROLE_ACT,
+ * and return MX_ERR_FORMAT for the other roles when it is elem_fmt; every
+ * GEMM call that would read it returns MX_ERR_FORMAT. */
+typedef enum { MX_E2M1 = 1, MX_E2M3 = 2, MX_E4M3 = 3, MX_UE2M1 = 4, MX_E3M2 = 5 } mx_elem_fmt;
 
 /* Which tensor of the layer a quantization applies to (§IV-B: activations
  * blocked over (C_in, N), weights over (C_out, C_in), output gradients over
@@ -91,9 +95,16 @@ typedef enum { MX_RNE = 0, MX_SR = 1 } mx_round;
 /* One convolution layer (the problem statement of §II-A). */
 typedef struct {
   int32_t n, c_in, c_out, h, w, k_h, k_w, stride_h, stride_w, pad_h, pad_w;
-  int32_t elem_fmt; /* mx_elem_fmt */
+  int32_t elem_fmt; /* mx_elem_fmt of weights and output gradients */
   int32_t block;    /* must be 8 (8x8 square blocks, §IV-B) */
+  int32_t act_fmt;  /* mx_elem_fmt of the activation X; 0 = elem_fmt */
 } mx_conv_desc;
+/* Format pairs the GEMMs take: elem_fmt == act_fmt (any format but
+ * MX_UE2M1), or elem_fmt MX_E2M1 with act_fmt MX_E2M3 or MX_E3M2 (FP4
+ * weights and gradients with FP6 activations, MicroQonv+).  mx_conv_dgrad
+ * reads no activation and needs only elem_fmt to be a GEMM format; the other
+ * GEMM calls, mx_wgrad_workspace_bytes and mx_fwd_amax_bytes check the pair
+ * (MX_ERR_FORMAT, or 0 bytes). */
 
 /* A quantized tensor: device pointers owned by the caller. */
 typedef struct {
@@ -103,8 +114,9 @@ typedef struct {
   float* amax;         /* one fp32: max |x| of the source */
 } mx_qtensor;
 
-/* Bytes of the codes / scales buffers of the tensor of `role` (0 on an
- * invalid descriptor or role).  The scales buffer holds ceil-to-16 of the
+/* Bytes of the codes / scales buffers of the tensor of `role`, in that
+ * role's format (act_fmt for MX_ROLE_ACT) (0 on an invalid descriptor or
+ * role).  The scales buffer holds ceil-to-16 of the
  * block count bytes of scales plus 2048 bytes of quantizer scratch (0 bytes
  * in all for an empty tensor). */
 size_t mx_code_bytes(const mx_conv_desc* desc, mx_role role);

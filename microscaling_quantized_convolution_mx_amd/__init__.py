@@ -22,6 +22,8 @@ LIB_PATH = os.path.join(PKG, "libmxconv.so")
 
 MX_E2M1, MX_E2M3, MX_E4M3 = 1, 2, 3
 MX_UE2M1 = 4  # compact 3-bit post-ReLU activation codes (quantize / dequantize only)
+MX_E3M2 = 5   # FP6 with the wider range: MicroQonv+ activations (act_fmt)
+CODE_BITS = {MX_E2M1: 4, MX_E2M3: 6, MX_E4M3: 8, MX_UE2M1: 3, MX_E3M2: 6}
 MX_ROLE_ACT, MX_ROLE_WEIGHT, MX_ROLE_GRAD = 0, 1, 2
 MX_RNE, MX_SR = 0, 1
 
@@ -43,7 +45,7 @@ class MxError(RuntimeError):
 class mx_conv_desc(ctypes.Structure):
     _fields_ = [(f, ctypes.c_int32) for f in
                 ("n", "c_in", "c_out", "h", "w", "k_h", "k_w", "stride_h", "stride_w",
-                 "pad_h", "pad_w", "elem_fmt", "block")]
+                 "pad_h", "pad_w", "elem_fmt", "block", "act_fmt")]
 
     @property
     def h_out(self) -> int:
@@ -105,14 +107,20 @@ def status_str(status: int) -> str:
 
 
 def desc(n, c_in, c_out, h, w, k_h, k_w, stride_h=1, stride_w=1, pad_h=0, pad_w=0,
-         elem_fmt=MX_E2M1, block=8) -> mx_conv_desc:
+         elem_fmt=MX_E2M1, block=8, act_fmt=0) -> mx_conv_desc:
+    """act_fmt: format of the activation X (0: elem_fmt, the format of W and dY)."""
     return mx_conv_desc(n, c_in, c_out, h, w, k_h, k_w, stride_h, stride_w, pad_h, pad_w,
-                        elem_fmt, block)
+                        elem_fmt, block, act_fmt)
 
 
-def desc_from_layer(layer, elem_fmt: int) -> mx_conv_desc:
+def desc_from_layer(layer, elem_fmt: int, act_fmt: int = 0) -> mx_conv_desc:
     return desc(layer.n, layer.c_in, layer.c_out, layer.h, layer.w, layer.k_h, layer.k_w,
-                layer.stride_h, layer.stride_w, layer.pad_h, layer.pad_w, elem_fmt)
+                layer.stride_h, layer.stride_w, layer.pad_h, layer.pad_w, elem_fmt, act_fmt=act_fmt)
+
+
+def role_fmt(d: mx_conv_desc, role: int) -> int:
+    """Element format of the tensor of `role` under descriptor d."""
+    return d.act_fmt if (role == MX_ROLE_ACT and d.act_fmt != 0) else d.elem_fmt
 
 
 def _ptr(t) -> int | None:
@@ -153,7 +161,7 @@ class QTensor:
     def __init__(self, d: mx_conv_desc, role: int, device="cuda"):
         import torch
         self.role = role
-        self.fmt = d.elem_fmt
+        self.fmt = role_fmt(d, role)
         nc = mx_code_bytes(d, role)
         ns = mx_scale_bytes(d, role)
         # at least 16 bytes, so that an empty tensor still has valid pointers
@@ -164,7 +172,7 @@ class QTensor:
         self.code_bytes, self.scale_bytes = nc, ns
         # stored block scales: one byte per 8x8 block (the rest of the
         # scales buffer is the quantizer's scratch)
-        self.nblocks = nc * 8 // (64 * {MX_E2M1: 4, MX_E2M3: 6, MX_E4M3: 8, MX_UE2M1: 3}[d.elem_fmt])
+        self.nblocks = nc * 8 // (64 * CODE_BITS[self.fmt])
 
     def c(self) -> mx_qtensor:
         return mx_qtensor(self.codes.data_ptr(), self.scales.data_ptr(),

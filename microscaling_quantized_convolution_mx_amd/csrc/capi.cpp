@@ -17,6 +17,7 @@ Geom make_geom(const mx_conv_desc* d) {
   g.n = d->n; g.c_in = d->c_in; g.c_out = d->c_out; g.h = d->h; g.w = d->w;
   g.k_h = d->k_h; g.k_w = d->k_w; g.sh = d->stride_h; g.sw = d->stride_w;
   g.ph = d->pad_h; g.pw = d->pad_w; g.fmt = d->elem_fmt;
+  g.afmt = d->act_fmt != 0 ? d->act_fmt : d->elem_fmt;
   g.ho = (d->h + 2 * d->pad_h - d->k_h) / d->stride_h + 1;
   g.wo = (d->w + 2 * d->pad_w - d->k_w) / d->stride_w + 1;
   return g;
@@ -32,7 +33,9 @@ int64_t role_numel(const Geom& g, mx_role role) {
 
 int64_t role_nblocks(const Geom& g, mx_role role) { return role_numel(g, role) / 64; }
 
-int code_bits(int fmt) { return fmt == MX_E2M1 ? 4 : fmt == MX_E2M3 ? 6 : fmt == MX_UE2M1 ? 3 : 8; }
+int code_bits(int fmt) {
+  return fmt == MX_E2M1 ? 4 : (fmt == MX_E2M3 || fmt == MX_E3M2) ? 6 : fmt == MX_UE2M1 ? 3 : 8;
+}
 
 }  // namespace mx
 
@@ -48,11 +51,14 @@ constexpr int64_t kMaxIndex = std::numeric_limits<int32_t>::max();
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+bool known_fmt(int32_t f) {
+  return f == MX_E2M1 || f == MX_E2M3 || f == MX_E4M3 || f == MX_UE2M1 || f == MX_E3M2;
+}
+
 mx_status check_desc(const mx_conv_desc* d) {
   if (!d) return MX_ERR_NULL;
   if (d->block != 8) return MX_ERR_BLOCK;
-  if (d->elem_fmt != MX_E2M1 && d->elem_fmt != MX_E2M3 && d->elem_fmt != MX_E4M3 && d->elem_fmt != MX_UE2M1)
-    return MX_ERR_FORMAT;
+  if (!known_fmt(d->elem_fmt) || (d->act_fmt != 0 && !known_fmt(d->act_fmt))) return MX_ERR_FORMAT;
   if (d->n < 0 || d->c_in <= 0 || d->c_out <= 0 || d->h <= 0 || d->w <= 0 || d->k_h <= 0 || d->k_w <= 0)
     return MX_ERR_SHAPE;
   if (d->stride_h <= 0 || d->stride_w <= 0 || d->pad_h < 0 || d->pad_w < 0) return MX_ERR_SHAPE;
@@ -75,13 +81,21 @@ mx_status check_desc(const mx_conv_desc* d) {
 
 // The compact 3-bit activation codes are a storage format (the replay
 // buffer): activations only, and no GEMM reads them.
-mx_status check_gemm_desc(const mx_conv_desc* d) {
+mx_status check_role_fmt(const mx_conv_desc* d, mx_role role) {
+  return (mx::role_fmt(mx::make_geom(d), role) == MX_UE2M1 && role != MX_ROLE_ACT) ? MX_ERR_FORMAT : MX_OK;
+}
+
+// Operand formats a GEMM takes: one format for both operands, or E2M1 with
+// an FP6 activation (MicroQonv+).  The data gradient reads no activation.
+enum class Gemm { Fwd, Dgrad, Wgrad };
+mx_status check_gemm_desc(const mx_conv_desc* d, Gemm op) {
   const mx_status st = check_desc(d);
   if (st != MX_OK) return st;
-  return d->elem_fmt == MX_UE2M1 ? MX_ERR_FORMAT : MX_OK;
-}
-mx_status check_role_fmt(const mx_conv_desc* d, mx_role role) {
-  return (d->elem_fmt == MX_UE2M1 && role != MX_ROLE_ACT) ? MX_ERR_FORMAT : MX_OK;
+  const Geom g = mx::make_geom(d);
+  const int fa = g.fmt, fb = op == Gemm::Dgrad ? g.fmt : g.afmt;
+  if (fa == MX_UE2M1 || fb == MX_UE2M1) return MX_ERR_FORMAT;
+  if (fa == fb || (fa == MX_E2M1 && (fb == MX_E2M3 || fb == MX_E3M2))) return MX_OK;
+  return MX_ERR_FORMAT;
 }
 
 
@@ -106,7 +120,7 @@ extern "C" {
 size_t mx_code_bytes(const mx_conv_desc* desc, mx_role role) {
   if (check_desc(desc) != MX_OK || check_role(role) != MX_OK) return 0;
   const Geom g = mx::make_geom(desc);
-  return static_cast<size_t>(mx::role_numel(g, role)) * mx::code_bits(desc->elem_fmt) / 8;
+  return static_cast<size_t>(mx::role_numel(g, role)) * mx::code_bits(mx::role_fmt(g, role)) / 8;
 }
 
 size_t mx_scale_bytes(const mx_conv_desc* desc, mx_role role) {
@@ -115,7 +129,7 @@ size_t mx_scale_bytes(const mx_conv_desc* desc, mx_role role) {
 }
 
 size_t mx_wgrad_workspace_bytes(const mx_conv_desc* desc) {
-  if (check_gemm_desc(desc) != MX_OK) return 0;
+  if (check_gemm_desc(desc, Gemm::Wgrad) != MX_OK) return 0;
   return mx::wgrad_workspace_bytes(mx::make_geom(desc));
 }
 
@@ -151,7 +165,7 @@ mx_status mx_dequantize(const mx_conv_desc* desc, mx_role role, const mx_qtensor
 
 mx_status mx_conv_fwd(const mx_conv_desc* desc, const mx_qtensor* wq, const mx_qtensor* xq, float* y,
                       hipStream_t stream) {
-  mx_status st = check_gemm_desc(desc);
+  mx_status st = check_gemm_desc(desc, Gemm::Fwd);
   if (st != MX_OK) return st;
   const Geom g = mx::make_geom(desc);
   if ((st = check_qtensor(wq, mx::role_nblocks(g, MX_ROLE_WEIGHT))) != MX_OK) return st;
@@ -173,13 +187,13 @@ mx_status mx_im2col_cbf(const mx_conv_desc* desc, const float* x, float* xcol, h
 }
 
 size_t mx_fwd_amax_bytes(const mx_conv_desc* desc) {
-  if (check_gemm_desc(desc) != MX_OK) return 0;
+  if (check_gemm_desc(desc, Gemm::Fwd) != MX_OK) return 0;
   return mx::fwd_amax_bytes(mx::make_geom(desc));
 }
 
 mx_status mx_conv_fwd_amax(const mx_conv_desc* desc, const mx_qtensor* wq, const mx_qtensor* xq, float* y,
                            float* y_amax, hipStream_t stream) {
-  mx_status st = check_gemm_desc(desc);
+  mx_status st = check_gemm_desc(desc, Gemm::Fwd);
   if (st != MX_OK) return st;
   const Geom g = mx::make_geom(desc);
   if ((st = check_qtensor(wq, mx::role_nblocks(g, MX_ROLE_WEIGHT))) != MX_OK) return st;
@@ -192,7 +206,7 @@ mx_status mx_conv_fwd_amax(const mx_conv_desc* desc, const mx_qtensor* wq, const
 
 mx_status mx_conv_dgrad(const mx_conv_desc* desc, const mx_qtensor* wq, const mx_qtensor* dyq,
                         float* dx, hipStream_t stream) {
-  mx_status st = check_gemm_desc(desc);
+  mx_status st = check_gemm_desc(desc, Gemm::Dgrad);
   if (st != MX_OK) return st;
   const Geom g = mx::make_geom(desc);
   if ((st = check_qtensor(wq, mx::role_nblocks(g, MX_ROLE_WEIGHT))) != MX_OK) return st;
@@ -204,7 +218,7 @@ mx_status mx_conv_dgrad(const mx_conv_desc* desc, const mx_qtensor* wq, const mx
 
 mx_status mx_conv_wgrad(const mx_conv_desc* desc, const mx_qtensor* dyq, const mx_qtensor* xq,
                         float* dw, void* workspace, size_t ws_bytes, hipStream_t stream) {
-  mx_status st = check_gemm_desc(desc);
+  mx_status st = check_gemm_desc(desc, Gemm::Wgrad);
   if (st != MX_OK) return st;
   const Geom g = mx::make_geom(desc);
   if ((st = check_qtensor(dyq, mx::role_nblocks(g, MX_ROLE_GRAD))) != MX_OK) return st;
@@ -222,7 +236,7 @@ const char* mx_status_str(mx_status s) {
     case MX_OK: return "ok";
     case MX_ERR_NULL: return "null pointer argument";
     case MX_ERR_SHAPE: return "invalid shape (dimensions, stride, padding, or C_in/C_out/N not multiples of 8)";
-    case MX_ERR_FORMAT: return "unknown element format";
+    case MX_ERR_FORMAT: return "unknown element format, or a format this call does not take";
     case MX_ERR_BLOCK: return "block size must be 8";
     case MX_ERR_ALIGN: return "misaligned pointer";
     case MX_ERR_WORKSPACE: return "workspace missing or smaller than mx_wgrad_workspace_bytes()";

@@ -10,9 +10,12 @@
 namespace mx {
 
 // Geometry shared by all launchers, derived from an mx_conv_desc.
+// fmt: element format of weights and output gradients; afmt: that of the
+// activation (the descriptor's act_fmt, or fmt where that is 0).
 struct Geom {
-  int32_t n, c_in, c_out, h, w, k_h, k_w, sh, sw, ph, pw, ho, wo, fmt;
+  int32_t n, c_in, c_out, h, w, k_h, k_w, sh, sw, ph, pw, ho, wo, fmt, afmt;
 };
+inline int role_fmt(const Geom& g, mx_role role) { return role == MX_ROLE_ACT ? g.afmt : g.fmt; }
 
 Geom make_geom(const mx_conv_desc* d);
 

@@ -1,7 +1,9 @@
 // Device-side microscaling formats for gfx950.
 //
 // Element formats E2M1 / E2M3 / E4M3 and the E4M3 block scale of MicroQonv's
-// NVFP4-style quantizer (arXiv 2609.28358, §II-D and §III-A).  Rounding works
+// NVFP4-style quantizer (arXiv 2609.28358, §II-D and §III-A), E3M2 (the FP6
+// activations of MicroQonv+, §IV-D and Table VI) and the sign-less 3-bit
+// E2M1 of post-ReLU activations (§VI-A).  Rounding works
 // on the fp32 bit pattern: subnormal values by an exact power-of-two rescale
 // and a round-to-integer, normal values by rounding the 23-bit mantissa to the
 // format's width with carry into the exponent.  Both are the IEEE
@@ -14,7 +16,7 @@
 
 namespace mx {
 
-enum { FMT_E2M1 = 1, FMT_E2M3 = 2, FMT_E4M3 = 3, FMT_UE2M1 = 4 };
+enum { FMT_E2M1 = 1, FMT_E2M3 = 2, FMT_E4M3 = 3, FMT_UE2M1 = 4, FMT_E3M2 = 5 };
 
 template <int FMT> struct Fmt;
 template <> struct Fmt<FMT_E2M1> {
@@ -23,7 +25,7 @@ template <> struct Fmt<FMT_E2M1> {
   static constexpr bool SIGNED = true;
 };
 // E2M1 magnitude without the sign bit (3-bit codes of post-ReLU activations,
-// §V-B): quantized like E2M1, a negative element keeps only its magnitude
+// §VI-A): quantized like E2M1, a negative element keeps only its magnitude
 template <> struct Fmt<FMT_UE2M1> {
   static constexpr int MB = 1, BIAS = 1, SIGN = 3, BITS = 3, MAXCODE = 7;
   static constexpr float MAXV = 6.0f;
@@ -32,6 +34,12 @@ template <> struct Fmt<FMT_UE2M1> {
 template <> struct Fmt<FMT_E2M3> {
   static constexpr int MB = 3, BIAS = 1, SIGN = 5, BITS = 6, MAXCODE = 31;
   static constexpr float MAXV = 7.5f;
+  static constexpr bool SIGNED = true;
+};
+// FP6 with the wider range (max 28, subnormal step 1/16)
+template <> struct Fmt<FMT_E3M2> {
+  static constexpr int MB = 2, BIAS = 3, SIGN = 5, BITS = 6, MAXCODE = 31;
+  static constexpr float MAXV = 28.0f;
   static constexpr bool SIGNED = true;
 };
 template <> struct Fmt<FMT_E4M3> {

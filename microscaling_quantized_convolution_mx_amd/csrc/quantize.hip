@@ -560,9 +560,10 @@ hipError_t launch_quantize(const Geom& g, mx_role role, const float* src, const 
                          reinterpret_cast<const uint4*>(src), n4, part);
     }
   }
-  switch (g.fmt) {
+  switch (role_fmt(g, role)) {
     case FMT_E2M1: launch_q_role<FMT_E2M1>(role, d, src, dst, sr, seed, part, nparts, one, s); break;
     case FMT_E2M3: launch_q_role<FMT_E2M3>(role, d, src, dst, sr, seed, part, nparts, one, s); break;
+    case FMT_E3M2: launch_q_role<FMT_E3M2>(role, d, src, dst, sr, seed, part, nparts, one, s); break;
     case FMT_UE2M1: launch_q<FMT_UE2M1, MX_ROLE_ACT>(d, src, dst, sr, seed, part, nparts, one, s); break;
     default: launch_q_role<FMT_E4M3>(role, d, src, dst, sr, seed, part, nparts, one, s); break;
   }
@@ -583,9 +584,10 @@ hipError_t launch_im2col(const Geom& g, const float* x, float* xcol, hipStream_t
 hipError_t launch_dequantize(const Geom& g, mx_role role, const mx_qtensor* q, float* dst,
                              hipStream_t s) {
   const QDims d = make_qdims(g, role);
-  switch (g.fmt) {
+  switch (role_fmt(g, role)) {
     case FMT_E2M1: launch_dq_role<FMT_E2M1>(role, d, q, dst, s); break;
     case FMT_E2M3: launch_dq_role<FMT_E2M3>(role, d, q, dst, s); break;
+    case FMT_E3M2: launch_dq_role<FMT_E3M2>(role, d, q, dst, s); break;
     case FMT_UE2M1: launch_dq<FMT_UE2M1, MX_ROLE_ACT>(d, q, dst, s); break;
     default: launch_dq_role<FMT_E4M3>(role, d, q, dst, s); break;
   }

@@ -22,9 +22,9 @@ from dataclasses import dataclass, field
 
 import torch
 
-E2M1, E2M3, E4M3 = 1, 2, 3
-FMT_NAMES = {E2M1: "e2m1", E2M3: "e2m3", E4M3: "e4m3"}
-FMT_BITS = {E2M1: 4, E2M3: 6, E4M3: 8}
+E2M1, E2M3, E4M3, E3M2 = 1, 2, 3, 5
+FMT_NAMES = {E2M1: "e2m1", E2M3: "e2m3", E4M3: "e4m3", E3M2: "e3m2"}
+FMT_BITS = {E2M1: 4, E2M3: 6, E4M3: 8, E3M2: 6}
 
 
 @dataclass(frozen=True)

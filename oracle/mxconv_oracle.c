@@ -52,8 +52,9 @@
 #define ORC_E4M3 3
 #define ORC_E3M2 4
 /* E2M1 magnitude without the sign bit: the 3-bit activation codes of a
- * post-ReLU tensor (§V-B: the sign bit "simply removed", 3 + 8/64 = 3.125
- * bits per element with the block scale), used by the compact latent-replay
+ * post-ReLU tensor (§VI-A: after a ReLU the sign bit carries nothing and is
+ * dropped, 3 + 8/64 = 3.125 bits per element with the block scale), used by
+ * the compact latent-replay
  * buffer (§VII).  Quantized like E2M1; a negative element keeps only its
  * magnitude. */
 #define ORC_UE2M1 5

@@ -32,8 +32,18 @@ def gpu_quantize(d, role, src: torch.Tensor, rounding=mx.MX_RNE, seed=0, amax=No
     return q
 
 
+# the oracle numbers the formats on its own
+OFMT = {mx.MX_E2M1: O.E2M1, mx.MX_E2M3: O.E2M3, mx.MX_E4M3: O.E4M3, mx.MX_E3M2: O.E3M2,
+        mx.MX_UE2M1: O.UE2M1}
+
+
+def ofmt(fmt: int) -> int:
+    """The oracle's number of the library's element format fmt."""
+    return OFMT[fmt]
+
+
 def oracle_quantize(d, role, src: torch.Tensor, rounding=mx.MX_RNE, seed=0, amax=None):
-    return O.quantize(role, d.elem_fmt, src.numpy(), rounding, seed, amax)
+    return O.quantize(role, ofmt(mx.role_fmt(d, role)), src.numpy(), rounding, seed, amax)
 
 
 def f32_bits(v: float) -> int:

@@ -76,7 +76,7 @@ GOOD = dict(n=8, c_in=16, c_out=16, h=8, w=8, k_h=3, k_w=3)
 
 @pytest.mark.parametrize("change,status", [
     (dict(block=4), -4), (dict(block=16), -4),
-    (dict(elem_fmt=0), -3), (dict(elem_fmt=5), -3),
+    (dict(elem_fmt=0), -3), (dict(elem_fmt=6), -3), (dict(act_fmt=6), -3), (dict(act_fmt=-1), -3),
     (dict(c_in=12), -2), (dict(c_out=20), -2), (dict(n=12), -2), (dict(n=-8), -2),
     (dict(stride_h=0), -2), (dict(stride_w=-1), -2), (dict(pad_h=-1), -2),
     (dict(k_h=11), -2), (dict(h=0), -2), (dict(k_w=0), -2), (dict(c_in=0), -2),
@@ -173,3 +173,38 @@ def test_compact_activation_format_is_storage_only():
     assert L.mx_conv_dgrad(ctypes.byref(d), ctypes.byref(good), ctypes.byref(good), A16, None) == -3
     assert L.mx_conv_wgrad(ctypes.byref(d), ctypes.byref(good), ctypes.byref(good), A16, A16, 1 << 20, None) == -3
     assert L.mx_conv_fwd_amax(ctypes.byref(d), ctypes.byref(good), ctypes.byref(good), A16, A16, None) == -3
+
+
+def test_activation_format_pairs():
+    # MicroQonv+ keeps X in FP6 while W and dY stay E2M1: each role is sized
+    # in its own format, and the GEMMs take E2M1 with an FP6 activation
+    L = mx.lib()
+    good = q()
+    for act, bits in ((mx.MX_E3M2, 6), (mx.MX_E2M3, 6)):
+        d = mx.desc(16, 24, 40, 9, 7, 3, 3, 2, 2, 1, 1, elem_fmt=mx.MX_E2M1, act_fmt=act)
+        assert mx.mx_code_bytes(d, mx.MX_ROLE_ACT) == 9 * 7 * 24 * 16 * bits // 8
+        assert mx.mx_code_bytes(d, mx.MX_ROLE_WEIGHT) == 40 * 24 * 9 * 4 // 8
+        assert mx.mx_code_bytes(d, mx.MX_ROLE_GRAD) == 5 * 4 * 40 * 16 * 4 // 8
+        assert mx.mx_wgrad_workspace_bytes(d) > 0 and mx.mx_fwd_amax_bytes(d) > 0
+        # past the format check: the misaligned output is what is rejected
+        assert L.mx_conv_fwd(ctypes.byref(d), ctypes.byref(good), ctypes.byref(good), MIS, None) == -5
+        assert L.mx_conv_wgrad(ctypes.byref(d), ctypes.byref(good), ctypes.byref(good), MIS, A16, 1 << 30, None) == -5
+    # E3M2 throughout is a GEMM format too
+    d = mx.desc(16, 24, 40, 9, 7, 3, 3, elem_fmt=mx.MX_E3M2)
+    assert mx.mx_code_bytes(d, mx.MX_ROLE_WEIGHT) == 40 * 24 * 9 * 6 // 8
+    assert L.mx_conv_dgrad(ctypes.byref(d), ctypes.byref(good), ctypes.byref(good), MIS, None) == -5
+    # pairs without kernels: FP8 or FP6 weights with another activation format
+    for fmt, act in ((mx.MX_E4M3, mx.MX_E3M2), (mx.MX_E2M3, mx.MX_E2M1), (mx.MX_E3M2, mx.MX_E2M3),
+                     (mx.MX_E2M1, mx.MX_E4M3)):
+        d = mx.desc(16, 24, 40, 9, 7, 3, 3, elem_fmt=fmt, act_fmt=act)
+        assert L.mx_conv_fwd(ctypes.byref(d), ctypes.byref(good), ctypes.byref(good), A16, None) == -3
+        assert L.mx_conv_wgrad(ctypes.byref(d), ctypes.byref(good), ctypes.byref(good), A16, A16, 1 << 30, None) == -3
+        assert mx.mx_wgrad_workspace_bytes(d) == 0 and mx.mx_fwd_amax_bytes(d) == 0
+        # the data gradient reads W and dY only
+        assert L.mx_conv_dgrad(ctypes.byref(d), ctypes.byref(good), ctypes.byref(good), MIS, None) == -5
+    # the compact codes as the activation format: storage only
+    d = mx.desc(16, 24, 40, 9, 7, 3, 3, elem_fmt=mx.MX_E2M1, act_fmt=mx.MX_UE2M1)
+    assert mx.mx_code_bytes(d, mx.MX_ROLE_ACT) == 9 * 7 * 24 * 16 * 3 // 8
+    assert quant(d, role=mx.MX_ROLE_WEIGHT, dst=q(codes=MIS)) == -5   # W stays E2M1
+    assert L.mx_conv_fwd(ctypes.byref(d), ctypes.byref(good), ctypes.byref(good), A16, None) == -3
+    assert L.mx_conv_dgrad(ctypes.byref(d), ctypes.byref(good), ctypes.byref(good), MIS, None) == -5

@@ -1,5 +1,5 @@
 """GPU parity of the compact 3-bit activation codes (MX_UE2M1) used for the
-latent-replay buffer (MicroQonv, arXiv 2609.28358, §V-B: the sign bit of
+latent-replay buffer (MicroQonv, arXiv 2609.28358, §VI-A: the sign bit of
 post-ReLU activations removed, 3.125 bits per element with the block scale;
 §VII).  Codes (packed 3-bit stream), block scales, T and amax bit-exact
 against the oracle; dequantization bit-exact; and for post-ReLU data the

@@ -1,7 +1,9 @@
 """GPU parity of the implicit-im2col GEMMs against the CPU oracle on shapes
 the oracle finishes in seconds: several tiles, ragged tails, stride 2, 1x1,
 rectangular kernels, padding wider than the kernel reach, empty batch.
-Every output within 2e-3 * sum|a*b| (MicroQonv, arXiv 2609.28358, §IV-B)."""
+Every output within 2e-3 * sum|a*b| (MicroQonv, arXiv 2609.28358, §IV-B).
+Format pairs: each element format throughout, and MicroQonv+ (§IV-D,
+Table VI): E2M1 weights and gradients with FP6 (E3M2, or E2M3) activations."""
 import numpy as np
 import pytest
 import torch
@@ -9,11 +11,14 @@ import torch
 import microscaling_quantized_convolution_mx_amd as mx
 import oracle as O
 from microscaling_quantized_convolution_mx_amd import workloads as WL
-from gpu_util import DEV, assert_close, conv_buffers, gpu_quantize, oracle_conv, run_layer, say
+from gpu_util import DEV, assert_close, conv_buffers, gpu_quantize, ofmt, oracle_conv, oracle_quantize, run_layer, say
 
 pytestmark = pytest.mark.gpu
 
-FMTS = [mx.MX_E2M1, mx.MX_E2M3, mx.MX_E4M3]
+# (elem_fmt of W and dY, act_fmt of X; 0 = the same)
+FMT_PAIRS = [(mx.MX_E2M1, 0), (mx.MX_E2M3, 0), (mx.MX_E4M3, 0), (mx.MX_E3M2, 0),
+             (mx.MX_E2M1, mx.MX_E3M2), (mx.MX_E2M1, mx.MX_E2M3)]
+PAIR_IDS = ["e2m1", "e2m3", "e4m3", "e3m2", "w4-x6e3m2", "w4-x6e2m3"]
 
 SHAPES = [
     # n, ci, co, h, w, kh, kw, sh, sw, ph, pw
@@ -47,16 +52,17 @@ def layer_inputs(shape, seed):
     return lay, WL.gen_x(lay, "normal", seed), WL.gen_w(lay, seed + 1), WL.gen_dy(lay, 1.0, seed + 2)
 
 
-@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("fmts", FMT_PAIRS, ids=PAIR_IDS)
 @pytest.mark.parametrize("shape", SHAPES)
-def test_conv_full(fmt, shape):
-    say("conv", fmt, shape)
+def test_conv_full(fmts, shape):
+    fmt, act_fmt = fmts
+    say("conv", fmt, act_fmt, shape)
     lay, x, w, dy = layer_inputs(shape, 100 + SHAPES.index(shape))
-    d = mx.desc_from_layer(lay, fmt)
+    d = mx.desc_from_layer(lay, fmt, act_fmt)
     (qx, qw, qdy), (y, dx, dw) = run_layer(d, x, w, dy, seed_sr=7)
-    ox = O.quantize(O.ACT, fmt, x.numpy())
-    ow = O.quantize(O.WEIGHT, fmt, w.numpy())
-    ody = O.quantize(O.GRAD, fmt, dy.numpy(), O.SR, 7)
+    ox = oracle_quantize(d, mx.MX_ROLE_ACT, x)
+    ow = oracle_quantize(d, mx.MX_ROLE_WEIGHT, w)
+    ody = oracle_quantize(d, mx.MX_ROLE_GRAD, dy, mx.MX_SR, 7)
     cv = oracle_conv(d)
     ref, s = O.conv_fwd(cv, ow.exact(), ox.exact())
     assert_close(y.cpu().numpy(), ref, s, "fwd")
@@ -104,3 +110,39 @@ def test_wgrad_is_deterministic():
     mx.mx_conv_wgrad(d, qdy, qx, dw2, ws)
     torch.cuda.synchronize()
     assert torch.equal(dw1, dw2)
+
+
+@pytest.mark.parametrize("fmts", [(mx.MX_E2M1, mx.MX_E3M2), (mx.MX_E2M1, mx.MX_E2M3), (mx.MX_E3M2, 0)],
+                         ids=["w4-x6e3m2", "w4-x6e2m3", "e3m2"])
+def test_fp6_decode_of_every_code(fmts):
+    # 1x1 conv with an identity weight: every output is one dequantized
+    # activation, so the bound 2e-3*S is a per-element relative bound and any
+    # wrong decode of an FP6 code (a relative error of at least 1/16 for
+    # E2M3, 1/8 for E3M2) fails.  The activations span 12 octaves, so every
+    # magnitude code, subnormals included, occurs with both signs.
+    fmt, act_fmt = fmts
+    c, n, hw = 64, 64, 8
+    d = mx.desc(n, c, c, hw, hw, 1, 1, elem_fmt=fmt, act_fmt=act_fmt)
+    say("fp6 decode", fmt, act_fmt)
+    g = torch.Generator().manual_seed(41)
+    mag = torch.exp2(torch.rand(hw, hw, c, n, generator=g) * 12.0 - 10.0)
+    sign = torch.where(torch.rand(hw, hw, c, n, generator=g) < 0.5, -1.0, 1.0)
+    x = (mag * sign).float()
+    w = torch.eye(c).reshape(c, c, 1, 1)
+    qx = gpu_quantize(d, mx.MX_ROLE_ACT, x)
+    qw = gpu_quantize(d, mx.MX_ROLE_WEIGHT, w)
+    y = torch.full((hw, hw, c, n), float("nan"), device=DEV)
+    mx.mx_conv_fwd(d, qw, qx, y)
+    torch.cuda.synchronize()
+    ox = oracle_quantize(d, mx.MX_ROLE_ACT, x)
+    ow = oracle_quantize(d, mx.MX_ROLE_WEIGHT, w)
+    xf = mx.role_fmt(d, mx.MX_ROLE_ACT)
+    nmag = O.fmt_grid(ofmt(xf)).size
+    sign_bit = 1 << O.sign_shift(ofmt(xf))
+    codes = ox.codes.astype(np.int64)
+    for m in range(nmag):
+        for sb in (0, sign_bit):
+            assert np.any(codes == (m | sb)), f"code {m | sb} absent"
+    cv = oracle_conv(d)
+    ref, s = O.conv_fwd(cv, ow.exact(), ox.exact())
+    assert_close(y.cpu().numpy(), ref, s, "fwd identity")

@@ -8,11 +8,11 @@ import torch
 import microscaling_quantized_convolution_mx_amd as mx
 import oracle as O
 from microscaling_quantized_convolution_mx_amd import workloads as WL
-from gpu_util import DEV, assert_quant_equal, gpu_quantize, oracle_quantize, say
+from gpu_util import DEV, assert_quant_equal, gpu_quantize, ofmt, oracle_quantize, say
 
 pytestmark = pytest.mark.gpu
 
-FMTS = [mx.MX_E2M1, mx.MX_E2M3, mx.MX_E4M3]
+FMTS = [mx.MX_E2M1, mx.MX_E2M3, mx.MX_E4M3, mx.MX_E3M2]
 
 # (n, c_in, c_out, h, w, k, stride, pad): ragged block rows (N/8 not a multiple
 # of the 32 blocks a wavefront covers), several workgroups, stride 2
@@ -81,7 +81,7 @@ def test_quantize_grid_ties(fmt):
     # T = 1 (amax = 448 * max) and every other block holds the element
     # maximum, so its scale is exactly 1 and the grid midpoints placed in it
     # are exact ties after scaling: both sides must pick the even code
-    grid = O.fmt_grid(fmt)
+    grid = O.fmt_grid(ofmt(fmt))
     mids = (grid[1:] + grid[:-1]) / 2
     vals = np.concatenate([mids, -mids, grid[:-1]]).astype(np.float32)
     npos = -(-vals.size // 63) + 1

@@ -1,8 +1,8 @@
 """The compact 3-bit activation codes of the latent-replay buffer.
 
-After a ReLU every activation is non-negative, so the E2M1 sign bit can be
-"simply removed, leaving activations at 3-bit precision": 3 + 8/64 = 3.125
-bits per element with the block scale (MicroQonv, arXiv 2609.28358, §V-B;
+After a ReLU every activation is non-negative, so the E2M1 sign bit carries
+nothing and can be dropped, leaving 3-bit codes: 3 + 8/64 = 3.125 bits per
+element with the block scale (MicroQonv, arXiv 2609.28358, §VI-A;
 §VII stores the replay buffer that way).  The oracle's UE2M1 format is that
 reading: E2M1 quantization with the sign dropped, packed as a 3-bit stream."""
 import numpy as np
@@ -52,7 +52,7 @@ def test_three_bit_stream_packing(orc):
 
 
 def test_three_point_one_two_five_bits_per_element(orc):
-    # §V-B: 3 bits per activation pixel + 8/64 for the E4M3 block scale
+    # §VI-A: 3 bits per activation pixel + 8/64 for the E4M3 block scale
     x = act((8, 8, 64, 16), 3)
     q = O.quantize(O.ACT, O.UE2M1, x)
     bits = (q.packed().size + q.scales.size) * 8 / x.size

@@ -19,7 +19,7 @@ import torch
 import oracle as O
 from microscaling_quantized_convolution_mx_amd import workloads as WL
 
-FMTS = [O.E2M1, O.E2M3, O.E4M3]
+FMTS = [O.E2M1, O.E2M3, O.E3M2, O.E4M3]
 
 
 def act(shape, seed, dist="normal"):
