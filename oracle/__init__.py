@@ -14,6 +14,8 @@ Training and Inference" (arXiv 2609.28358):
 * channel-batch-first layouts -- §IV-A, Fig. 3
 * explicit im2col and the three GEMMs -- §II-C, §IV-B
 * quantization-event counts of the three flows -- §IV-C, Table I
+* the original microscaling format (E8M0 power-of-two scale per square block,
+  no tensor scale) on 32x32 blocks -- §II-D, §IV-B
 """
 from __future__ import annotations
 
@@ -106,6 +108,19 @@ def lib():
         getattr(L, f).restype = ctypes.c_int
         getattr(L, f).argtypes = [ctypes.c_int, ctypes.c_int, _I64, _I64, _I64, _I64, _P, _P,
                                   ctypes.c_float, _P]
+    L.orc_e8m0_code.restype = ctypes.c_int
+    L.orc_e8m0_code.argtypes = [ctypes.c_int, ctypes.c_float, ctypes.c_int]
+    L.orc_mx_nblocks.restype = _I64
+    L.orc_mx_nblocks.argtypes = [ctypes.c_int, ctypes.c_int, _I64, _I64, _I64, _I64]
+    L.orc_mx_src_index.restype = _I64
+    L.orc_mx_src_index.argtypes = [ctypes.c_int, ctypes.c_int, _I64, _I64, _I64, _I64, _I64,
+                                   ctypes.c_int, ctypes.c_int]
+    L.orc_quantize_mx.restype = ctypes.c_int
+    L.orc_quantize_mx.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint64, ctypes.c_int, _P,
+                                  _I64, _I64, _I64, _I64, _P, _P]
+    L.orc_dequantize_mx.restype = ctypes.c_int
+    L.orc_dequantize_mx.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _I64, _I64, _I64, _I64, _P, _P,
+                                    _P, _P]
     L.orc_pack.restype = ctypes.c_int
     L.orc_pack.argtypes = [ctypes.c_int, _P, _I64, _P]
     L.orc_im2col_src.restype = _I64
@@ -259,6 +274,64 @@ def dequantize64(q: QTensor) -> np.ndarray:
     out = np.zeros(q.dims, dtype=np.float64)
     lib().orc_dequantize64(q.role, q.fmt, *q.dims, _ptr(q.codes), _ptr(q.scales), q.t, _ptr(out))
     return out
+
+
+# --------------------------------------------------------------------------
+# the original microscaling format on square blocks (E8M0 scale per block)
+# --------------------------------------------------------------------------
+
+MX_BLOCK = 32
+
+
+def e8m0_code(fmt: int, amax: float, nonfinite: bool = False) -> int:
+    return lib().orc_e8m0_code(fmt, amax, int(bool(nonfinite)))
+
+
+def mx_nblocks(role: int, dims, block: int = MX_BLOCK) -> int:
+    return lib().orc_mx_nblocks(role, block, *dims)
+
+
+def mx_src_index(role: int, dims, b: int, r: int, c: int, block: int = MX_BLOCK) -> int:
+    return lib().orc_mx_src_index(role, block, *dims, b, r, c)
+
+
+class MxTensor:
+    """Oracle-side MX tensor: unpacked codes (one byte per element in block
+    order), one E8M0 scale per S x S block, no tensor scale."""
+
+    def __init__(self, role, fmt, dims, block, codes, scales):
+        self.role, self.fmt, self.dims, self.block = role, fmt, dims, block
+        self.codes, self.scales = codes, scales
+
+    def packed(self) -> np.ndarray:
+        return pack(self.fmt, self.codes)
+
+    def _deq(self, want64: bool):
+        out = np.zeros(self.dims, dtype=np.float64 if want64 else np.float32)
+        args = (_ptr(out), None) if want64 else (None, _ptr(out))
+        if lib().orc_dequantize_mx(self.role, self.fmt, self.block, *self.dims, _ptr(self.codes),
+                                   _ptr(self.scales), *args) != 0:
+            raise ValueError("bad format")
+        return out
+
+    def dequantize(self) -> np.ndarray:
+        return self._deq(False)
+
+    def exact(self) -> np.ndarray:
+        return self._deq(True)
+
+
+def quantize_mx(role: int, fmt: int, src: np.ndarray, rounding: int = RNE, seed: int = 0,
+                block: int = MX_BLOCK) -> MxTensor:
+    src = np.ascontiguousarray(src, dtype=np.float32)
+    dims = role_dims(role, src.shape)
+    nb = mx_nblocks(role, dims, block)
+    codes = np.zeros(nb * block * block, dtype=np.uint8)
+    scales = np.zeros(nb, dtype=np.uint8)
+    rc = lib().orc_quantize_mx(role, fmt, rounding, seed, block, _ptr(src), *dims, _ptr(codes), _ptr(scales))
+    if rc != 0:
+        raise ValueError("oracle quantize_mx rejected its arguments")
+    return MxTensor(role, fmt, dims, block, codes, scales)
 
 
 def pack(fmt: int, codes: np.ndarray) -> np.ndarray:

@@ -428,6 +428,143 @@ int orc_dequantize64(int role, int fmt, int64_t d0, int64_t d1, int64_t d2, int6
   return 0;
 }
 
+/* ------------------------------------------------------------------------ */
+/* The original microscaling format (§II-D: a power-of-two block scale in   */
+/* E8M0, no tensor scale) on square S x S blocks in the same channel-batch- */
+/* first block order (§IV-A, §IV-B: MicroQonv holds for any block scale).   */
+/* The shared scale of a block is 2^e with e = floor(log2 amax_block) minus  */
+/* the exponent of the element format's largest value (the OCP MX rule),    */
+/* clamped to the E8M0 range [-127, 127]; each element is |x| / 2^e rounded  */
+/* onto the element grid (saturating), sign kept.                           */
+/* ------------------------------------------------------------------------ */
+
+static int64_t mx_nblocks(int role, const int64_t d[4], int S) {
+  if (role == ORC_WEIGHT) return d[2] * d[3] * (d[0] / S) * (d[1] / S);
+  return d[0] * d[1] * (d[2] / S) * (d[3] / S);
+}
+
+/* Source index of element (r, c) of block b: blocks [H][W][C/S][N/S] with
+ * (r, c) = (channel, sample) for activations and gradients, blocks
+ * [Kh][Kw][Co/S][Ci/S] with (r, c) = (co, ci) for weights. */
+static int64_t mx_src_index(int role, const int64_t d[4], int S, int64_t b, int r, int c) {
+  if (role == ORC_WEIGHT) {
+    int64_t Co = d[0], Ci = d[1], Kh = d[2], Kw = d[3];
+    int64_t cib = b % (Ci / S), t = b / (Ci / S);
+    int64_t cob = t % (Co / S);
+    t /= (Co / S);
+    int64_t kw = t % Kw, kh = t / Kw;
+    return (((cob * S + r) * Ci + cib * S + c) * Kh + kh) * Kw + kw;
+  }
+  int64_t C = d[2], N = d[3];
+  int64_t nb = b % (N / S), t = b / (N / S);
+  int64_t cb = t % (C / S), pos = t / (C / S);
+  return (pos * C + cb * S + r) * N + nb * S + c;
+}
+
+int64_t orc_mx_nblocks(int role, int S, int64_t d0, int64_t d1, int64_t d2, int64_t d3) {
+  int64_t d[4] = {d0, d1, d2, d3};
+  return mx_nblocks(role, d, S);
+}
+int64_t orc_mx_src_index(int role, int S, int64_t d0, int64_t d1, int64_t d2, int64_t d3, int64_t b, int r,
+                         int c) {
+  int64_t d[4] = {d0, d1, d2, d3};
+  return mx_src_index(role, d, S, b, r, c);
+}
+
+/* floor(log2 a) for a finite a > 0, from the binary exponent (exact). */
+static int floor_log2f(float a) {
+  int e;
+  frexpf(a, &e); /* a = m * 2^e, m in [0.5, 1) */
+  return e - 1;
+}
+
+/* E8M0 code of the shared scale of a block with maximum magnitude amax:
+ * 0xFF when the block holds a non-finite value, 0 (2^-127) for an all-zero
+ * block. */
+int orc_e8m0_code(int fmt, float amax, int nonfinite) {
+  if (nonfinite) return 0xFF;
+  if (amax == 0.0f) return 0;
+  int e = floor_log2f(amax) - floor_log2f(fmt_max_f(fmt));
+  if (e < -127) e = -127;
+  if (e > 127) e = 127;
+  return e + 127;
+}
+
+/* Quantize one tensor in S x S MX blocks: codes one byte per element in
+ * block order (block, then row, column), scales one E8M0 byte per block.
+ * Returns 0, or -1 on a bad format, role or shape. */
+int orc_quantize_mx(int role, int fmt, int rounding, uint64_t seed, int S, const float* src, int64_t d0,
+                    int64_t d1, int64_t d2, int64_t d3, uint8_t* codes, uint8_t* scales) {
+  orc_fmt_t f;
+  if (fmt_desc(fmt, &f) || !f.signed_ || S <= 0) return -1;
+  int64_t d[4] = {d0, d1, d2, d3};
+  if (role == ORC_WEIGHT) {
+    if (d0 % S || d1 % S) return -1;
+  } else if (role == ORC_ACT || role == ORC_GRAD) {
+    if (d2 % S || d3 % S) return -1;
+  } else {
+    return -1;
+  }
+  int64_t nb = mx_nblocks(role, d, S);
+  int sign_shift = f.ebits + f.mbits;
+  int64_t bs = (int64_t)S * S;
+#pragma omp parallel for schedule(static)
+  for (int64_t b = 0; b < nb; ++b) {
+    float amax = 0.0f;
+    int nonfinite = 0;
+    for (int r = 0; r < S; ++r)
+      for (int c = 0; c < S; ++c) {
+        float a = fabsf(src[mx_src_index(role, d, S, b, r, c)]);
+        if (!isfinite(a)) nonfinite = 1;
+        else if (a > amax) amax = a;
+      }
+    int code = orc_e8m0_code(fmt, amax, nonfinite);
+    scales[b] = (uint8_t)code;
+    /* 1 / 2^e, exact for e in [-127, 127] */
+    float inv = ldexpf(1.0f, 127 - code);
+    for (int r = 0; r < S; ++r)
+      for (int c = 0; c < S; ++c) {
+        int64_t si = mx_src_index(role, d, S, b, r, c);
+        float x = src[si];
+        int mag = 0;
+        if (!nonfinite) {
+          float v = fabsf(x) * inv;
+          mag = (rounding == ORC_SR) ? orc_round_sr(fmt, v, orc_sr_uniform(seed, (uint64_t)si)) : orc_round_rne(fmt, v);
+        }
+        int sgn = (!nonfinite && signbit(x)) ? 1 : 0;
+        codes[b * bs + (int64_t)r * S + c] = (uint8_t)(mag | (sgn << sign_shift));
+      }
+  }
+  return 0;
+}
+
+/* Exact dequantized values g * 2^e (NaN for a 0xFF scale) in the role's
+ * layout, as fp64 (dst64) and/or fp32 (dst32, exact as well: the products
+ * lie within fp32's range down to its subnormals). */
+int orc_dequantize_mx(int role, int fmt, int S, int64_t d0, int64_t d1, int64_t d2, int64_t d3,
+                      const uint8_t* codes, const uint8_t* scales, double* dst64, float* dst32) {
+  orc_fmt_t f;
+  if (fmt_desc(fmt, &f) || S <= 0) return -1;
+  int64_t d[4] = {d0, d1, d2, d3};
+  int64_t nb = mx_nblocks(role, d, S);
+  int sign_shift = f.ebits + f.mbits;
+  int64_t bs = (int64_t)S * S;
+#pragma omp parallel for schedule(static)
+  for (int64_t b = 0; b < nb; ++b) {
+    double scale = scales[b] == 0xFF ? NAN : ldexp(1.0, (int)scales[b] - 127);
+    for (int r = 0; r < S; ++r)
+      for (int c = 0; c < S; ++c) {
+        uint8_t code = codes[b * bs + (int64_t)r * S + c];
+        double v = orc_fmt_value(fmt, code & ((1 << sign_shift) - 1)) * scale;
+        if ((code >> sign_shift) & 1) v = -v;
+        int64_t si = mx_src_index(role, d, S, b, r, c);
+        if (dst64) dst64[si] = v;
+        if (dst32) dst32[si] = (float)v;
+      }
+  }
+  return 0;
+}
+
 /* Pack codes (O6): E2M1 two per byte, element 2j in the low nibble; E2M3 and
  * E3M2 as a little-endian 6-bit stream (48 bytes per 64-element block), the
  * unsigned 3-bit E2M1 as a 3-bit stream (24 bytes per block); E4M3 one byte
