@@ -30,8 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM = 8.0e12                    # bytes/s, MI355X HBM3E
-PEAK_MFMA = {"bf16": 2.5e15, "f16": 2.5e15}  # dense flop/s
-RIDGE = PEAK_MFMA["bf16"] / PEAK_HBM  # flop per byte
+PEAK_MFMA = {"bf16": 2.5e15, "f16": 2.5e15, "fp4": 10.1e15}  # dense flop/s
 
 
 def parse():
@@ -44,6 +43,9 @@ def parse():
     ap.add_argument("--act-fmt", default=None, choices=["e3m2", "e2m3"],
                     help="MicroQonv+: activations in this FP6 format, weights and gradients in the "
                          "element format (E2M1)")
+    ap.add_argument("--block", type=int, default=8, choices=[8, 32],
+                    help="8: E4M3 scale per 8x8 block + fp32 tensor scale; 32: E8M0 scale per 32x32 block "
+                         "(original microscaling, E2M1, scaled FP4 MFMA)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate budget of the CPU-baseline sample")
@@ -164,14 +166,18 @@ def main():
     afmt = fmts[a.act_fmt] if a.act_fmt else 0   # 0: activations in fmt too
     if afmt and a.flow:
         raise SystemExit("--act-fmt applies to the MicroQonv step, not to --flow")
-    qb = mx.CODE_BITS[fmt] / 8 + 1 / 64          # quantized bytes per element (codes + block scales)
-    qbx = mx.CODE_BITS[afmt or fmt] / 8 + 1 / 64  # the same for the activation X
+    if a.block == 32 and (afmt or a.flow or a.producer_amax or fmt != mx.MX_E2M1):
+        raise SystemExit("--block 32 runs the E2M1 MicroQonv step only")
+    sb = 1 / (a.block * a.block)                   # scale bytes per element
+    qb = mx.CODE_BITS[fmt] / 8 + sb                # quantized bytes per element (codes + block scales)
+    qbx = mx.CODE_BITS[afmt or fmt] / 8 + sb       # the same for the activation X
+    rd = 8 if a.block == 8 else 4                  # fp32 source bytes read per element: amax pass + pass, or once
     stream = torch.cuda.current_stream().cuda_stream
 
     D = ctypes.byref
     calls: list[Call] = []
     keep = []                         # keeps every buffer and ctypes struct alive
-    ws_bytes = max(mx.mx_wgrad_workspace_bytes(mx.desc_from_layer(l, fmt, afmt)) for l in wl.layers)
+    ws_bytes = max(mx.mx_wgrad_workspace_bytes(mx.desc_from_layer(l, fmt, afmt, a.block)) for l in wl.layers)
     ws = torch.empty(max(ws_bytes // 4, 4), device=dev)
     keep.append(ws)
 
@@ -180,7 +186,7 @@ def main():
     flow_stats = {"activation_elements": 0, "quantized_elements": 0, "stored_activation_bytes": 0.0}
     n_chained = 0
     for li, lay in enumerate(wl.layers):
-        d = mx.desc_from_layer(lay, fmt, afmt)
+        d = mx.desc_from_layer(lay, fmt, afmt, a.block)
         x = WL.gen_x(lay, wl.x_dist, WL.seed_for(wl.cfg_index, li, 1)).to(dev)
         w = WL.gen_w(lay, WL.seed_for(wl.cfg_index, li, 2)).to(dev)
         dy = WL.gen_dy(lay, wl.dy_sigma, WL.seed_for(wl.cfg_index, li, 3)).to(dev)
@@ -223,14 +229,14 @@ def main():
             x_src, x_given, x_bytes = py.data_ptr(), 1, nx * (4 + qbx)
             n_chained += 1
         else:
-            x_src, x_given, x_bytes = x.data_ptr(), 0, nx * (8 + qbx)
+            x_src, x_given, x_bytes = x.data_ptr(), 0, nx * (rd + qbx)
         calls += [
             Call(L.mx_quantize_cbf, (D(d), mx.MX_ROLE_ACT, x_src, D(cq[0]), mx.MX_RNE, 0, x_given, stream),
                  "quantize", ("quantize_act", shape), 0, x_bytes, "quantize X"),
             Call(L.mx_quantize_cbf, (D(d), mx.MX_ROLE_WEIGHT, w.data_ptr(), D(cq[1]), mx.MX_RNE, 0, 0, stream),
-                 "quantize", ("quantize_weight", shape), 0, nw * (8 + qb), "quantize W"),
+                 "quantize", ("quantize_weight", shape), 0, nw * (rd + qb), "quantize W"),
             Call(L.mx_quantize_cbf, (D(d), mx.MX_ROLE_GRAD, dy.data_ptr(), D(cq[2]), mx.MX_SR, sr_seed, 0, stream),
-                 "quantize", ("quantize_grad", shape), 0, ny * (8 + qb), "quantize dY"),
+                 "quantize", ("quantize_grad", shape), 0, ny * (rd + qb), "quantize dY"),
             Call(L.mx_conv_fwd, (D(d), D(cq[1]), D(cq[0]), y.data_ptr(), stream),
                  "fwd", ("conv_fwd", shape), f, nw * qb + nx * qbx + 4 * ny, "fwd"),
             Call(L.mx_conv_dgrad, (D(d), D(cq[1]), D(cq[2]), dx.data_ptr(), stream),
@@ -357,10 +363,13 @@ def main():
     dom_key, dom = max(groups.items(), key=lambda kv: kv[1]["ms"])
     launch_s = dom["ms"] / dom["n"] / 1e3
     ai = dom["flops"] / dom["bytes"] if dom["bytes"] else 0.0
-    if dom["flops"] and ai >= RIDGE:
+    # the GEMMs' MFMA type: fp4 (scaled, 32x32 E8M0 blocks), else the
+    # exact fp16 decode (bf16 for E4M3 operands); both 16-bit peaks are equal
+    mfma_t = "fp4" if a.block == 32 else ("bf16" if fmt == mx.MX_E4M3 else "f16")
+    if dom["flops"] and ai >= PEAK_MFMA[mfma_t] / PEAK_HBM:
         achieved = dom["flops"] / launch_s
-        roof = {"bound": "mfma", "achieved": achieved / 1e12, "peak": PEAK_MFMA["bf16"] / 1e12,
-                "unit": "TFLOP/s"}
+        roof = {"bound": "mfma", "achieved": achieved / 1e12, "peak": PEAK_MFMA[mfma_t] / 1e12,
+                "unit": "TFLOP/s", "mfma_dtype": mfma_t}
     else:
         achieved = dom["bytes"] / launch_s
         roof = {"bound": "hbm", "achieved": achieved / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
@@ -395,12 +404,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": mfma_t,
         "data": "synthetic",
         "config": {"workload": f"{a.workload}: {wl.name}", "layers": len(wl.layers),
                    "batch": wl.layers[0].n, "elem_fmt": WL.FMT_NAMES[fmt],
                    **({"act_fmt": a.act_fmt, "variant": "MicroQonv+ (FP6 activations)"} if afmt else {}),
-                   "block": "8x8 E4M3 scale + fp32 tensor scale",
+                   "block": "8x8 E4M3 scale + fp32 tensor scale" if a.block == 8
+                            else "32x32 E8M0 scale, no tensor scale (scaled FP4 MFMA)",
                    "step": "per layer: quantize X,W,dY; fwd; dgrad; wgrad; dequantize Xq"
                            + ("; replay buffer quantize+dequantize" if wl.lr_buffer else ""),
                    "graph": bool(graph is not None),

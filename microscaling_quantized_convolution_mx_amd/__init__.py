@@ -108,14 +108,16 @@ def status_str(status: int) -> str:
 
 def desc(n, c_in, c_out, h, w, k_h, k_w, stride_h=1, stride_w=1, pad_h=0, pad_w=0,
          elem_fmt=MX_E2M1, block=8, act_fmt=0) -> mx_conv_desc:
-    """act_fmt: format of the activation X (0: elem_fmt, the format of W and dY)."""
+    """act_fmt: format of the activation X (0: elem_fmt, the format of W and dY).
+    block: 8 (E4M3 block scale and fp32 tensor scale) or 32 (E8M0 scale per
+    32x32 block, E2M1 elements)."""
     return mx_conv_desc(n, c_in, c_out, h, w, k_h, k_w, stride_h, stride_w, pad_h, pad_w,
                         elem_fmt, block, act_fmt)
 
 
-def desc_from_layer(layer, elem_fmt: int, act_fmt: int = 0) -> mx_conv_desc:
+def desc_from_layer(layer, elem_fmt: int, act_fmt: int = 0, block: int = 8) -> mx_conv_desc:
     return desc(layer.n, layer.c_in, layer.c_out, layer.h, layer.w, layer.k_h, layer.k_w,
-                layer.stride_h, layer.stride_w, layer.pad_h, layer.pad_w, elem_fmt, act_fmt=act_fmt)
+                layer.stride_h, layer.stride_w, layer.pad_h, layer.pad_w, elem_fmt, block=block, act_fmt=act_fmt)
 
 
 def role_fmt(d: mx_conv_desc, role: int) -> int:
@@ -170,9 +172,10 @@ class QTensor:
         self.tensor_scale = torch.zeros(1, dtype=torch.float32, device=device)
         self.amax = torch.zeros(1, dtype=torch.float32, device=device)
         self.code_bytes, self.scale_bytes = nc, ns
-        # stored block scales: one byte per 8x8 block (the rest of the
-        # scales buffer is the quantizer's scratch)
-        self.nblocks = nc * 8 // (64 * CODE_BITS[self.fmt])
+        # stored block scales: one byte per block (8x8 E4M3 or 32x32 E8M0;
+        # the rest of the scales buffer is the quantizer's scratch)
+        self.block = d.block
+        self.nblocks = nc * 8 // (d.block * d.block * CODE_BITS[self.fmt])
 
     def c(self) -> mx_qtensor:
         return mx_qtensor(self.codes.data_ptr(), self.scales.data_ptr(),

@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmxconv.so")
 ARCH = os.environ.get("MXCONV_ARCH", "gfx950")
 
-SOURCES = ["capi.cpp", "quantize.hip", "conv.hip", "conv_mixed.hip"]
+SOURCES = ["capi.cpp", "quantize.hip", "quantize_mx.hip", "conv.hip", "conv_mixed.hip", "conv_mx.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC", "-ffp-contract=off",

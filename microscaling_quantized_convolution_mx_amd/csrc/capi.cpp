@@ -18,6 +18,7 @@ Geom make_geom(const mx_conv_desc* d) {
   g.k_h = d->k_h; g.k_w = d->k_w; g.sh = d->stride_h; g.sw = d->stride_w;
   g.ph = d->pad_h; g.pw = d->pad_w; g.fmt = d->elem_fmt;
   g.afmt = d->act_fmt != 0 ? d->act_fmt : d->elem_fmt;
+  g.block = d->block;
   g.ho = (d->h + 2 * d->pad_h - d->k_h) / d->stride_h + 1;
   g.wo = (d->w + 2 * d->pad_w - d->k_w) / d->stride_w + 1;
   return g;
@@ -31,7 +32,9 @@ int64_t role_numel(const Geom& g, mx_role role) {
   }
 }
 
-int64_t role_nblocks(const Geom& g, mx_role role) { return role_numel(g, role) / 64; }
+int64_t role_nblocks(const Geom& g, mx_role role) {
+  return role_numel(g, role) / (static_cast<int64_t>(g.block) * g.block);
+}
 
 int code_bits(int fmt) {
   return fmt == MX_E2M1 ? 4 : (fmt == MX_E2M3 || fmt == MX_E3M2) ? 6 : fmt == MX_UE2M1 ? 3 : 8;
@@ -57,12 +60,15 @@ bool known_fmt(int32_t f) {
 
 mx_status check_desc(const mx_conv_desc* d) {
   if (!d) return MX_ERR_NULL;
-  if (d->block != 8) return MX_ERR_BLOCK;
+  if (d->block != 8 && d->block != 32) return MX_ERR_BLOCK;
   if (!known_fmt(d->elem_fmt) || (d->act_fmt != 0 && !known_fmt(d->act_fmt))) return MX_ERR_FORMAT;
   if (d->n < 0 || d->c_in <= 0 || d->c_out <= 0 || d->h <= 0 || d->w <= 0 || d->k_h <= 0 || d->k_w <= 0)
     return MX_ERR_SHAPE;
   if (d->stride_h <= 0 || d->stride_w <= 0 || d->pad_h < 0 || d->pad_w < 0) return MX_ERR_SHAPE;
-  if (d->n % 8 || d->c_in % 8 || d->c_out % 8) return MX_ERR_SHAPE;
+  if (d->n % d->block || d->c_in % d->block || d->c_out % d->block) return MX_ERR_SHAPE;
+  // the E8M0 32x32-block format is implemented for E2M1 elements throughout
+  if (d->block == 32 && (d->elem_fmt != MX_E2M1 || (d->act_fmt != 0 && d->act_fmt != MX_E2M1)))
+    return MX_ERR_FORMAT;
   if (static_cast<int64_t>(d->h) + 2 * static_cast<int64_t>(d->pad_h) < d->k_h) return MX_ERR_SHAPE;
   if (static_cast<int64_t>(d->w) + 2 * static_cast<int64_t>(d->pad_w) < d->k_w) return MX_ERR_SHAPE;
   const Geom g = mx::make_geom(d);
@@ -125,7 +131,8 @@ size_t mx_code_bytes(const mx_conv_desc* desc, mx_role role) {
 
 size_t mx_scale_bytes(const mx_conv_desc* desc, mx_role role) {
   if (check_desc(desc) != MX_OK || check_role(role) != MX_OK) return 0;
-  return static_cast<size_t>(mx::scale_buffer_bytes(mx::role_nblocks(mx::make_geom(desc), role)));
+  const int64_t nb = mx::role_nblocks(mx::make_geom(desc), role);
+  return static_cast<size_t>(desc->block == 32 ? mx::mx_scale_buffer_bytes(nb) : mx::scale_buffer_bytes(nb));
 }
 
 size_t mx_wgrad_workspace_bytes(const mx_conv_desc* desc) {
@@ -146,6 +153,7 @@ mx_status mx_quantize_cbf(const mx_conv_desc* desc, mx_role role, const float* s
   if ((st = check_qtensor(dst, nb)) != MX_OK) return st;
   if (nb > 0 && !src) return MX_ERR_NULL;
   if (!aligned(src, 16) || !aligned(dst->scales, 16)) return MX_ERR_ALIGN;
+  if (g.block == 32) return launched(mx::launch_quantize_mx(g, role, src, dst, rounding, seed, stream));
   return launched(mx::launch_quantize(g, role, src, dst, rounding, seed, amax_given, stream));
 }
 
@@ -160,6 +168,7 @@ mx_status mx_dequantize(const mx_conv_desc* desc, mx_role role, const mx_qtensor
   if ((st = check_qtensor(q, nb)) != MX_OK) return st;
   if (nb > 0 && !dst) return MX_ERR_NULL;
   if (!aligned(dst, 16)) return MX_ERR_ALIGN;
+  if (g.block == 32) return launched(mx::launch_dequantize_mx(g, role, q, dst, stream));
   return launched(mx::launch_dequantize(g, role, q, dst, stream));
 }
 
@@ -187,7 +196,7 @@ mx_status mx_im2col_cbf(const mx_conv_desc* desc, const float* x, float* xcol, h
 }
 
 size_t mx_fwd_amax_bytes(const mx_conv_desc* desc) {
-  if (check_gemm_desc(desc, Gemm::Fwd) != MX_OK) return 0;
+  if (check_gemm_desc(desc, Gemm::Fwd) != MX_OK || desc->block != 8) return 0;
   return mx::fwd_amax_bytes(mx::make_geom(desc));
 }
 
@@ -195,6 +204,8 @@ mx_status mx_conv_fwd_amax(const mx_conv_desc* desc, const mx_qtensor* wq, const
                            float* y_amax, hipStream_t stream) {
   mx_status st = check_gemm_desc(desc, Gemm::Fwd);
   if (st != MX_OK) return st;
+  // a tensor amax feeds the two-level format only
+  if (desc->block != 8) return MX_ERR_BLOCK;
   const Geom g = mx::make_geom(desc);
   if ((st = check_qtensor(wq, mx::role_nblocks(g, MX_ROLE_WEIGHT))) != MX_OK) return st;
   if ((st = check_qtensor(xq, mx::role_nblocks(g, MX_ROLE_ACT))) != MX_OK) return st;
@@ -237,7 +248,7 @@ const char* mx_status_str(mx_status s) {
     case MX_ERR_NULL: return "null pointer argument";
     case MX_ERR_SHAPE: return "invalid shape (dimensions, stride, padding, or C_in/C_out/N not multiples of 8)";
     case MX_ERR_FORMAT: return "unknown element format, or a format this call does not take";
-    case MX_ERR_BLOCK: return "block size must be 8";
+    case MX_ERR_BLOCK: return "block size must be 8 or 32 (and 8 for the producer-fused amax)";
     case MX_ERR_ALIGN: return "misaligned pointer";
     case MX_ERR_WORKSPACE: return "workspace missing or smaller than mx_wgrad_workspace_bytes()";
     case MX_ERR_ROLE: return "unknown tensor role";

@@ -718,6 +718,19 @@ WgradPlan wgrad_plan(const Geom& g) {
   return {t, static_cast<int>(splits)};
 }
 
+// Weight gradient on E8M0 32x32 blocks: 256x256 tiles, K steps of 64; about
+// one round of workgroups (1024 waves) with at least 4 K steps per split.
+WgradPlan wgrad_plan_mx(const Geom& g) {
+  const int64_t ksteps = (static_cast<int64_t>(g.ho) * g.wo * (g.n / 32) + 1) / 2;
+  const int64_t ncol = static_cast<int64_t>(g.k_h) * g.k_w * g.c_in;
+  const int64_t tiles = ((g.c_out + 255) / 256) * ((ncol + 255) / 256);
+  int64_t splits = (1024 / 4) / tiles;
+  if (splits > ksteps / 4) splits = ksteps / 4;
+  if (splits < 1) splits = 1;
+  if (splits > 65535) splits = 65535;
+  return {Tile{256, 256, 2, 4, 4}, static_cast<int>(splits)};
+}
+
 // Forward launch geometry: tile, grid and waves per workgroup.
 struct FwdPlan {
   Tile t;
@@ -753,6 +766,10 @@ hipError_t launch_conv_fwd(const Geom& g, const mx_qtensor* wq, const mx_qtensor
   p.out = y;
   p.amax_out = reinterpret_cast<uint32_t*>(y_amax);
   int64_t nslots = 0;
+  if (g.block == 32) {
+    if (p.ncb > 0) launch_mx(OP_FWD, p, dim3((p.ncb * 8 + 255) / 256, (p.M + 255) / 256, 1), s);
+    return hipGetLastError();
+  }
   if (p.ncb > 0) {
     const FwdPlan pl = fwd_plan(g, p);
     nslots = static_cast<int64_t>(pl.grid.x) * pl.grid.y * pl.grid.z * pl.t.waves;
@@ -774,6 +791,10 @@ hipError_t launch_conv_dgrad(const Geom& g, const mx_qtensor* wq, const mx_qtens
   p.b_codes = static_cast<const uint8_t*>(dyq->codes); p.b_scales = dyq->scales; p.b_t = dyq->tensor_scale;
   p.out = dx;
   if (p.ncb == 0) return hipSuccess;
+  if (g.block == 32) {
+    launch_mx(OP_DGRAD, p, dim3((p.ncb * 8 + 255) / 256, (p.M + 255) / 256, g.sh * g.sw), s);
+    return hipGetLastError();
+  }
   const Tile t = pick_tile(p.M, static_cast<int64_t>(p.ncb) * 8, g.sh * g.sw, g.fmt);
   dim3 grid((p.ncb * 8 + t.nt - 1) / t.nt, (p.M + t.mt - 1) / t.mt, g.sh * g.sw);
   if (!launch_op<OP_DGRAD>(p, g.fmt, g.fmt, t, grid, s)) return hipErrorNotSupported;
@@ -781,25 +802,28 @@ hipError_t launch_conv_dgrad(const Geom& g, const mx_qtensor* wq, const mx_qtens
 }
 
 size_t wgrad_workspace_bytes(const Geom& g) {
-  const WgradPlan pl = wgrad_plan(g);
+  const WgradPlan pl = g.block == 32 ? wgrad_plan_mx(g) : wgrad_plan(g);
   return static_cast<size_t>(pl.splits) * g.c_out * g.k_h * g.k_w * g.c_in * sizeof(float);
 }
 
 hipError_t launch_conv_wgrad(const Geom& g, const mx_qtensor* dyq, const mx_qtensor* xq, float* dw,
                              void* workspace, hipStream_t s) {
   ConvParams p = base_params(g);
-  const WgradPlan pl = wgrad_plan(g);
+  const bool mxb = g.block == 32;
+  const WgradPlan pl = mxb ? wgrad_plan_mx(g) : wgrad_plan(g);
   p.M = g.c_out;
   p.ncol = g.k_h * g.k_w * g.c_in;
   p.ncb = p.ncol / 8;
   p.kb_total = g.ho * g.wo * (g.n / 8);
-  const int ksteps = (p.kb_total + pl.t.kb - 1) / pl.t.kb;
+  // K steps: of the tile's KB 8-blocks, or of two 32-blocks
+  const int ksteps = mxb ? (g.ho * g.wo * (g.n / 32) + 1) / 2 : (p.kb_total + pl.t.kb - 1) / pl.t.kb;
   p.ks_split = (ksteps + pl.splits - 1) / pl.splits;
   p.a_codes = static_cast<const uint8_t*>(dyq->codes); p.a_scales = dyq->scales; p.a_t = dyq->tensor_scale;
   p.b_codes = static_cast<const uint8_t*>(xq->codes); p.b_scales = xq->scales; p.b_t = xq->tensor_scale;
   p.out = static_cast<float*>(workspace);
   dim3 grid((p.ncol + pl.t.nt - 1) / pl.t.nt, (p.M + pl.t.mt - 1) / pl.t.mt, pl.splits);
-  if (!launch_op<OP_WGRAD>(p, g.fmt, g.afmt, pl.t, grid, s)) return hipErrorNotSupported;
+  if (mxb) launch_mx(OP_WGRAD, p, grid, s);
+  else if (!launch_op<OP_WGRAD>(p, g.fmt, g.afmt, pl.t, grid, s)) return hipErrorNotSupported;
   // ncol = Kh*Kw*C_in is a multiple of 8: whole quads of outputs
   const int64_t quads = static_cast<int64_t>(p.M) * p.ncol / 4;
   int gsplit = 1;  // split groups: at least 2^18 threads where the splits allow

@@ -71,6 +71,11 @@ struct Tile {
 // and weight-gradient GEMMs.  Returns false for a pair it does not take.
 bool launch_mixed(int op, const ConvParams& p, int fmt_a, int fmt_b, const Tile& t, dim3 grid, hipStream_t s);
 
+// Launches the E8M0 32x32-block GEMM on the scaled FP4 MFMA (defined in
+// conv_mx.hip): 256x256 tiles, the grid as for the generic kernel; for the
+// weight gradient p.ks_split counts its 64-wide K steps per split.
+void launch_mx(int op, const ConvParams& p, dim3 grid, hipStream_t s);
+
 }  // namespace gemm
 
 // The kernels have internal linkage: every translation unit that includes

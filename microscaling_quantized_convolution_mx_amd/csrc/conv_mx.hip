@@ -1,0 +1,277 @@
+// Convolution GEMMs on the original microscaling format (E8M0 scale per
+// 32x32 square block, E2M1 elements, no tensor scale) with gfx950's scaled
+// FP4 MFMA (MicroQonv, arXiv 2609.28358, §II-D, §IV-B).
+//
+// v_mfma_scale_f32_32x32x64_f8f6f4 takes, per lane, 32 consecutive K values
+// of one row (A) or column (B) and one E8M0 scale for them: lane l holds
+// row / column l%32 and K half l/32.  A 32x32 square block is therefore
+// exactly one half-wave operand with one scale, whichever of its two
+// directions K runs along, so every operand is read straight from the
+// quantized blocks: no decode, no im2col, and the same blocks serve the
+// forward, data-gradient and weight-gradient GEMMs.
+//
+// Blocks are stored as 32 rows of 16 bytes (channel rows for activations
+// and gradients, output-channel rows for weights).  Where K runs along a
+// block's rows (wgrad's A and B, fwd's A) a lane reads its 16 bytes
+// directly; where K runs down the columns (fwd's B, dgrad's A and B) two
+// transposing LDS reads (ds_read_b64_tr_b4: 16x16 nibble transpose within
+// each group of 16 lanes) gather the 32 nibbles of a column.
+//
+// Tile 256x256, 4 waves of 128x128 (4x4 MFMAs of 32x32), one K step = 64
+// K values = two 32-blocks per row/column block.  Every thread copies four
+// 16-byte block rows per step from global memory into one of three LDS
+// stages (the blocks unchanged).  The rows are fetched into registers two
+// steps before they are written to LDS, so an L2 or HBM load has two steps
+// of MFMAs to arrive.  Tile placement, the stride phases of dgrad and the
+// epilogue are those of the generic kernel.
+#include "conv_kernels.h"
+
+namespace mx {
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x2v __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2v lds_i32x2v;
+
+constexpr int kMxB = 512;        // bytes of one 32x32 E2M1 block
+constexpr int kOpnd = 16 * kMxB; // one operand of a stage: 8 line blocks x 2 k-blocks
+constexpr int kStage = 2 * kOpnd + 64;  // codes of A and B, then scales [A: 2x8][B: 2x8] (+pad)
+
+template <int OP>
+__global__ __launch_bounds__(256) void k_conv_mx(const ConvParams p) {
+  constexpr int MT = 256, NT = 256, WM = 2;
+  constexpr int WTM = 128, WTN = 128, RM = 4, RN = 4;
+  // K runs along the stored rows of A for fwd and wgrad, of B for wgrad
+  constexpr bool A_DIRECT = (OP != OP_DGRAD);
+  constexpr bool B_DIRECT = (OP == OP_WGRAD);
+  __shared__ __attribute__((aligned(16))) uint8_t lds[3 * kStage];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % WM, wn = wave / WM;
+  TileCtx<OP, MT, NT, 4> t;  // placement, dgrad phase and epilogue geometry (8-column units)
+  if (!t.init(p, tid)) return;
+
+  // 32-block counts
+  const int cbi = p.c_in >> 5, cbo = p.c_out >> 5, nbk = p.n >> 5;
+  const int rb0 = (t.rb0 * 8) >> 5;               // first row block of the tile
+  const int cb0 = (t.cb0 * 8) >> 5;               // first column block
+  const int nrb = p.M >> 5;                       // row blocks of the GEMM
+  const int ncb = (t.ncb_launch * 8) >> 5;        // column blocks of the launch
+  // K extent in 32-blocks and this launch's range of K steps (2 blocks each)
+  int k_total;
+  if constexpr (OP == OP_FWD) k_total = p.k_h * p.k_w * cbi;
+  else if constexpr (OP == OP_DGRAD) k_total = t.nkh * t.nkw * cbo;
+  else k_total = p.ho * p.wo * nbk;
+  const int nsteps_all = (k_total + 1) >> 1;
+  int s_begin = 0, s_end = nsteps_all;
+  if constexpr (OP == OP_WGRAD) {
+    s_begin = t.bz * p.ks_split;
+    s_end = min(nsteps_all, s_begin + p.ks_split);
+    if (s_begin > s_end) s_begin = s_end;
+  }
+  // k-blocks past this launch's range read as zeros
+  const int k_end = min(k_total, 2 * s_end);
+
+  // Staging: thread t copies row (t & 31) of block (operand, line block lb,
+  // k half kk) for lb in {lb_lo, lb_lo + 4}, kk = (t >> 5) & 1.
+  const int row = tid & 31, kk = (tid >> 5) & 1, lb_lo = tid >> 6;
+  // the four block rows this thread copies: A lb_lo, A lb_lo+4, B lb_lo, B lb_lo+4
+  int gline[4];
+  bool gline_ok[4];
+  // column-block geometry of B (fixed over the K loop)
+  int col_y[2] = {0, 0}, col_x[2] = {0, 0}, col_nb[2] = {0, 0}, col_cib[2] = {0, 0};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int lb = lb_lo + (q & 1) * 4;
+    if (q < 2) {
+      gline[q] = rb0 + lb;
+      gline_ok[q] = gline[q] < nrb;
+    } else {
+      const int cb = cb0 + lb;
+      gline[q] = cb;
+      gline_ok[q] = cb < ncb;
+      const int i = q - 2;
+      if constexpr (OP == OP_FWD) {
+        const int pos = cb / nbk;
+        col_nb[i] = cb - pos * nbk;
+        const int ho = pos / p.wo;
+        col_y[i] = ho * p.sh - p.ph;
+        col_x[i] = (pos - ho * p.wo) * p.sw - p.pw;
+      } else if constexpr (OP == OP_DGRAD) {
+        const int pos = cb / nbk;
+        col_nb[i] = cb - pos * nbk;
+        const int hq = pos / t.wp;
+        const int h = t.phh + p.sh * hq, w = t.phw + p.sw * (pos - hq * t.wp);
+        // dY row of tap kh = kh0 + sh*a is (h + ph - kh0)/sh - a (exact)
+        col_y[i] = (h + p.ph - t.kh0) / p.sh;
+        col_x[i] = (w + p.pw - t.kw0) / p.sw;
+      } else {
+        const int tap = cb / cbi;
+        col_cib[i] = cb - tap * cbi;
+        const int kh = tap / p.k_w;
+        col_y[i] = kh - p.ph;
+        col_x[i] = (tap - kh * p.k_w) - p.pw;
+      }
+    }
+  }
+  FastDiv div_in, div_b;
+  if constexpr (OP == OP_FWD) { div_in.init(cbi); div_b.init(p.k_w); }
+  else if constexpr (OP == OP_DGRAD) { div_in.init(cbo); div_b.init(t.nkw > 0 ? t.nkw : 1); }
+  else { div_in.init(nbk); div_b.init(p.wo); }
+
+  // global block index of block row q at k-block k (and whether it exists)
+  auto locate = [&](int q, int k, uint32_t& blk) -> bool {
+    const uint32_t outer = div_in.div(static_cast<uint32_t>(k));
+    const uint32_t inner = static_cast<uint32_t>(k) - outer * div_in.d;
+    const uint32_t a = div_b.div(outer);
+    const uint32_t b = outer - a * div_b.d;
+    const bool kin = k < k_end;
+    if (q < 2) {
+      const uint32_t rb = static_cast<uint32_t>(gline[q]);
+      if constexpr (OP == OP_FWD) blk = ((a * p.k_w + b) * cbo + rb) * cbi + inner;                 // W[tap][co][ci]
+      else if constexpr (OP == OP_DGRAD)
+        blk = (((t.kh0 + p.sh * a) * p.k_w + (t.kw0 + p.sw * b)) * cbo + inner) * cbi + rb;         // W[tap][co][ci]
+      else blk = ((a * p.wo + b) * cbo + rb) * nbk + inner;                                            // dY[pos][co][n]
+      return gline_ok[q] && kin;
+    }
+    const int i = q - 2;
+    int y, x;
+    bool inb;
+    if constexpr (OP == OP_FWD) {
+      y = col_y[i] + static_cast<int>(a);
+      x = col_x[i] + static_cast<int>(b);
+      inb = static_cast<uint32_t>(y) < static_cast<uint32_t>(p.h) && static_cast<uint32_t>(x) < static_cast<uint32_t>(p.w);
+      blk = ((static_cast<uint32_t>(y) * p.w + x) * cbi + inner) * nbk + col_nb[i];                // X[pos][ci][n]
+    } else if constexpr (OP == OP_DGRAD) {
+      y = col_y[i] - static_cast<int>(a);
+      x = col_x[i] - static_cast<int>(b);
+      inb = static_cast<uint32_t>(y) < static_cast<uint32_t>(p.ho) && static_cast<uint32_t>(x) < static_cast<uint32_t>(p.wo);
+      blk = ((static_cast<uint32_t>(y) * p.wo + x) * cbo + inner) * nbk + col_nb[i];               // dY[pos][co][n]
+    } else {
+      y = col_y[i] + static_cast<int>(a) * p.sh;
+      x = col_x[i] + static_cast<int>(b) * p.sw;
+      inb = static_cast<uint32_t>(y) < static_cast<uint32_t>(p.h) && static_cast<uint32_t>(x) < static_cast<uint32_t>(p.w);
+      blk = ((static_cast<uint32_t>(y) * p.w + x) * cbi + col_cib[i]) * nbk + inner;               // X[pos][ci][n]
+    }
+    return gline_ok[q] && kin && inb;
+  };
+
+  // one step's block rows in registers: codes, and the scale (thread row 0)
+  struct Raw {
+    uint4 v[4];
+    uint32_t sc[4];
+  };
+  Raw r0, r1;
+  auto fetch = [&](Raw& raw, int step) {
+    const int k = 2 * step + kk;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t blk = 0;
+      const bool ok = locate(q, k, blk);
+      const uint8_t* codes = q < 2 ? p.a_codes : p.b_codes;
+      const uint8_t* scales = q < 2 ? p.a_scales : p.b_scales;
+      const uint64_t b = ok ? blk : 0u;
+      const uint4 v = *reinterpret_cast<const uint4*>(codes + b * kMxB + row * 16);
+      const uint32_t sc = scales[b];
+      // a block outside the operand is zeros with scale 2^0
+      raw.v[q] = ok ? v : make_uint4(0u, 0u, 0u, 0u);
+      raw.sc[q] = ok ? sc : 127u;
+    }
+  };
+  auto stage_write = [&](const Raw& raw, uint8_t* st) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int lb = lb_lo + (q & 1) * 4;
+      *reinterpret_cast<uint4*>(st + (q < 2 ? 0 : kOpnd) + (lb * 2 + kk) * kMxB + row * 16) = raw.v[q];
+      // scales [kk][lb]: the 4 line blocks of a wave half in one word
+      if (row == 0) st[2 * kOpnd + (q < 2 ? 0 : 16) + kk * 8 + lb] = static_cast<uint8_t>(raw.sc[q]);
+    }
+  };
+
+  f32x16 acc[RM][RN];
+#pragma unroll
+  for (int i = 0; i < RM; ++i)
+#pragma unroll
+    for (int j = 0; j < RN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  const int l32 = lane & 31, half = lane >> 5;
+  // operand of line block lb for this lane: direct = its row l32 of block
+  // (lb, half); transposed = column l32 of that block, gathered 16 rows at a
+  // time (lane group g = lane/16 covers columns 16*(g%2) .. +15)
+  const int direct_off = half * kMxB + l32 * 16;
+  const int trans_off = half * kMxB + (lane & 15) * 16 + ((lane >> 4) & 1) * 8;
+  auto read_opnd = [&](const uint8_t* base, int lb, bool direct) -> i32x8 {
+    const uint8_t* blk = base + lb * 2 * kMxB;
+    if (direct) {
+      const uint4 v = *reinterpret_cast<const uint4*>(blk + direct_off);
+      return i32x8{static_cast<int>(v.x), static_cast<int>(v.y), static_cast<int>(v.z), static_cast<int>(v.w), 0, 0, 0, 0};
+    }
+    const i32x2v r0 = __builtin_amdgcn_ds_read_tr4_b64_v2i32((lds_i32x2v*)(blk + trans_off));
+    const i32x2v r1 = __builtin_amdgcn_ds_read_tr4_b64_v2i32((lds_i32x2v*)(blk + trans_off + 16 * 16));
+    return i32x8{r0.x, r0.y, r1.x, r1.y, 0, 0, 0, 0};
+  };
+
+  // step s: MFMAs on stage s%3; write the rows of step s+1 (fetched two
+  // steps earlier) into stage (s+1)%3, free since step s-2; fetch step s+3.
+  // Steps run in pairs with no exit in between (an exit there makes the
+  // compiler spill the accumulators); fetches past the last step give zero
+  // rows, so the extra step of an odd count adds nothing.
+  const int nsteps = s_end - s_begin;
+  auto step = [&](int s, uint8_t* cur, uint8_t* nxt, Raw& raw_next) {
+    {
+      const int sa = *reinterpret_cast<const int*>(cur + 2 * kOpnd + half * 8 + wm * 4);
+      const int sb = *reinterpret_cast<const int*>(cur + 2 * kOpnd + 16 + half * 8 + wn * 4);
+      i32x8 fa[RM], fb[RN];
+#pragma unroll
+      for (int i = 0; i < RM; ++i) fa[i] = read_opnd(cur, wm * 4 + i, A_DIRECT);
+#pragma unroll
+      for (int j = 0; j < RN; ++j) fb[j] = read_opnd(cur + kOpnd, wn * 4 + j, B_DIRECT);
+#define MX_MFMA(I, J) \
+  acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[I], fb[J], acc[I][J], 4, 4, I, sa, J, sb)
+      MX_MFMA(0, 0); MX_MFMA(0, 1); MX_MFMA(0, 2); MX_MFMA(0, 3);
+      MX_MFMA(1, 0); MX_MFMA(1, 1); MX_MFMA(1, 2); MX_MFMA(1, 3);
+      MX_MFMA(2, 0); MX_MFMA(2, 1); MX_MFMA(2, 2); MX_MFMA(2, 3);
+      MX_MFMA(3, 0); MX_MFMA(3, 1); MX_MFMA(3, 2); MX_MFMA(3, 3);
+#undef MX_MFMA
+    }
+    stage_write(raw_next, nxt);
+    fetch(raw_next, s_begin + s + 3);
+    __syncthreads();
+  };
+  if (nsteps > 0) {
+    fetch(r0, s_begin);
+    fetch(r1, s_begin + 1);
+    stage_write(r0, lds);
+    fetch(r0, s_begin + 2);
+    __syncthreads();
+    int c = 0;  // stage of step s
+    for (int s = 0; s < nsteps; s += 2) {
+      const int c1 = c == 2 ? 0 : c + 1, c2 = c1 == 2 ? 0 : c1 + 1;
+      // step s: rows of s+1 in r1; step s+1: rows of s+2 in r0
+      step(s, lds + c * kStage, lds + c1 * kStage, r1);
+      step(s + 1, lds + c1 * kStage, lds + c2 * kStage, r0);
+      c = c2;
+    }
+  }
+
+  store_tile<OP, MT, NT, 4, WTM, WTN, RM, RN>(p, t, acc, lane, wm, wn);
+}
+
+}  // namespace
+
+namespace gemm {
+
+void launch_mx(int op, const ConvParams& p, dim3 grid, hipStream_t s) {
+  switch (op) {
+    case OP_FWD: hipLaunchKernelGGL(k_conv_mx<OP_FWD>, grid, dim3(256), 0, s, p); break;
+    case OP_DGRAD: hipLaunchKernelGGL(k_conv_mx<OP_DGRAD>, grid, dim3(256), 0, s, p); break;
+    default: hipLaunchKernelGGL(k_conv_mx<OP_WGRAD>, grid, dim3(256), 0, s, p); break;
+  }
+}
+
+}  // namespace gemm
+}  // namespace mx

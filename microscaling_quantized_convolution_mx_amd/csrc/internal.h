@@ -12,8 +12,9 @@ namespace mx {
 // Geometry shared by all launchers, derived from an mx_conv_desc.
 // fmt: element format of weights and output gradients; afmt: that of the
 // activation (the descriptor's act_fmt, or fmt where that is 0).
+// block: 8 (the two-level E4M3 x fp32 format) or 32 (E8M0 per 32x32 block).
 struct Geom {
-  int32_t n, c_in, c_out, h, w, k_h, k_w, sh, sw, ph, pw, ho, wo, fmt, afmt;
+  int32_t n, c_in, c_out, h, w, k_h, k_w, sh, sw, ph, pw, ho, wo, fmt, afmt, block;
 };
 inline int role_fmt(const Geom& g, mx_role role) { return role == MX_ROLE_ACT ? g.afmt : g.fmt; }
 
@@ -37,11 +38,17 @@ inline int64_t amax_partials(int64_t nblocks) {
 inline int64_t scale_buffer_bytes(int64_t nblocks) {
   return nblocks > 0 ? scale_tail_offset(nblocks) + 4 * kAmaxMaxPartials : 0;
 }
+// E8M0 32x32 blocks: the scales alone (no amax pass, no scratch tail).
+inline int64_t mx_scale_buffer_bytes(int64_t nblocks) { return nblocks > 0 ? scale_tail_offset(nblocks) : 0; }
 
 hipError_t launch_quantize(const Geom& g, mx_role role, const float* src, const mx_qtensor* dst,
                            mx_round rounding, uint64_t seed, int amax_given, hipStream_t s);
 hipError_t launch_dequantize(const Geom& g, mx_role role, const mx_qtensor* q, float* dst,
                              hipStream_t s);
+// The E8M0 32x32-block format (quantize_mx.hip).
+hipError_t launch_quantize_mx(const Geom& g, mx_role role, const float* src, const mx_qtensor* dst,
+                              mx_round rounding, uint64_t seed, hipStream_t s);
+hipError_t launch_dequantize_mx(const Geom& g, mx_role role, const mx_qtensor* q, float* dst, hipStream_t s);
 hipError_t launch_im2col(const Geom& g, const float* x, float* xcol, hipStream_t s);
 
 // y_amax: nullptr, or a device buffer of fwd_amax_bytes(g) bytes whose first

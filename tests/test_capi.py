@@ -75,7 +75,7 @@ GOOD = dict(n=8, c_in=16, c_out=16, h=8, w=8, k_h=3, k_w=3)
 
 
 @pytest.mark.parametrize("change,status", [
-    (dict(block=4), -4), (dict(block=16), -4),
+    (dict(block=4), -4), (dict(block=16), -4), (dict(block=32), -2),
     (dict(elem_fmt=0), -3), (dict(elem_fmt=6), -3), (dict(act_fmt=6), -3), (dict(act_fmt=-1), -3),
     (dict(c_in=12), -2), (dict(c_out=20), -2), (dict(n=12), -2), (dict(n=-8), -2),
     (dict(stride_h=0), -2), (dict(stride_w=-1), -2), (dict(pad_h=-1), -2),
@@ -208,3 +208,31 @@ def test_activation_format_pairs():
     assert quant(d, role=mx.MX_ROLE_WEIGHT, dst=q(codes=MIS)) == -5   # W stays E2M1
     assert L.mx_conv_fwd(ctypes.byref(d), ctypes.byref(good), ctypes.byref(good), A16, None) == -3
     assert L.mx_conv_dgrad(ctypes.byref(d), ctypes.byref(good), ctypes.byref(good), MIS, None) == -5
+
+
+def test_e8m0_block32_format():
+    # E8M0 scale per 32x32 block: C_in, C_out and N multiples of 32, E2M1
+    # elements throughout, one scale byte per block and no quantizer scratch
+    L = mx.lib()
+    good = q()
+    d = mx.desc(64, 32, 96, 9, 7, 3, 3, 2, 2, 1, 1, block=32)
+    assert mx.mx_code_bytes(d, mx.MX_ROLE_ACT) == 9 * 7 * 32 * 64 // 2
+    assert mx.mx_code_bytes(d, mx.MX_ROLE_WEIGHT) == 96 * 32 * 9 // 2
+    pad16 = lambda v: (v + 15) // 16 * 16
+    assert mx.mx_scale_bytes(d, mx.MX_ROLE_ACT) == pad16(9 * 7 * 1 * 2)
+    assert mx.mx_scale_bytes(d, mx.MX_ROLE_GRAD) == pad16(5 * 4 * 3 * 2)
+    assert mx.mx_scale_bytes(d, mx.MX_ROLE_WEIGHT) == pad16(9 * 3 * 1)
+    ws = mx.mx_wgrad_workspace_bytes(d)
+    assert ws > 0 and ws % (96 * 9 * 32 * 4) == 0
+    # the producer-fused amax feeds the two-level format only
+    assert mx.mx_fwd_amax_bytes(d) == 0
+    assert L.mx_conv_fwd_amax(ctypes.byref(d), ctypes.byref(good), ctypes.byref(good), A16, A16, None) == -4
+    assert L.mx_conv_fwd(ctypes.byref(d), ctypes.byref(good), ctypes.byref(good), MIS, None) == -5
+    for bad, status in ((dict(n=48), -2), (dict(c_in=16), -2), (dict(c_out=40), -2),
+                        (dict(elem_fmt=mx.MX_E2M3), -3), (dict(act_fmt=mx.MX_E3M2), -3),
+                        (dict(elem_fmt=mx.MX_E4M3), -3)):
+        kw = dict(n=64, c_in=32, c_out=96, h=9, w=7, k_h=3, k_w=3, block=32)
+        kw.update(bad)
+        bd = mx.desc(kw.pop("n"), kw.pop("c_in"), kw.pop("c_out"), kw.pop("h"), kw.pop("w"), kw.pop("k_h"),
+                     kw.pop("k_w"), **kw)
+        assert quant(bd) == status, bad
