@@ -158,35 +158,41 @@ __global__ __launch_bounds__(256) void k_conv_mx(const ConvParams p) {
     return gline_ok[q] && kin && inb;
   };
 
-  // one step's block rows in registers: codes, and the scale (thread row 0)
+  // one step's block rows in registers: codes, scale (used by row 0) and
+  // whether the block exists.  The mask is applied when the rows are
+  // written to LDS, so that nothing waits for a load before then.
   struct Raw {
     uint4 v[4];
     uint32_t sc[4];
+    uint32_t mask[4];
   };
   Raw r0, r1;
-  auto fetch = [&](Raw& raw, int step) {
+  auto fetch_one = [&](Raw& raw, int step, int q) {
     const int k = 2 * step + kk;
+    uint32_t blk = 0;
+    const bool ok = locate(q, k, blk);
+    const uint8_t* codes = q < 2 ? p.a_codes : p.b_codes;
+    const uint8_t* scales = q < 2 ? p.a_scales : p.b_scales;
+    const uint64_t b = ok ? blk : 0u;
+    raw.v[q] = *reinterpret_cast<const uint4*>(codes + b * kMxB + row * 16);
+    raw.sc[q] = scales[b];
+    raw.mask[q] = ok ? ~0u : 0u;
+  };
+  auto fetch = [&](Raw& raw, int step) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint32_t blk = 0;
-      const bool ok = locate(q, k, blk);
-      const uint8_t* codes = q < 2 ? p.a_codes : p.b_codes;
-      const uint8_t* scales = q < 2 ? p.a_scales : p.b_scales;
-      const uint64_t b = ok ? blk : 0u;
-      const uint4 v = *reinterpret_cast<const uint4*>(codes + b * kMxB + row * 16);
-      const uint32_t sc = scales[b];
-      // a block outside the operand is zeros with scale 2^0
-      raw.v[q] = ok ? v : make_uint4(0u, 0u, 0u, 0u);
-      raw.sc[q] = ok ? sc : 127u;
-    }
+    for (int q = 0; q < 4; ++q) fetch_one(raw, step, q);
   };
   auto stage_write = [&](const Raw& raw, uint8_t* st) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int lb = lb_lo + (q & 1) * 4;
-      *reinterpret_cast<uint4*>(st + (q < 2 ? 0 : kOpnd) + (lb * 2 + kk) * kMxB + row * 16) = raw.v[q];
+      const uint32_t m = raw.mask[q];
+      // a block outside the operand is zeros with scale 2^0
+      *reinterpret_cast<uint4*>(st + (q < 2 ? 0 : kOpnd) + (lb * 2 + kk) * kMxB + row * 16) =
+          make_uint4(raw.v[q].x & m, raw.v[q].y & m, raw.v[q].z & m, raw.v[q].w & m);
       // scales [kk][lb]: the 4 line blocks of a wave half in one word
-      if (row == 0) st[2 * kOpnd + (q < 2 ? 0 : 16) + kk * 8 + lb] = static_cast<uint8_t>(raw.sc[q]);
+      if (row == 0)
+        st[2 * kOpnd + (q < 2 ? 0 : 16) + kk * 8 + lb] = static_cast<uint8_t>((raw.sc[q] & m) | (127u & ~m));
     }
   };
 
@@ -214,46 +220,70 @@ __global__ __launch_bounds__(256) void k_conv_mx(const ConvParams p) {
     const i32x2v r1 = __builtin_amdgcn_ds_read_tr4_b64_v2i32((lds_i32x2v*)(blk + trans_off + 16 * 16));
     return i32x8{r0.x, r0.y, r1.x, r1.y, 0, 0, 0, 0};
   };
+  // the MFMA operands of one step: fragments and scale words
+  struct Frags {
+    i32x8 a[RM], b[RN];
+    int sa, sb;
+  };
+  Frags f0, f1;
+  auto read_frags = [&](const uint8_t* st, Frags& f) {
+    // scale words: bytes (the wave half's line blocks 0..3) for this lane's k half
+    f.sa = *reinterpret_cast<const int*>(st + 2 * kOpnd + half * 8 + wm * 4);
+    f.sb = *reinterpret_cast<const int*>(st + 2 * kOpnd + 16 + half * 8 + wn * 4);
+#pragma unroll
+    for (int i = 0; i < RM; ++i) f.a[i] = read_opnd(st, wm * 4 + i, A_DIRECT);
+#pragma unroll
+    for (int j = 0; j < RN; ++j) f.b[j] = read_opnd(st + kOpnd, wn * 4 + j, B_DIRECT);
+  };
 
-  // step s: MFMAs on stage s%3; write the rows of step s+1 (fetched two
-  // steps earlier) into stage (s+1)%3, free since step s-2; fetch step s+3.
-  // Steps run in pairs with no exit in between (an exit there makes the
-  // compiler spill the accumulators); fetches past the last step give zero
-  // rows, so the extra step of an odd count adds nothing.
+  // Step s, on stage s%3 whose operands were read into registers during
+  // step s-1:
+  //   write the rows of step s+2 (fetched two steps earlier) into stage
+  //   (s+2)%3, last read during step s-1;
+  //   read the operands of step s+1 from stage (s+1)%3, complete since the
+  //   barrier of step s-1;
+  //   16 MFMAs, with the global fetches of step s+4 between them;
+  //   barrier.
+  // Steps run in pairs so that the two register sets alternate statically,
+  // with no exit in between (an exit there makes the compiler spill the
+  // accumulators); fetches at or past the last step give zero rows, so the
+  // extra step of an odd count adds nothing.
   const int nsteps = s_end - s_begin;
-  auto step = [&](int s, uint8_t* cur, uint8_t* nxt, Raw& raw_next) {
-    {
-      const int sa = *reinterpret_cast<const int*>(cur + 2 * kOpnd + half * 8 + wm * 4);
-      const int sb = *reinterpret_cast<const int*>(cur + 2 * kOpnd + 16 + half * 8 + wn * 4);
-      i32x8 fa[RM], fb[RN];
-#pragma unroll
-      for (int i = 0; i < RM; ++i) fa[i] = read_opnd(cur, wm * 4 + i, A_DIRECT);
-#pragma unroll
-      for (int j = 0; j < RN; ++j) fb[j] = read_opnd(cur + kOpnd, wn * 4 + j, B_DIRECT);
-#define MX_MFMA(I, J) \
-  acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[I], fb[J], acc[I][J], 4, 4, I, sa, J, sb)
-      MX_MFMA(0, 0); MX_MFMA(0, 1); MX_MFMA(0, 2); MX_MFMA(0, 3);
-      MX_MFMA(1, 0); MX_MFMA(1, 1); MX_MFMA(1, 2); MX_MFMA(1, 3);
-      MX_MFMA(2, 0); MX_MFMA(2, 1); MX_MFMA(2, 2); MX_MFMA(2, 3);
-      MX_MFMA(3, 0); MX_MFMA(3, 1); MX_MFMA(3, 2); MX_MFMA(3, 3);
+  auto step = [&](int s, const Frags& fc, Frags& fn, uint8_t* next_st, uint8_t* write_st, Raw& raw) {
+    stage_write(raw, write_st);
+    read_frags(next_st, fn);
+    __builtin_amdgcn_sched_barrier(0);
+#define MX_MFMA(I, J)                                                                                          \
+  acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fc.a[I], fc.b[J], acc[I][J], 4, 4, I, fc.sa, J, \
+                                                              fc.sb);                                        \
+  __builtin_amdgcn_sched_barrier(0)
+    MX_MFMA(0, 0); fetch_one(raw, s_begin + s + 4, 0); __builtin_amdgcn_sched_barrier(0);
+    MX_MFMA(0, 1); MX_MFMA(0, 2); MX_MFMA(0, 3);
+    MX_MFMA(1, 0); fetch_one(raw, s_begin + s + 4, 1); __builtin_amdgcn_sched_barrier(0);
+    MX_MFMA(1, 1); MX_MFMA(1, 2); MX_MFMA(1, 3);
+    MX_MFMA(2, 0); fetch_one(raw, s_begin + s + 4, 2); __builtin_amdgcn_sched_barrier(0);
+    MX_MFMA(2, 1); MX_MFMA(2, 2); MX_MFMA(2, 3);
+    MX_MFMA(3, 0); fetch_one(raw, s_begin + s + 4, 3); __builtin_amdgcn_sched_barrier(0);
+    MX_MFMA(3, 1); MX_MFMA(3, 2); MX_MFMA(3, 3);
 #undef MX_MFMA
-    }
-    stage_write(raw_next, nxt);
-    fetch(raw_next, s_begin + s + 3);
     __syncthreads();
   };
   if (nsteps > 0) {
     fetch(r0, s_begin);
     fetch(r1, s_begin + 1);
     stage_write(r0, lds);
+    stage_write(r1, lds + kStage);
     fetch(r0, s_begin + 2);
+    fetch(r1, s_begin + 3);
     __syncthreads();
+    read_frags(lds, f0);
     int c = 0;  // stage of step s
     for (int s = 0; s < nsteps; s += 2) {
       const int c1 = c == 2 ? 0 : c + 1, c2 = c1 == 2 ? 0 : c1 + 1;
-      // step s: rows of s+1 in r1; step s+1: rows of s+2 in r0
-      step(s, lds + c * kStage, lds + c1 * kStage, r1);
-      step(s + 1, lds + c1 * kStage, lds + c2 * kStage, r0);
+      // step s: operands in f0, reads step s+1 into f1, writes rows s+2 (r0)
+      step(s, f0, f1, lds + c1 * kStage, lds + c2 * kStage, r0);
+      // step s+1: operands in f1, reads step s+2 into f0, writes rows s+3 (r1)
+      step(s + 1, f1, f0, lds + c2 * kStage, lds + c * kStage, r1);
       c = c2;
     }
   }

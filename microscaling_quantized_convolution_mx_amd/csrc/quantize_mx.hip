@@ -14,9 +14,11 @@
 // codes: a block is 32 rows of 16 bytes, element 2j of a row in the low
 // nibble of byte j; scales: one E8M0 byte per block.
 //
-// One wave per block: lane l handles row l/2, elements 16*(l%2) .. +15.
-// Unlike the two-level format there is no tensor-wide statistic, so the
-// quantizer reads its source once.
+// One wave per block: lane l handles elements 4*(l%8) .. +3 of rows
+// l/8 + 8q, q = 0..3, so that each memory instruction of the wave covers 8
+// whole rows (8 x 128 bytes of fp32, 8 x 16 bytes of codes).  Unlike the
+// two-level format there is no tensor-wide statistic, so the quantizer reads
+// its source once.
 #include "internal.h"
 #include "mx_formats.h"
 
@@ -93,19 +95,20 @@ __global__ __launch_bounds__(kMxWaves * 64) void k_quantize_mx(const float* __re
   const int64_t b = static_cast<int64_t>(blockIdx.x) * kMxWaves + (threadIdx.x >> 6);
   if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = 1.0f;  // no tensor scale
   if (b >= d.nblocks) return;  // whole waves
-  const int r = lane >> 1, c0 = (lane & 1) * 16;
+  const int r0 = lane >> 3, c0 = (lane & 7) * 4;
   int64_t step;
-  const int64_t s0 = mx_src<ROLE>(d, b, r, c0, step);
+  int64_t s0[4];  // source index of element (r0 + 8q, c0)
+#pragma unroll
+  for (int q = 0; q < 4; ++q) s0[q] = mx_src<ROLE>(d, b, r0 + 8 * q, c0, step);
 
-  float x[16];
-  if constexpr (ROLE == MX_ROLE_WEIGHT) {
+  float x[16];  // x[4q + j] = element (r0 + 8q, c0 + j)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) x[j] = src[s0 + j * step];
-  } else {
-    const float4* p = reinterpret_cast<const float4*>(src + s0);
+  for (int q = 0; q < 4; ++q) {
+    if constexpr (ROLE == MX_ROLE_WEIGHT) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float4 v = p[q];
+      for (int j = 0; j < 4; ++j) x[4 * q + j] = src[s0[q] + j * step];
+    } else {
+      const float4 v = *reinterpret_cast<const float4*>(src + s0[q]);
       x[4 * q] = v.x; x[4 * q + 1] = v.y; x[4 * q + 2] = v.z; x[4 * q + 3] = v.w;
     }
   }
@@ -119,47 +122,47 @@ __global__ __launch_bounds__(kMxWaves * 64) void k_quantize_mx(const float* __re
   const float inv = __uint_as_float((254u - min(code, 253u)) << 23);
   const bool nonfinite = code == 0xFFu;
 
-  uint32_t w[2] = {0u, 0u};
+  uint32_t w[4] = {0u, 0u, 0u, 0u};  // 4 codes (16 bits) of each of the lane's rows
   if constexpr (!SR) {
     // the hardware conversion rounds to nearest even and keeps the sign of
     // its input; the magnitude is clamped to the format maximum first
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      float sv[8];
+    for (int q = 0; q < 4; ++q) {
+      float sv[4];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float v = nonfinite ? 0.0f : fminf(fabsf(x[8 * h + j]) * inv, F::MAXV);
-        sv[j] = __builtin_copysignf(v, nonfinite ? 1.0f : x[8 * h + j]);
+      for (int j = 0; j < 4; ++j) {
+        const float v = nonfinite ? 0.0f : fminf(fabsf(x[4 * q + j]) * inv, F::MAXV);
+        sv[j] = __builtin_copysignf(v, nonfinite ? 1.0f : x[4 * q + j]);
       }
       uint32_t t = 0;
       t = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(t, sv[0], sv[1], 1.0f, 0);
       t = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(t, sv[2], sv[3], 1.0f, 1);
-      t = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(t, sv[4], sv[5], 1.0f, 2);
-      t = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(t, sv[6], sv[7], 1.0f, 3);
-      w[h] = t;
+      w[q] = t;
     }
   } else {
     float u[16];
-    if constexpr (ROLE == MX_ROLE_WEIGHT) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) u[j] = sr_uniform(seed, static_cast<uint64_t>(s0 + j * step));
-    } else {
-      // 16 consecutive elements from an even index: 8 draws
-      uint64_t gk = kGolden64 * (static_cast<uint64_t>(s0 >> 1) + 1ull);
+    for (int q = 0; q < 4; ++q) {
+      if constexpr (ROLE == MX_ROLE_WEIGHT) {
 #pragma unroll
-      for (int j = 0; j < 16; j += 2) {
-        sr_uniform_pair(seed, gk, u[j], u[j + 1]);
-        gk += kGolden64;
+        for (int j = 0; j < 4; ++j) u[4 * q + j] = sr_uniform(seed, static_cast<uint64_t>(s0[q] + j * step));
+      } else {
+        // 4 consecutive elements from an even index: 2 draws
+        const uint64_t gk = kGolden64 * (static_cast<uint64_t>(s0[q] >> 1) + 1ull);
+        sr_uniform_pair(seed, gk, u[4 * q], u[4 * q + 1]);
+        sr_uniform_pair(seed, gk + kGolden64, u[4 * q + 2], u[4 * q + 3]);
       }
     }
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const uint32_t mag = nonfinite ? 0u : sr_code<F>(fabsf(x[j]) * inv, u[j]);
       const uint32_t sign = nonfinite ? 0u : (__float_as_uint(x[j]) >> 31);
-      w[j >> 3] |= (mag | (sign << F::SIGN)) << (4 * (j & 7));
+      w[j >> 2] |= (mag | (sign << F::SIGN)) << (4 * (j & 3));
     }
   }
-  *reinterpret_cast<uint2*>(codes + b * 512 + r * 16 + (lane & 1) * 8) = make_uint2(w[0], w[1]);
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    *reinterpret_cast<uint16_t*>(codes + b * 512 + (r0 + 8 * q) * 16 + (lane & 7) * 2) = static_cast<uint16_t>(w[q]);
   if (lane == 0) scales[b] = static_cast<uint8_t>(code);
 }
 
@@ -171,28 +174,31 @@ __global__ __launch_bounds__(kMxWaves * 64) void k_dequantize_mx(const uint8_t* 
   const int lane = threadIdx.x & 63;
   const int64_t b = static_cast<int64_t>(blockIdx.x) * kMxWaves + (threadIdx.x >> 6);
   if (b >= d.nblocks) return;
-  const int r = lane >> 1, c0 = (lane & 1) * 16;
+  const int r0 = lane >> 3, c0 = (lane & 7) * 4;
   int64_t step;
-  const int64_t s0 = mx_src<ROLE>(d, b, r, c0, step);
+  int64_t s0[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) s0[q] = mx_src<ROLE>(d, b, r0 + 8 * q, c0, step);
   const uint32_t code = scales[b];
   // 2^(code - 127): 2^-127 is the fp32 subnormal 0x00400000; 0xFF is NaN
   const float scale = code == 0xFFu ? __uint_as_float(0x7FC00000u)
                                     : (code == 0u ? __uint_as_float(0x00400000u) : __uint_as_float(code << 23));
-  const uint2 w = *reinterpret_cast<const uint2*>(codes + b * 512 + r * 16 + (lane & 1) * 8);
-  float y[16];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const uint32_t c = ((j < 8 ? w.x : w.y) >> (4 * (j & 7))) & 0xFu;
-    const float v = code_value<F>(c & 7u) * scale;  // exact: a multiple of 2^-128 within range
-    y[j] = (c >> 3) ? -v : v;
-  }
-  if constexpr (ROLE == MX_ROLE_WEIGHT) {
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t w = *reinterpret_cast<const uint16_t*>(codes + b * 512 + (r0 + 8 * q) * 16 + (lane & 7) * 2);
+    float y[4];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) dst[s0 + j * step] = y[j];
-  } else {
-    float4* p = reinterpret_cast<float4*>(dst + s0);
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t c = (w >> (4 * j)) & 0xFu;
+      const float v = code_value<F>(c & 7u) * scale;  // exact: a multiple of 2^-128 within range
+      y[j] = (c >> 3) ? -v : v;
+    }
+    if constexpr (ROLE == MX_ROLE_WEIGHT) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) p[q] = make_float4(y[4 * q], y[4 * q + 1], y[4 * q + 2], y[4 * q + 3]);
+      for (int j = 0; j < 4; ++j) dst[s0[q] + j * step] = y[j];
+    } else {
+      *reinterpret_cast<float4*>(dst + s0[q]) = make_float4(y[0], y[1], y[2], y[3]);
+    }
   }
 }
 
