@@ -41,6 +41,15 @@
  *   fp32, max |x|.
  * - C_in, C_out and N must be multiples of 8 (zero-pad otherwise: padding
  *   changes neither the amax nor any result) and block must be 8.  N may be 0.
+ * - block = 32 selects the original microscaling format instead (§II-D: a
+ *   power-of-two E8M0 scale per block and no tensor scale; §IV-B: MicroQonv
+ *   holds for any block scale), on 32x32 square blocks in the same order
+ *   (ACT blocks [H][W][C_in/32][N/32], and so on), E2M1 elements throughout.
+ *   C_in, C_out and N must then be multiples of 32.  A block's codes are 32
+ *   rows of 16 bytes (element 2j of a row in the low nibble of byte j);
+ *   scales hold one E8M0 byte per block (code e + 127 for 2^e, 0xFF NaN) and
+ *   no quantizer scratch; tensor_scale is written as 1 and amax is not
+ *   written.  The GEMMs run on the scaled FP4 MFMA.
  */
 #ifndef MXCONV_H
 #define MXCONV_H
@@ -59,7 +68,7 @@ typedef enum {
   MX_ERR_NULL = -1,      /* a required pointer is NULL */
   MX_ERR_SHAPE = -2,     /* bad dimension, stride, padding, or not a multiple of 8 */
   MX_ERR_FORMAT = -3,    /* unknown element format, or one this call does not take */
-  MX_ERR_BLOCK = -4,     /* block size other than 8 */
+  MX_ERR_BLOCK = -4,     /* block size other than 8 or 32 (or 32 where a call takes 8 only) */
   MX_ERR_ALIGN = -5,     /* misaligned pointer */
   MX_ERR_WORKSPACE = -6, /* workspace missing or too small */
   MX_ERR_ROLE = -7,      /* unknown tensor role */
@@ -96,7 +105,7 @@ typedef enum { MX_RNE = 0, MX_SR = 1 } mx_round;
 typedef struct {
   int32_t n, c_in, c_out, h, w, k_h, k_w, stride_h, stride_w, pad_h, pad_w;
   int32_t elem_fmt; /* mx_elem_fmt of weights and output gradients */
-  int32_t block;    /* must be 8 (8x8 square blocks, §IV-B) */
+  int32_t block;    /* 8 (8x8 blocks, E4M3 scale, fp32 tensor scale, §IV-B) or 32 (E8M0, see above) */
   int32_t act_fmt;  /* mx_elem_fmt of the activation X; 0 = elem_fmt */
 } mx_conv_desc;
 /* Format pairs the GEMMs take: elem_fmt == act_fmt (any format but
@@ -144,7 +153,12 @@ size_t mx_wgrad_workspace_bytes(const mx_conv_desc* desc);
  *              1: *dst->amax already holds the amax to use (e.g. a
  *              statistic carried over from a previous step); not written
  * Non-finite input (Inf/NaN, or a non-finite given amax) is reported in-band:
- * *tensor_scale = NaN, every scale byte 0x7F (E4M3 NaN), all codes 0. */
+ * *tensor_scale = NaN, every scale byte 0x7F (E4M3 NaN), all codes 0.
+ * With block = 32 (E8M0 scales, one pass over src, amax_given ignored):
+ *   e     = floor(log2 blockamax) - 2, clamped to [-127, 127]  (OCP MX rule)
+ *   code  = Round(|x| / 2^e) on the E2M1 grid, saturating, sign of x
+ *   scale byte e + 127; 0 for an all-zero block; a block holding Inf or NaN
+ *   gets scale 0xFF and codes 0 (other blocks are unaffected). */
 mx_status mx_quantize_cbf(const mx_conv_desc* desc, mx_role role, const float* src,
                           const mx_qtensor* dst, mx_round rounding, uint64_t seed,
                           int amax_given, hipStream_t stream);
@@ -168,7 +182,9 @@ mx_status mx_conv_fwd(const mx_conv_desc* desc, const mx_qtensor* wq, const mx_q
  *          NaN amax, which quantizes as non-finite input); the rest of the
  *          buffer receives one partial maximum per wave of the GEMM (no
  *          atomics), so its contents are unspecified
- * Errors as mx_conv_fwd, plus MX_ERR_NULL / MX_ERR_ALIGN for y_amax. */
+ * Errors as mx_conv_fwd, plus MX_ERR_NULL / MX_ERR_ALIGN for y_amax, and
+ * MX_ERR_BLOCK for block = 32 (no tensor amax there; mx_fwd_amax_bytes
+ * returns 0). */
 size_t mx_fwd_amax_bytes(const mx_conv_desc* desc);
 mx_status mx_conv_fwd_amax(const mx_conv_desc* desc, const mx_qtensor* wq, const mx_qtensor* xq,
                            float* y, float* y_amax, hipStream_t stream);
