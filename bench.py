@@ -58,9 +58,15 @@ def parse():
                          "(X' formed and quantized again for the backward)")
     ap.add_argument("--replay-compact", action="store_true",
                     help="store the latent-replay buffer in the compact 3-bit codes (MX_UE2M1, 3.125 b/element)")
-    ap.add_argument("--graph", action="store_true",
-                    help="replay the step as one captured HIP graph (per-call timing then comes "
-                         "from a separate eager pass)")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch the calls one by one, in order, in the timed region instead of replaying the "
+                         "step as one captured HIP graph (the default; per-call timing always comes from an "
+                         "eager pass)")
+    ap.add_argument("--graph", action="store_true", help="the default; kept for old command lines")
+    ap.add_argument("--serial", action="store_true",
+                    help="issue every call on one stream, in order (default: within a layer, the three "
+                         "quantizations and then fwd / dgrad / wgrad run on three streams, each call after "
+                         "the quantizations it reads; layers stay in order)")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--verbose", action="store_true")
@@ -185,6 +191,7 @@ def main():
     prev = None  # --producer-amax: (layer, y, its fwd Call) of the previous layer
     flow_stats = {"activation_elements": 0, "quantized_elements": 0, "stored_activation_bytes": 0.0}
     n_chained = 0
+    layer_starts = []  # index of each layer's first call (the 7-call MicroQonv step)
     for li, lay in enumerate(wl.layers):
         d = mx.desc_from_layer(lay, fmt, afmt, a.block)
         x = WL.gen_x(lay, wl.x_dist, WL.seed_for(wl.cfg_index, li, 1)).to(dev)
@@ -247,6 +254,7 @@ def main():
                  "dequantize", ("dequantize_act", shape), 0, nx * (qbx + 4), "dequantize X"),
         ]
         prev = (d, y, calls[-4])
+        layer_starts.append(len(calls) - 7)
     if wl.lr_buffer is not None and not a.flow:
         nmaps, c, h, w_ = wl.lr_buffer
         lr_fmt = mx.MX_UE2M1 if a.replay_compact else mx.MX_E2M1
@@ -270,14 +278,76 @@ def main():
 
     total_flops = sum(c.flops for c in calls)
 
-    def run_step(events=None):
-        if events is None:
+    # Layer DAG on three streams (lanes): lane 0 quantizes X, runs fwd and
+    # dequantizes X; lane 1 quantizes W and runs dgrad; lane 2 quantizes dY
+    # and runs wgrad.  fwd waits for W, dgrad for dY, wgrad for X; each layer
+    # forks from lane 0 and joins back into it, so layers run in order.
+    # Calls outside the layers (the replay buffer) run on lane 0 after them.
+    # (graph replay only: issued eagerly, the event calls between the launches
+    # cost more host time than the overlap saves)
+    dag = (not a.serial and not a.eager and not a.flow and n_chained == 0
+           and len(layer_starts) == len(wl.layers))
+    LANE = (0, 1, 2, 0, 1, 2, 0)
+    lanes = [torch.cuda.current_stream(), torch.cuda.Stream(), torch.cuda.Stream()]
+    in_layer = set()
+    for st in layer_starts:
+        in_layer.update(range(st, st + 7))
+    dag_ev = [[torch.cuda.Event() for _ in range(6)] for _ in layer_starts]
+
+    def set_stream(h):
+        for c in calls:
+            c.args = c.args[:-1] + (h,)
+
+    def set_lanes(main):
+        # lane streams: `main` for lane 0 (the stream the step is issued on)
+        handles = [main.cuda_stream, lanes[1].cuda_stream, lanes[2].cuda_stream]
+        set_stream(main.cuda_stream)
+        for st in layer_starts:
+            for k in range(7):
+                c = calls[st + k]
+                c.args = c.args[:-1] + (handles[LANE[k]],)
+
+    def run_step_dag(main):
+        l1, l2 = lanes[1], lanes[2]
+        for li, st in enumerate(layer_starts):
+            fork, ex, ew, edy, j1, j2 = dag_ev[li]
+            fork.record(main)
+            l1.wait_event(fork)
+            l2.wait_event(fork)
+            calls[st]()               # quantize X   (lane 0)
+            ex.record(main)
+            calls[st + 1]()           # quantize W   (lane 1)
+            ew.record(l1)
+            calls[st + 2]()           # quantize dY  (lane 2)
+            edy.record(l2)
+            main.wait_event(ew)
+            calls[st + 3]()           # fwd: X, W    (lane 0)
+            l1.wait_event(edy)
+            calls[st + 4]()           # dgrad: W, dY (lane 1)
+            l2.wait_event(ex)
+            calls[st + 5]()           # wgrad: dY, X (lane 2)
+            calls[st + 6]()           # dequantize X (lane 0)
+            j1.record(l1)
+            j2.record(l2)
+            main.wait_event(j1)
+            main.wait_event(j2)
+        for i, c in enumerate(calls):
+            if i not in in_layer:
+                c()
+
+    def run_step(events=None, main=None):
+        if events is None and dag:
+            run_step_dag(main or torch.cuda.current_stream())
+        elif events is None:
             for c in calls:
                 c()
         else:
             for i, c in enumerate(calls):
                 c()
                 events[i].record()
+
+    if dag:
+        set_lanes(torch.cuda.current_stream())
 
     for _ in range(a.warmup):
         run_step()
@@ -288,22 +358,25 @@ def main():
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     graph = None
-    if a.graph:
+    if not a.eager:
         # every C-ABI call takes the stream as its last argument
-        def set_stream(h):
-            for c in calls:
-                c.args = c.args[:-1] + (h,)
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
-        set_stream(s.cuda_stream)
+        if dag:
+            set_lanes(s)
+        else:
+            set_stream(s.cuda_stream)
         with torch.cuda.stream(s):
-            run_step()          # eager pass on the capture stream first
+            run_step(main=s)    # eager pass on the capture stream first
             torch.cuda.synchronize()
             with torch.cuda.graph(g, stream=s):
-                run_step()
+                run_step(main=s)
         torch.cuda.current_stream().wait_stream(s)
-        set_stream(stream)
+        if dag:
+            set_lanes(torch.cuda.current_stream())
+        else:
+            set_stream(stream)
         graph = g
         for _ in range(2):
             graph.replay()
@@ -315,6 +388,8 @@ def main():
     for k in range(a.steps):
         if graph is not None:
             graph.replay()
+        elif dag:
+            run_step()
         else:
             run_step(ev[k])
     end.record()
@@ -323,8 +398,13 @@ def main():
     ms_total = start.elapsed_time(end)
     ms_step = ms_total / a.steps
 
-    if graph is not None:
-        # per-call durations from an eager pass with events (outside the timed region)
+    # per-call durations from an eager pass with events, one call at a time on
+    # one stream (outside the timed region when the step is a graph or a DAG)
+    pstart = None
+    if graph is not None or dag:
+        set_stream(stream)
+        pstart = torch.cuda.Event(enable_timing=True)
+        pstart.record()
         for k in range(a.steps):
             run_step(ev[k])
         torch.cuda.synchronize()
@@ -336,12 +416,12 @@ def main():
             if i == 0:
                 prev = ev[k - 1][-1] if k > 0 else None
                 if prev is None:
-                    per_call[k][i] = start.elapsed_time(ev[k][0]) if graph is None else float("nan")
+                    per_call[k][i] = (pstart or start).elapsed_time(ev[k][0])
                 else:
                     per_call[k][i] = prev.elapsed_time(ev[k][0])
             else:
                 per_call[k][i] = ev[k][i - 1].elapsed_time(ev[k][i])
-    # average over steps (skip NaN of the first call in graph mode)
+    # average over steps (NaN-safe)
     avg_ms = []
     for i in range(len(calls)):
         vals = [per_call[k][i] for k in range(a.steps) if per_call[k][i] == per_call[k][i]]
@@ -414,6 +494,7 @@ def main():
                    "step": "per layer: quantize X,W,dY; fwd; dgrad; wgrad; dequantize Xq"
                            + ("; replay buffer quantize+dequantize" if wl.lr_buffer else ""),
                    "graph": bool(graph is not None),
+                   "streams": "layer DAG on 3 streams" if dag else "1 (serial)",
                    "producer_amax": {"chained_layers": n_chained} if a.producer_amax else False,
                    **({"replay_buffer_fmt": "ue2m1" if a.replay_compact else "e2m1"} if wl.lr_buffer else {})},
         "conv_tflops": total_flops / (conv_ms / 1e3) / 1e12 if conv_ms > 0 else None,
