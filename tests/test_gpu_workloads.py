@@ -6,7 +6,12 @@ For every distinct layer shape of each stack: the quantized X, W and dY
 the three GEMMs on a seeded sample of outputs (plus the corner outputs) that
 the oracle evaluates one by one, within 2e-3 * sum|a*b|.  The latent-replay
 buffer (10k maps of 64 channels at 8x8) is quantized and dequantized in full
-and compared bit-exactly."""
+and compared bit-exactly.
+
+The same checks run for the two variants beside the hot path, on the stacks
+whose channels and batch allow them: the E8M0 32x32-block format
+(`bench.py --block 32`) and MicroQonv+ with E3M2 activations
+(`bench.py --act-fmt e3m2`)."""
 import numpy as np
 import pytest
 import torch
@@ -14,8 +19,8 @@ import torch
 import microscaling_quantized_convolution_mx_amd as mx
 import oracle as O
 from microscaling_quantized_convolution_mx_amd import workloads as WL
-from gpu_util import (DEV, assert_close, assert_quant_equal, conv_buffers, gpu_quantize,
-                      oracle_conv, say)
+from gpu_util import (DEV, assert_close, assert_quant_equal, conv_buffers, gpu_quantize, ofmt,
+                      oracle_conv, oracle_quantize, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -36,13 +41,26 @@ def sample_idx(n, rng):
     return np.unique(np.concatenate([idx, [0, n - 1, n // 2]])).astype(np.int64)
 
 
-def check_layer(wl, li, lay, fmt):
-    d = mx.desc_from_layer(lay, fmt)
+ORACLE_ROLE = {mx.MX_ROLE_ACT: O.ACT, mx.MX_ROLE_WEIGHT: O.WEIGHT, mx.MX_ROLE_GRAD: O.GRAD}
+
+
+def assert_mx_equal(gq, oq, what):
+    torch.cuda.synchronize()
+    assert gq.tensor_scale.item() == 1.0, what
+    scales = gq.scales[:gq.nblocks].cpu().numpy()
+    bad = np.flatnonzero(scales != oq.scales)
+    assert bad.size == 0, f"{what}: {bad.size} scales differ, first {bad[:5]}"
+    bad = np.flatnonzero(gq.codes[:gq.code_bytes].cpu().numpy() != oq.packed())
+    assert bad.size == 0, f"{what}: {bad.size} code bytes differ, first at {bad[:5]}"
+
+
+def check_layer(wl, li, lay, fmt, act_fmt=0, block=8):
+    d = mx.desc_from_layer(lay, fmt, act_fmt, block)
     x = WL.gen_x(lay, wl.x_dist, WL.seed_for(wl.cfg_index, li, 1))
     w = WL.gen_w(lay, WL.seed_for(wl.cfg_index, li, 2))
     dy = WL.gen_dy(lay, wl.dy_sigma, WL.seed_for(wl.cfg_index, li, 3))
     seed = WL.seed_for(wl.cfg_index, li, 4)
-    say(f"{wl.key} layer {li} {lay.tag()} fmt {fmt}")
+    say(f"{wl.key} layer {li} {lay.tag()} fmt {fmt} act_fmt {act_fmt} block {block}")
     qx = gpu_quantize(d, mx.MX_ROLE_ACT, x)
     qw = gpu_quantize(d, mx.MX_ROLE_WEIGHT, w)
     qdy = gpu_quantize(d, mx.MX_ROLE_GRAD, dy, mx.MX_SR, seed)
@@ -52,16 +70,23 @@ def check_layer(wl, li, lay, fmt):
     mx.mx_conv_wgrad(d, qdy, qx, dw, ws)
     torch.cuda.synchronize()
 
-    ox = O.quantize(O.ACT, fmt, x.numpy())
-    ow = O.quantize(O.WEIGHT, fmt, w.numpy())
-    ody = O.quantize(O.GRAD, fmt, dy.numpy(), O.SR, seed)
-    assert_quant_equal(qx, ox, "X")
-    assert_quant_equal(qw, ow, "W")
-    assert_quant_equal(qdy, ody, "dY")
+    if block == 32:
+        ox = O.quantize_mx(O.ACT, O.E2M1, x.numpy())
+        ow = O.quantize_mx(O.WEIGHT, O.E2M1, w.numpy())
+        ody = O.quantize_mx(O.GRAD, O.E2M1, dy.numpy(), O.SR, seed)
+        for gq, oq, nm in ((qx, ox, "X"), (qw, ow, "W"), (qdy, ody, "dY")):
+            assert_mx_equal(gq, oq, nm)
+    else:
+        ox = oracle_quantize(d, mx.MX_ROLE_ACT, x)
+        ow = oracle_quantize(d, mx.MX_ROLE_WEIGHT, w)
+        ody = oracle_quantize(d, mx.MX_ROLE_GRAD, dy, mx.MX_SR, seed)
+        assert_quant_equal(qx, ox, "X")
+        assert_quant_equal(qw, ow, "W")
+        assert_quant_equal(qdy, ody, "dY")
     del x, dy
 
     cv = oracle_conv(d)
-    rng = np.random.default_rng(li * 7 + fmt)
+    rng = np.random.default_rng(li * 7 + fmt + 100 * act_fmt + block)
     xe, we, dye = ox.exact(), ow.exact(), ody.exact()
     idx = sample_idx(y.numel(), rng)
     ref, s = O.conv_fwd_points(cv, we, xe, idx)
@@ -87,6 +112,24 @@ def cases():
 def test_workload_layer(key, li, fmt):
     wl = WL.workloads()[key]
     check_layer(wl, li, wl.layers[li], fmt)
+
+
+def variant_cases():
+    out = []
+    for key in ("c3", "c5"):
+        wl = WL.workloads()[key]
+        for li, lay in distinct_layers(wl):
+            out.append(pytest.param(key, li, 0, 32, id=f"{key}-L{li}-e8m0"))
+            out.append(pytest.param(key, li, mx.MX_E3M2, 8, id=f"{key}-L{li}-x6e3m2"))
+    return out
+
+
+@pytest.mark.parametrize("key,li,act_fmt,block", variant_cases())
+def test_workload_layer_variant(key, li, act_fmt, block):
+    wl = WL.workloads()[key]
+    lay = wl.layers[li]
+    assert block == 8 or (lay.c_in % 32 == 0 and lay.c_out % 32 == 0 and lay.n % 32 == 0)
+    check_layer(wl, li, lay, mx.MX_E2M1, act_fmt, block)
 
 
 def test_replay_buffer_codec():
