@@ -469,6 +469,25 @@ def main():
             pass
     roof["ai_flop_per_byte"] = ai
 
+    # every call group (one call of one layer shape), slowest first: GEMMs
+    # against the dense MFMA peak and against what the roofline allows at
+    # their arithmetic intensity (algorithmic bytes: quantized operands read
+    # once, fp32 output written once); codec calls against 8 TB/s
+    pk = PEAK_MFMA[mfma_t]
+    per_layer = []
+    for (gop, tag), g in sorted(groups.items(), key=lambda kv: -kv[1]["ms"]):
+        ls = g["ms"] / g["n"] / 1e3
+        ent = {"call": gop, "shape": tag, "launches": g["n"], "launch_us": round(ls * 1e6, 2)}
+        if g["flops"]:
+            att = min(pk, g["flops"] / g["bytes"] * PEAK_HBM) if g["bytes"] else pk
+            ach = g["flops"] / ls
+            ent.update({"tflops": round(ach / 1e12, 2), "frac_of_peak": round(ach / pk, 4),
+                        "attainable_frac_of_peak": round(att / pk, 4), "frac_of_attainable": round(ach / att, 4)})
+        else:
+            ach = g["bytes"] / ls
+            ent.update({"gbps": round(ach / 1e9, 1), "frac_of_hbm": round(ach / PEAK_HBM, 4)})
+        per_layer.append(ent)
+
     conv_ms = sum(by_op.get(o, {"ms": 0.0})["ms"] for o in ("fwd", "dgrad", "wgrad"))
     q_ms = by_op.get("quantize", {"ms": 0.0})["ms"]
     q_bytes = by_op.get("quantize", {"bytes": 0})["bytes"]
@@ -507,6 +526,7 @@ def main():
                      "note": "value and conv_tflops count fwd + wgrad only (the activation path)"}}
            if a.flow else {}),
         "roofline": roof,
+        "per_layer": per_layer,
         "wall_s_timed": wall,
         "kernel_source": kernel_source_hash(),
     }

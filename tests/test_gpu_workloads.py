@@ -4,7 +4,10 @@ bench.py times (same descriptors, seeds and entry points).
 For every distinct layer shape of each stack: the quantized X, W and dY
 (codes, scales, T, amax) are compared bit-exactly over the whole tensors, and
 the three GEMMs on a seeded sample of outputs (plus the corner outputs) that
-the oracle evaluates one by one, within 2e-3 * sum|a*b|.  The latent-replay
+the oracle evaluates one by one, within 2e-3 * sum|a*b|: 65,536 outputs of
+fwd and of dgrad (all of them where there are fewer), and as many wgrad
+outputs as 2^30 oracle multiply-adds allow (a wgrad output sums over
+Ho*Wo*N products), at least 256.  The latent-replay
 buffer (10k maps of 64 channels at 8x8) is quantized and dequantized in full
 and compared bit-exactly.
 
@@ -24,7 +27,8 @@ from gpu_util import (DEV, assert_close, assert_quant_equal, conv_buffers, gpu_q
 
 pytestmark = pytest.mark.gpu
 
-NPTS = 1536
+NPTS = 65536
+WGRAD_MACS = 1 << 30
 
 
 def distinct_layers(wl):
@@ -36,8 +40,10 @@ def distinct_layers(wl):
     return out
 
 
-def sample_idx(n, rng):
-    idx = rng.integers(0, n, NPTS)
+def sample_idx(n, rng, npts=NPTS):
+    if n <= npts:
+        return np.arange(n, dtype=np.int64)
+    idx = rng.integers(0, n, npts)
     return np.unique(np.concatenate([idx, [0, n - 1, n // 2]])).astype(np.int64)
 
 
@@ -94,7 +100,8 @@ def check_layer(wl, li, lay, fmt, act_fmt=0, block=8):
     idx = sample_idx(dx.numel(), rng)
     ref, s = O.conv_dgrad_points(cv, we, dye, idx)
     assert_close(dx.view(-1)[torch.from_numpy(idx).to(DEV)].cpu().numpy(), ref, s, "dgrad")
-    idx = sample_idx(dw.numel(), rng)[:256]
+    k_wgrad = lay.h_out * lay.w_out * lay.n
+    idx = sample_idx(dw.numel(), rng, max(256, min(NPTS, WGRAD_MACS // k_wgrad)))
     ref, s = O.conv_wgrad_points(cv, dye, xe, idx)
     assert_close(dw.view(-1)[torch.from_numpy(idx).to(DEV)].cpu().numpy(), ref, s, "wgrad")
 
