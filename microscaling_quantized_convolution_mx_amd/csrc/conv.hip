@@ -718,10 +718,10 @@ WgradPlan wgrad_plan(const Geom& g) {
   return {t, static_cast<int>(splits)};
 }
 
-// Weight gradient on E8M0 32x32 blocks: 256x256 tiles, K steps of 64; about
+// Weight gradient on E8M0 32x32 blocks: 256x256 tiles, K steps of 128; about
 // one round of workgroups (1024 waves) with at least 4 K steps per split.
 WgradPlan wgrad_plan_mx(const Geom& g) {
-  const int64_t ksteps = (static_cast<int64_t>(g.ho) * g.wo * (g.n / 32) + 1) / 2;
+  const int64_t ksteps = (static_cast<int64_t>(g.ho) * g.wo * (g.n / 32) + kMxStepBlocks - 1) / kMxStepBlocks;
   const int64_t ncol = static_cast<int64_t>(g.k_h) * g.k_w * g.c_in;
   const int64_t tiles = ((g.c_out + 255) / 256) * ((ncol + 255) / 256);
   int64_t splits = (1024 / 4) / tiles;
@@ -815,8 +815,9 @@ hipError_t launch_conv_wgrad(const Geom& g, const mx_qtensor* dyq, const mx_qten
   p.ncol = g.k_h * g.k_w * g.c_in;
   p.ncb = p.ncol / 8;
   p.kb_total = g.ho * g.wo * (g.n / 8);
-  // K steps: of the tile's KB 8-blocks, or of two 32-blocks
-  const int ksteps = mxb ? (g.ho * g.wo * (g.n / 32) + 1) / 2 : (p.kb_total + pl.t.kb - 1) / pl.t.kb;
+  // K steps: of the tile's KB 8-blocks, or of kMxStepBlocks 32-blocks
+  const int ksteps = mxb ? (g.ho * g.wo * (g.n / 32) + kMxStepBlocks - 1) / kMxStepBlocks
+                         : (p.kb_total + pl.t.kb - 1) / pl.t.kb;
   p.ks_split = (ksteps + pl.splits - 1) / pl.splits;
   p.a_codes = static_cast<const uint8_t*>(dyq->codes); p.a_scales = dyq->scales; p.a_t = dyq->tensor_scale;
   p.b_codes = static_cast<const uint8_t*>(xq->codes); p.b_scales = xq->scales; p.b_t = xq->tensor_scale;

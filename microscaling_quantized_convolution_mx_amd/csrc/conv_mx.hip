@@ -17,31 +17,34 @@
 // transposing LDS reads (ds_read_b64_tr_b4: 16x16 nibble transpose within
 // each group of 16 lanes) gather the 32 nibbles of a column.
 //
-// Tile 256x256, 4 waves of 128x128 (4x4 MFMAs of 32x32), one K step = 64
-// K values = two 32-blocks per row/column block.  Every thread copies four
-// 16-byte block rows per step from global memory into one of three LDS
-// stages (the blocks unchanged).  The rows are fetched into registers two
-// steps before they are written to LDS, so an L2 or HBM load has two steps
-// of MFMAs to arrive.  Tile placement, the stride phases of dgrad and the
-// epilogue are those of the generic kernel.
+// Tile 256x256, 4 waves of 128x128 (4x4 MFMAs of 32x32).  One K step is
+// 128 K values: 4 32-blocks per row / column block of the tile, two MFMA
+// k-slices of 16 MFMAs per wave behind one barrier.  Every thread copies
+// eight 16-byte block rows per step from global memory into one of three
+// LDS stages (the blocks unchanged).  The rows are fetched into registers
+// two steps before they are written to LDS, so an L2 or HBM load has two
+// steps of MFMAs to arrive.  Tile placement, the stride phases of dgrad and
+// the epilogue are those of the generic kernel.
 #include "conv_kernels.h"
 
 namespace mx {
 namespace {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x2v __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i32x2v lds_i32x2v;
 
-constexpr int kMxB = 512;        // bytes of one 32x32 E2M1 block
-constexpr int kOpnd = 16 * kMxB; // one operand of a stage: 8 line blocks x 2 k-blocks
-constexpr int kStage = 2 * kOpnd + 64;  // codes of A and B, then scales [A: 2x8][B: 2x8] (+pad)
+constexpr int kKB = kMxStepBlocks;              // 32-blocks along K per step
+constexpr int kMxB = 512;                       // bytes of one 32x32 E2M1 block
+constexpr int kOpnd = 8 * kKB * kMxB;           // one operand of a stage: 8 line blocks x kKB k-blocks
+constexpr int kStage = 2 * kOpnd + 2 * 8 * kKB; // codes of A and B, then scales [A: kKB x 8][B: kKB x 8]
+constexpr int kRows = 2 * 8 * kKB * 32 / 256;   // block rows each thread stages per step
 
 template <int OP>
 __global__ __launch_bounds__(256) void k_conv_mx(const ConvParams p) {
   constexpr int MT = 256, NT = 256, WM = 2;
   constexpr int WTM = 128, WTN = 128, RM = 4, RN = 4;
+  static_assert(kRows == 8, "staging map below assumes 8 rows per thread");
   // K runs along the stored rows of A for fwd and wgrad, of B for wgrad
   constexpr bool A_DIRECT = (OP != OP_DGRAD);
   constexpr bool B_DIRECT = (OP == OP_WGRAD);
@@ -59,12 +62,12 @@ __global__ __launch_bounds__(256) void k_conv_mx(const ConvParams p) {
   const int cb0 = (t.cb0 * 8) >> 5;               // first column block
   const int nrb = p.M >> 5;                       // row blocks of the GEMM
   const int ncb = (t.ncb_launch * 8) >> 5;        // column blocks of the launch
-  // K extent in 32-blocks and this launch's range of K steps (2 blocks each)
+  // K extent in 32-blocks and this launch's range of K steps (kKB blocks each)
   int k_total;
   if constexpr (OP == OP_FWD) k_total = p.k_h * p.k_w * cbi;
   else if constexpr (OP == OP_DGRAD) k_total = t.nkh * t.nkw * cbo;
   else k_total = p.ho * p.wo * nbk;
-  const int nsteps_all = (k_total + 1) >> 1;
+  const int nsteps_all = (k_total + kKB - 1) / kKB;
   int s_begin = 0, s_end = nsteps_all;
   if constexpr (OP == OP_WGRAD) {
     s_begin = t.bz * p.ks_split;
@@ -72,27 +75,28 @@ __global__ __launch_bounds__(256) void k_conv_mx(const ConvParams p) {
     if (s_begin > s_end) s_begin = s_end;
   }
   // k-blocks past this launch's range read as zeros
-  const int k_end = min(k_total, 2 * s_end);
+  const int k_end = min(k_total, kKB * s_end);
 
-  // Staging: thread t copies row (t & 31) of block (operand, line block lb,
-  // k half kk) for lb in {lb_lo, lb_lo + 4}, kk = (t >> 5) & 1.
-  const int row = tid & 31, kk = (tid >> 5) & 1, lb_lo = tid >> 6;
-  // the four block rows this thread copies: A lb_lo, A lb_lo+4, B lb_lo, B lb_lo+4
-  int gline[4];
-  bool gline_ok[4];
+  // Staging: thread t copies row (t & 31) of the blocks (operand, line block
+  // lb, k-block kb) with kb = (t >> 5) & 3 and lb = (t >> 7) + 2j, j = 0..3,
+  // for A (q = j) and for B (q = 4 + j).
+  const int row = tid & 31, kb = (tid >> 5) & 3, lbq = tid >> 7;
+  auto q_lb = [&](int q) { return lbq + 2 * (q & 3); };
+  int gline[8];
+  bool gline_ok[8];
   // column-block geometry of B (fixed over the K loop)
-  int col_y[2] = {0, 0}, col_x[2] = {0, 0}, col_nb[2] = {0, 0}, col_cib[2] = {0, 0};
+  int col_y[4] = {0, 0, 0, 0}, col_x[4] = {0, 0, 0, 0}, col_nb[4] = {0, 0, 0, 0}, col_cib[4] = {0, 0, 0, 0};
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int lb = lb_lo + (q & 1) * 4;
-    if (q < 2) {
+  for (int q = 0; q < 8; ++q) {
+    const int lb = q_lb(q);
+    if (q < 4) {
       gline[q] = rb0 + lb;
       gline_ok[q] = gline[q] < nrb;
     } else {
       const int cb = cb0 + lb;
       gline[q] = cb;
       gline_ok[q] = cb < ncb;
-      const int i = q - 2;
+      const int i = q - 4;
       if constexpr (OP == OP_FWD) {
         const int pos = cb / nbk;
         col_nb[i] = cb - pos * nbk;
@@ -128,7 +132,7 @@ __global__ __launch_bounds__(256) void k_conv_mx(const ConvParams p) {
     const uint32_t a = div_b.div(outer);
     const uint32_t b = outer - a * div_b.d;
     const bool kin = k < k_end;
-    if (q < 2) {
+    if (q < 4) {
       const uint32_t rb = static_cast<uint32_t>(gline[q]);
       if constexpr (OP == OP_FWD) blk = ((a * p.k_w + b) * cbo + rb) * cbi + inner;                 // W[tap][co][ci]
       else if constexpr (OP == OP_DGRAD)
@@ -136,7 +140,7 @@ __global__ __launch_bounds__(256) void k_conv_mx(const ConvParams p) {
       else blk = ((a * p.wo + b) * cbo + rb) * nbk + inner;                                            // dY[pos][co][n]
       return gline_ok[q] && kin;
     }
-    const int i = q - 2;
+    const int i = q - 4;
     int y, x;
     bool inb;
     if constexpr (OP == OP_FWD) {
@@ -162,17 +166,17 @@ __global__ __launch_bounds__(256) void k_conv_mx(const ConvParams p) {
   // whether the block exists.  The mask is applied when the rows are
   // written to LDS, so that nothing waits for a load before then.
   struct Raw {
-    uint4 v[4];
-    uint32_t sc[4];
-    uint32_t mask[4];
+    uint4 v[8];
+    uint32_t sc[8];
+    uint32_t mask[8];
   };
   Raw r0, r1;
   auto fetch_one = [&](Raw& raw, int step, int q) {
-    const int k = 2 * step + kk;
+    const int k = kKB * step + kb;
     uint32_t blk = 0;
     const bool ok = locate(q, k, blk);
-    const uint8_t* codes = q < 2 ? p.a_codes : p.b_codes;
-    const uint8_t* scales = q < 2 ? p.a_scales : p.b_scales;
+    const uint8_t* codes = q < 4 ? p.a_codes : p.b_codes;
+    const uint8_t* scales = q < 4 ? p.a_scales : p.b_scales;
     const uint64_t b = ok ? blk : 0u;
     raw.v[q] = *reinterpret_cast<const uint4*>(codes + b * kMxB + row * 16);
     raw.sc[q] = scales[b];
@@ -180,19 +184,20 @@ __global__ __launch_bounds__(256) void k_conv_mx(const ConvParams p) {
   };
   auto fetch = [&](Raw& raw, int step) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) fetch_one(raw, step, q);
+    for (int q = 0; q < 8; ++q) fetch_one(raw, step, q);
   };
+  // stage layout: block (lb, kb) of an operand at (lb * kKB + kb) * kMxB;
+  // scales [kb][lb] (A at 2*kOpnd, B 8*kKB bytes later)
   auto stage_write = [&](const Raw& raw, uint8_t* st) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int lb = lb_lo + (q & 1) * 4;
+    for (int q = 0; q < 8; ++q) {
+      const int lb = q_lb(q);
       const uint32_t m = raw.mask[q];
       // a block outside the operand is zeros with scale 2^0
-      *reinterpret_cast<uint4*>(st + (q < 2 ? 0 : kOpnd) + (lb * 2 + kk) * kMxB + row * 16) =
+      *reinterpret_cast<uint4*>(st + (q < 4 ? 0 : kOpnd) + (lb * kKB + kb) * kMxB + row * 16) =
           make_uint4(raw.v[q].x & m, raw.v[q].y & m, raw.v[q].z & m, raw.v[q].w & m);
-      // scales [kk][lb]: the 4 line blocks of a wave half in one word
       if (row == 0)
-        st[2 * kOpnd + (q < 2 ? 0 : 16) + kk * 8 + lb] = static_cast<uint8_t>((raw.sc[q] & m) | (127u & ~m));
+        st[2 * kOpnd + (q < 4 ? 0 : 8 * kKB) + kb * 8 + lb] = static_cast<uint8_t>((raw.sc[q] & m) | (127u & ~m));
     }
   };
 
@@ -205,13 +210,13 @@ __global__ __launch_bounds__(256) void k_conv_mx(const ConvParams p) {
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
   const int l32 = lane & 31, half = lane >> 5;
-  // operand of line block lb for this lane: direct = its row l32 of block
-  // (lb, half); transposed = column l32 of that block, gathered 16 rows at a
-  // time (lane group g = lane/16 covers columns 16*(g%2) .. +15)
+  // operand of line block lb, k-slice j, for this lane: block (lb, 2j +
+  // half); direct = its row l32; transposed = its column l32, gathered 16
+  // rows at a time (lane group g = lane/16 covers columns 16*(g%2) .. +15)
   const int direct_off = half * kMxB + l32 * 16;
   const int trans_off = half * kMxB + (lane & 15) * 16 + ((lane >> 4) & 1) * 8;
-  auto read_opnd = [&](const uint8_t* base, int lb, bool direct) -> i32x8 {
-    const uint8_t* blk = base + lb * 2 * kMxB;
+  auto read_opnd = [&](const uint8_t* base, int lb, int j, bool direct) -> i32x8 {
+    const uint8_t* blk = base + (lb * kKB + 2 * j) * kMxB;
     if (direct) {
       const uint4 v = *reinterpret_cast<const uint4*>(blk + direct_off);
       return i32x8{static_cast<int>(v.x), static_cast<int>(v.y), static_cast<int>(v.z), static_cast<int>(v.w), 0, 0, 0, 0};
@@ -220,54 +225,73 @@ __global__ __launch_bounds__(256) void k_conv_mx(const ConvParams p) {
     const i32x2v r1 = __builtin_amdgcn_ds_read_tr4_b64_v2i32((lds_i32x2v*)(blk + trans_off + 16 * 16));
     return i32x8{r0.x, r0.y, r1.x, r1.y, 0, 0, 0, 0};
   };
-  // the MFMA operands of one step: fragments and scale words
+  // the MFMA operands of one k-slice: fragments and scale words
   struct Frags {
     i32x8 a[RM], b[RN];
     int sa, sb;
   };
-  Frags f0, f1;
-  auto read_frags = [&](const uint8_t* st, Frags& f) {
-    // scale words: bytes (the wave half's line blocks 0..3) for this lane's k half
-    f.sa = *reinterpret_cast<const int*>(st + 2 * kOpnd + half * 8 + wm * 4);
-    f.sb = *reinterpret_cast<const int*>(st + 2 * kOpnd + 16 + half * 8 + wn * 4);
+  Frags fA, fB;
+  auto read_frags = [&](const uint8_t* st, int j, Frags& f) {
+    // scale words: bytes (the wave half's line blocks 0..3) of k-block 2j + half
+    f.sa = *reinterpret_cast<const int*>(st + 2 * kOpnd + (2 * j + half) * 8 + wm * 4);
+    f.sb = *reinterpret_cast<const int*>(st + 2 * kOpnd + 8 * kKB + (2 * j + half) * 8 + wn * 4);
 #pragma unroll
-    for (int i = 0; i < RM; ++i) f.a[i] = read_opnd(st, wm * 4 + i, A_DIRECT);
+    for (int i = 0; i < RM; ++i) f.a[i] = read_opnd(st, wm * 4 + i, j, A_DIRECT);
 #pragma unroll
-    for (int j = 0; j < RN; ++j) f.b[j] = read_opnd(st + kOpnd, wn * 4 + j, B_DIRECT);
+    for (int i = 0; i < RN; ++i) f.b[i] = read_opnd(st + kOpnd, wn * 4 + i, j, B_DIRECT);
   };
 
-  // Step s, on stage s%3 whose operands were read into registers during
-  // step s-1:
+  // Step s, on stage s%3, with slice 0's operands read into fA during step
+  // s-1:
   //   write the rows of step s+2 (fetched two steps earlier) into stage
   //   (s+2)%3, last read during step s-1;
-  //   read the operands of step s+1 from stage (s+1)%3, complete since the
-  //   barrier of step s-1;
-  //   16 MFMAs, with the global fetches of step s+4 between them;
+  //   read slice 1 into fB; 16 MFMAs on fA, with fetches of step s+4;
+  //   read slice 0 of step s+1 from stage (s+1)%3 (complete since the
+  //   barrier of step s-1) into fA; 16 MFMAs on fB, with more fetches;
   //   barrier.
-  // Steps run in pairs so that the two register sets alternate statically,
-  // with no exit in between (an exit there makes the compiler spill the
-  // accumulators); fetches at or past the last step give zero rows, so the
-  // extra step of an odd count adds nothing.
+  // Steps run in pairs so that the two row register sets alternate
+  // statically, with no exit in between (an exit there makes the compiler
+  // spill the accumulators); fetches at or past the last step give zero
+  // rows, so the extra step of an odd count adds nothing.
   const int nsteps = s_end - s_begin;
-  auto step = [&](int s, const Frags& fc, Frags& fn, uint8_t* next_st, uint8_t* write_st, Raw& raw) {
-    stage_write(raw, write_st);
-    read_frags(next_st, fn);
-    __builtin_amdgcn_sched_barrier(0);
-#define MX_MFMA(I, J)                                                                                          \
-  acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fc.a[I], fc.b[J], acc[I][J], 4, 4, I, fc.sa, J, \
-                                                              fc.sb);                                        \
+#define MX_MFMA(F, I, J)                                                                                     \
+  acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.a[I], F.b[J], acc[I][J], 4, 4, I, F.sa, J, \
+                                                              F.sb);                                     \
   __builtin_amdgcn_sched_barrier(0)
-    MX_MFMA(0, 0); fetch_one(raw, s_begin + s + 4, 0); __builtin_amdgcn_sched_barrier(0);
-    MX_MFMA(0, 1); MX_MFMA(0, 2); MX_MFMA(0, 3);
-    MX_MFMA(1, 0); fetch_one(raw, s_begin + s + 4, 1); __builtin_amdgcn_sched_barrier(0);
-    MX_MFMA(1, 1); MX_MFMA(1, 2); MX_MFMA(1, 3);
-    MX_MFMA(2, 0); fetch_one(raw, s_begin + s + 4, 2); __builtin_amdgcn_sched_barrier(0);
-    MX_MFMA(2, 1); MX_MFMA(2, 2); MX_MFMA(2, 3);
-    MX_MFMA(3, 0); fetch_one(raw, s_begin + s + 4, 3); __builtin_amdgcn_sched_barrier(0);
-    MX_MFMA(3, 1); MX_MFMA(3, 2); MX_MFMA(3, 3);
-#undef MX_MFMA
+  auto step = [&](int s, const uint8_t* cur, const uint8_t* next_st, uint8_t* write_st, Raw& raw) {
+    const int fs = s_begin + s + 4;
+    stage_write(raw, write_st);
+    read_frags(cur, 1, fB);
+    __builtin_amdgcn_sched_barrier(0);
+    MX_MFMA(fA, 0, 0); fetch_one(raw, fs, 0); __builtin_amdgcn_sched_barrier(0);
+    MX_MFMA(fA, 0, 1); MX_MFMA(fA, 0, 2); MX_MFMA(fA, 0, 3);
+    MX_MFMA(fA, 1, 0); fetch_one(raw, fs, 1); __builtin_amdgcn_sched_barrier(0);
+    MX_MFMA(fA, 1, 1); MX_MFMA(fA, 1, 2); MX_MFMA(fA, 1, 3);
+    MX_MFMA(fA, 2, 0); fetch_one(raw, fs, 2); __builtin_amdgcn_sched_barrier(0);
+    MX_MFMA(fA, 2, 1); MX_MFMA(fA, 2, 2); MX_MFMA(fA, 2, 3);
+    MX_MFMA(fA, 3, 0); fetch_one(raw, fs, 3); __builtin_amdgcn_sched_barrier(0);
+    MX_MFMA(fA, 3, 1); MX_MFMA(fA, 3, 2); MX_MFMA(fA, 3, 3);
+    read_frags(next_st, 0, fA);
+    __builtin_amdgcn_sched_barrier(0);
+    MX_MFMA(fB, 0, 0); fetch_one(raw, fs, 4); __builtin_amdgcn_sched_barrier(0);
+    MX_MFMA(fB, 0, 1); MX_MFMA(fB, 0, 2); MX_MFMA(fB, 0, 3);
+    MX_MFMA(fB, 1, 0); fetch_one(raw, fs, 5); __builtin_amdgcn_sched_barrier(0);
+    MX_MFMA(fB, 1, 1); MX_MFMA(fB, 1, 2); MX_MFMA(fB, 1, 3);
+    MX_MFMA(fB, 2, 0); fetch_one(raw, fs, 6); __builtin_amdgcn_sched_barrier(0);
+    MX_MFMA(fB, 2, 1); MX_MFMA(fB, 2, 2); MX_MFMA(fB, 2, 3);
+    MX_MFMA(fB, 3, 0); fetch_one(raw, fs, 7); __builtin_amdgcn_sched_barrier(0);
+    MX_MFMA(fB, 3, 1); MX_MFMA(fB, 3, 2); MX_MFMA(fB, 3, 3);
+    // The MFMAs carry no ordering of their own: without a use here, the
+    // first step of a pair has its MFMAs emitted after the barrier below,
+    // leaving the MFMA pipe idle while the waves wait there.  An empty asm
+    // that takes each accumulator keeps them ahead of the barrier.
+#pragma unroll
+    for (int i = 0; i < RM; ++i)
+#pragma unroll
+      for (int j = 0; j < RN; ++j) asm volatile("" : "+a"(acc[i][j]));
     __syncthreads();
   };
+#undef MX_MFMA
   if (nsteps > 0) {
     fetch(r0, s_begin);
     fetch(r1, s_begin + 1);
@@ -276,14 +300,13 @@ __global__ __launch_bounds__(256) void k_conv_mx(const ConvParams p) {
     fetch(r0, s_begin + 2);
     fetch(r1, s_begin + 3);
     __syncthreads();
-    read_frags(lds, f0);
+    read_frags(lds, 0, fA);
     int c = 0;  // stage of step s
     for (int s = 0; s < nsteps; s += 2) {
       const int c1 = c == 2 ? 0 : c + 1, c2 = c1 == 2 ? 0 : c1 + 1;
-      // step s: operands in f0, reads step s+1 into f1, writes rows s+2 (r0)
-      step(s, f0, f1, lds + c1 * kStage, lds + c2 * kStage, r0);
-      // step s+1: operands in f1, reads step s+2 into f0, writes rows s+3 (r1)
-      step(s + 1, f1, f0, lds + c2 * kStage, lds + c * kStage, r1);
+      // step s writes rows s+2 (r0) into c2; step s+1 writes rows s+3 (r1) into c
+      step(s, lds + c * kStage, lds + c1 * kStage, lds + c2 * kStage, r0);
+      step(s + 1, lds + c1 * kStage, lds + c2 * kStage, lds + c * kStage, r1);
       c = c2;
     }
   }
