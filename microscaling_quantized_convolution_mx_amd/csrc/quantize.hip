@@ -50,6 +50,19 @@ __device__ __forceinline__ uint32_t magic_quot(uint32_t x, uint32_t m, int32_t s
 }
 
 __device__ __forceinline__ uint32_t absbits(uint32_t v) { return v & 0x7FFFFFFFu; }
+
+// Streaming 16-byte load with the nontemporal hint: the source of a
+// quantization pass is read once per pass, and on this GPU the hinted loads
+// sustain ~15% more read bandwidth than plain ones.
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+  const u32x4v v = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float4 load_stream(const float* p) {
+  const uint4 v = load_stream(reinterpret_cast<const uint4*>(p));
+  return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
+}
 __device__ __forceinline__ uint32_t max4(uint4 v) {
   return max(max(absbits(v.x), absbits(v.y)), max(absbits(v.z), absbits(v.w)));
 }
@@ -68,11 +81,11 @@ __global__ __launch_bounds__(kAmaxThreads) void k_amax_part(const uint4* __restr
   for (; i + 7 * stride < n4; i += 8 * stride) {
     uint4 v[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = src[i + k * stride];
+    for (int k = 0; k < 8; ++k) v[k] = load_stream(src + i + k * stride);
 #pragma unroll
     for (int k = 0; k < 8; ++k) m = max(m, max4(v[k]));
   }
-  for (; i < n4; i += stride) m = max(m, max4(src[i]));
+  for (; i < n4; i += stride) m = max(m, max4(load_stream(src + i)));
   for (int off = 32; off > 0; off >>= 1) m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), off)));
   __shared__ uint32_t wmax[kAmaxThreads / 64];
   if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
@@ -202,8 +215,8 @@ struct RowIn {
 #pragma unroll
       for (int j = 0; j < 8; ++j) x[j] = src[rowbase + j * ad.col];
     } else {
-      const float4 v0 = *reinterpret_cast<const float4*>(src + rowbase);
-      const float4 v1 = *reinterpret_cast<const float4*>(src + rowbase + 4);
+      const float4 v0 = load_stream(src + rowbase);
+      const float4 v1 = load_stream(src + rowbase + 4);
       x[0] = v0.x; x[1] = v0.y; x[2] = v0.z; x[3] = v0.w;
       x[4] = v1.x; x[5] = v1.y; x[6] = v1.z; x[7] = v1.w;
     }
@@ -386,6 +399,209 @@ __global__ __launch_bounds__(ONE ? kOneThreads : kThreads) void k_quantize(const
   }
 }
 
+// The bulk path for activations and gradients (N contiguous): 32 blocks per
+// wave iteration, two lanes per block.  Lane 2b + h holds columns 4h..4h+3
+// of the 8 rows of block b, so each of a wave's 8 row loads reads 32
+// consecutive 16-byte pieces (1 KiB contiguous when N >= 256, 512-byte runs
+// at N = 128), twice the rows in flight of the row-per-lane kernel above.
+// After the codes are formed, the lanes of a pair swap half rows so that
+// lane h holds whole rows 4h..4h+3 and stores them (half a block) as one
+// contiguous run.  The arithmetic per element and per block is that of
+// k_quantize, so the codes are identical.
+constexpr int kWideBlocks = 32;
+template <int FMT, int ROLE, bool SR>
+__global__ __launch_bounds__(kThreads) void k_quantize_wide(const float* __restrict__ src,
+                                                            uint8_t* __restrict__ codes,
+                                                            uint8_t* __restrict__ scales,
+                                                            float* __restrict__ tensor_scale,
+                                                            float* __restrict__ amax,
+                                                            const uint32_t* __restrict__ part, int nparts,
+                                                            QDims d, uint64_t seed) {
+  static_assert(ROLE != MX_ROLE_WEIGHT, "rows of 8 contiguous elements");
+  using F = Fmt<FMT>;
+  constexpr int B = F::BITS;
+  const int lane = threadIdx.x & 63, h = lane & 1;
+  const int64_t ngroups = (d.nblocks + kWideBlocks - 1) / kWideBlocks;
+  const int64_t gstride = static_cast<int64_t>(gridDim.x) * kGroupsPerWG;
+  int64_t grp = static_cast<int64_t>(blockIdx.x) * kGroupsPerWG + (threadIdx.x >> 6);
+  const int64_t row = d.d3;  // N
+  struct Rows {
+    float4 x[8];  // columns 4h..4h+3 of rows 0..7
+    int64_t base;  // source offset of column 4h of row 0
+  };
+  auto load = [&](Rows& R, int64_t g) {
+    int64_t b = g * kWideBlocks + (lane >> 1);
+    b = b < d.nblocks ? b : 0;  // past the tensor: block 0, loaded, never stored
+    R.base = block_addr<ROLE>(d, b).base + 4 * h;
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+      R.x[r] = d.nblocks ? load_stream(src + R.base + r * row) : make_float4(0.f, 0.f, 0.f, 0.f);
+  };
+  Rows cur;
+  load(cur, grp);  // requested before the partials: the two loads overlap
+
+  uint32_t ab;
+  if (nparts >= 0) {
+    uint32_t m = 0;
+    for (int i = lane; i < nparts; i += 64) m = max(m, part[i]);
+    for (int off = 32; off > 0; off >>= 1) m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), off)));
+    ab = m;
+  } else {
+    ab = __float_as_uint(*amax) & 0x7FFFFFFFu;
+  }
+  const bool nonfinite = ab >= NONFINITE_BITS;
+  const float T = nonfinite ? __uint_as_float(0x7FC00000u) : __uint_as_float(ab) / (448.0f * F::MAXV);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    *tensor_scale = T;
+    if (nparts >= 0) *amax = __uint_as_float(ab);
+  }
+  const float den = F::MAXV * T;
+  const float y_den = 1.0f / den;
+  const bool den_ok = (den >= 0x1p-125f) & (den <= 0x1p125f);
+  const float thr_den = fmaxf(0x1p-100f, den * 0x1p-98f);
+
+  for (; grp < ngroups; grp += gstride) {
+    const int64_t blk = grp * kWideBlocks + (lane >> 1);
+    const bool valid = blk < d.nblocks;
+    Rows nxt;
+    load(nxt, grp + gstride);
+    uint32_t words[B];  // rows 4h..4h+3 of the block, packed
+    uint32_t bcode = 0x7F;  // T = NaN: scales 0x7F, codes 0
+#pragma unroll
+    for (int k = 0; k < B; ++k) words[k] = 0u;
+    if (!nonfinite) {
+      float am = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        am = fmaxf(fmaxf(am, fmaxf(fabsf(cur.x[r].x), fabsf(cur.x[r].y))),
+                   fmaxf(fabsf(cur.x[r].z), fabsf(cur.x[r].w)));
+      am = fmaxf(am, swap_pair(am));
+
+      float braw = div_by_recip(am, den, y_den);
+      if (!((T == 0.0f) | (den_ok & ((am == 0.0f) | (am >= thr_den))))) braw = am / den;
+      braw = (T == 0.0f) ? 0.0f : braw;
+      bcode = rne_e4m3_hw(braw);
+      const float dd = code_value<ScaleFmt>(bcode) * T;
+      const float y = 1.0f / dd;
+      const bool dd_ok = (dd >= 0x1p-125f) & (dd <= 0x1p125f);
+      const float thr = fmaxf(0x1p-100f, dd * 0x1p-98f);
+      float xs[32], v[32];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        xs[4 * r] = cur.x[r].x; xs[4 * r + 1] = cur.x[r].y;
+        xs[4 * r + 2] = cur.x[r].z; xs[4 * r + 3] = cur.x[r].w;
+      }
+      bool any_slow = false;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        const float ax = fabsf(xs[j]);
+        v[j] = div_by_recip(ax, dd, y);
+        any_slow |= (ax != 0.0f) & (ax < thr);
+      }
+      any_slow = (any_slow | !dd_ok) & (dd != 0.0f);
+      if (any_slow) {  // rare: tiny elements or an extreme block scale
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+          const float ax = fabsf(xs[j]);
+          if (!dd_ok | ((ax != 0.0f) & (ax < thr))) v[j] = ax / dd;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 32; ++j) v[j] = (dd == 0.0f) ? 0.0f : v[j];
+
+      // the 4 codes of each row of this lane, BITS each
+      uint32_t chunk[8];
+      if constexpr (!SR && (FMT == FMT_E2M1 || FMT == FMT_E4M3)) {
+        // hardware round to nearest even on copysign(min(v, max), x)
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          float sv[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) sv[j] = __builtin_copysignf(fminf(v[4 * r + j], F::MAXV), xs[4 * r + j]);
+          if constexpr (FMT == FMT_E2M1) {
+            uint32_t w = 0;
+            w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, sv[0], sv[1], 1.0f, 0);
+            w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, sv[2], sv[3], 1.0f, 1);
+            chunk[r] = w & 0xFFFFu;
+          } else {
+            short2v c = {0, 0};
+            c = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(c, sv[0], sv[1], 1.0f, false);
+            c = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(c, sv[2], sv[3], 1.0f, true);
+            chunk[r] = __builtin_bit_cast(uint32_t, c);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          float u[4];
+          if constexpr (SR) {
+            // elements base + r N + j; pairs from an even index
+            uint64_t gk = kGolden64 * (static_cast<uint64_t>((cur.base + r * row) >> 1) + 1ull);
+            sr_uniform_pair(seed, gk, u[0], u[1]);
+            sr_uniform_pair(seed, gk + kGolden64, u[2], u[3]);
+          }
+          uint32_t c = 0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            uint32_t mag;
+            if constexpr (SR) mag = sr_code<F>(v[4 * r + j], u[j]);
+            else mag = rne_code<F>(v[4 * r + j]);
+            const uint32_t code = F::SIGNED ? (mag | ((__float_as_uint(xs[4 * r + j]) >> 31) << F::SIGN)) : mag;
+            c |= code << (B * j);
+          }
+          chunk[r] = c;
+        }
+      }
+
+      // pair exchange: lane 0 of the pair keeps rows 0..3 and takes their
+      // columns 4..7 from lane 1, which keeps rows 4..7 and takes their
+      // columns 0..3
+      uint64_t rows4[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t recv = swap_pair(h ? chunk[r] : chunk[r + 4]);
+        const uint32_t lo = h ? recv : chunk[r];
+        const uint32_t hi = h ? chunk[r + 4] : recv;
+        rows4[r] = static_cast<uint64_t>(lo) | (static_cast<uint64_t>(hi) << (4 * B));
+      }
+      // 4 rows of 8 B bits, little-endian, into B words
+      uint64_t acc = 0;
+      int nb = 0, nw = 0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        acc |= rows4[r] << nb;
+        const uint64_t spill = (8 * B + nb > 64) ? (rows4[r] >> (64 - nb)) : 0u;
+        nb += 8 * B;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          if (nb >= 32) {
+            words[nw++] = static_cast<uint32_t>(acc);
+            acc = (acc >> 32) | (spill << 32);
+            nb -= 32;
+          }
+        }
+      }
+    }
+    if (valid) {
+      uint8_t* q = codes + blk * (8 * B) + h * (4 * B);
+      if constexpr (B == 4) {
+        *reinterpret_cast<uint4*>(q) = make_uint4(words[0], words[1], words[2], words[3]);
+      } else if constexpr (B == 8) {
+        reinterpret_cast<uint4*>(q)[0] = make_uint4(words[0], words[1], words[2], words[3]);
+        reinterpret_cast<uint4*>(q)[1] = make_uint4(words[4], words[5], words[6], words[7]);
+      } else if constexpr (B == 6) {
+#pragma unroll
+        for (int k = 0; k < 3; ++k) reinterpret_cast<uint2*>(q)[k] = make_uint2(words[2 * k], words[2 * k + 1]);
+      } else {
+#pragma unroll
+        for (int k = 0; k < B; ++k) reinterpret_cast<uint32_t*>(q)[k] = words[k];
+      }
+      if (h == 0) scales[blk] = static_cast<uint8_t>(bcode);
+    }
+    cur = nxt;
+  }
+}
+
 // One code row of a block as a 64-bit value (8 codes, BITS each).
 template <int FMT>
 __device__ __forceinline__ uint64_t load_row(const uint8_t* __restrict__ codes, int64_t blk, int r) {
@@ -502,6 +718,20 @@ void launch_q(const QDims& d, const float* src, const mx_qtensor* q, bool sr, ui
     else
       hipLaunchKernelGGL((k_quantize<FMT, ROLE, false, true>), dim3(1), dim3(kOneThreads), 0, s, src, codes,
                          q->scales, q->tensor_scale, q->amax, part, nparts, d, seed);
+    return;
+  }
+  if constexpr (ROLE != MX_ROLE_WEIGHT) {
+    // at least one workgroup, so that an empty tensor still publishes T
+    int64_t wgs = (d.nblocks + kWideBlocks * kGroupsPerWG - 1) / (kWideBlocks * kGroupsPerWG);
+    if (wgs > kQuantMaxWGs) wgs = kQuantMaxWGs;
+    if (wgs < 1) wgs = 1;
+    const dim3 grid(static_cast<unsigned>(wgs));
+    if (sr)
+      hipLaunchKernelGGL((k_quantize_wide<FMT, ROLE, true>), grid, dim3(kThreads), 0, s, src, codes, q->scales,
+                         q->tensor_scale, q->amax, part, nparts, d, seed);
+    else
+      hipLaunchKernelGGL((k_quantize_wide<FMT, ROLE, false>), grid, dim3(kThreads), 0, s, src, codes, q->scales,
+                         q->tensor_scale, q->amax, part, nparts, d, seed);
     return;
   }
   // at least one workgroup, so that an empty tensor still publishes T
