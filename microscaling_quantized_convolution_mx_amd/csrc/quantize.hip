@@ -662,6 +662,69 @@ __global__ __launch_bounds__(kThreads) void k_dequantize(const uint8_t* __restri
   }
 }
 
+// Activations and gradients, the layout of k_quantize_wide: two lanes per
+// block, lane 2b + h writing columns 4h..4h+3 of the 8 rows of block b, so
+// that each of a wave's 8 row stores covers 32 consecutive 16-byte pieces
+// (1 KiB contiguous when N >= 256).  Both lanes of a pair read the whole
+// block of codes (the same 64-byte segment).  Values as in k_dequantize.
+template <int FMT, int ROLE>
+__global__ __launch_bounds__(kThreads) void k_dequantize_wide(const uint8_t* __restrict__ codes,
+                                                              const uint8_t* __restrict__ scales,
+                                                              const float* __restrict__ tensor_scale,
+                                                              float* __restrict__ dst, QDims d) {
+  static_assert(ROLE != MX_ROLE_WEIGHT, "rows of 8 contiguous elements");
+  using F = Fmt<FMT>;
+  constexpr int B = F::BITS;
+  constexpr int NW = 2 * B;  // 32-bit words of a block (8 rows of 8 B bits)
+  const int h = threadIdx.x & 1;
+  const int64_t blk = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) >> 1;
+  if (blk >= d.nblocks) return;
+  uint32_t w[NW];
+  const uint8_t* q = codes + blk * (8 * B);
+  if constexpr (NW % 4 == 0) {
+#pragma unroll
+    for (int k = 0; k < NW / 4; ++k) {
+      const uint4 v = reinterpret_cast<const uint4*>(q)[k];
+      w[4 * k] = v.x; w[4 * k + 1] = v.y; w[4 * k + 2] = v.z; w[4 * k + 3] = v.w;
+    }
+  } else if constexpr (NW % 2 == 0 && (8 * B) % 8 == 0) {
+#pragma unroll
+    for (int k = 0; k < NW / 2; ++k) {
+      const uint2 v = reinterpret_cast<const uint2*>(q)[k];
+      w[2 * k] = v.x; w[2 * k + 1] = v.y;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < NW; ++k) w[k] = reinterpret_cast<const uint32_t*>(q)[k];
+  }
+  // 4B bits at a compile-time bit offset o of the block
+  auto field = [&](int o) -> uint32_t {
+    const int k = o >> 5, sh = o & 31;
+    const uint64_t v = static_cast<uint64_t>(w[k]) | (k + 1 < NW ? static_cast<uint64_t>(w[k + 1]) << 32 : 0ull);
+    return static_cast<uint32_t>(v >> sh) & static_cast<uint32_t>((1ull << (4 * B)) - 1ull);
+  };
+  const uint32_t sb = scales[blk];
+  const float Bv = (sb == 0x7Fu) ? __uint_as_float(0x7FC00000u) : code_value<ScaleFmt>(sb);
+  const float T = *tensor_scale;
+  const int64_t base = block_addr<ROLE>(d, blk).base + 4 * h;
+  const int64_t row = d.d3;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const uint32_t f = h ? field(8 * B * r + 4 * B) : field(8 * B * r);
+    float o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t code = (f >> (B * j)) & ((1u << B) - 1u);
+      const float g = code_value<F>(code & ((1u << F::SIGN) - 1u));
+      const float gb = g * Bv;
+      float v = gb * T;
+      if (F::SIGNED && ((code >> F::SIGN) & 1u)) v = -v;
+      o[j] = v;
+    }
+    *reinterpret_cast<float4*>(dst + base + r * row) = make_float4(o[0], o[1], o[2], o[3]);
+  }
+}
+
 // Explicit channel-batch-first im2col, the baseline the paper compares
 // against (quantize after im2col, §III-C): X' [Ho][Wo][Kh][Kw][C][N] from X
 // [H][W][C][N], zero where a tap falls in the padding.  Each (ho, wo, kh, kw)
@@ -757,6 +820,13 @@ void launch_q_role(mx_role role, const QDims& d, const float* src, const mx_qten
 
 template <int FMT, int ROLE>
 void launch_dq(const QDims& d, const mx_qtensor* q, float* dst, hipStream_t s) {
+  if constexpr (ROLE != MX_ROLE_WEIGHT) {
+    const int64_t wgs = (d.nblocks * 2 + kThreads - 1) / kThreads;
+    if (wgs == 0) return;
+    hipLaunchKernelGGL((k_dequantize_wide<FMT, ROLE>), dim3(static_cast<unsigned>(wgs)), dim3(kThreads), 0, s,
+                       static_cast<const uint8_t*>(q->codes), q->scales, q->tensor_scale, dst, d);
+    return;
+  }
   const int64_t wgs = (d.nblocks * 8 + kThreads - 1) / kThreads;
   if (wgs == 0) return;
   hipLaunchKernelGGL((k_dequantize<FMT, ROLE>), dim3(static_cast<unsigned>(wgs)), dim3(kThreads), 0, s,
