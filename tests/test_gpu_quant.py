@@ -21,7 +21,21 @@ SHAPES = [
     (8, 16, 32, 9, 7, 3, 2, 1),
     (264, 8, 8, 4, 4, 1, 1, 0),
     (16, 64, 136, 6, 5, 3, 1, 0),
+    (72, 16, 24, 9, 8, 3, 1, 1),    # X 1296 and dY 1944 blocks: the bulk path
 ]
+
+
+# Tensors above the quantizer's one-workgroup limit (1024 blocks) take the
+# bulk path (an amax pass, then two lanes per block); the edge cases below
+# run at both sizes.  BULK: H, W, C, N with 1296 blocks, N/8 = 9 blocks per
+# channel row, so the 32-block groups of a wave straddle positions.
+BULK_BLOCKS = 1100
+BULK = (9, 8, 16, 72)
+
+
+def bulk_desc(fmt):
+    h, w, c, n = BULK
+    return mx.desc(n, c, c, h, w, 1, 1, elem_fmt=fmt)
 
 
 def src_for(d, role, seed, dist="normal", sigma=1.0):
@@ -77,19 +91,22 @@ def test_quantize_extreme_magnitudes(fmt):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-def test_quantize_grid_ties(fmt):
+@pytest.mark.parametrize("min_blocks", [0, BULK_BLOCKS])
+def test_quantize_grid_ties(fmt, min_blocks):
     # T = 1 (amax = 448 * max) and every other block holds the element
     # maximum, so its scale is exactly 1 and the grid midpoints placed in it
     # are exact ties after scaling: both sides must pick the even code
     grid = O.fmt_grid(ofmt(fmt))
     mids = (grid[1:] + grid[:-1]) / 2
     vals = np.concatenate([mids, -mids, grid[:-1]]).astype(np.float32)
-    npos = -(-vals.size // 63) + 1
+    nchunks = -(-vals.size // 63)
+    npos = max(nchunks + 1, min_blocks)
     d = mx.desc(8, 8, 8, 1, npos, 1, 1, elem_fmt=fmt)
     x = np.zeros((1, npos, 8, 8), dtype=np.float32)
     for p in range(npos - 1):
         blk = x[0, p].reshape(-1)
-        chunk = vals[p * 63:(p + 1) * 63]
+        c = p % nchunks
+        chunk = vals[c * 63:(c + 1) * 63]
         blk[0] = grid[-1]
         blk[1:1 + chunk.size] = chunk
     x[0, npos - 1, 7, 7] = 448.0 * grid[-1]
@@ -101,6 +118,56 @@ def test_quantize_grid_ties(fmt):
     for rnd in (mx.MX_SR,):
         assert_quant_equal(gpu_quantize(d, mx.MX_ROLE_GRAD, xt, rnd, 11),
                            oracle_quantize(d, mx.MX_ROLE_GRAD, xt, rnd, 11))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_quantize_extreme_magnitudes_bulk(fmt):
+    d = bulk_desc(fmt)
+    say("quantize extremes bulk", fmt)
+    g = torch.Generator().manual_seed(6)
+    x = torch.randn(*BULK, generator=g)
+    x[0, 0] *= 1e-38           # whole positions of fp32 subnormals, tiny and huge values
+    x[3, 5] *= 1e-30
+    x[8, 7, :8] *= 3e30        # the last position: its first channel block only
+    x[4, 4, 0, :4] = torch.tensor([0.0, -0.0, 1e-45, -1e-45])
+    for role, rnd in ((mx.MX_ROLE_ACT, mx.MX_RNE), (mx.MX_ROLE_GRAD, mx.MX_SR), (mx.MX_ROLE_GRAD, mx.MX_RNE)):
+        assert_quant_equal(gpu_quantize(d, role, x, rnd, seed=9), oracle_quantize(d, role, x, rnd, seed=9))
+    # without the huge values: blocks of tiny elements next to normal ones
+    xm = x.clone()
+    xm[8, 7] = torch.randn(16, 72, generator=g)
+    for role, rnd in ((mx.MX_ROLE_ACT, mx.MX_RNE), (mx.MX_ROLE_GRAD, mx.MX_SR)):
+        assert_quant_equal(gpu_quantize(d, role, xm, rnd, seed=4), oracle_quantize(d, role, xm, rnd, seed=4))
+    xs = xm * 1e-8             # T itself subnormal
+    assert_quant_equal(gpu_quantize(d, mx.MX_ROLE_ACT, xs), oracle_quantize(d, mx.MX_ROLE_ACT, xs))
+
+
+@pytest.mark.parametrize("bad", [float("nan"), float("inf"), float("-inf")])
+def test_quantize_nonfinite_bulk(bad):
+    d = bulk_desc(mx.MX_E2M1)
+    x = WL.gen_tensor(BULK, "normal", 13)
+    x[6, 2, 11, 70] = bad
+    say("quantize nonfinite bulk", bad)
+    for role, rnd in ((mx.MX_ROLE_ACT, mx.MX_RNE), (mx.MX_ROLE_GRAD, mx.MX_SR)):
+        gq = gpu_quantize(d, role, x, rnd, 2)
+        assert_quant_equal(gq, oracle_quantize(d, role, x, rnd, 2))
+        assert np.isnan(gq.tensor_scale.item())
+        assert (gq.scales[:gq.nblocks] == 0x7F).all()
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_quantize_zero_and_given_amax_bulk(fmt):
+    d = bulk_desc(fmt)
+    say("quantize zero / given amax bulk", fmt)
+    z = torch.zeros(*BULK)
+    gq = gpu_quantize(d, mx.MX_ROLE_GRAD, z, mx.MX_SR, 1)
+    assert_quant_equal(gq, oracle_quantize(d, mx.MX_ROLE_GRAD, z, mx.MX_SR, 1))
+    assert gq.tensor_scale.item() == 0.0
+    x = WL.gen_tensor(BULK, "normal", 21)
+    true_amax = float(x.abs().max())
+    for a in (true_amax * 3.0, true_amax * 0.25):
+        assert_quant_equal(gpu_quantize(d, mx.MX_ROLE_ACT, x, amax=a),
+                           oracle_quantize(d, mx.MX_ROLE_ACT, x, amax=np.float32(a)), f"amax {a}")
+    assert np.isnan(gpu_quantize(d, mx.MX_ROLE_ACT, x, amax=float("nan")).tensor_scale.item())
 
 
 @pytest.mark.parametrize("bad", [float("nan"), float("inf"), float("-inf")])
