@@ -225,11 +225,11 @@ struct RowIn {
 
 // ONE: a single 1024-thread workgroup that also computes the amax (nparts
 // >= 0) over the whole tensor first, for tensors of at most kOneBlocks
-// blocks (up to 16 loads of 16 bytes per thread, then 8 groups of 8 blocks
-// per wave): one launch instead of two, which is what small tensors take
-// (an amax pass of its own costs a launch and a memory round trip).
+// blocks (up to 4 loads of 16 bytes per thread): one launch instead of two.
+// Beyond 256 blocks one workgroup is slower than the two launches (weights,
+// whose rows are strided gathers, most of all).
 constexpr int kOneThreads = 1024;
-constexpr int64_t kOneBlocks = 1024;
+constexpr int64_t kOneBlocks = 256;  // at most 2 groups per wave
 template <int FMT, int ROLE, bool SR, bool ONE>
 __global__ __launch_bounds__(ONE ? kOneThreads : kThreads) void k_quantize(const float* __restrict__ src,
                                                        uint8_t* __restrict__ codes,

@@ -25,7 +25,7 @@ SHAPES = [
 ]
 
 
-# Tensors above the quantizer's one-workgroup limit (1024 blocks) take the
+# Tensors above the quantizer's one-workgroup limit (256 blocks) take the
 # bulk path (an amax pass, then two lanes per block); the edge cases below
 # run at both sizes.  BULK: H, W, C, N with 1296 blocks, N/8 = 9 blocks per
 # channel row, so the 32-block groups of a wave straddle positions.
