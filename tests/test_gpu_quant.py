@@ -141,6 +141,40 @@ def test_quantize_extreme_magnitudes_bulk(fmt):
     assert_quant_equal(gpu_quantize(d, mx.MX_ROLE_ACT, xs), oracle_quantize(d, mx.MX_ROLE_ACT, xs))
 
 
+@pytest.mark.parametrize("size", ["small", "bulk"])
+def test_quantize_sr_thresholds(size):
+    # T = 1 (amax 448 * 6) and a 6 in every other block (scale exactly 1), so
+    # that v = |x| exactly; every other element sits on, one representable
+    # step below or one step above its own stochastic-rounding threshold u
+    # (the oracle's uniform for that element), in each part of the E2M1 grid
+    # (below 0.5, [0.5, 1), [1, 1.5), [2, 3), [4, 6)).  Round up iff frac > u
+    # (MicroQonv, arXiv 2609.28358, §III-A; the rule of the oracle): both
+    # sides must take the same decision at the threshold itself.
+    shape = (2, 2, 16, 16) if size == "small" else BULK
+    h, w, c, n = shape
+    d = mx.desc(n, c, c, h, w, 1, 1, elem_fmt=mx.MX_E2M1)
+    seed = 77
+    u = np.array([O.sr_uniform(seed, i) for i in range(h * w * c * n)], np.float64).reshape(shape)
+    rng = np.random.default_rng(5 if size == "small" else 6)
+    region = rng.integers(0, 5, shape)
+    lo = np.array([0.0, 0.5, 1.0, 2.0, 4.0])[region]
+    step = np.array([0.5, 0.5, 0.5, 1.0, 2.0])[region]
+    res = np.array([2.0 ** -24, 2.0 ** -23, 2.0 ** -22, 2.0 ** -22, 2.0 ** -22])[region]  # finest frac there
+    frac = np.clip(np.floor(u / res) * res + rng.integers(-1, 2, shape) * res, 0.0, 1.0 - res)
+    v = lo + frac * step
+    assert np.array_equal(v.astype(np.float32).astype(np.float64), v)  # every value exact in fp32
+    x = (v * np.where(rng.random(shape) < 0.5, -1.0, 1.0)).astype(np.float32)
+    x[:, :, ::8, ::8] = 6.0
+    x[0, 0, 0, 0] = 448.0 * 6.0
+    ties = np.sum((frac == u) & (u > 0))
+    assert ties > (5 if size == "small" else 500), ties   # elements exactly on their threshold
+    say("quantize SR thresholds", size)
+    xt = torch.from_numpy(x)
+    oq = oracle_quantize(d, mx.MX_ROLE_GRAD, xt, mx.MX_SR, seed)
+    assert oq.t == 1.0 and np.sum(oq.scales != 0x38) == 1
+    assert_quant_equal(gpu_quantize(d, mx.MX_ROLE_GRAD, xt, mx.MX_SR, seed), oq)
+
+
 @pytest.mark.parametrize("bad", [float("nan"), float("inf"), float("-inf")])
 def test_quantize_nonfinite_bulk(bad):
     d = bulk_desc(mx.MX_E2M1)
