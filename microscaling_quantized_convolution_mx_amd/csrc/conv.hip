@@ -764,6 +764,7 @@ hipError_t launch_conv_fwd(const Geom& g, const mx_qtensor* wq, const mx_qtensor
   p.a_codes = static_cast<const uint8_t*>(wq->codes); p.a_scales = wq->scales; p.a_t = wq->tensor_scale;
   p.b_codes = static_cast<const uint8_t*>(xq->codes); p.b_scales = xq->scales; p.b_t = xq->tensor_scale;
   p.out = y;
+  p.stream_out = static_cast<int64_t>(g.ho) * g.wo * g.c_out * g.n * 4 > static_cast<int64_t>(kStreamOutBytes);
   p.amax_out = reinterpret_cast<uint32_t*>(y_amax);
   int64_t nslots = 0;
   if (g.block == 32) {
@@ -790,6 +791,7 @@ hipError_t launch_conv_dgrad(const Geom& g, const mx_qtensor* wq, const mx_qtens
   p.a_codes = static_cast<const uint8_t*>(wq->codes); p.a_scales = wq->scales; p.a_t = wq->tensor_scale;
   p.b_codes = static_cast<const uint8_t*>(dyq->codes); p.b_scales = dyq->scales; p.b_t = dyq->tensor_scale;
   p.out = dx;
+  p.stream_out = static_cast<int64_t>(g.h) * g.w * g.c_in * g.n * 4 > static_cast<int64_t>(kStreamOutBytes);
   if (p.ncb == 0) return hipSuccess;
   if (g.block == 32) {
     launch_mx(OP_DGRAD, p, dim3((p.ncb * 8 + 255) / 256, (p.M + 255) / 256, g.sh * g.sw), s);

@@ -58,6 +58,7 @@ struct ConvParams {
   const float* b_t;
   float* out;
   uint32_t* amax_out;  // fwd: per-wave max |y| slots (slot 1 + global wave index; nullptr: not wanted)
+  int32_t stream_out;  // fwd / dgrad: write the output with nontemporal stores (outputs above kStreamOutBytes)
 };
 
 // Tile of one launch: MT x NT outputs, waves along M, waves, k-blocks per stage.
@@ -449,8 +450,12 @@ __device__ __forceinline__ void store_tile(const ConvParams& p, const TileCtx<OP
   else row_stride = p.n;
 
   uint32_t ymax = 0;  // fwd: max over the written outputs of their sign-cleared bits
+  // the weight gradient's split partials are read back at once by the
+  // reduce, so they always stay cacheable
+  const bool stream = OP != OP_WGRAD && p.stream_out;
   auto put = [&](float* q, float v) {
-    *q = v;
+    if (stream) __builtin_nontemporal_store(v, q);
+    else *q = v;
     if constexpr (OP == OP_FWD) ymax = max(ymax, __float_as_uint(v) & 0x7FFFFFFFu);
   };
 #pragma unroll

@@ -715,7 +715,7 @@ __global__ __launch_bounds__(kThreads) void k_dequantize(const uint8_t* __restri
 // that each of a wave's 8 row stores covers 32 consecutive 16-byte pieces
 // (1 KiB contiguous when N >= 256).  Both lanes of a pair read the whole
 // block of codes (the same 64-byte segment).  Values as in k_dequantize.
-template <int FMT, int ROLE>
+template <int FMT, int ROLE, bool STREAM>
 __global__ __launch_bounds__(kThreads) void k_dequantize_wide(const uint8_t* __restrict__ codes,
                                                               const uint8_t* __restrict__ scales,
                                                               const float* __restrict__ tensor_scale,
@@ -769,7 +769,11 @@ __global__ __launch_bounds__(kThreads) void k_dequantize_wide(const uint8_t* __r
       if (F::SIGNED && ((code >> F::SIGN) & 1u)) v = -v;
       o[j] = v;
     }
-    *reinterpret_cast<float4*>(dst + base + r * row) = make_float4(o[0], o[1], o[2], o[3]);
+    typedef float f32x4v __attribute__((ext_vector_type(4)));
+    const f32x4v ov = {o[0], o[1], o[2], o[3]};
+    f32x4v* q = reinterpret_cast<f32x4v*>(dst + base + r * row);
+    if constexpr (STREAM) __builtin_nontemporal_store(ov, q);  // outputs above kStreamOutBytes
+    else *q = ov;
   }
 }
 
@@ -871,8 +875,13 @@ void launch_dq(const QDims& d, const mx_qtensor* q, float* dst, hipStream_t s) {
   if constexpr (ROLE != MX_ROLE_WEIGHT) {
     const int64_t wgs = (d.nblocks * 2 + kThreads - 1) / kThreads;
     if (wgs == 0) return;
-    hipLaunchKernelGGL((k_dequantize_wide<FMT, ROLE>), dim3(static_cast<unsigned>(wgs)), dim3(kThreads), 0, s,
-                       static_cast<const uint8_t*>(q->codes), q->scales, q->tensor_scale, dst, d);
+    const auto* codes = static_cast<const uint8_t*>(q->codes);
+    if (static_cast<size_t>(d.nblocks) * 64 * sizeof(float) > kStreamOutBytes)
+      hipLaunchKernelGGL((k_dequantize_wide<FMT, ROLE, true>), dim3(static_cast<unsigned>(wgs)), dim3(kThreads), 0, s,
+                         codes, q->scales, q->tensor_scale, dst, d);
+    else
+      hipLaunchKernelGGL((k_dequantize_wide<FMT, ROLE, false>), dim3(static_cast<unsigned>(wgs)), dim3(kThreads), 0, s,
+                         codes, q->scales, q->tensor_scale, dst, d);
     return;
   }
   const int64_t wgs = (d.nblocks * 8 + kThreads - 1) / kThreads;
