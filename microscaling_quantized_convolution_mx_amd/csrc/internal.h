@@ -25,13 +25,13 @@ int64_t role_numel(const Geom& g, mx_role role);
 int64_t role_nblocks(const Geom& g, mx_role role);
 int code_bits(int fmt);
 
-// The scales buffer of a quantized tensor holds the block scales (one byte
-// per block), padded to 16 bytes, then the quantizer's amax partials: one
 // fp32 outputs larger than this (the 256 MB last-level cache of the GPU)
 // are written with nontemporal stores: they stream past the cache, which
 // cannot hold them for a consumer anyway.  Smaller outputs stay cacheable.
 constexpr size_t kStreamOutBytes = size_t{256} << 20;
 
+// The scales buffer of a quantized tensor holds the block scales (one byte
+// per block), padded to 16 bytes, then the quantizer's amax partials: one
 // 32-bit max per workgroup of the amax pass, at most kAmaxMaxPartials.
 constexpr int kAmaxMaxPartials = 512;
 inline int64_t scale_tail_offset(int64_t nblocks) { return (nblocks + 15) & ~static_cast<int64_t>(15); }
