@@ -7,16 +7,17 @@
 // the tensor amax and an E4M3 per-block scale (§III-A).
 //
 // Two kernels per tensor, no atomics:
-//   k_amax_part  each workgroup writes the max |x| of its grid-stride share
-//                as one 32-bit partial into a scratch tail behind the block
-//                scales (the scales buffer is sized for it);
-//   k_quantize   every wave reduces the partials to the tensor amax and T,
-//                then quantizes 8 blocks per iteration (the next 8 already
-//                in flight), 8 lanes per block
-//                (lane = block row: 8 consecutive batch elements, 32 bytes,
-//                for activations and gradients).  The block amax is a DPP
-//                max across the 8 lanes; each lane packs and stores its own
-//                code row, so a wave writes whole contiguous runs of blocks.
+//   k_amax_part       each workgroup writes the max |x| of its grid-stride
+//                     share as one 32-bit partial into a scratch tail behind
+//                     the block scales (the scales buffer is sized for it);
+//   k_quantize_wide   activations and gradients: every wave reduces the
+//                     partials to the tensor amax and T, then quantizes 32
+//                     blocks per iteration (the next 32 in flight), two lanes
+//                     per block, each row load of a wave 1 KiB contiguous;
+//   k_quantize        weights (strided rows): the same arithmetic with one
+//                     lane per block row, 8 blocks per wave iteration.
+// Tensors of at most kOneBlocks blocks take k_quantize in a single
+// workgroup that computes the amax itself: one launch.
 #include "internal.h"
 #include "mx_formats.h"
 
@@ -612,19 +613,21 @@ __global__ __launch_bounds__(kThreads) void k_quantize_wide(const float* __restr
         const uint32_t hi = h ? chunk[r + 4] : recv;
         rows4[r] = static_cast<uint64_t>(lo) | (static_cast<uint64_t>(hi) << (4 * B));
       }
-      // 4 rows of 8 B bits, little-endian, into B words
+      // 4 rows of 8 B bits, little-endian, into B words.  The bits still
+      // pending when a row is added (0 for B = 4 and 8, 0 or 16 for B = 6,
+      // 0, 8, 16 or 24 for B = 3) plus the row never exceed 64.
+      static_assert(B == 3 || B == 4 || B == 6 || B == 8, "code widths of the formats");
       uint64_t acc = 0;
       int nb = 0, nw = 0;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         acc |= rows4[r] << nb;
-        const uint64_t spill = (8 * B + nb > 64) ? (rows4[r] >> (64 - nb)) : 0u;
         nb += 8 * B;
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
           if (nb >= 32) {
             words[nw++] = static_cast<uint32_t>(acc);
-            acc = (acc >> 32) | (spill << 32);
+            acc >>= 32;
             nb -= 32;
           }
         }
@@ -847,19 +850,19 @@ void launch_q(const QDims& d, const float* src, const mx_qtensor* q, bool sr, ui
     else
       hipLaunchKernelGGL((k_quantize_wide<FMT, ROLE, false>), grid, dim3(kThreads), 0, s, src, codes, q->scales,
                          q->tensor_scale, q->amax, part, nparts, d, seed);
-    return;
+  } else {
+    // weights: one lane per block row (the rows are strided gathers)
+    int64_t wgs = (d.nblocks + 8 * kGroupsPerWG - 1) / (8 * kGroupsPerWG);
+    if (wgs > kQuantMaxWGs) wgs = kQuantMaxWGs;
+    if (wgs < 1) wgs = 1;
+    const dim3 grid(static_cast<unsigned>(wgs));
+    if (sr)
+      hipLaunchKernelGGL((k_quantize<FMT, ROLE, true, false>), grid, dim3(kThreads), 0, s, src, codes, q->scales,
+                         q->tensor_scale, q->amax, part, nparts, d, seed);
+    else
+      hipLaunchKernelGGL((k_quantize<FMT, ROLE, false, false>), grid, dim3(kThreads), 0, s, src, codes, q->scales,
+                         q->tensor_scale, q->amax, part, nparts, d, seed);
   }
-  // at least one workgroup, so that an empty tensor still publishes T
-  int64_t wgs = (d.nblocks + 8 * kGroupsPerWG - 1) / (8 * kGroupsPerWG);
-  if (wgs > kQuantMaxWGs) wgs = kQuantMaxWGs;
-  if (wgs < 1) wgs = 1;
-  const dim3 grid(static_cast<unsigned>(wgs));
-  if (sr)
-    hipLaunchKernelGGL((k_quantize<FMT, ROLE, true, false>), grid, dim3(kThreads), 0, s, src, codes, q->scales,
-                       q->tensor_scale, q->amax, part, nparts, d, seed);
-  else
-    hipLaunchKernelGGL((k_quantize<FMT, ROLE, false, false>), grid, dim3(kThreads), 0, s, src, codes, q->scales,
-                       q->tensor_scale, q->amax, part, nparts, d, seed);
 }
 
 template <int FMT>
