@@ -718,17 +718,33 @@ WgradPlan wgrad_plan(const Geom& g) {
   return {t, static_cast<int>(splits)};
 }
 
-// Weight gradient on E8M0 32x32 blocks: 256x256 tiles, K steps of 128; about
-// one round of workgroups (1024 waves) with at least 4 K steps per split.
+// Weight gradient on E8M0 32x32 blocks: K steps of 128, about one round of
+// workgroups with at least 4 K steps per split.
+// E8M0 GEMM tile.  The 256x256 tile (one workgroup per CU) reuses each
+// operand block most; the 128x128 tile runs two workgroups per CU, so one
+// workgroup's barrier and load waits are covered by the other's MFMAs, and
+// wastes less on 64- and 128-row GEMMs.  256 only where M > 128 and the
+// launch still has about four workgroups per CU (fwd, dgrad: zdim = stride
+// phases), or for the weight gradient (zdim = K steps) one full round with
+// the largest K split.
+int mx_tile(int op, int64_t M, int64_t ncols, int64_t zdim) {
+  if (M <= 128) return 128;
+  const int64_t tiles256 = ((M + 255) / 256) * ((ncols + 255) / 256);
+  if (op == OP_WGRAD) return tiles256 * (zdim / 4) >= 256 ? 256 : 128;
+  return tiles256 * zdim >= 1024 ? 256 : 128;
+}
+
 WgradPlan wgrad_plan_mx(const Geom& g) {
   const int64_t ksteps = (static_cast<int64_t>(g.ho) * g.wo * (g.n / 32) + kMxStepBlocks - 1) / kMxStepBlocks;
+  const int T = mx_tile(OP_WGRAD, g.c_out, static_cast<int64_t>(g.k_h) * g.k_w * g.c_in, ksteps);
   const int64_t ncol = static_cast<int64_t>(g.k_h) * g.k_w * g.c_in;
-  const int64_t tiles = ((g.c_out + 255) / 256) * ((ncol + 255) / 256);
-  int64_t splits = (1024 / 4) / tiles;
+  const int64_t tiles = ((g.c_out + T - 1) / T) * ((ncol + T - 1) / T);
+  // about one round of workgroups: one per CU for the 256 tile, two for 128
+  int64_t splits = (T == 256 ? 256 : 512) / tiles;
   if (splits > ksteps / 4) splits = ksteps / 4;
   if (splits < 1) splits = 1;
   if (splits > 65535) splits = 65535;
-  return {Tile{256, 256, 2, 4, 4}, static_cast<int>(splits)};
+  return {Tile{T, T, 2, 4, 4}, static_cast<int>(splits)};
 }
 
 // Forward launch geometry: tile, grid and waves per workgroup.
@@ -768,7 +784,8 @@ hipError_t launch_conv_fwd(const Geom& g, const mx_qtensor* wq, const mx_qtensor
   p.amax_out = reinterpret_cast<uint32_t*>(y_amax);
   int64_t nslots = 0;
   if (g.block == 32) {
-    if (p.ncb > 0) launch_mx(OP_FWD, p, dim3((p.ncb * 8 + 255) / 256, (p.M + 255) / 256, 1), s);
+    const int T = mx_tile(OP_FWD, p.M, static_cast<int64_t>(p.ncb) * 8, 1);
+    if (p.ncb > 0) launch_mx(OP_FWD, T, p, dim3((p.ncb * 8 + T - 1) / T, (p.M + T - 1) / T, 1), s);
     return hipGetLastError();
   }
   if (p.ncb > 0) {
@@ -794,7 +811,8 @@ hipError_t launch_conv_dgrad(const Geom& g, const mx_qtensor* wq, const mx_qtens
   p.stream_out = static_cast<int64_t>(g.h) * g.w * g.c_in * g.n * 4 > static_cast<int64_t>(kStreamOutBytes);
   if (p.ncb == 0) return hipSuccess;
   if (g.block == 32) {
-    launch_mx(OP_DGRAD, p, dim3((p.ncb * 8 + 255) / 256, (p.M + 255) / 256, g.sh * g.sw), s);
+    const int T = mx_tile(OP_DGRAD, p.M, static_cast<int64_t>(p.ncb) * 8, g.sh * g.sw);
+    launch_mx(OP_DGRAD, T, p, dim3((p.ncb * 8 + T - 1) / T, (p.M + T - 1) / T, g.sh * g.sw), s);
     return hipGetLastError();
   }
   const Tile t = pick_tile(p.M, static_cast<int64_t>(p.ncb) * 8, g.sh * g.sw, g.fmt);
@@ -825,7 +843,7 @@ hipError_t launch_conv_wgrad(const Geom& g, const mx_qtensor* dyq, const mx_qten
   p.b_codes = static_cast<const uint8_t*>(xq->codes); p.b_scales = xq->scales; p.b_t = xq->tensor_scale;
   p.out = static_cast<float*>(workspace);
   dim3 grid((p.ncol + pl.t.nt - 1) / pl.t.nt, (p.M + pl.t.mt - 1) / pl.t.mt, pl.splits);
-  if (mxb) launch_mx(OP_WGRAD, p, grid, s);
+  if (mxb) launch_mx(OP_WGRAD, pl.t.mt, p, grid, s);
   else if (!launch_op<OP_WGRAD>(p, g.fmt, g.afmt, pl.t, grid, s)) return hipErrorNotSupported;
   // ncol = Kh*Kw*C_in is a multiple of 8: whole quads of outputs
   const int64_t quads = static_cast<int64_t>(p.M) * p.ncol / 4;

@@ -73,10 +73,10 @@ struct Tile {
 bool launch_mixed(int op, const ConvParams& p, int fmt_a, int fmt_b, const Tile& t, dim3 grid, hipStream_t s);
 
 // Launches the E8M0 32x32-block GEMM on the scaled FP4 MFMA (defined in
-// conv_mx.hip): 256x256 tiles, the grid as for the generic kernel; for the
-// weight gradient p.ks_split counts its K steps (kMxStepBlocks 32-blocks
-// each) per split.
-void launch_mx(int op, const ConvParams& p, dim3 grid, hipStream_t s);
+// conv_mx.hip): tile x tile outputs per workgroup (tile 256 or 128), the
+// grid as for the generic kernel; for the weight gradient p.ks_split counts
+// its K steps (kMxStepBlocks 32-blocks each) per split.
+void launch_mx(int op, int tile, const ConvParams& p, dim3 grid, hipStream_t s);
 // 32-blocks along K per step of that kernel (each row / column block of a
 // tile stages this many blocks per step)
 constexpr int kMxStepBlocks = 4;

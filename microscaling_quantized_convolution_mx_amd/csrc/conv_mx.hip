@@ -34,17 +34,28 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x2v __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i32x2v lds_i32x2v;
 
-constexpr int kKB = kMxStepBlocks;              // 32-blocks along K per step
-constexpr int kMxB = 512;                       // bytes of one 32x32 E2M1 block
-constexpr int kOpnd = 8 * kKB * kMxB;           // one operand of a stage: 8 line blocks x kKB k-blocks
-constexpr int kStage = 2 * kOpnd + 2 * 8 * kKB; // codes of A and B, then scales [A: kKB x 8][B: kKB x 8]
-constexpr int kRows = 2 * 8 * kKB * 32 / 256;   // block rows each thread stages per step
+constexpr int kKB = kMxStepBlocks;  // 32-blocks along K per step
+constexpr int kMxB = 512;           // bytes of one 32x32 E2M1 block
 
-template <int OP>
+template <int I>
+struct Idx {
+  static constexpr int value = I;
+};
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  [&]<int... I>(std::integer_sequence<int, I...>) { (f(Idx<I>{}), ...); }(std::make_integer_sequence<int, N>());
+}
+
+// TILE x TILE outputs per workgroup, 4 waves of TILE/2 x TILE/2.
+template <int OP, int TILE>
 __global__ __launch_bounds__(256) void k_conv_mx(const ConvParams p) {
-  constexpr int MT = 256, NT = 256, WM = 2;
-  constexpr int WTM = 128, WTN = 128, RM = 4, RN = 4;
-  static_assert(kRows == 8, "staging map below assumes 8 rows per thread");
+  constexpr int MT = TILE, NT = TILE, WM = 2;
+  constexpr int WTM = TILE / 2, WTN = TILE / 2, RM = TILE / 64, RN = TILE / 64;
+  constexpr int NLB = TILE / 32;                     // line blocks (32 lines) of an operand in the tile
+  constexpr int NQ = NLB / 2;                        // block rows a thread stages per operand and step
+  constexpr int kOpnd = NLB * kKB * kMxB;            // one operand of a stage: NLB line blocks x kKB k-blocks
+  constexpr int kStage = 2 * kOpnd + 2 * NLB * kKB;  // codes of A and B, then scales [A: kKB x NLB][B: kKB x NLB]
+  static_assert(RM == NQ && RN == NQ, "one staged row of each operand per MFMA row of a k-slice");
   // K runs along the stored rows of A for fwd and wgrad, of B for wgrad
   constexpr bool A_DIRECT = (OP != OP_DGRAD);
   constexpr bool B_DIRECT = (OP == OP_WGRAD);
@@ -78,25 +89,26 @@ __global__ __launch_bounds__(256) void k_conv_mx(const ConvParams p) {
   const int k_end = min(k_total, kKB * s_end);
 
   // Staging: thread t copies row (t & 31) of the blocks (operand, line block
-  // lb, k-block kb) with kb = (t >> 5) & 3 and lb = (t >> 7) + 2j, j = 0..3,
-  // for A (q = j) and for B (q = 4 + j).
+  // lb, k-block kb) with kb = (t >> 5) & 3 and lb = (t >> 7) + 2j,
+  // j = 0..NQ-1, for A (q = j) and for B (q = NQ + j).
   const int row = tid & 31, kb = (tid >> 5) & 3, lbq = tid >> 7;
-  auto q_lb = [&](int q) { return lbq + 2 * (q & 3); };
-  int gline[8];
-  bool gline_ok[8];
+  auto q_lb = [&](int q) { return lbq + 2 * (q % NQ); };
+  int gline[2 * NQ];
+  bool gline_ok[2 * NQ];
   // column-block geometry of B (fixed over the K loop)
-  int col_y[4] = {0, 0, 0, 0}, col_x[4] = {0, 0, 0, 0}, col_nb[4] = {0, 0, 0, 0}, col_cib[4] = {0, 0, 0, 0};
+  int col_y[NQ], col_x[NQ], col_nb[NQ], col_cib[NQ];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
+  for (int q = 0; q < 2 * NQ; ++q) {
     const int lb = q_lb(q);
-    if (q < 4) {
+    if (q < NQ) {
       gline[q] = rb0 + lb;
       gline_ok[q] = gline[q] < nrb;
     } else {
       const int cb = cb0 + lb;
       gline[q] = cb;
       gline_ok[q] = cb < ncb;
-      const int i = q - 4;
+      const int i = q - NQ;
+      col_y[i] = col_x[i] = col_nb[i] = col_cib[i] = 0;
       if constexpr (OP == OP_FWD) {
         const int pos = cb / nbk;
         col_nb[i] = cb - pos * nbk;
@@ -132,7 +144,7 @@ __global__ __launch_bounds__(256) void k_conv_mx(const ConvParams p) {
     const uint32_t a = div_b.div(outer);
     const uint32_t b = outer - a * div_b.d;
     const bool kin = k < k_end;
-    if (q < 4) {
+    if (q < NQ) {
       const uint32_t rb = static_cast<uint32_t>(gline[q]);
       if constexpr (OP == OP_FWD) blk = ((a * p.k_w + b) * cbo + rb) * cbi + inner;                 // W[tap][co][ci]
       else if constexpr (OP == OP_DGRAD)
@@ -140,7 +152,7 @@ __global__ __launch_bounds__(256) void k_conv_mx(const ConvParams p) {
       else blk = ((a * p.wo + b) * cbo + rb) * nbk + inner;                                            // dY[pos][co][n]
       return gline_ok[q] && kin;
     }
-    const int i = q - 4;
+    const int i = q - NQ;
     int y, x;
     bool inb;
     if constexpr (OP == OP_FWD) {
@@ -166,17 +178,17 @@ __global__ __launch_bounds__(256) void k_conv_mx(const ConvParams p) {
   // whether the block exists.  The mask is applied when the rows are
   // written to LDS, so that nothing waits for a load before then.
   struct Raw {
-    uint4 v[8];
-    uint32_t sc[8];
-    uint32_t mask[8];
+    uint4 v[2 * NQ];
+    uint32_t sc[2 * NQ];
+    uint32_t mask[2 * NQ];
   };
   Raw r0, r1;
   auto fetch_one = [&](Raw& raw, int step, int q) {
     const int k = kKB * step + kb;
     uint32_t blk = 0;
     const bool ok = locate(q, k, blk);
-    const uint8_t* codes = q < 4 ? p.a_codes : p.b_codes;
-    const uint8_t* scales = q < 4 ? p.a_scales : p.b_scales;
+    const uint8_t* codes = q < NQ ? p.a_codes : p.b_codes;
+    const uint8_t* scales = q < NQ ? p.a_scales : p.b_scales;
     const uint64_t b = ok ? blk : 0u;
     raw.v[q] = *reinterpret_cast<const uint4*>(codes + b * kMxB + row * 16);
     raw.sc[q] = scales[b];
@@ -184,20 +196,20 @@ __global__ __launch_bounds__(256) void k_conv_mx(const ConvParams p) {
   };
   auto fetch = [&](Raw& raw, int step) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) fetch_one(raw, step, q);
+    for (int q = 0; q < 2 * NQ; ++q) fetch_one(raw, step, q);
   };
   // stage layout: block (lb, kb) of an operand at (lb * kKB + kb) * kMxB;
-  // scales [kb][lb] (A at 2*kOpnd, B 8*kKB bytes later)
+  // scales [kb][lb] (A at 2*kOpnd, B NLB*kKB bytes later)
   auto stage_write = [&](const Raw& raw, uint8_t* st) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < 2 * NQ; ++q) {
       const int lb = q_lb(q);
       const uint32_t m = raw.mask[q];
       // a block outside the operand is zeros with scale 2^0
-      *reinterpret_cast<uint4*>(st + (q < 4 ? 0 : kOpnd) + (lb * kKB + kb) * kMxB + row * 16) =
+      *reinterpret_cast<uint4*>(st + (q < NQ ? 0 : kOpnd) + (lb * kKB + kb) * kMxB + row * 16) =
           make_uint4(raw.v[q].x & m, raw.v[q].y & m, raw.v[q].z & m, raw.v[q].w & m);
       if (row == 0)
-        st[2 * kOpnd + (q < 4 ? 0 : 8 * kKB) + kb * 8 + lb] = static_cast<uint8_t>((raw.sc[q] & m) | (127u & ~m));
+        st[2 * kOpnd + (q < NQ ? 0 : NLB * kKB) + kb * NLB + lb] = static_cast<uint8_t>((raw.sc[q] & m) | (127u & ~m));
     }
   };
 
@@ -225,62 +237,63 @@ __global__ __launch_bounds__(256) void k_conv_mx(const ConvParams p) {
     const i32x2v r1 = __builtin_amdgcn_ds_read_tr4_b64_v2i32((lds_i32x2v*)(blk + trans_off + 16 * 16));
     return i32x8{r0.x, r0.y, r1.x, r1.y, 0, 0, 0, 0};
   };
-  // the MFMA operands of one k-slice: fragments and scale words
+  // the MFMA operands of one k-slice: fragments and scale words (byte i of
+  // a scale word is the scale of fragment i: the MFMA's op_sel)
   struct Frags {
     i32x8 a[RM], b[RN];
     int sa, sb;
   };
   Frags fA, fB;
+  auto scale_word = [&](const uint8_t* q) -> int {
+    if constexpr (RM == 4) return *reinterpret_cast<const int*>(q);
+    else return static_cast<int>(*reinterpret_cast<const uint16_t*>(q));
+  };
   auto read_frags = [&](const uint8_t* st, int j, Frags& f) {
-    // scale words: bytes (the wave half's line blocks 0..3) of k-block 2j + half
-    f.sa = *reinterpret_cast<const int*>(st + 2 * kOpnd + (2 * j + half) * 8 + wm * 4);
-    f.sb = *reinterpret_cast<const int*>(st + 2 * kOpnd + 8 * kKB + (2 * j + half) * 8 + wn * 4);
+    // the wave's line blocks of k-block 2j + half
+    f.sa = scale_word(st + 2 * kOpnd + (2 * j + half) * NLB + wm * RM);
+    f.sb = scale_word(st + 2 * kOpnd + NLB * kKB + (2 * j + half) * NLB + wn * RN);
 #pragma unroll
-    for (int i = 0; i < RM; ++i) f.a[i] = read_opnd(st, wm * 4 + i, j, A_DIRECT);
+    for (int i = 0; i < RM; ++i) f.a[i] = read_opnd(st, wm * RM + i, j, A_DIRECT);
 #pragma unroll
-    for (int i = 0; i < RN; ++i) f.b[i] = read_opnd(st + kOpnd, wn * 4 + i, j, B_DIRECT);
+    for (int i = 0; i < RN; ++i) f.b[i] = read_opnd(st + kOpnd, wn * RN + i, j, B_DIRECT);
   };
 
   // Step s, on stage s%3, with slice 0's operands read into fA during step
   // s-1:
   //   write the rows of step s+2 (fetched two steps earlier) into stage
   //   (s+2)%3, last read during step s-1;
-  //   read slice 1 into fB; 16 MFMAs on fA, with fetches of step s+4;
+  //   read slice 1 into fB; the MFMAs on fA, with fetches of step s+4 for A;
   //   read slice 0 of step s+1 from stage (s+1)%3 (complete since the
-  //   barrier of step s-1) into fA; 16 MFMAs on fB, with more fetches;
+  //   barrier of step s-1) into fA; the MFMAs on fB, with fetches for B;
   //   barrier.
   // Steps run in pairs so that the two row register sets alternate
   // statically, with no exit in between (an exit there makes the compiler
   // spill the accumulators); fetches at or past the last step give zero
   // rows, so the extra step of an odd count adds nothing.
   const int nsteps = s_end - s_begin;
-#define MX_MFMA(F, I, J)                                                                                     \
-  acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.a[I], F.b[J], acc[I][J], 4, 4, I, F.sa, J, \
-                                                              F.sb);                                     \
-  __builtin_amdgcn_sched_barrier(0)
+  auto slice = [&](const Frags& F, Raw& raw, int fs, int q0) {
+    static_for<RM>([&](auto ic) {
+      constexpr int I = decltype(ic)::value;
+      static_for<RN>([&](auto jc) {
+        constexpr int J = decltype(jc)::value;
+        acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.a[I], F.b[J], acc[I][J], 4, 4, I, F.sa, J, F.sb);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (J == 0) {
+          fetch_one(raw, fs, q0 + I);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      });
+    });
+  };
   auto step = [&](int s, const uint8_t* cur, const uint8_t* next_st, uint8_t* write_st, Raw& raw) {
     const int fs = s_begin + s + 4;
     stage_write(raw, write_st);
     read_frags(cur, 1, fB);
     __builtin_amdgcn_sched_barrier(0);
-    MX_MFMA(fA, 0, 0); fetch_one(raw, fs, 0); __builtin_amdgcn_sched_barrier(0);
-    MX_MFMA(fA, 0, 1); MX_MFMA(fA, 0, 2); MX_MFMA(fA, 0, 3);
-    MX_MFMA(fA, 1, 0); fetch_one(raw, fs, 1); __builtin_amdgcn_sched_barrier(0);
-    MX_MFMA(fA, 1, 1); MX_MFMA(fA, 1, 2); MX_MFMA(fA, 1, 3);
-    MX_MFMA(fA, 2, 0); fetch_one(raw, fs, 2); __builtin_amdgcn_sched_barrier(0);
-    MX_MFMA(fA, 2, 1); MX_MFMA(fA, 2, 2); MX_MFMA(fA, 2, 3);
-    MX_MFMA(fA, 3, 0); fetch_one(raw, fs, 3); __builtin_amdgcn_sched_barrier(0);
-    MX_MFMA(fA, 3, 1); MX_MFMA(fA, 3, 2); MX_MFMA(fA, 3, 3);
+    slice(fA, raw, fs, 0);
     read_frags(next_st, 0, fA);
     __builtin_amdgcn_sched_barrier(0);
-    MX_MFMA(fB, 0, 0); fetch_one(raw, fs, 4); __builtin_amdgcn_sched_barrier(0);
-    MX_MFMA(fB, 0, 1); MX_MFMA(fB, 0, 2); MX_MFMA(fB, 0, 3);
-    MX_MFMA(fB, 1, 0); fetch_one(raw, fs, 5); __builtin_amdgcn_sched_barrier(0);
-    MX_MFMA(fB, 1, 1); MX_MFMA(fB, 1, 2); MX_MFMA(fB, 1, 3);
-    MX_MFMA(fB, 2, 0); fetch_one(raw, fs, 6); __builtin_amdgcn_sched_barrier(0);
-    MX_MFMA(fB, 2, 1); MX_MFMA(fB, 2, 2); MX_MFMA(fB, 2, 3);
-    MX_MFMA(fB, 3, 0); fetch_one(raw, fs, 7); __builtin_amdgcn_sched_barrier(0);
-    MX_MFMA(fB, 3, 1); MX_MFMA(fB, 3, 2); MX_MFMA(fB, 3, 3);
+    slice(fB, raw, fs, NQ);
     // The MFMAs carry no ordering of their own: without a use here, the
     // first step of a pair has its MFMAs emitted after the barrier below,
     // leaving the MFMA pipe idle while the waves wait there.  An empty asm
@@ -291,7 +304,6 @@ __global__ __launch_bounds__(256) void k_conv_mx(const ConvParams p) {
       for (int j = 0; j < RN; ++j) asm volatile("" : "+a"(acc[i][j]));
     __syncthreads();
   };
-#undef MX_MFMA
   if (nsteps > 0) {
     fetch(r0, s_begin);
     fetch(r1, s_begin + 1);
@@ -318,11 +330,20 @@ __global__ __launch_bounds__(256) void k_conv_mx(const ConvParams p) {
 
 namespace gemm {
 
-void launch_mx(int op, const ConvParams& p, dim3 grid, hipStream_t s) {
-  switch (op) {
-    case OP_FWD: hipLaunchKernelGGL(k_conv_mx<OP_FWD>, grid, dim3(256), 0, s, p); break;
-    case OP_DGRAD: hipLaunchKernelGGL(k_conv_mx<OP_DGRAD>, grid, dim3(256), 0, s, p); break;
-    default: hipLaunchKernelGGL(k_conv_mx<OP_WGRAD>, grid, dim3(256), 0, s, p); break;
+void launch_mx(int op, int tile, const ConvParams& p, dim3 grid, hipStream_t s) {
+  auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, p); };
+  if (tile == 128) {
+    switch (op) {
+      case OP_FWD: go(k_conv_mx<OP_FWD, 128>); break;
+      case OP_DGRAD: go(k_conv_mx<OP_DGRAD, 128>); break;
+      default: go(k_conv_mx<OP_WGRAD, 128>); break;
+    }
+  } else {
+    switch (op) {
+      case OP_FWD: go(k_conv_mx<OP_FWD, 256>); break;
+      case OP_DGRAD: go(k_conv_mx<OP_DGRAD, 256>); break;
+      default: go(k_conv_mx<OP_WGRAD, 256>); break;
+    }
   }
 }
 

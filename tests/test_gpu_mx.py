@@ -138,6 +138,49 @@ def test_conv_mx(shape):
     assert_close(dw.cpu().numpy(), ref, s, "wgrad")
 
 
+# Shapes on which the launch takes the 256x256 tile (M above 128 and at
+# least 1024 such tiles, or for wgrad a full round of splits), with M and N
+# not multiples of 256; the small shapes above all take the 128x128 tile.
+# Quantized tensors are compared in full, the GEMMs on sampled outputs.
+BIG = [
+    # n, ci, co, h, w, kh, kw, sh, sw, ph, pw
+    (256, 32, 160, 32, 32, 3, 3, 1, 1, 1, 1),   # fwd and wgrad: 160 rows of the tile, wgrad 288 columns of 512
+    (256, 160, 32, 32, 32, 3, 3, 1, 1, 1, 1),   # dgrad: 160 rows of the tile
+]
+
+
+def sample_points(n, rng, npts=16384):
+    if n <= npts:
+        return np.arange(n, dtype=np.int64)
+    return np.unique(np.concatenate([rng.integers(0, n, npts), [0, n - 1, n // 2]])).astype(np.int64)
+
+
+@pytest.mark.parametrize("shape", BIG)
+def test_conv_mx_large_tile(shape):
+    say("mx conv, large tile", shape)
+    lay = WL.ConvLayer(*shape)
+    seed = 500 + BIG.index(shape)
+    x, w, dy = WL.gen_x(lay, "normal", seed), WL.gen_w(lay, seed + 1), WL.gen_dy(lay, 1.0, seed + 2)
+    d = mx.desc_from_layer(lay, mx.MX_E2M1, block=32)
+    (qx, qw, qdy), (y, dx, dw) = run_layer(d, x, w, dy, seed_sr=9)
+    ox = oracle_mx(mx.MX_ROLE_ACT, x)
+    ow = oracle_mx(mx.MX_ROLE_WEIGHT, w)
+    ody = oracle_mx(mx.MX_ROLE_GRAD, dy, mx.MX_SR, 9)
+    assert_mx_equal(qx, ox, "X")
+    assert_mx_equal(qw, ow, "W")
+    assert_mx_equal(qdy, ody, "dY")
+    cv = oracle_conv(d)
+    rng = np.random.default_rng(seed)
+    xe, we, dye = ox.exact(), ow.exact(), ody.exact()
+    for name, out, fn, a, b, npts in (("fwd", y, O.conv_fwd_points, we, xe, 16384),
+                                      ("dgrad", dx, O.conv_dgrad_points, we, dye, 16384),
+                                      ("wgrad", dw, O.conv_wgrad_points, dye, xe, 2048)):
+        assert not torch.isnan(out).any(), f"{name}: outputs left unwritten"
+        idx = sample_points(out.numel(), rng, npts)
+        ref, sabs = fn(cv, a, b, idx)
+        assert_close(out.reshape(-1)[torch.from_numpy(idx).to(DEV)].cpu().numpy(), ref, sabs, name)
+
+
 def test_identity_weight_is_exact():
     # W = I quantizes exactly (scale 2^-2, code 4.0), so a 1x1 fwd returns the
     # dequantized X and a 1x1 dgrad the dequantized dY, bit for bit: every
