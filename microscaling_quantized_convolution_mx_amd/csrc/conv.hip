@@ -84,7 +84,10 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
   constexpr int RM = WTM / 32, RN = WTN / 32;
   constexpr int ABLK = (MT / 8) * KB, BBLK = (NT / 8) * KB;
   static_assert(ABLK + BBLK <= WAVES * 64, "one block per thread per stage");
-  static_assert(ABLK % 64 == 0, "the A/B staging split falls on wave boundaries");
+  // Where the A/B staging split falls inside a wave (MT = 64) and A and B
+  // are staged differently (fwd), that wave runs both sides of the
+  // transpose branch in stage_block; nothing else depends on the split.
+  static_assert(ABLK % 32 == 0, "the A/B staging split falls on a half wave");
   static_assert(RM >= 1 && RN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile of 32x32 MFMAs");
   constexpr int LINES = MT + NT + 8;  // + 8 spare lines for threads without a block
   constexpr int CODE_B = LINES * 16;
@@ -99,7 +102,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
   const bool is_a = t.is_a;
   constexpr bool A_ROWS = (OP != OP_DGRAD);
   constexpr bool B_ROWS = (OP == OP_WGRAD);
-  const bool rows = is_a ? A_ROWS : B_ROWS;  // uniform per wave
+  const bool rows = is_a ? A_ROWS : B_ROWS;
 
   // staging addresses of this thread's block: row r goes to physical line
   // lb*8 + (r ^ (lb & 7)) at the k-block's slot
@@ -667,6 +670,7 @@ void launch_fmt(const ConvParams& p, const Tile& t, dim3 grid, hipStream_t s) {
       return;
     }
     if (t.mt == 128 && t.nt == 256) return launch_tile4<OP, 128, 256, 2, 4>(p, grid, s);
+    if (t.mt == 64 && t.nt == 256) return launch_tile4<OP, 64, 256, 1, 4>(p, grid, s);
   }
   launch_generic<OP, FMT, FMT>(p, t, grid, s);
 }
@@ -701,15 +705,19 @@ struct WgradPlan {
 WgradPlan wgrad_plan(const Geom& g) {
   const int64_t kb_total = static_cast<int64_t>(g.ho) * g.wo * (g.n / 8);
   const int64_t ncol = static_cast<int64_t>(g.k_h) * g.k_w * g.c_in;
-  const Tile t = pick_wgrad_tile(g.c_out, ncol, g.fmt);
+  Tile t = pick_wgrad_tile(g.c_out, ncol, g.fmt);
+  // all-E2M1 128x256 and 64x256 tiles run k_conv4 (decode at fragment read,
+  // K steps of 4 k-blocks, two workgroups per CU); p.ks_split counts its steps
+  const bool decode_tile = g.fmt == FMT_E2M1 && g.afmt == FMT_E2M1 && (t.mt == 128 || t.mt == 64) && t.nt == 256;
+  if (decode_tile) t.kb = 4;
   const int64_t ksteps = (kb_total + t.kb - 1) / t.kb;
   const int64_t tiles = ((g.c_out + t.mt - 1) / t.mt) * ((ncol + t.nt - 1) / t.nt);
-  // About one round of workgroups: 1024 waves, or 2048 for the 128x256
-  // all-E2M1 tile, which runs two workgroups per CU.  More splits shorten each K loop
+  // About one round of workgroups: 1024 waves, or 2048 for the k_conv4
+  // tiles, which run two workgroups per CU.  More splits shorten each K loop
   // but add partials to write and reduce (a sweep over the ResNet stacks put
   // the optimum there).  Rounded down: a last, nearly empty round of
   // workgroups costs a full one.
-  const int64_t target_waves = (g.fmt == FMT_E2M1 && g.afmt == FMT_E2M1 && t.mt == 128 && t.nt == 256) ? 2048 : 1024;
+  const int64_t target_waves = decode_tile ? 2048 : 1024;
   int64_t splits = (target_waves / t.waves) / tiles;
   const int64_t max_by_k = ksteps / 4;
   if (splits > max_by_k) splits = max_by_k;
