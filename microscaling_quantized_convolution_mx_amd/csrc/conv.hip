@@ -84,10 +84,9 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
   constexpr int RM = WTM / 32, RN = WTN / 32;
   constexpr int ABLK = (MT / 8) * KB, BBLK = (NT / 8) * KB;
   static_assert(ABLK + BBLK <= WAVES * 64, "one block per thread per stage");
-  // Where the A/B staging split falls inside a wave (MT = 64) and A and B
+  // Where the A/B staging split falls inside a wave (MT < 128) and A and B
   // are staged differently (fwd), that wave runs both sides of the
   // transpose branch in stage_block; nothing else depends on the split.
-  static_assert(ABLK % 32 == 0, "the A/B staging split falls on a half wave");
   static_assert(RM >= 1 && RN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile of 32x32 MFMAs");
   constexpr int LINES = MT + NT + 8;  // + 8 spare lines for threads without a block
   constexpr int CODE_B = LINES * 16;
@@ -671,6 +670,7 @@ void launch_fmt(const ConvParams& p, const Tile& t, dim3 grid, hipStream_t s) {
     }
     if (t.mt == 128 && t.nt == 256) return launch_tile4<OP, 128, 256, 2, 4>(p, grid, s);
     if (t.mt == 64 && t.nt == 256) return launch_tile4<OP, 64, 256, 1, 4>(p, grid, s);
+    if (t.mt == 32 && t.nt == 256) return launch_tile4<OP, 32, 256, 1, 4>(p, grid, s);
   }
   launch_generic<OP, FMT, FMT>(p, t, grid, s);
 }
@@ -706,9 +706,9 @@ WgradPlan wgrad_plan(const Geom& g) {
   const int64_t kb_total = static_cast<int64_t>(g.ho) * g.wo * (g.n / 8);
   const int64_t ncol = static_cast<int64_t>(g.k_h) * g.k_w * g.c_in;
   Tile t = pick_wgrad_tile(g.c_out, ncol, g.fmt);
-  // all-E2M1 128x256 and 64x256 tiles run k_conv4 (decode at fragment read,
+  // all-E2M1 128x256, 64x256 and 32x256 tiles run k_conv4 (decode at fragment read,
   // K steps of 4 k-blocks, two workgroups per CU); p.ks_split counts its steps
-  const bool decode_tile = g.fmt == FMT_E2M1 && g.afmt == FMT_E2M1 && (t.mt == 128 || t.mt == 64) && t.nt == 256;
+  const bool decode_tile = g.fmt == FMT_E2M1 && g.afmt == FMT_E2M1 && t.mt <= 128 && t.nt == 256;
   if (decode_tile) t.kb = 4;
   const int64_t ksteps = (kb_total + t.kb - 1) / t.kb;
   const int64_t tiles = ((g.c_out + t.mt - 1) / t.mt) * ((ncol + t.nt - 1) / t.nt);
