@@ -712,12 +712,13 @@ WgradPlan wgrad_plan(const Geom& g) {
   if (decode_tile) t.kb = 4;
   const int64_t ksteps = (kb_total + t.kb - 1) / t.kb;
   const int64_t tiles = ((g.c_out + t.mt - 1) / t.mt) * ((ncol + t.nt - 1) / t.nt);
-  // About one round of workgroups: 1024 waves, or 2048 for the k_conv4
-  // tiles, which run two workgroups per CU.  More splits shorten each K loop
-  // but add partials to write and reduce (a sweep over the ResNet stacks put
-  // the optimum there).  Rounded down: a last, nearly empty round of
-  // workgroups costs a full one.
-  const int64_t target_waves = decode_tile ? 2048 : 1024;
+  // About one round of workgroups: 1024 waves, or 2048 for the 128- and
+  // 64-row k_conv4 tiles, which run two workgroups per CU.  More splits
+  // shorten each K loop but add partials to write and reduce (sweeps over
+  // the ResNet stacks put the optimum there; the 32-row tile of ResNet-32's
+  // 16- and 32-channel layers does better with 1024).  Rounded down: a last,
+  // nearly empty round of workgroups costs a full one.
+  const int64_t target_waves = decode_tile && t.mt >= 64 ? 2048 : 1024;
   int64_t splits = (target_waves / t.waves) / tiles;
   const int64_t max_by_k = ksteps / 4;
   if (splits > max_by_k) splits = max_by_k;

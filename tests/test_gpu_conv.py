@@ -146,3 +146,43 @@ def test_fp6_decode_of_every_code(fmts):
     cv = oracle_conv(d)
     ref, s = O.conv_fwd(cv, ow.exact(), ox.exact())
     assert_close(y.cpu().numpy(), ref, s, "fwd identity")
+
+
+# Shapes on which the tile choice takes the decode-at-read 64x256 and 32x256
+# tiles with rows and columns both ragged (48 of 64 rows, 16 of 32, and
+# 139392 columns = 544.5 tiles); the shapes above are too small for them.
+# Quantized tensors in full, the GEMMs on sampled outputs, every output written.
+DECODE_TILE_SHAPES = [
+    # n, ci, co, h, w, kh, kw, sh, sw, ph, pw
+    (128, 32, 48, 33, 33, 3, 3, 1, 1, 1, 1),   # fwd 64x256, dgrad 32x256
+    (128, 48, 16, 33, 33, 3, 3, 1, 1, 1, 1),   # fwd 32x256, dgrad 64x256
+]
+
+
+def sample_points(n, rng, npts):
+    if n <= npts:
+        return np.arange(n, dtype=np.int64)
+    return np.unique(np.concatenate([rng.integers(0, n, npts), [0, n - 1, n // 2]])).astype(np.int64)
+
+
+@pytest.mark.parametrize("shape", DECODE_TILE_SHAPES)
+def test_conv_decode_tiles_ragged(shape):
+    say("conv decode tiles", shape)
+    lay = WL.ConvLayer(*shape)
+    seed = 700 + DECODE_TILE_SHAPES.index(shape)
+    x, w, dy = WL.gen_x(lay, "normal", seed), WL.gen_w(lay, seed + 1), WL.gen_dy(lay, 1.0, seed + 2)
+    d = mx.desc_from_layer(lay, mx.MX_E2M1)
+    (qx, qw, qdy), (y, dx, dw) = run_layer(d, x, w, dy, seed_sr=11)
+    ox = oracle_quantize(d, mx.MX_ROLE_ACT, x)
+    ow = oracle_quantize(d, mx.MX_ROLE_WEIGHT, w)
+    ody = oracle_quantize(d, mx.MX_ROLE_GRAD, dy, mx.MX_SR, 11)
+    cv = oracle_conv(d)
+    rng = np.random.default_rng(seed)
+    xe, we, dye = ox.exact(), ow.exact(), ody.exact()
+    for name, out, fn, a, b, npts in (("fwd", y, O.conv_fwd_points, we, xe, 16384),
+                                      ("dgrad", dx, O.conv_dgrad_points, we, dye, 16384),
+                                      ("wgrad", dw, O.conv_wgrad_points, dye, xe, 4096)):
+        assert not torch.isnan(out).any(), f"{name}: outputs left unwritten"
+        idx = sample_points(out.numel(), rng, npts)
+        ref, sabs = fn(cv, a, b, idx)
+        assert_close(out.reshape(-1)[torch.from_numpy(idx).to(DEV)].cpu().numpy(), ref, sabs, name)
