@@ -171,7 +171,7 @@ def test_stochastic_rounding(orc):
     hi = np.array([grid[grid >= t].min() if t < grid[-1] else 0 for t in v.ravel()]).reshape(32, 32)
     var = (v - lo) * (hi - v)
     err = np.abs(vals.mean(0) - v)
-    assert np.all(err[inside] <= 5 * np.sqrt(var[inside] / len(seeds)) + 1e-12)
+    assert np.all(err[inside] <= 4 * np.sqrt(var[inside] / len(seeds)) + 1e-12)
 
 
 def test_blocked_dot_product_factorisation(orc):
