@@ -135,10 +135,19 @@ def lib():
     L.orc_conv_direct.argtypes = [ctypes.POINTER(OrcConv), _P, _P, _P]
     L.orc_count_act_quant.restype = _I64
     L.orc_count_act_quant.argtypes = [ctypes.POINTER(OrcConv), ctypes.c_int, _P]
+    L.orc_count_operand_quant.restype = _I64
+    L.orc_count_operand_quant.argtypes = [ctypes.POINTER(OrcConv), ctypes.c_int, ctypes.c_int, _P]
     L.orc_quantize_after_im2col.restype = ctypes.c_int
+    L.orc_threads.restype = ctypes.c_int
+    L.orc_threads.argtypes = []
     L.orc_quantize_after_im2col.argtypes = [ctypes.POINTER(OrcConv), ctypes.c_int, _P, _P, _P, _P, _P]
     _lib = L
     return L
+
+
+def threads() -> int:
+    """Threads the oracle's OpenMP loops run on."""
+    return lib().orc_threads()
 
 
 def _ptr(a: np.ndarray):
@@ -420,6 +429,24 @@ def count_act_quant(cv: OrcConv, flow: int):
     """Per-activation quantization counts and total events of one flow."""
     counts = np.zeros((cv.h, cv.w, cv.c_in, cv.n), dtype=np.int32)
     events = lib().orc_count_act_quant(ctypes.byref(cv), flow, _ptr(counts))
+    return counts, int(events)
+
+
+TENSOR_W, TENSOR_DY = 1, 2
+
+
+def count_operand_quant(cv: OrcConv, flow: int, tensor: int):
+    """Per-element quantization counts and total events of the weight
+    (TENSOR_W, counts [Kh*Kw][C_out][C_in]) or the output gradient
+    (TENSOR_DY, counts [C_out][Ho*Wo*N]) under one flow."""
+    if tensor == TENSOR_W:
+        shape = (cv.k_h * cv.k_w, cv.c_out, cv.c_in)
+    else:
+        shape = (cv.c_out, cv.h_out * cv.w_out * cv.n)
+    counts = np.zeros(shape, dtype=np.int32)
+    events = lib().orc_count_operand_quant(ctypes.byref(cv), flow, tensor, _ptr(counts))
+    if events < 0:
+        raise ValueError("bad flow or tensor")
     return counts, int(events)
 
 

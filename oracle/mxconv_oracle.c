@@ -43,6 +43,7 @@
  * (q * B * T is exact in fp64: at most 8 + 24 significant bits).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -908,6 +909,73 @@ int64_t orc_count_act_quant(const orc_conv* cv, int flow, int32_t* counts) {
   return events;
 }
 
+/* The same count for the weight (tensor 1) and the output gradient (tensor  */
+/* 2), in one training step of the three GEMMs (§II-A, §IV-B):                 */
+/*   W  is the A operand of the forward GEMM, whose K runs along C_in, and of  */
+/*      the data-gradient GEMM, whose K runs along C_out;                       */
+/*   dY is the B operand of the data-gradient GEMM (K along C_out) and the A    */
+/*      operand of the weight-gradient GEMM (K along the output positions and   */
+/*      the batch).                                                             */
+/* A GEMM reads its operands in blocks that lie along its K.  A square 8x8      */
+/* block (MicroQonv, flow 0, and the square-block flow 1) lies along both       */
+/* dimensions, so one quantization serves both GEMMs; a 64-element line         */
+/* (DaCapo, flow 2) lies along one, so each K direction takes a quantization   */
+/* of its own (§IV-C).  The tensor is viewed per tap as a rows x cols matrix:   */
+/* W as [C_out][C_in] at each of the Kh*Kw taps, dY as [C_out][Ho*Wo*N];       */
+/* counts[(tap * rows + r) * cols + c] receives the quantizations of that       */
+/* element.  Returns the total number of quantization events, -1 on a bad      */
+/* argument.                                                                   */
+int64_t orc_count_operand_quant(const orc_conv* cv, int flow, int tensor, int32_t* counts) {
+  int64_t taps, rows, cols;
+  int kdir[2]; /* K direction of the two GEMMs that read the tensor: 0 rows, 1 cols */
+  if (tensor == 1) {
+    taps = (int64_t)cv->k_h * cv->k_w; rows = cv->c_out; cols = cv->c_in;
+    kdir[0] = 1; /* forward: K = C_in */
+    kdir[1] = 0; /* data gradient: K = C_out */
+  } else if (tensor == 2) {
+    taps = 1; rows = cv->c_out; cols = out_h(cv) * out_w(cv) * cv->n;
+    kdir[0] = 0; /* data gradient: K = C_out */
+    kdir[1] = 1; /* weight gradient: K = (ho, wo, n) */
+  } else {
+    return -1;
+  }
+  if (flow < 0 || flow > 2) return -1;
+  for (int64_t i = 0; i < taps * rows * cols; ++i) counts[i] = 0;
+  /* the block shapes (br x bc) the flow quantizes the tensor in, one per K
+   * direction, a shape that serves several GEMMs quantized once */
+  int64_t shapes[2][2];
+  int nshapes = 0;
+  for (int u = 0; u < 2; ++u) {
+    int64_t br = 8, bc = 8;
+    if (flow == 2) {
+      br = kdir[u] == 0 ? 64 : 1;
+      bc = kdir[u] == 1 ? 64 : 1;
+    }
+    int dup = 0;
+    for (int v = 0; v < nshapes; ++v) dup |= shapes[v][0] == br && shapes[v][1] == bc;
+    if (!dup) {
+      shapes[nshapes][0] = br;
+      shapes[nshapes][1] = bc;
+      ++nshapes;
+    }
+  }
+  int64_t events = 0;
+  for (int v = 0; v < nshapes; ++v) {
+    int64_t br = shapes[v][0], bc = shapes[v][1];
+    /* every block of the tiling (the last ones cut at the tensor's edge) is
+     * quantized once; each of its elements is counted */
+    for (int64_t t = 0; t < taps; ++t)
+      for (int64_t r0 = 0; r0 < rows; r0 += br)
+        for (int64_t c0 = 0; c0 < cols; c0 += bc)
+          for (int64_t r = r0; r < r0 + br && r < rows; ++r)
+            for (int64_t c = c0; c < c0 + bc && c < cols; ++c) {
+              counts[(t * rows + r) * cols + c] += 1;
+              events += 1;
+            }
+  }
+  return events;
+}
+
 /* Square-block quantization of the explicit quantize-after-im2col matrix
  * (flow 1).  That flow works on the conventional im2col of §II-C, whose rows
  * are the channel-major flattened kernel positions (ci, kh, kw) and whose
@@ -962,3 +1030,6 @@ int orc_quantize_after_im2col(const orc_conv* cv, int fmt, const float* x, uint8
   free(scales);
   return rc;
 }
+
+/* Threads the OpenMP loops above run on (for reporting only). */
+int orc_threads(void) { return omp_get_max_threads(); }

@@ -90,9 +90,25 @@ def test_im2col_copies_carry_the_same_quantized_value(orc, layer):
     assert differ > 0
 
 
-def test_weight_and_gradient_counts(orc):
-    # MicroQonv quantizes W and G_Y once each; a line-blocked flow that needs
-    # both GEMM directions quantizes them once per direction.
-    assert T1["microqonv"]["W"] == 1 and T1["microqonv"]["G"] == 1
-    assert T1["dacapo"]["W"] == 2 and T1["dacapo"]["G"] == 2
-    assert T1["cuyckens"]["W"] == 1 and T1["cuyckens"]["G"] == 1
+@pytest.mark.parametrize("flow,name", [(O.FLOW_MICROQONV, "microqonv"), (O.FLOW_IM2COL_SQUARE, "cuyckens"),
+                                       (O.FLOW_DACAPO, "dacapo")])
+def test_weight_and_gradient_counts(orc, layer, flow, name):
+    # Table I's W and G columns: MicroQonv and the square-block flow quantize
+    # W and G_Y once (a square block serves both GEMMs that read them);
+    # DaCapo's lines serve one K direction each, so twice.  The oracle counts
+    # the quantization events of the flow; the table is the paper's.
+    for tensor, col in ((O.TENSOR_W, "W"), (O.TENSOR_DY, "G")):
+        counts, events = O.count_operand_quant(layer, flow, tensor)
+        assert np.all(counts == T1[name][col]), (name, col, np.unique(counts))
+        assert events == T1[name][col] * counts.size
+
+
+def test_operand_counts_on_a_wider_layer(orc):
+    # the same on a layer whose channels hold several 64-element lines and
+    # blocks in both directions (stride 2, 5x5 kernel)
+    cv = O.conv(16, 64, 128, 12, 12, 5, 5, 2, 2, 2, 2)
+    for flow, name in ((O.FLOW_MICROQONV, "microqonv"), (O.FLOW_IM2COL_SQUARE, "cuyckens"),
+                       (O.FLOW_DACAPO, "dacapo")):
+        for tensor, col in ((O.TENSOR_W, "W"), (O.TENSOR_DY, "G")):
+            counts, _ = O.count_operand_quant(cv, flow, tensor)
+            assert np.all(counts == T1[name][col]), (name, col)
