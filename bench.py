@@ -38,7 +38,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c2", help="c1..c5 (default c2: ResNet-32 stack)")
+    ap.add_argument("--workload", default="c5",
+                    help="c1..c5 (default c5: the 256-channel stress layer in its three element formats, "
+                         "plus the replay buffer)")
     ap.add_argument("--fmt", default=None, help="element format override: e2m1|e2m3|e4m3")
     ap.add_argument("--act-fmt", default=None, choices=["e3m2", "e2m3"],
                     help="MicroQonv+: activations in this FP6 format, weights and gradients in the "
@@ -97,7 +99,7 @@ class Call:
             raise RuntimeError(f"{self.name}: status {rc}")
 
 
-def flow_calls(flow, L, mx, torch, D, d, lay, x, w, dy, sr_seed, fmt, qb, ws, ws_bytes, stream, keep, dev):
+def flow_calls(flow, L, mx, torch, D, d, lay, x, w, dy, sr_seed, fmt, fname, qb, stream, keep, dev):
     """The activation path (fwd + wgrad) of one layer under one flow.  W and dY
     are quantized here, outside the timed step (they are the same in every
     flow).  The baseline flows run the GEMMs as 1x1 convolutions over X'
@@ -122,22 +124,40 @@ def flow_calls(flow, L, mx, torch, D, d, lay, x, w, dy, sr_seed, fmt, qb, ws, ws
     keep += [g, w, xs, qx, qw, qdy, y, dw, wsf, cq]
     nxc = xs.numel() if flow != "microqonv" else nx
     q_x = Call(L.mx_quantize_cbf, (D(g), mx.MX_ROLE_ACT, xs.data_ptr(), D(cq[0]), mx.MX_RNE, 0, 0, stream),
-               "quantize", ("quantize_act", shape), 0, nxc * (8 + qb), "quantize X" if flow == "microqonv" else "quantize X'")
+               "quantize", ("quantize_act", shape, fname), 0, nxc * (8 + qb), "quantize X" if flow == "microqonv" else "quantize X'")
     fwd = Call(L.mx_conv_fwd, (D(g), D(cq[1]), D(cq[0]), y.data_ptr(), stream),
-               "fwd", ("conv_fwd", shape), f, (nw + nxc) * qb + 4 * ny, "fwd")
+               "fwd", ("conv_fwd", shape, fname), f, (nw + nxc) * qb + 4 * ny, "fwd")
     wgrad = Call(L.mx_conv_wgrad, (D(g), D(cq[2]), D(cq[0]), dw.data_ptr(), wsf.data_ptr(), wsb, stream),
-                 "wgrad", ("conv_wgrad", shape), f, (ny + nxc) * qb + 4 * nw, "wgrad")
+                 "wgrad", ("conv_wgrad", shape, fname), f, (ny + nxc) * qb + 4 * nw, "wgrad")
     if flow == "microqonv":
         return [q_x, fwd, wgrad]
 
     def im2col():
         return Call(L.mx_im2col_cbf, (D(d), x.data_ptr(), xs.data_ptr(), stream),
-                    "im2col", ("im2col", shape), 0, 4 * (nx + nxc), "im2col")
+                    "im2col", ("im2col", shape, fname), 0, 4 * (nx + nxc), "im2col")
     if flow == "im2col-square":
         return [im2col(), q_x, fwd, wgrad]
     # dacapo: X kept in fp32; X' formed and quantized in the forward and again in the backward
-    q_x2 = Call(q_x.fn, q_x.args, "quantize", ("quantize_act", shape), 0, nxc * (8 + qb), "quantize X' (backward)")
+    q_x2 = Call(q_x.fn, q_x.args, "quantize", ("quantize_act", shape, fname), 0, nxc * (8 + qb), "quantize X' (backward)")
     return [im2col(), q_x, fwd, im2col(), q_x2, wgrad]
+
+
+def fmt_list(a, wl, mx):
+    """Element formats of one step: all of the workload's (the stress layer
+    runs E2M1, E2M3 and E4M3), or the one --fmt names.  The variants
+    (--block 32, --act-fmt, --flow, --producer-amax) run one format."""
+    names = {"e2m1": mx.MX_E2M1, "e2m3": mx.MX_E2M3, "e4m3": mx.MX_E4M3, "e3m2": mx.MX_E3M2}
+    if a.fmt:
+        return [names[a.fmt]]
+    if a.block == 32 or a.act_fmt or a.flow or a.producer_amax:
+        return [wl.elem_fmts[0]]
+    return list(wl.elem_fmts)
+
+
+def mfma_dtype(block, fmt, mx):
+    """Operand type of the GEMMs' MFMA: fp4 (scaled, 32x32 E8M0 blocks), else
+    the exact decode: fp16 (E2M1, E2M3, E3M2), bf16 (E4M3)."""
+    return "fp4" if block == 32 else ("bf16" if fmt == mx.MX_E4M3 else "f16")
 
 
 def main():
@@ -167,94 +187,100 @@ def main():
 
     L = mx.lib()
     wl = WL.workloads()[a.workload]
-    fmts = {"e2m1": mx.MX_E2M1, "e2m3": mx.MX_E2M3, "e4m3": mx.MX_E4M3, "e3m2": mx.MX_E3M2}
-    fmt = fmts[a.fmt] if a.fmt else wl.elem_fmts[0]
-    afmt = fmts[a.act_fmt] if a.act_fmt else 0   # 0: activations in fmt too
+    fmts_by_name = {"e2m1": mx.MX_E2M1, "e2m3": mx.MX_E2M3, "e4m3": mx.MX_E4M3, "e3m2": mx.MX_E3M2}
+    fmts = fmt_list(a, wl, mx)
+    afmt = fmts_by_name[a.act_fmt] if a.act_fmt else 0   # 0: activations in the element format too
     if afmt and a.flow:
         raise SystemExit("--act-fmt applies to the MicroQonv step, not to --flow")
-    if a.block == 32 and (afmt or a.flow or a.producer_amax or fmt != mx.MX_E2M1):
+    if a.block == 32 and (afmt or a.flow or a.producer_amax or fmts != [mx.MX_E2M1]):
         raise SystemExit("--block 32 runs the E2M1 MicroQonv step only")
     sb = 1 / (a.block * a.block)                   # scale bytes per element
-    qb = mx.CODE_BITS[fmt] / 8 + sb                # quantized bytes per element (codes + block scales)
-    qbx = mx.CODE_BITS[afmt or fmt] / 8 + sb       # the same for the activation X
     rd = 8 if a.block == 8 else 4                  # fp32 source bytes read per element: amax pass + pass, or once
     stream = torch.cuda.current_stream().cuda_stream
 
     D = ctypes.byref
     calls: list[Call] = []
     keep = []                         # keeps every buffer and ctypes struct alive
-    ws_bytes = max(mx.mx_wgrad_workspace_bytes(mx.desc_from_layer(l, fmt, afmt, a.block)) for l in wl.layers)
+    ws_bytes = max(mx.mx_wgrad_workspace_bytes(mx.desc_from_layer(l, f, afmt, a.block))
+                   for l in wl.layers for f in fmts)
     ws = torch.empty(max(ws_bytes // 4, 4), device=dev)
     keep.append(ws)
 
     t_gen = time.time()
-    prev = None  # --producer-amax: (layer, y, its fwd Call) of the previous layer
+    inputs = {}  # layer index -> (x, w, dy) on the device, shared by the formats
     flow_stats = {"activation_elements": 0, "quantized_elements": 0, "stored_activation_bytes": 0.0}
     n_chained = 0
-    layer_starts = []  # index of each layer's first call (the 7-call MicroQonv step)
-    for li, lay in enumerate(wl.layers):
-        d = mx.desc_from_layer(lay, fmt, afmt, a.block)
-        x = WL.gen_x(lay, wl.x_dist, WL.seed_for(wl.cfg_index, li, 1)).to(dev)
-        w = WL.gen_w(lay, WL.seed_for(wl.cfg_index, li, 2)).to(dev)
-        dy = WL.gen_dy(lay, wl.dy_sigma, WL.seed_for(wl.cfg_index, li, 3)).to(dev)
-        sr_seed = WL.seed_for(wl.cfg_index, li, 4)
-        qx, qw, qdy = (mx.QTensor(d, r, dev) for r in (mx.MX_ROLE_ACT, mx.MX_ROLE_WEIGHT, mx.MX_ROLE_GRAD))
-        y = torch.empty(lay.h_out, lay.w_out, lay.c_out, lay.n, device=dev)
-        dx = torch.empty(lay.h, lay.w, lay.c_in, lay.n, device=dev)
-        dw = torch.empty(lay.c_out, lay.c_in, lay.k_h, lay.k_w, device=dev)
-        xdq = torch.empty_like(x)
-        cq = [q.c() for q in (qx, qw, qdy)]
-        keep += [d, x, w, dy, qx, qw, qdy, y, dx, dw, xdq, cq]
-        shape = lay.tag()
-        nx, nw, ny = lay.numel_x(), lay.numel_w(), lay.numel_dy()
-        f = lay.flops()
-        if a.flow:
-            calls += flow_calls(a.flow, L, mx, torch, D, d, lay, x, w, dy, sr_seed, fmt, qb, ws, ws_bytes, stream, keep,
-                                dev)
-            nx = lay.numel_x()
-            nxc = lay.h_out * lay.w_out * lay.k_h * lay.k_w * lay.c_in * lay.n
-            flow_stats["activation_elements"] += nx
-            flow_stats["quantized_elements"] += {"microqonv": nx, "im2col-square": nxc, "dacapo": 2 * nxc}[a.flow]
-            flow_stats["stored_activation_bytes"] += {"microqonv": nx * qb, "im2col-square": nxc * qb,
-                                                      "dacapo": nx * 4.0}[a.flow]
-            continue
-        # --producer-amax: where the previous layer's output has this layer's
-        # input shape, X is that output, its fwd writes max|y| into qx.amax
-        # and X is quantized in one pass (amax given)
-        chained = (a.producer_amax and prev is not None and (prev[0].h_out, prev[0].w_out, prev[0].c_out, prev[0].n)
-                   == (lay.h, lay.w, lay.c_in, lay.n))  # prev[0] is the previous layer's descriptor
-        if chained:
-            pd, py, pcall = prev
-            # the previous fwd's amax buffer: word 0 is the amax this layer's X is quantized with
-            abuf = torch.empty(mx.mx_fwd_amax_bytes(pd) // 4, device=dev)
-            keep.append(abuf)
-            qx.amax = abuf[:1]
-            cq[0] = qx.c()
-            pcall.fn = L.mx_conv_fwd_amax
-            pcall.args = pcall.args[:-1] + (abuf.data_ptr(), stream)
-            pcall.name = "fwd (+amax)"
-            x_src, x_given, x_bytes = py.data_ptr(), 1, nx * (4 + qbx)
-            n_chained += 1
-        else:
-            x_src, x_given, x_bytes = x.data_ptr(), 0, nx * (rd + qbx)
-        calls += [
-            Call(L.mx_quantize_cbf, (D(d), mx.MX_ROLE_ACT, x_src, D(cq[0]), mx.MX_RNE, 0, x_given, stream),
-                 "quantize", ("quantize_act", shape), 0, x_bytes, "quantize X"),
-            Call(L.mx_quantize_cbf, (D(d), mx.MX_ROLE_WEIGHT, w.data_ptr(), D(cq[1]), mx.MX_RNE, 0, 0, stream),
-                 "quantize", ("quantize_weight", shape), 0, nw * (rd + qb), "quantize W"),
-            Call(L.mx_quantize_cbf, (D(d), mx.MX_ROLE_GRAD, dy.data_ptr(), D(cq[2]), mx.MX_SR, sr_seed, 0, stream),
-                 "quantize", ("quantize_grad", shape), 0, ny * (rd + qb), "quantize dY"),
-            Call(L.mx_conv_fwd, (D(d), D(cq[1]), D(cq[0]), y.data_ptr(), stream),
-                 "fwd", ("conv_fwd", shape), f, nw * qb + nx * qbx + 4 * ny, "fwd"),
-            Call(L.mx_conv_dgrad, (D(d), D(cq[1]), D(cq[2]), dx.data_ptr(), stream),
-                 "dgrad", ("conv_dgrad", shape), f, (nw + ny) * qb + 4 * nx, "dgrad"),
-            Call(L.mx_conv_wgrad, (D(d), D(cq[2]), D(cq[0]), dw.data_ptr(), ws.data_ptr(), ws_bytes, stream),
-                 "wgrad", ("conv_wgrad", shape), f, ny * qb + nx * qbx + 4 * nw, "wgrad"),
-            Call(L.mx_dequantize, (D(d), mx.MX_ROLE_ACT, D(cq[0]), xdq.data_ptr(), stream),
-                 "dequantize", ("dequantize_act", shape), 0, nx * (qbx + 4), "dequantize X"),
-        ]
-        prev = (d, y, calls[-4])
-        layer_starts.append(len(calls) - 7)
+    layer_starts = []  # index of each (format, layer)'s first call (the 7-call MicroQonv step)
+    for fmt in fmts:
+        fname = WL.FMT_NAMES[fmt]
+        qb = mx.CODE_BITS[fmt] / 8 + sb                # quantized bytes per element (codes + block scales)
+        qbx = mx.CODE_BITS[afmt or fmt] / 8 + sb       # the same for the activation X
+        prev = None  # --producer-amax: (descriptor, y, fwd Call) of the previous layer
+        for li, lay in enumerate(wl.layers):
+            d = mx.desc_from_layer(lay, fmt, afmt, a.block)
+            if li not in inputs:
+                inputs[li] = (WL.gen_x(lay, wl.x_dist, WL.seed_for(wl.cfg_index, li, 1)).to(dev),
+                              WL.gen_w(lay, WL.seed_for(wl.cfg_index, li, 2)).to(dev),
+                              WL.gen_dy(lay, wl.dy_sigma, WL.seed_for(wl.cfg_index, li, 3)).to(dev))
+            x, w, dy = inputs[li]
+            sr_seed = WL.seed_for(wl.cfg_index, li, 4)
+            shape = lay.tag()
+            nx, nw, ny = lay.numel_x(), lay.numel_w(), lay.numel_dy()
+            f = lay.flops()
+            if a.flow:
+                calls += flow_calls(a.flow, L, mx, torch, D, d, lay, x, w, dy, sr_seed, fmt, fname, qb, stream, keep, dev)
+                nxc = lay.h_out * lay.w_out * lay.k_h * lay.k_w * lay.c_in * lay.n
+                flow_stats["activation_elements"] += nx
+                flow_stats["quantized_elements"] += {"microqonv": nx, "im2col-square": nxc, "dacapo": 2 * nxc}[a.flow]
+                flow_stats["stored_activation_bytes"] += {"microqonv": nx * qb, "im2col-square": nxc * qb,
+                                                          "dacapo": nx * 4.0}[a.flow]
+                continue
+            qx, qw, qdy = (mx.QTensor(d, r, dev) for r in (mx.MX_ROLE_ACT, mx.MX_ROLE_WEIGHT, mx.MX_ROLE_GRAD))
+            y = torch.empty(lay.h_out, lay.w_out, lay.c_out, lay.n, device=dev)
+            dx = torch.empty(lay.h, lay.w, lay.c_in, lay.n, device=dev)
+            dw = torch.empty(lay.c_out, lay.c_in, lay.k_h, lay.k_w, device=dev)
+            xdq = torch.empty_like(x)
+            cq = [q.c() for q in (qx, qw, qdy)]
+            keep += [d, qx, qw, qdy, y, dx, dw, xdq, cq]
+            # --producer-amax: where the previous layer's output has this
+            # layer's input shape, X is that output, its fwd writes max|y|
+            # into qx.amax and X is quantized in one pass (amax given)
+            chained = (a.producer_amax and prev is not None
+                       and (prev[0].h_out, prev[0].w_out, prev[0].c_out, prev[0].n) == (lay.h, lay.w, lay.c_in, lay.n))
+            if chained:
+                pd, py, pcall = prev
+                # the previous fwd's amax buffer: word 0 is the amax this layer's X is quantized with
+                abuf = torch.empty(mx.mx_fwd_amax_bytes(pd) // 4, device=dev)
+                keep.append(abuf)
+                qx.amax = abuf[:1]
+                cq[0] = qx.c()
+                pcall.fn = L.mx_conv_fwd_amax
+                pcall.args = pcall.args[:-1] + (abuf.data_ptr(), stream)
+                pcall.name = "fwd (+amax)"
+                x_src, x_given, x_bytes = py.data_ptr(), 1, nx * (4 + qbx)
+                n_chained += 1
+            else:
+                x_src, x_given, x_bytes = x.data_ptr(), 0, nx * (rd + qbx)
+            calls += [
+                Call(L.mx_quantize_cbf, (D(d), mx.MX_ROLE_ACT, x_src, D(cq[0]), mx.MX_RNE, 0, x_given, stream),
+                     "quantize", ("quantize_act", shape, fname), 0, x_bytes, "quantize X"),
+                Call(L.mx_quantize_cbf, (D(d), mx.MX_ROLE_WEIGHT, w.data_ptr(), D(cq[1]), mx.MX_RNE, 0, 0, stream),
+                     "quantize", ("quantize_weight", shape, fname), 0, nw * (rd + qb), "quantize W"),
+                Call(L.mx_quantize_cbf, (D(d), mx.MX_ROLE_GRAD, dy.data_ptr(), D(cq[2]), mx.MX_SR, sr_seed, 0,
+                                         stream),
+                     "quantize", ("quantize_grad", shape, fname), 0, ny * (rd + qb), "quantize dY"),
+                Call(L.mx_conv_fwd, (D(d), D(cq[1]), D(cq[0]), y.data_ptr(), stream),
+                     "fwd", ("conv_fwd", shape, fname), f, nw * qb + nx * qbx + 4 * ny, "fwd"),
+                Call(L.mx_conv_dgrad, (D(d), D(cq[1]), D(cq[2]), dx.data_ptr(), stream),
+                     "dgrad", ("conv_dgrad", shape, fname), f, (nw + ny) * qb + 4 * nx, "dgrad"),
+                Call(L.mx_conv_wgrad, (D(d), D(cq[2]), D(cq[0]), dw.data_ptr(), ws.data_ptr(), ws_bytes, stream),
+                     "wgrad", ("conv_wgrad", shape, fname), f, ny * qb + nx * qbx + 4 * nw, "wgrad"),
+                Call(L.mx_dequantize, (D(d), mx.MX_ROLE_ACT, D(cq[0]), xdq.data_ptr(), stream),
+                     "dequantize", ("dequantize_act", shape, fname), 0, nx * (qbx + 4), "dequantize X"),
+            ]
+            prev = (d, y, calls[-4])
+            layer_starts.append(len(calls) - 7)
+    keep.append(inputs)
     if wl.lr_buffer is not None and not a.flow:
         nmaps, c, h, w_ = wl.lr_buffer
         lr_fmt = mx.MX_UE2M1 if a.replay_compact else mx.MX_E2M1
@@ -267,11 +293,12 @@ def main():
         n_el = maps.numel()
         qb4 = (3 if a.replay_compact else 4) / 8 + 1 / 64
         shape = f"replay buffer {nmaps}x{c}@{h}x{w_}"
+        lrn = "ue2m1" if a.replay_compact else "e2m1"
         calls += [
             Call(L.mx_quantize_cbf, (D(d), mx.MX_ROLE_ACT, maps.data_ptr(), D(cq), mx.MX_RNE, 0, 0, stream),
-                 "quantize", ("quantize_replay", shape), 0, n_el * (8 + qb4), "quantize replay buffer"),
+                 "quantize", ("quantize_replay", shape, lrn), 0, n_el * (8 + qb4), "quantize replay buffer"),
             Call(L.mx_dequantize, (D(d), mx.MX_ROLE_ACT, D(cq), back.data_ptr(), stream),
-                 "dequantize", ("dequantize_replay", shape), 0, n_el * (qb4 + 4), "dequantize replay buffer"),
+                 "dequantize", ("dequantize_replay", shape, lrn), 0, n_el * (qb4 + 4), "dequantize replay buffer"),
         ]
     torch.cuda.synchronize()
     t_gen = time.time() - t_gen
@@ -281,12 +308,13 @@ def main():
     # Layer DAG on three streams (lanes): lane 0 quantizes X, runs fwd and
     # dequantizes X; lane 1 quantizes W and runs dgrad; lane 2 quantizes dY
     # and runs wgrad.  fwd waits for W, dgrad for dY, wgrad for X; each layer
-    # forks from lane 0 and joins back into it, so layers run in order.
-    # Calls outside the layers (the replay buffer) run on lane 0 after them.
-    # (graph replay only: issued eagerly, the event calls between the launches
-    # cost more host time than the overlap saves)
+    # (of each format) forks from lane 0 and joins back into it, so layers run
+    # in order, as the layers of a network would.  Calls outside the layers
+    # (the replay buffer) run on lane 0 after them.  (graph replay only:
+    # issued eagerly, the event calls between the launches cost more host
+    # time than the overlap saves)
     dag = (not a.serial and not a.eager and not a.flow and n_chained == 0
-           and len(layer_starts) == len(wl.layers))
+           and len(layer_starts) == len(wl.layers) * len(fmts))
     LANE = (0, 1, 2, 0, 1, 2, 0)
     lanes = [torch.cuda.current_stream(), torch.cuda.Stream(), torch.cuda.Stream()]
     in_layer = set()
@@ -414,11 +442,11 @@ def main():
     for k in range(a.steps):
         for i in range(len(calls)):
             if i == 0:
-                prev = ev[k - 1][-1] if k > 0 else None
-                if prev is None:
+                prev_ev = ev[k - 1][-1] if k > 0 else None
+                if prev_ev is None:
                     per_call[k][i] = (pstart or start).elapsed_time(ev[k][0])
                 else:
-                    per_call[k][i] = prev.elapsed_time(ev[k][0])
+                    per_call[k][i] = prev_ev.elapsed_time(ev[k][0])
             else:
                 per_call[k][i] = ev[k][i - 1].elapsed_time(ev[k][i])
     # average over steps (NaN-safe)
@@ -429,8 +457,7 @@ def main():
 
     groups = {}
     for i, c in enumerate(calls):
-        gkey = c.group
-        gi = groups.setdefault(gkey, {"ms": 0.0, "n": 0, "flops": c.flops, "bytes": c.bytes, "op": c.op})
+        gi = groups.setdefault(c.group, {"ms": 0.0, "n": 0, "flops": c.flops, "bytes": c.bytes, "op": c.op})
         gi["ms"] += avg_ms[i]
         gi["n"] += 1
     by_op = {}
@@ -440,21 +467,22 @@ def main():
         o["flops"] += c.flops
         o["bytes"] += c.bytes
 
+    def peak_of(fname):
+        return PEAK_MFMA[mfma_dtype(a.block, fmts_by_name.get(fname, mx.MX_E2M1), mx)]
+
     dom_key, dom = max(groups.items(), key=lambda kv: kv[1]["ms"])
     launch_s = dom["ms"] / dom["n"] / 1e3
     ai = dom["flops"] / dom["bytes"] if dom["bytes"] else 0.0
-    # the GEMMs' MFMA type: fp4 (scaled, 32x32 E8M0 blocks), else the
-    # exact fp16 decode (bf16 for E4M3 operands); both 16-bit peaks are equal
-    mfma_t = "fp4" if a.block == 32 else ("bf16" if fmt == mx.MX_E4M3 else "f16")
-    if dom["flops"] and ai >= PEAK_MFMA[mfma_t] / PEAK_HBM:
+    dom_peak = peak_of(dom_key[2])
+    if dom["flops"] and ai >= dom_peak / PEAK_HBM:
         achieved = dom["flops"] / launch_s
-        roof = {"bound": "mfma", "achieved": achieved / 1e12, "peak": PEAK_MFMA[mfma_t] / 1e12,
-                "unit": "TFLOP/s", "mfma_dtype": mfma_t}
+        roof = {"bound": "mfma", "achieved": achieved / 1e12, "peak": dom_peak / 1e12,
+                "unit": "TFLOP/s", "mfma_dtype": mfma_dtype(a.block, fmts_by_name.get(dom_key[2]), mx)}
     else:
         achieved = dom["bytes"] / launch_s
         roof = {"bound": "hbm", "achieved": achieved / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["kernel"] = f"{dom_key[0]} [{dom_key[1]}]"
+    roof["kernel"] = f"{dom_key[0]} [{dom_key[1]}] {dom_key[2]}"
     roof["launch_us"] = launch_s * 1e6
     roof["algorithmic_per_launch"] = {"flops": dom["flops"], "bytes": dom["bytes"]}
     roof["traffic"] = None
@@ -462,23 +490,23 @@ def main():
     if os.path.exists(tfile):
         try:
             tr = json.load(open(tfile))
-            ent = tr.get("kernels", {}).get(f"{a.workload}:{dom_key[0]}:{dom_key[1]}")
+            ent = tr.get("kernels", {}).get(f"{a.workload}:{dom_key[2]}:{dom_key[0]}:{dom_key[1]}")
             if ent and tr.get("source_hash") == kernel_source_hash():
                 roof["traffic"] = ent["hbm_bytes_per_launch"]
         except (ValueError, KeyError):
             pass
     roof["ai_flop_per_byte"] = ai
 
-    # every call group (one call of one layer shape), slowest first: GEMMs
-    # against the dense MFMA peak and against what the roofline allows at
-    # their arithmetic intensity (algorithmic bytes: quantized operands read
-    # once, fp32 output written once); codec calls against 8 TB/s
-    pk = PEAK_MFMA[mfma_t]
+    # every call group (one call of one layer shape in one format), slowest
+    # first: GEMMs against the dense MFMA peak and against what the roofline
+    # allows at their arithmetic intensity (algorithmic bytes: quantized
+    # operands read once, fp32 output written once); codec calls against 8 TB/s
     per_layer = []
-    for (gop, tag), g in sorted(groups.items(), key=lambda kv: -kv[1]["ms"]):
+    for (gop, tag, fname), g in sorted(groups.items(), key=lambda kv: -kv[1]["ms"]):
         ls = g["ms"] / g["n"] / 1e3
-        ent = {"call": gop, "shape": tag, "launches": g["n"], "launch_us": round(ls * 1e6, 2)}
+        ent = {"call": gop, "shape": tag, "fmt": fname, "launches": g["n"], "launch_us": round(ls * 1e6, 2)}
         if g["flops"]:
+            pk = peak_of(fname)
             att = min(pk, g["flops"] / g["bytes"] * PEAK_HBM) if g["bytes"] else pk
             ach = g["flops"] / ls
             ent.update({"tflops": round(ach / 1e12, 2), "frac_of_peak": round(ach / pk, 4),
@@ -488,9 +516,42 @@ def main():
             ent.update({"gbps": round(ach / 1e9, 1), "frac_of_hbm": round(ach / PEAK_HBM, 4)})
         per_layer.append(ent)
 
+    # per element format: its GEMM and codec rates and its share of the step
+    per_fmt = {}
+    for i, c in enumerate(calls):
+        pf = per_fmt.setdefault(c.group[2], {"ms": 0.0, "gemm_ms": 0.0, "gemm_flops": 0, "q_ms": 0.0,
+                                             "q_bytes": 0.0, "calls_ms": {}})
+        pf["ms"] += avg_ms[i]
+        pf["calls_ms"][c.group[0]] = pf["calls_ms"].get(c.group[0], 0.0) + avg_ms[i]
+        if c.flops:
+            pf["gemm_ms"] += avg_ms[i]
+            pf["gemm_flops"] += c.flops
+        elif c.op == "quantize":
+            pf["q_ms"] += avg_ms[i]
+            pf["q_bytes"] += c.bytes
+    formats = {}
+    for fname, pf in per_fmt.items():
+        e = {"calls_ms_per_step": {k: round(v, 4) for k, v in pf["calls_ms"].items()},
+             "ms_per_step_calls_alone": round(pf["ms"], 4)}
+        if pf["gemm_flops"]:
+            e["gemm_tflops"] = round(pf["gemm_flops"] / (pf["gemm_ms"] / 1e3) / 1e12, 2)
+            e["gemm_frac_of_peak"] = round(pf["gemm_flops"] / (pf["gemm_ms"] / 1e3) / peak_of(fname), 4)
+            e["step_tflops_calls_alone"] = round(pf["gemm_flops"] / (pf["ms"] / 1e3) / 1e12, 2)
+        if pf["q_ms"]:
+            e["quantize_gbps"] = round(pf["q_bytes"] / (pf["q_ms"] / 1e3) / 1e9, 1)
+        formats[fname] = e
+
     conv_ms = sum(by_op.get(o, {"ms": 0.0})["ms"] for o in ("fwd", "dgrad", "wgrad"))
     q_ms = by_op.get("quantize", {"ms": 0.0})["ms"]
     q_bytes = by_op.get("quantize", {"bytes": 0})["bytes"]
+    fnames = [WL.FMT_NAMES[f] for f in fmts]
+    dtypes = sorted({mfma_dtype(a.block, f, mx) for f in fmts})
+    lay0 = wl.layers[0]
+    wdesc = f"{a.workload}: {wl.name}"
+    if len(fmts) > 1:
+        wdesc += ", run in " + " + ".join(n.upper() for n in fnames)
+    if wl.lr_buffer is not None and not a.flow:
+        wdesc += ", + latent-replay buffer %dx%d@%dx%d codec" % wl.lr_buffer
 
     result = {
         "metric": "effective TFLOP/s of MX conv fwd+dgrad+wgrad (implicit im2col); quantize GB/s",
@@ -503,15 +564,16 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": mfma_t,
+        "dtype": "+".join(dtypes),
         "data": "synthetic",
-        "config": {"workload": f"{a.workload}: {wl.name}", "layers": len(wl.layers),
-                   "batch": wl.layers[0].n, "elem_fmt": WL.FMT_NAMES[fmt],
+        "config": {"workload": wdesc, "layers": len(wl.layers),
+                   "batch": lay0.n, "elem_fmts": fnames,
                    **({"act_fmt": a.act_fmt, "variant": "MicroQonv+ (FP6 activations)"} if afmt else {}),
                    "block": "8x8 E4M3 scale + fp32 tensor scale" if a.block == 8
                             else "32x32 E8M0 scale, no tensor scale (scaled FP4 MFMA)",
-                   "step": "per layer: quantize X,W,dY; fwd; dgrad; wgrad; dequantize Xq"
-                           + ("; replay buffer quantize+dequantize" if wl.lr_buffer else ""),
+                   "step": ("per format and layer: quantize X,W,dY; fwd; dgrad; wgrad; dequantize Xq"
+                            + ("; then the replay buffer quantize+dequantize" if wl.lr_buffer else "")),
+                   "step_flops": total_flops,
                    "graph": bool(graph is not None),
                    "streams": "layer DAG on 3 streams" if dag else "1 (serial)",
                    "producer_amax": {"chained_layers": n_chained} if a.producer_amax else False,
@@ -519,6 +581,7 @@ def main():
         "conv_tflops": total_flops / (conv_ms / 1e3) / 1e12 if conv_ms > 0 else None,
         "quantize_gbps": q_bytes / (q_ms / 1e3) / 1e9 if q_ms > 0 else None,
         "step_breakdown_ms": {k: v["ms"] for k, v in by_op.items()},
+        "formats": formats,
         **({"flow": {"name": a.flow,
                      "quantizations_per_activation_element": flow_stats["quantized_elements"]
                      / max(flow_stats["activation_elements"], 1),
@@ -531,58 +594,164 @@ def main():
         "kernel_source": kernel_source_hash(),
     }
     if a.verbose:
-        result["groups"] = {f"{k[0]} [{k[1]}]": {"ms_total": v["ms"], "launches": v["n"],
-                                                 "flops": v["flops"], "bytes": v["bytes"]}
+        result["groups"] = {f"{k[0]} [{k[1]}] {k[2]}": {"ms_total": v["ms"], "launches": v["n"],
+                                                        "flops": v["flops"], "bytes": v["bytes"]}
                             for k, v in sorted(groups.items(), key=lambda kv: -kv[1]["ms"])}
 
     if not a.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, fmt, afmt, a.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(wl, fmts, afmt, a.cpu_seconds, a.flow is None)
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(wl, fmt, afmt, budget_s):
-    """The CPU oracle, as it stands, on a bounded sample of the workload: the
-    full quantize X/W/dY + fp64 fwd/dgrad/wgrad of the stack's layers, taken in
-    stack order (repeated layers included, wrapping round to the first) until
-    the time budget is spent; reported in the metric's unit.  Input generation
-    is outside the timed region, as it is for the GPU."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, fmts, afmt, budget_s, with_replay=True):
+    """The CPU oracle, as it stands, on a bounded sample of the workload,
+    reported in the metric's unit (input generation is outside the timed
+    region, as it is for the GPU).
+
+    Stacks whose layers the oracle can compute in full within the budget:
+    the full quantize X/W/dY + fp64 fwd/dgrad/wgrad of the stack's layers,
+    taken in stack order (wrapping round) until the budget is spent.
+
+    A layer too large for that (the 256-channel stress layer: 2.8 TFLOP per
+    format): per format, the full quantize of X, W and dY, the fp32
+    dequantize of Xq, the fp64 operands of the GEMMs, and each GEMM on a
+    seeded sample of outputs, evaluated one by one; the step time is the
+    measured time of the full parts plus the sampled GEMM time scaled to all
+    outputs (every output of one GEMM costs the same: one dot product over
+    its K).  The replay buffer is quantized and dequantized in full."""
+    import numpy as np
+
     import oracle as O
     from microscaling_quantized_convolution_mx_amd import workloads as WL
 
     O.lib()
     import microscaling_quantized_convolution_mx_amd as mx
     ofmt = {mx.MX_E2M1: O.E2M1, mx.MX_E2M3: O.E2M3, mx.MX_E4M3: O.E4M3, mx.MX_E3M2: O.E3M2}
-    fmt_w, fmt_x = ofmt[fmt], ofmt[afmt or fmt]
-    flops = 0
-    spent = 0.0
-    done = 0
-    li = 0
-    while spent < budget_s and done < 4 * len(wl.layers):
-        lay = wl.layers[li % len(wl.layers)]
-        x = WL.gen_x(lay, wl.x_dist, WL.seed_for(wl.cfg_index, li % len(wl.layers), 1)).numpy()
-        w = WL.gen_w(lay, WL.seed_for(wl.cfg_index, li % len(wl.layers), 2)).numpy()
-        dy = WL.gen_dy(lay, wl.dy_sigma, WL.seed_for(wl.cfg_index, li % len(wl.layers), 3)).numpy()
-        cv = O.conv(lay.n, lay.c_in, lay.c_out, lay.h, lay.w, lay.k_h, lay.k_w,
-                    lay.stride_h, lay.stride_w, lay.pad_h, lay.pad_w)
-        t0 = time.perf_counter()
-        qx = O.quantize(O.ACT, fmt_x, x)
-        qw = O.quantize(O.WEIGHT, fmt_w, w)
-        qdy = O.quantize(O.GRAD, fmt_w, dy, O.SR, WL.seed_for(wl.cfg_index, li % len(wl.layers), 4))
-        xe, we, dye = qx.exact(), qw.exact(), qdy.exact()
-        O.conv_fwd(cv, we, xe)
-        O.conv_dgrad(cv, we, dye)
-        O.conv_wgrad(cv, dye, xe)
-        spent += time.perf_counter() - t0
-        flops += 3 * lay.flops()
-        done += 1
-        li += 1
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    threads = O.threads()
     nl = len(wl.layers)
-    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"full quantize X/W/dY + fp64 fwd/dgrad/wgrad of {done} layer(s) of the "
-                      f"{nl}-layer stack taken in order from the first, {flops / 1e9:.2f} GFLOP "
-                      f"in {spent:.1f} s",
-            "seconds": spent}
+    if max(3 * l.flops() for l in wl.layers) <= 200e9:
+        fmt_w = ofmt[fmts[0]]
+        fmt_x = ofmt[afmt or fmts[0]]
+        flops = 0
+        spent = 0.0
+        done = 0
+        li = 0
+        while spent < budget_s and done < 4 * nl:
+            lay = wl.layers[li % nl]
+            x = WL.gen_x(lay, wl.x_dist, WL.seed_for(wl.cfg_index, li % nl, 1)).numpy()
+            w = WL.gen_w(lay, WL.seed_for(wl.cfg_index, li % nl, 2)).numpy()
+            dy = WL.gen_dy(lay, wl.dy_sigma, WL.seed_for(wl.cfg_index, li % nl, 3)).numpy()
+            cv = O.conv(lay.n, lay.c_in, lay.c_out, lay.h, lay.w, lay.k_h, lay.k_w,
+                        lay.stride_h, lay.stride_w, lay.pad_h, lay.pad_w)
+            t0 = time.perf_counter()
+            qx = O.quantize(O.ACT, fmt_x, x)
+            qw = O.quantize(O.WEIGHT, fmt_w, w)
+            qdy = O.quantize(O.GRAD, fmt_w, dy, O.SR, WL.seed_for(wl.cfg_index, li % nl, 4))
+            xe, we, dye = qx.exact(), qw.exact(), qdy.exact()
+            O.conv_fwd(cv, we, xe)
+            O.conv_dgrad(cv, we, dye)
+            O.conv_wgrad(cv, dye, xe)
+            spent += time.perf_counter() - t0
+            flops += 3 * lay.flops()
+            done += 1
+            li += 1
+        return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+                "cpu_model": cpu_model(), "nproc": os.cpu_count(),
+                "sample": f"full quantize X/W/dY + fp64 fwd/dgrad/wgrad of {done} layer(s) of the "
+                          f"{nl}-layer stack ({WL.FMT_NAMES[fmts[0]]}) taken in order from the first, "
+                          f"{flops / 1e9:.2f} GFLOP in {spent:.1f} s",
+                "seconds": spent}
+
+    # sampled stress layer
+    npts = {"fwd": 65536, "dgrad": 65536, "wgrad": 4096}
+    measured = 0.0      # seconds actually spent in the oracle
+    step_s = 0.0        # the same plus the sampled GEMMs scaled to all outputs
+    flops = 0
+    q_bytes = 0.0
+    q_s = 0.0
+    gemm_pts_flops = 0.0
+    gemm_pts_s = 0.0
+    detail = {}
+    rng = np.random.default_rng(12345)
+    for fmt in fmts:
+        fw, fx = ofmt[fmt], ofmt[afmt or fmt]
+        for li, lay in enumerate(wl.layers):
+            x = WL.gen_x(lay, wl.x_dist, WL.seed_for(wl.cfg_index, li, 1)).numpy()
+            w = WL.gen_w(lay, WL.seed_for(wl.cfg_index, li, 2)).numpy()
+            dy = WL.gen_dy(lay, wl.dy_sigma, WL.seed_for(wl.cfg_index, li, 3)).numpy()
+            cv = O.conv(lay.n, lay.c_in, lay.c_out, lay.h, lay.w, lay.k_h, lay.k_w,
+                        lay.stride_h, lay.stride_w, lay.pad_h, lay.pad_w)
+            t = {}
+            t0 = time.perf_counter()
+            qx = O.quantize(O.ACT, fx, x)
+            qw = O.quantize(O.WEIGHT, fw, w)
+            qdy = O.quantize(O.GRAD, fw, dy, O.SR, WL.seed_for(wl.cfg_index, li, 4))
+            t["quantize"] = time.perf_counter() - t0
+            t0 = time.perf_counter()
+            O.dequantize(qx)
+            t["dequantize"] = time.perf_counter() - t0
+            t0 = time.perf_counter()
+            xe, we, dye = qx.exact(), qw.exact(), qdy.exact()
+            t["gemm_operands"] = time.perf_counter() - t0
+            del qx, qw, qdy
+            full = {}
+            for op, n_out, fn, args in (("fwd", lay.numel_dy(), O.conv_fwd_points, (we, xe)),
+                                        ("dgrad", lay.numel_x(), O.conv_dgrad_points, (we, dye)),
+                                        ("wgrad", lay.numel_w(), O.conv_wgrad_points, (dye, xe))):
+                k = min(npts[op], n_out)
+                idx = np.sort(rng.choice(n_out, size=k, replace=False)).astype(np.int64)
+                t0 = time.perf_counter()
+                fn(cv, *args, idx)
+                dt = time.perf_counter() - t0
+                t[op + "_points"] = dt
+                full[op] = dt * n_out / k
+                gemm_pts_flops += lay.flops() * k / n_out
+                gemm_pts_s += dt
+            del xe, we, dye
+            meas = sum(t.values())
+            measured += meas
+            step_s += t["quantize"] + t["dequantize"] + t["gemm_operands"] + sum(full.values())
+            flops += 3 * lay.flops()
+            nq = lay.numel_x() + lay.numel_w() + lay.numel_dy()
+            q_bytes += nq * (8 + WL.FMT_BITS[fmt] / 8 + 1 / 64)
+            q_s += t["quantize"]
+            detail[f"{WL.FMT_NAMES[fmt]} L{li}"] = {k: round(v, 3) for k, v in t.items()}
+    if wl.lr_buffer is not None and with_replay:
+        nmaps, c, h, w_ = wl.lr_buffer
+        maps = WL.gen_lr_maps(nmaps, c, h, w_, WL.seed_for(wl.cfg_index, 0, 5)).numpy()
+        t0 = time.perf_counter()
+        q = O.quantize(O.ACT, O.E2M1, maps)
+        tq = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        O.dequantize(q)
+        tdq = time.perf_counter() - t0
+        measured += tq + tdq
+        step_s += tq + tdq
+        q_bytes += maps.size * (8 + 4 / 8 + 1 / 64)
+        q_s += tq
+        detail["replay buffer"] = {"quantize": round(tq, 3), "dequantize": round(tdq, 3)}
+    return {"value": flops / step_s / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(), "nproc": os.cpu_count(),
+            "sample": (f"per format ({', '.join(WL.FMT_NAMES[f] for f in fmts)}) and layer: full quantize X/W/dY, "
+                       f"fp32 dequantize Xq and fp64 GEMM operands; fwd, dgrad and wgrad on "
+                       f"{npts['fwd']}, {npts['dgrad']} and {npts['wgrad']} seeded sampled outputs, their time "
+                       f"scaled to all outputs; replay buffer quantize + dequantize in full"
+                       if wl.lr_buffer else ""),
+            "seconds": measured,
+            "extrapolated_step_seconds": step_s,
+            "oracle_gemm_gflops_on_sample": gemm_pts_flops / gemm_pts_s / 1e9 if gemm_pts_s else None,
+            "oracle_quantize_gbps": q_bytes / q_s / 1e9 if q_s else None,
+            "detail_seconds": detail}
 
 
 if __name__ == "__main__":

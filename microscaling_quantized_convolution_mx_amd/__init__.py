@@ -125,11 +125,41 @@ def role_fmt(d: mx_conv_desc, role: int) -> int:
     return d.act_fmt if (role == MX_ROLE_ACT and d.act_fmt != 0) else d.elem_fmt
 
 
-def _ptr(t) -> int | None:
+def role_numel(d: mx_conv_desc, role: int) -> int:
+    """fp32 elements of the tensor of `role` under d (0 for a bad role)."""
+    if role == MX_ROLE_ACT:
+        return d.h * d.w * d.c_in * d.n
+    if role == MX_ROLE_GRAD:
+        return max(d.h_out, 0) * max(d.w_out, 0) * d.c_out * d.n
+    if role == MX_ROLE_WEIGHT:
+        return d.c_out * d.c_in * d.k_h * d.k_w
+    return 0
+
+
+def _buf(t, need: int, what: str, fp32: bool = True) -> int | None:
+    """Device address of a caller buffer after checking that it can take the
+    call: a float32 tensor (fp32 data; any dtype for workspace and scratch
+    words), contiguous, at least `need` bytes, in device memory.  The checks
+    run before anything touches the GPU, so a host, strided, mistyped or
+    short tensor raises ValueError instead of reaching a kernel.  An int is
+    taken as a raw device address that the caller vouches for, as at the C
+    ABI; None passes through (the library reports MX_ERR_NULL)."""
     if t is None:
         return None
     if isinstance(t, int):
         return t
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what}: expected a torch tensor or a device address, got {type(t).__name__}")
+    if fp32 and t.dtype != torch.float32:
+        raise ValueError(f"{what}: must be float32, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what}: must be contiguous")
+    nbytes = t.numel() * t.element_size()
+    if nbytes < need:
+        raise ValueError(f"{what}: {nbytes} bytes, the call needs {need}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{what}: must be in device memory, got a {t.device.type} tensor")
     return t.data_ptr() if t.numel() > 0 else None
 
 
@@ -182,21 +212,36 @@ class QTensor:
                           self.tensor_scale.data_ptr(), self.amax.data_ptr())
 
 
-def _q(q) -> ctypes.POINTER(mx_qtensor):
+def _q(q, d: mx_conv_desc | None = None, role: int | None = None, what: str = "q"):
+    """Pointer to the mx_qtensor of q.  A QTensor is checked against the
+    buffers the call needs for `role` under d (as _buf does for plain
+    tensors); an mx_qtensor struct holds raw device addresses and passes
+    through unchecked."""
     if q is None:
         return None
-    return ctypes.byref(q.c() if isinstance(q, QTensor) else q)
+    if isinstance(q, QTensor):
+        if d is not None and role is not None:
+            _buf(q.codes, mx_code_bytes(d, role), f"{what}.codes", fp32=False)
+            _buf(q.scales, mx_scale_bytes(d, role), f"{what}.scales", fp32=False)
+        _buf(q.tensor_scale, 4, f"{what}.tensor_scale")
+        _buf(q.amax, 4, f"{what}.amax")
+        return ctypes.byref(q.c())
+    if isinstance(q, mx_qtensor):
+        return ctypes.byref(q)
+    raise TypeError(f"{what}: expected a QTensor or an mx_qtensor, got {type(q).__name__}")
 
 
 def mx_quantize_cbf(d: mx_conv_desc, role: int, src, dst, rounding: int = MX_RNE, seed: int = 0,
                     amax_given: bool = False, stream=None) -> None:
-    _check(lib().mx_quantize_cbf(ctypes.byref(d), role, _ptr(src), _q(dst), rounding,
-                                 seed & (2 ** 64 - 1), int(bool(amax_given)), _stream(stream)),
-           "mx_quantize_cbf")
+    args = (ctypes.byref(d), role, _buf(src, 4 * role_numel(d, role), "src"), _q(dst, d, role, "dst"), rounding,
+            seed & (2 ** 64 - 1), int(bool(amax_given)))
+    _check(lib().mx_quantize_cbf(*args, _stream(stream)), "mx_quantize_cbf")
 
 
 def mx_conv_fwd(d: mx_conv_desc, wq, xq, y, stream=None) -> None:
-    _check(lib().mx_conv_fwd(ctypes.byref(d), _q(wq), _q(xq), _ptr(y), _stream(stream)), "mx_conv_fwd")
+    args = (ctypes.byref(d), _q(wq, d, MX_ROLE_WEIGHT, "wq"), _q(xq, d, MX_ROLE_ACT, "xq"),
+            _buf(y, 4 * role_numel(d, MX_ROLE_GRAD), "y"))
+    _check(lib().mx_conv_fwd(*args, _stream(stream)), "mx_conv_fwd")
 
 
 def mx_fwd_amax_bytes(d: mx_conv_desc) -> int:
@@ -204,27 +249,34 @@ def mx_fwd_amax_bytes(d: mx_conv_desc) -> int:
 
 
 def mx_conv_fwd_amax(d: mx_conv_desc, wq, xq, y, y_amax, stream=None) -> None:
-    _check(lib().mx_conv_fwd_amax(ctypes.byref(d), _q(wq), _q(xq), _ptr(y), _ptr(y_amax), _stream(stream)),
-           "mx_conv_fwd_amax")
+    args = (ctypes.byref(d), _q(wq, d, MX_ROLE_WEIGHT, "wq"), _q(xq, d, MX_ROLE_ACT, "xq"),
+            _buf(y, 4 * role_numel(d, MX_ROLE_GRAD), "y"), _buf(y_amax, mx_fwd_amax_bytes(d), "y_amax", fp32=False))
+    _check(lib().mx_conv_fwd_amax(*args, _stream(stream)), "mx_conv_fwd_amax")
 
 
 def mx_conv_dgrad(d: mx_conv_desc, wq, dyq, dx, stream=None) -> None:
-    _check(lib().mx_conv_dgrad(ctypes.byref(d), _q(wq), _q(dyq), _ptr(dx), _stream(stream)),
-           "mx_conv_dgrad")
+    args = (ctypes.byref(d), _q(wq, d, MX_ROLE_WEIGHT, "wq"), _q(dyq, d, MX_ROLE_GRAD, "dyq"),
+            _buf(dx, 4 * role_numel(d, MX_ROLE_ACT), "dx"))
+    _check(lib().mx_conv_dgrad(*args, _stream(stream)), "mx_conv_dgrad")
 
 
 def mx_conv_wgrad(d: mx_conv_desc, dyq, xq, dw, workspace, ws_bytes: int | None = None,
                   stream=None) -> None:
+    """ws_bytes: bytes of workspace the library may use (default: all of it)."""
     if ws_bytes is None:
-        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().mx_conv_wgrad(ctypes.byref(d), _q(dyq), _q(xq), _ptr(dw), _ptr(workspace),
-                               ws_bytes, _stream(stream)), "mx_conv_wgrad")
+        ws_bytes = 0 if workspace is None or isinstance(workspace, int) else workspace.numel() * workspace.element_size()
+    args = (ctypes.byref(d), _q(dyq, d, MX_ROLE_GRAD, "dyq"), _q(xq, d, MX_ROLE_ACT, "xq"),
+            _buf(dw, 4 * role_numel(d, MX_ROLE_WEIGHT), "dw"), _buf(workspace, ws_bytes, "workspace", fp32=False),
+            ws_bytes)
+    _check(lib().mx_conv_wgrad(*args, _stream(stream)), "mx_conv_wgrad")
 
 
 def mx_im2col_cbf(d: mx_conv_desc, x, xcol, stream=None) -> None:
-    _check(lib().mx_im2col_cbf(ctypes.byref(d), _ptr(x), _ptr(xcol), _stream(stream)), "mx_im2col_cbf")
+    ncol = max(d.h_out, 0) * max(d.w_out, 0) * d.k_h * d.k_w * d.c_in * d.n
+    args = (ctypes.byref(d), _buf(x, 4 * role_numel(d, MX_ROLE_ACT), "x"), _buf(xcol, 4 * ncol, "xcol"))
+    _check(lib().mx_im2col_cbf(*args, _stream(stream)), "mx_im2col_cbf")
 
 
 def mx_dequantize(d: mx_conv_desc, role: int, q, dst, stream=None) -> None:
-    _check(lib().mx_dequantize(ctypes.byref(d), role, _q(q), _ptr(dst), _stream(stream)),
-           "mx_dequantize")
+    args = (ctypes.byref(d), role, _q(q, d, role, "q"), _buf(dst, 4 * role_numel(d, role), "dst"))
+    _check(lib().mx_dequantize(*args, _stream(stream)), "mx_dequantize")

@@ -599,14 +599,12 @@ constexpr Tile kTiles[] = {{256, 256, 2, 4, 4}, {128, 256, 2, 4, 4}, {128, 128, 
 // it over more CUs beats operand reuse inside a workgroup.
 int mt_cap(int64_t M) { return M > 128 ? 256 : M > 64 ? 128 : M > 32 ? 64 : 32; }
 
-bool tile_ok(const Tile&, int) { return true; }
-
-Tile pick_tile(int64_t M, int64_t ncols, int64_t zdim, int fmt) {
+Tile pick_tile(int64_t M, int64_t ncols, int64_t zdim) {
   const int cap = mt_cap(M);
   Tile best = {0, 0, 0, 0, 0};
   int64_t best_reach = -1;
   for (const Tile& t : kTiles) {
-    if (t.mt > cap || !tile_ok(t, fmt)) continue;
+    if (t.mt > cap) continue;
     const int64_t wgs = ((M + t.mt - 1) / t.mt) * ((ncols + t.nt - 1) / t.nt) * zdim;
     if (wgs * t.waves >= 2048) return t;
     const int64_t reach = wgs < 256 ? wgs : 256;
@@ -621,17 +619,17 @@ Tile pick_tile(int64_t M, int64_t ncols, int64_t zdim, int fmt) {
 // wgrad: split K supplies the parallelism, so the tile is chosen for operand
 // reuse: the largest one whose share of useful (unpadded) outputs is within
 // 3/4 of the best share any tile reaches.
-Tile pick_wgrad_tile(int64_t M, int64_t ncols, int fmt) {
+Tile pick_wgrad_tile(int64_t M, int64_t ncols) {
   const int cap = mt_cap(M);
   double best_eff = 0.0;
   for (const Tile& t : kTiles) {
-    if (t.mt > cap || !tile_ok(t, fmt)) continue;
+    if (t.mt > cap) continue;
     const double eff = static_cast<double>(M * ncols) /
                        (static_cast<double>((M + t.mt - 1) / t.mt * t.mt) * ((ncols + t.nt - 1) / t.nt * t.nt));
     if (eff > best_eff) best_eff = eff;
   }
   for (const Tile& t : kTiles) {
-    if (t.mt > cap || !tile_ok(t, fmt)) continue;
+    if (t.mt > cap) continue;
     const double eff = static_cast<double>(M * ncols) /
                        (static_cast<double>((M + t.mt - 1) / t.mt * t.mt) * ((ncols + t.nt - 1) / t.nt * t.nt));
     if (eff * 4.0 >= best_eff * 3.0) return t;
@@ -705,7 +703,7 @@ struct WgradPlan {
 WgradPlan wgrad_plan(const Geom& g) {
   const int64_t kb_total = static_cast<int64_t>(g.ho) * g.wo * (g.n / 8);
   const int64_t ncol = static_cast<int64_t>(g.k_h) * g.k_w * g.c_in;
-  Tile t = pick_wgrad_tile(g.c_out, ncol, g.fmt);
+  Tile t = pick_wgrad_tile(g.c_out, ncol);
   // all-E2M1 128x256, 64x256 and 32x256 tiles run k_conv4 (decode at fragment read,
   // K steps of 4 k-blocks, two workgroups per CU); p.ks_split counts its steps
   const bool decode_tile = g.fmt == FMT_E2M1 && g.afmt == FMT_E2M1 && t.mt <= 128 && t.nt == 256;
@@ -762,7 +760,7 @@ struct FwdPlan {
   dim3 grid;
 };
 FwdPlan fwd_plan(const Geom& g, const ConvParams& p) {
-  const Tile t = pick_tile(p.M, static_cast<int64_t>(p.ncb) * 8, 1, g.fmt);
+  const Tile t = pick_tile(p.M, static_cast<int64_t>(p.ncb) * 8, 1);
   return {t, dim3((p.ncb * 8 + t.nt - 1) / t.nt, (p.M + t.mt - 1) / t.mt, 1)};
 }
 
@@ -824,7 +822,7 @@ hipError_t launch_conv_dgrad(const Geom& g, const mx_qtensor* wq, const mx_qtens
     launch_mx(OP_DGRAD, T, p, dim3((p.ncb * 8 + T - 1) / T, (p.M + T - 1) / T, g.sh * g.sw), s);
     return hipGetLastError();
   }
-  const Tile t = pick_tile(p.M, static_cast<int64_t>(p.ncb) * 8, g.sh * g.sw, g.fmt);
+  const Tile t = pick_tile(p.M, static_cast<int64_t>(p.ncb) * 8, g.sh * g.sw);
   dim3 grid((p.ncb * 8 + t.nt - 1) / t.nt, (p.M + t.mt - 1) / t.mt, g.sh * g.sw);
   if (!launch_op<OP_DGRAD>(p, g.fmt, g.fmt, t, grid, s)) return hipErrorNotSupported;
   return hipGetLastError();

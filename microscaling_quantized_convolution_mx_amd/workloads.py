@@ -203,3 +203,51 @@ def gen_tensor(shape, dist: str, seed: int, sigma: float = 1.0) -> torch.Tensor:
     elif dist == "uniform":
         x = torch.rand(*shape, generator=_gen(seed)) * 2 - 1
     return (x * sigma).contiguous()
+
+
+# Grid-aligned inputs for GEMM checks that must hold bit for bit.  Every 8x8
+# block of a tensor holds one element of the format's largest magnitude (at
+# a fixed in-block position per tensor) and small grid values elsewhere,
+# all times 448 * 2^k.  With the tensor maximum in every block, a
+# microscaling quantizer of the two-level kind gives a power-of-two tensor
+# scale and the largest block scale in every block, so the elements sit on
+# the grid unchanged.  The fixed positions never pair two largest elements
+# in a product of the three GEMMs (the weight's sits at in-block (c_out 0,
+# c_in 0), the activation's at (c_in 1, n 1), the gradient's at (c_out 1,
+# n 0)), which keeps every output's sum of |products| small.
+EXACT_LARGEST = {E2M1: 6.0, E2M3: 7.5, E4M3: 448.0}
+EXACT_SMALL = {E2M1: (0.5, 1.0), E2M3: (0.5, 1.0), E4M3: (64.0, 128.0)}
+EXACT_POW2 = {"x": -8, "w": -10, "dy": -6}
+
+
+def _exact_fill(shape, fmt, seed):
+    g = _gen(seed)
+    small = EXACT_SMALL[fmt]
+    pick = torch.randint(0, 5, shape, generator=g)   # 0, +-small[0], +-small[1]
+    mag = torch.tensor([0.0, small[0], small[0], small[1], small[1]])[pick]
+    sign = torch.where(torch.randint(0, 2, shape, generator=g) == 0, 1.0, -1.0)
+    return mag * sign, torch.where(torch.randint(0, 2, shape, generator=g) == 0, 1.0, -1.0)
+
+
+def gen_exact(layer: ConvLayer, which: str, fmt: int, seed: int) -> torch.Tensor:
+    """which: "x" ([H][W][Cin][N]), "w" (OIHW) or "dy" ([Ho][Wo][Cout][N])."""
+    if which == "x":
+        shape = (layer.h, layer.w, layer.c_in, layer.n)
+    elif which == "dy":
+        shape = (layer.h_out, layer.w_out, layer.c_out, layer.n)
+    else:
+        shape = (layer.c_out, layer.c_in, layer.k_h, layer.k_w)
+    v, sgn = _exact_fill(shape, fmt, seed)
+    big = EXACT_LARGEST[fmt]
+    if which == "x":
+        v[:, :, 1::8, 1::8] = big * sgn[:, :, 1::8, 1::8]
+    elif which == "dy":
+        v[:, :, 1::8, 0::8] = big * sgn[:, :, 1::8, 0::8]
+    else:
+        v[0::8, 0::8, :, :] = big * sgn[0::8, 0::8, :, :]
+    return (v * (448.0 * 2.0 ** EXACT_POW2[which])).contiguous()
+
+
+def exact_quantum(which: str, fmt: int) -> float:
+    """Step of the tensor's dequantized values (every value is a multiple)."""
+    return EXACT_SMALL[fmt][0] * 448.0 * 2.0 ** EXACT_POW2[which]

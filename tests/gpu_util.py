@@ -86,10 +86,13 @@ def assert_close(got: np.ndarray, ref: np.ndarray, s: np.ndarray, what=""):
 
 
 def conv_buffers(d):
-    y = torch.empty(d.h_out, d.w_out, d.c_out, d.n, device=DEV)
-    dx = torch.empty(d.h, d.w, d.c_in, d.n, device=DEV)
-    dw = torch.empty(d.c_out, d.c_in, d.k_h, d.k_w, device=DEV)
-    ws = torch.empty(max(mx.mx_wgrad_workspace_bytes(d) // 4, 4), device=DEV)
+    """Output buffers of the three GEMMs and the weight-gradient workspace,
+    filled with NaN: an output the kernels never write, or a split partial
+    the reduce reads without the GEMM having written it, shows up as NaN."""
+    y = torch.full((d.h_out, d.w_out, d.c_out, d.n), float("nan"), device=DEV)
+    dx = torch.full((d.h, d.w, d.c_in, d.n), float("nan"), device=DEV)
+    dw = torch.full((d.c_out, d.c_in, d.k_h, d.k_w), float("nan"), device=DEV)
+    ws = torch.full((max(mx.mx_wgrad_workspace_bytes(d) // 4, 4),), float("nan"), device=DEV)
     return y, dx, dw, ws
 
 
@@ -100,9 +103,6 @@ def run_layer(d, x, w, dy, seed_sr, ops=("fwd", "dgrad", "wgrad")):
     qw = gpu_quantize(d, mx.MX_ROLE_WEIGHT, w)
     qdy = gpu_quantize(d, mx.MX_ROLE_GRAD, dy, mx.MX_SR, seed_sr)
     y, dx, dw, ws = conv_buffers(d)
-    # poison the outputs: every element must be written
-    for t in (y, dx, dw):
-        t.fill_(float("nan"))
     if "fwd" in ops:
         mx.mx_conv_fwd(d, qw, qx, y)
     if "dgrad" in ops:

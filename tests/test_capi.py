@@ -236,3 +236,49 @@ def test_e8m0_block32_format():
         bd = mx.desc(kw.pop("n"), kw.pop("c_in"), kw.pop("c_out"), kw.pop("h"), kw.pop("w"), kw.pop("k_h"),
                      kw.pop("k_w"), **kw)
         assert quant(bd) == status, bad
+
+
+def test_binding_rejects_unusable_tensors():
+    # Every tensor argument is checked before anything touches the GPU: a
+    # mistyped, strided, short or host tensor raises ValueError.  Host
+    # tensors stand in here, so no GPU call is made.
+    import torch
+    d = mx.desc(**GOOD)
+    nx = 8 * 8 * 16 * 8
+    good_x = torch.zeros(8, 8, 16, 8)
+    with pytest.raises(ValueError, match="float32"):
+        mx.mx_quantize_cbf(d, mx.MX_ROLE_ACT, good_x.double(), None)
+    with pytest.raises(ValueError, match="contiguous"):
+        mx.mx_quantize_cbf(d, mx.MX_ROLE_ACT, good_x.transpose(0, 3), None)
+    with pytest.raises(ValueError, match="needs %d" % (4 * nx)):
+        mx.mx_quantize_cbf(d, mx.MX_ROLE_ACT, good_x[:4], None)
+    with pytest.raises(ValueError, match="device memory"):
+        mx.mx_quantize_cbf(d, mx.MX_ROLE_ACT, good_x, None)
+    with pytest.raises(TypeError):
+        mx.mx_quantize_cbf(d, mx.MX_ROLE_ACT, good_x.numpy(), None)
+    # a quantized tensor's buffers: sized for the role under the descriptor
+    qcpu = mx.QTensor(d, mx.MX_ROLE_ACT, device="cpu")
+    with pytest.raises(ValueError, match="dst.codes: .*device memory"):
+        mx.mx_quantize_cbf(d, mx.MX_ROLE_ACT, None, qcpu)
+    small = mx.QTensor(mx.desc(**dict(GOOD, h=4, w=4)), mx.MX_ROLE_ACT, device="cpu")
+    with pytest.raises(ValueError, match="dst.codes: .*needs %d" % mx.mx_code_bytes(d, mx.MX_ROLE_ACT)):
+        mx.mx_quantize_cbf(d, mx.MX_ROLE_ACT, None, small)
+    # GEMM outputs and the weight-gradient workspace
+    ny = d.h_out * d.w_out * 16 * 8
+    with pytest.raises(ValueError, match="y: .*needs %d" % (4 * ny)):
+        mx.mx_conv_fwd(d, q(), q(), torch.zeros(ny - 1))
+    with pytest.raises(ValueError, match="dx: .*float32"):
+        mx.mx_conv_dgrad(d, q(), q(), torch.zeros(nx, dtype=torch.float16))
+    with pytest.raises(ValueError, match="dw: .*needs"):
+        mx.mx_conv_wgrad(d, q(), q(), torch.zeros(16 * 16 * 9 - 4), A16)
+    need = mx.mx_wgrad_workspace_bytes(d)
+    with pytest.raises(ValueError, match="workspace: .*needs %d" % (need + 4)):
+        mx.mx_conv_wgrad(d, q(), q(), A16, torch.zeros(need // 4), ws_bytes=need + 4)
+    with pytest.raises(ValueError, match="workspace: .*device memory"):
+        mx.mx_conv_wgrad(d, q(), q(), A16, torch.zeros(need // 4))
+    with pytest.raises(ValueError, match="y_amax: .*needs %d" % mx.mx_fwd_amax_bytes(d)):
+        mx.mx_conv_fwd_amax(d, q(), q(), A16, torch.zeros(1, dtype=torch.int32))
+    with pytest.raises(ValueError, match="xcol: .*needs"):
+        mx.mx_im2col_cbf(d, A16, torch.zeros(nx))
+    with pytest.raises(ValueError, match="dst: .*needs"):
+        mx.mx_dequantize(d, mx.MX_ROLE_WEIGHT, q(), torch.zeros(16 * 16 * 9 - 1))

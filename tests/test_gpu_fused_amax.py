@@ -3,20 +3,25 @@
 The paper loads each tensor once and estimates its statistics ahead of time
 (MicroQonv, arXiv 2609.28358, §VII, with Hindsight).  Here the forward GEMM
 that produces Y also returns max |y| exactly, so the next quantization of Y
-can skip its amax pass.  Checked through the C ABI:
+can skip its amax pass.  Checked through the C ABI, against the oracle:
+  - the quantized W and X are the oracle's, bit for bit, and Y is within
+    2e-3 * sum|a*b| of the oracle's fp64 forward GEMM on them;
   - Y is bit-identical to mx_conv_fwd's (the same kernels);
   - the returned amax equals max |y| over every output, computed on the host
     from Y's bits (the order of the sign-cleared bit patterns);
-  - quantizing Y as the next layer's activation with that amax given gives
-    the same codes, block scales and tensor scale as the two-pass quantizer.
-Y itself is held to the oracle by test_gpu_conv.py on the same kernels."""
+  - quantizing Y as the next layer's activation in one pass with that amax
+    given equals the oracle's quantization of the same Y with the same
+    given amax (codes, block scales, tensor scale) bit for bit, and equals
+    the two-pass quantizer's result."""
 import numpy as np
 import pytest
 import torch
 
 import microscaling_quantized_convolution_mx_amd as mx
 from microscaling_quantized_convolution_mx_amd import workloads as WL
-from gpu_util import DEV, gpu_quantize, say
+import oracle as O
+from gpu_util import (DEV, assert_close, assert_quant_equal, gpu_quantize, oracle_conv, oracle_quantize,
+                      say)
 
 pytestmark = pytest.mark.gpu
 
@@ -54,6 +59,13 @@ def test_fused_amax_matches_output_and_two_pass_quantize(shape, fmt):
     assert torch.equal(y0.view(torch.int32), y1.view(torch.int32))
     got = int(ya[:1].cpu().view(torch.int32).numpy().view(np.uint32)[0])
     assert got == amax_bits(y1)
+    # the fused forward against the oracle's fp64 GEMM on the oracle's own
+    # quantization of the same inputs
+    ox, ow = oracle_quantize(d, mx.MX_ROLE_ACT, x), oracle_quantize(d, mx.MX_ROLE_WEIGHT, w)
+    assert_quant_equal(qx, ox, "X")
+    assert_quant_equal(qw, ow, "W")
+    ref, sabs = O.conv_fwd(oracle_conv(d), ow.exact(), ox.exact())
+    assert_close(y1.cpu().numpy(), ref, sabs, "fused fwd")
 
     # Y as the activation of a next layer with C_in = C_out, same image
     nd = mx.desc(d.n, d.c_out, 8, d.h_out, d.w_out, 1, 1, elem_fmt=fmt)
@@ -68,6 +80,10 @@ def test_fused_amax_matches_output_and_two_pass_quantize(shape, fmt):
     assert torch.equal(two.scales[:two.nblocks], one.scales[:one.nblocks])
     assert torch.equal(two.tensor_scale.view(torch.int32), one.tensor_scale.view(torch.int32))
     assert torch.equal(two.amax.view(torch.int32), ya[:1].view(torch.int32))
+    # the single-pass quantization against the oracle given the same amax
+    amax = float(ya[:1].cpu().numpy()[0])
+    oy = oracle_quantize(nd, mx.MX_ROLE_ACT, src.cpu(), amax=amax)
+    assert_quant_equal(one, oy, "single-pass Y")
 
 
 def test_fused_amax_repeated_calls_reset_the_word():
