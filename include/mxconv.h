@@ -13,8 +13,9 @@
  * ---------------------------------------
  * - Every pointer argument except the descriptor and mx_qtensor structs
  *   themselves (which live in host memory) is a DEVICE pointer.  The caller
- *   allocates and owns all buffers; the library allocates nothing, keeps no
- *   global state and may be called from several host threads.
+ *   allocates and owns all buffers; the library allocates nothing and may be
+ *   called from several host threads.  Its only global state is the
+ *   static workspace of mx_conv_wgrad_noalloc (see there).
  * - fp32 tensors and code buffers must be 16-byte aligned; scale buffers,
  *   tensor_scale and amax 4-byte aligned.  Sources and destinations must not
  *   overlap.
@@ -206,6 +207,27 @@ mx_status mx_conv_dgrad(const mx_conv_desc* desc, const mx_qtensor* wq, const mx
  *             bit-reproducible run to run. */
 mx_status mx_conv_wgrad(const mx_conv_desc* desc, const mx_qtensor* dyq, const mx_qtensor* xq,
                         float* dw, void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* mx_conv_wgrad for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The split partials go to a static array in device memory that the library
+ * holds on each GPU it runs on, MX_NOALLOC_SCRATCH_BYTES bytes (64 MiB,
+ * enough for every layer of the five workloads this library is measured
+ * on: 63 MiB at most), until the process ends; the call allocates nothing
+ * and calls no allocating routine.  The first call on a device looks up
+ * that device's copy (once; cached).
+ *   dyq, xq, dw as for mx_conv_wgrad; the result is bit-identical to it
+ *   (same kernels, same split plan, same reduction order)
+ * Errors as mx_conv_wgrad, except that there is no workspace argument:
+ * MX_ERR_WORKSPACE when the layer needs more than MX_NOALLOC_SCRATCH_BYTES
+ * (mx_wgrad_workspace_bytes(desc) tells); MX_ERR_LAUNCH also when the
+ * array's address cannot be obtained.  Every call on one GPU shares that
+ * GPU's array and the partials are written before they are read, so nothing
+ * needs clearing between calls, but calls that overlap in time on one GPU
+ * (concurrent streams, or host threads) race on it: serialize them. */
+#define MX_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+mx_status mx_conv_wgrad_noalloc(const mx_conv_desc* desc, const mx_qtensor* dyq, const mx_qtensor* xq,
+                                float* dw, hipStream_t stream);
 
 /* Explicit channel-batch-first im2col: the expanded activation X' that the
  * quantize-after-im2col flow (§III-C, the extrapolation of Cuyckens et al.

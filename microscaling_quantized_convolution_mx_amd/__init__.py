@@ -32,8 +32,10 @@ STATUS = {0: "MX_OK", -1: "MX_ERR_NULL", -2: "MX_ERR_SHAPE", -3: "MX_ERR_FORMAT"
           -8: "MX_ERR_LAUNCH", -9: "MX_ERR_ROUND"}
 
 EXPORTS = ("mx_code_bytes", "mx_scale_bytes", "mx_wgrad_workspace_bytes", "mx_fwd_amax_bytes", "mx_quantize_cbf",
-           "mx_conv_fwd", "mx_conv_fwd_amax", "mx_conv_dgrad", "mx_conv_wgrad", "mx_dequantize",
-           "mx_im2col_cbf", "mx_status_str")
+           "mx_conv_fwd", "mx_conv_fwd_amax", "mx_conv_dgrad", "mx_conv_wgrad", "mx_conv_wgrad_noalloc",
+           "mx_dequantize", "mx_im2col_cbf", "mx_status_str")
+# bytes of the static workspace of mx_conv_wgrad_noalloc (MX_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class MxError(RuntimeError):
@@ -92,6 +94,8 @@ def lib() -> ctypes.CDLL:
     L.mx_conv_fwd_amax.argtypes = [D, Q, Q, P, P, P]
     L.mx_conv_wgrad.restype = ctypes.c_int
     L.mx_conv_wgrad.argtypes = [D, Q, Q, P, P, ctypes.c_size_t, P]
+    L.mx_conv_wgrad_noalloc.restype = ctypes.c_int
+    L.mx_conv_wgrad_noalloc.argtypes = [D, Q, Q, P, P]
     L.mx_dequantize.restype = ctypes.c_int
     L.mx_dequantize.argtypes = [D, ctypes.c_int, Q, P, P]
     L.mx_im2col_cbf.restype = ctypes.c_int
@@ -269,6 +273,14 @@ def mx_conv_wgrad(d: mx_conv_desc, dyq, xq, dw, workspace, ws_bytes: int | None 
             _buf(dw, 4 * role_numel(d, MX_ROLE_WEIGHT), "dw"), _buf(workspace, ws_bytes, "workspace", fp32=False),
             ws_bytes)
     _check(lib().mx_conv_wgrad(*args, _stream(stream)), "mx_conv_wgrad")
+
+
+def mx_conv_wgrad_noalloc(d: mx_conv_desc, dyq, xq, dw, stream=None) -> None:
+    """mx_conv_wgrad with the library's static per-GPU workspace (for callers
+    that cannot allocate); calls that overlap in time on one GPU race."""
+    args = (ctypes.byref(d), _q(dyq, d, MX_ROLE_GRAD, "dyq"), _q(xq, d, MX_ROLE_ACT, "xq"),
+            _buf(dw, 4 * role_numel(d, MX_ROLE_WEIGHT), "dw"))
+    _check(lib().mx_conv_wgrad_noalloc(*args, _stream(stream)), "mx_conv_wgrad_noalloc")
 
 
 def mx_im2col_cbf(d: mx_conv_desc, x, xcol, stream=None) -> None:

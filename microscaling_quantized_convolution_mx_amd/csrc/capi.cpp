@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include <limits>
+#include <mutex>
 
 #include "internal.h"
 
@@ -118,6 +119,36 @@ mx_status check_qtensor(const mx_qtensor* q, int64_t nblocks) {
 }
 
 mx_status launched(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ERR_LAUNCH; }
+
+// Weight-gradient workspace of mx_conv_wgrad_noalloc: a static array in
+// device memory, one copy per GPU, held until the process ends.  Host code
+// never uses the array's name as an address (on the host it names a
+// stand-in, not device memory): the device address of each GPU's copy is
+// looked up once per device with hipGetSymbolAddress, with that device
+// current, and cached here.
+static __device__ __align__(256) uint8_t scratch[MX_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each device, nullptr until looked up
+
+// Device address of the current device's `scratch`.
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 }  // namespace
 
@@ -240,6 +271,21 @@ mx_status mx_conv_wgrad(const mx_conv_desc* desc, const mx_qtensor* dyq, const m
   if (need > 0 && (!workspace || ws_bytes < need)) return MX_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return MX_ERR_ALIGN;
   return launched(mx::launch_conv_wgrad(g, dyq, xq, dw, workspace, stream));
+}
+
+mx_status mx_conv_wgrad_noalloc(const mx_conv_desc* desc, const mx_qtensor* dyq, const mx_qtensor* xq,
+                                float* dw, hipStream_t stream) {
+  mx_status st = check_gemm_desc(desc, Gemm::Wgrad);
+  if (st != MX_OK) return st;
+  const Geom g = mx::make_geom(desc);
+  if ((st = check_qtensor(dyq, mx::role_nblocks(g, MX_ROLE_GRAD))) != MX_OK) return st;
+  if ((st = check_qtensor(xq, mx::role_nblocks(g, MX_ROLE_ACT))) != MX_OK) return st;
+  if (!dw) return MX_ERR_NULL;
+  if (!aligned(dw, 16)) return MX_ERR_ALIGN;
+  if (mx::wgrad_workspace_bytes(g) > MX_NOALLOC_SCRATCH_BYTES) return MX_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (scratch_address(&ws) != hipSuccess) return MX_ERR_LAUNCH;
+  return launched(mx::launch_conv_wgrad(g, dyq, xq, dw, ws, stream));
 }
 
 const char* mx_status_str(mx_status s) {
