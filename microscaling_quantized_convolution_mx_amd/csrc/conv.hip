@@ -220,108 +220,6 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
   store_tile<OP, MT, NT, KB, WTM, WTN, RM, RN>(p, t, acc, lane, wm, wn);
 }
 
-// The k-blocks kb0, kb0 + KB, kb0 + 2 KB, ... of one staging thread, walked
-// with additions only.  kb splits into (outer, mid, inner) as in
-// TileCtx::locate; the block index and the source position are affine in the
-// three, and when inner's extent is at least KB a step carries at most once
-// into mid and once into outer.
-template <int OP, int MT, int NT, int KB>
-struct KWalk {
-  uint32_t lim;            // k-blocks of this thread's range left at step 0 (kb_end - kb0)
-  uint32_t inner, mid, blk;
-  uint32_t d_in, d_mid;
-  uint32_t s_step, s_c1, s_c2;  // block increments: per step, carry into mid, carry into outer
-  int y, x, x_c1, y_c2, x_c2;   // source position and its increments on carries
-  uint32_t hlim, wlim;          // position bounds (all ones: no spatial gather)
-
-  __device__ __forceinline__ void init(const ConvParams& p, const TileCtx<OP, MT, NT, KB>& t) {
-    const uint32_t kb0 = static_cast<uint32_t>(t.kb_begin + t.kbl);
-    lim = (t.in_range && static_cast<int>(kb0) < t.kb_end) ? static_cast<uint32_t>(t.kb_end) - kb0 : 0u;
-    const int cbin = p.c_in >> 3, cbout = p.c_out >> 3;
-    int e_in, e_mid, s_in, s_mid, s_out, base;
-    int sx1 = 0, sy2 = 0, sx2 = 0;
-    hlim = ~0u; wlim = ~0u;
-    if constexpr (OP == OP_FWD) {
-      e_in = cbin; e_mid = p.k_w;
-      if (t.is_a) { s_in = 1; s_mid = cbout * cbin; s_out = p.k_w * s_mid; base = t.gblk * cbin; }
-      else {
-        s_in = p.nb; s_mid = cbin * p.nb; s_out = p.w * s_mid;
-        base = (t.sp_y * p.w + t.sp_x) * s_mid + t.col_nb;
-        sx1 = 1; sy2 = 1; sx2 = -p.k_w;
-        hlim = p.h; wlim = p.w;
-      }
-    } else if constexpr (OP == OP_DGRAD) {
-      e_in = cbout; e_mid = t.nkw;
-      if (t.is_a) {
-        s_in = cbin; s_mid = p.sw * cbout * cbin; s_out = p.sh * p.k_w * cbout * cbin;
-        base = (t.kh0 * p.k_w + t.kw0) * cbout * cbin + t.gblk;
-      } else {
-        s_in = p.nb; s_mid = -cbout * p.nb; s_out = -p.wo * cbout * p.nb;
-        base = (t.sp_y * p.wo + t.sp_x) * cbout * p.nb + t.col_nb;
-        sx1 = -1; sy2 = -1; sx2 = t.nkw;
-        hlim = p.ho; wlim = p.wo;
-      }
-    } else {
-      e_in = p.nb; e_mid = p.wo;
-      if (t.is_a) { s_in = 1; s_mid = cbout * p.nb; s_out = p.wo * s_mid; base = t.gblk * p.nb; }
-      else {
-        s_in = 1; s_mid = p.sw * cbin * p.nb; s_out = p.sh * p.w * cbin * p.nb;
-        base = (t.sp_y * p.w + t.sp_x) * cbin * p.nb + t.col_cib * p.nb;
-        sx1 = p.sw; sy2 = p.sh; sx2 = -p.wo * p.sw;
-        hlim = p.h; wlim = p.w;
-      }
-    }
-    d_in = static_cast<uint32_t>(e_in);
-    d_mid = static_cast<uint32_t>(e_mid > 0 ? e_mid : 1);
-    const uint32_t outer_all = kb0 / d_in;
-    inner = kb0 - outer_all * d_in;
-    const uint32_t outer = outer_all / d_mid;
-    mid = outer_all - outer * d_mid;
-    blk = static_cast<uint32_t>(base) + outer * static_cast<uint32_t>(s_out) + mid * static_cast<uint32_t>(s_mid) +
-          inner * static_cast<uint32_t>(s_in);
-    // operands without a spatial gather stay at (0, 0)
-    const bool gather = hlim != ~0u;
-    y = (gather ? t.sp_y : 0) + static_cast<int>(outer) * sy2;
-    x = (gather ? t.sp_x : 0) + static_cast<int>(mid) * sx1;
-    s_step = static_cast<uint32_t>(KB * s_in);
-    s_c1 = static_cast<uint32_t>(s_mid - e_in * s_in);
-    s_c2 = static_cast<uint32_t>(s_out - e_mid * s_mid);
-    x_c1 = sx1; y_c2 = sy2; x_c2 = sx2;
-  }
-
-  // the block of step s (s * KB < lim and inside the source) and advance
-  __device__ __forceinline__ bool next(uint32_t s_kb, uint32_t& b) {
-    const bool ok = (s_kb < lim) & (static_cast<uint32_t>(y) < hlim) & (static_cast<uint32_t>(x) < wlim);
-    b = blk;
-    inner += KB;
-    blk += s_step;
-    const bool c1 = inner >= d_in;
-    inner = c1 ? inner - d_in : inner;
-    mid = c1 ? mid + 1u : mid;
-    blk = c1 ? blk + s_c1 : blk;
-    x = c1 ? x + x_c1 : x;
-    const bool c2 = mid >= d_mid;
-    mid = c2 ? 0u : mid;
-    blk = c2 ? blk + s_c2 : blk;
-    y = c2 ? y + y_c2 : y;
-    x = c2 ? x + x_c2 : x;
-    return ok;
-  }
-};
-
-// True when every step of KWalk carries at most once: the innermost extent
-// of the K split (input channel blocks, output channel blocks, batch blocks)
-// is at least the K step.
-inline bool kwalk_ok(int op, const ConvParams& p, int kb) {
-  const int e_in = op == OP_FWD ? p.c_in / 8 : op == OP_DGRAD ? p.c_out / 8 : p.nb;
-  return e_in >= kb;
-}
-
-template <int V>
-struct IC {
-  static constexpr int value = V;
-};
-
 // E2M1, 256x256 tile, 4 waves of 128x128, one workgroup per CU (the 256
 // accumulator registers of a wave fill the AGPR file).  LDS holds the raw
 // 4-bit codes of two K steps; each wave decodes its MFMA fragments from
@@ -669,6 +567,9 @@ void launch_fmt(const ConvParams& p, const Tile& t, dim3 grid, hipStream_t s) {
     if (t.mt == 128 && t.nt == 256) return launch_tile4<OP, 128, 256, 2, 4>(p, grid, s);
     if (t.mt == 64 && t.nt == 256) return launch_tile4<OP, 64, 256, 1, 4>(p, grid, s);
     if (t.mt == 32 && t.nt == 256) return launch_tile4<OP, 32, 256, 1, 4>(p, grid, s);
+  } else if constexpr (FMT == FMT_E4M3) {
+    // E4M3 on the 256x256 tile: byte codes in LDS, decoded at fragment read
+    if (t.mt == 256 && t.nt == 256 && launch_conv8(OP, p, grid, s)) return;
   }
   launch_generic<OP, FMT, FMT>(p, t, grid, s);
 }

@@ -186,3 +186,44 @@ def test_conv_decode_tiles_ragged(shape):
         idx = sample_points(out.numel(), rng, npts)
         ref, sabs = fn(cv, a, b, idx)
         assert_close(out.reshape(-1)[torch.from_numpy(idx).to(DEV)].cpu().numpy(), ref, sabs, name)
+
+
+def test_e4m3_block_scales_in_the_subnormal_range():
+    # E4M3 operands decode to fp16 as g * B * 2^-2: exact for every E4M3
+    # element g and block scale B (both multiples of 2^-9 with at most 4
+    # significant bits), the smallest of them fp16 subnormals.  Half of the
+    # batch of X and of dY sits 2^-16 below the rest, so their blocks take
+    # E4M3 scales below 2^-6 (subnormal codes) and their small elements decode
+    # below 2^-14.  With an identity 1x1 weight every fwd and dgrad output is
+    # one product, so the bound is per element (2e-3 relative): every output
+    # whose operand decodes to an fp16 subnormal is checked, plus a sample.
+    # The shape takes the 256x256 decode-at-read kernel (fwd: line-layout
+    # weight, transposed reads of X; dgrad: transposed reads of both).
+    lay = WL.ConvLayer(256, 256, 256, 16, 16, 1, 1, 1, 1, 0, 0)
+    d = mx.desc_from_layer(lay, mx.MX_E4M3)
+    x = WL.gen_x(lay, "normal", 901)
+    x[..., 128:] *= 2.0 ** -16
+    dy = WL.gen_dy(lay, 1.0, 903)
+    dy[..., 128:] *= 2.0 ** -16
+    w = torch.eye(256).reshape(256, 256, 1, 1).contiguous()
+    ox = oracle_quantize(d, mx.MX_ROLE_ACT, x)
+    ody = oracle_quantize(d, mx.MX_ROLE_GRAD, dy, mx.MX_SR, 904)
+    ow = oracle_quantize(d, mx.MX_ROLE_WEIGHT, w)
+    (qx, qw, qdy), (y, dx, _) = run_layer(d, x, w, dy, 904, ops=("fwd", "dgrad"))
+    from gpu_util import assert_quant_equal
+    assert_quant_equal(qx, ox, "X")
+    assert_quant_equal(qdy, ody, "dY")
+    assert_quant_equal(qw, ow, "W")
+    cv = oracle_conv(d)
+    we = ow.exact()
+    assert np.count_nonzero(we) == 256  # the identity stays diagonal
+    rng = np.random.default_rng(905)
+    for name, got, q, fn in (("fwd", y, ox, O.conv_fwd_points), ("dgrad", dx, ody, O.conv_dgrad_points)):
+        e = q.exact()
+        # the value the decode forms: g * B * 2^-2 = |x^| / T / 4
+        small = np.flatnonzero((np.abs(e) / q.t * 0.25 < 2.0 ** -14) & (e != 0))
+        assert small.size > 1000 and np.count_nonzero((q.scales >= 1) & (q.scales <= 7)) > 1000
+        idx = np.unique(np.concatenate([small, rng.integers(0, e.size, 8192)])).astype(np.int64)
+        ref, s = fn(cv, we, e, idx)
+        assert np.all(s[np.isin(idx, small)] > 0)
+        assert_close(got.view(-1)[torch.from_numpy(idx).to(DEV)].cpu().numpy(), ref, s, name)
