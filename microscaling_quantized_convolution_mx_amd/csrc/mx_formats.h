@@ -73,29 +73,24 @@ __device__ __forceinline__ uint32_t rne_code(float v) {
   return v < F::MAXV ? c : static_cast<uint32_t>(F::MAXCODE);
 }
 
-// Stochastic rounding: with lo <= v < hi the neighbouring grid points, round
-// up iff u * (hi - lo) < v - lo (both fp32 operations exact).  Branch-free
-// like rne_code.
+// Stochastic rounding of v >= 0 (v may be +inf) with the uniform u24 / 2^24:
+// with lo <= v < hi the neighbouring grid points, round up iff
+// u24 / 2^24 < (v - lo) / (hi - lo).  The grid step at v is 2^(e - MB) for v
+// in the normal binade [2^e, 2^(e+1)) and the subnormal step 2^(1-BIAS-MB)
+// below the smallest normal; q = v / step is an exact power-of-two rescale,
+// lo is its integer part and the fraction of q is (v - lo) / (hi - lo), so
+// the comparison u24 < frac(q) * 2^24 is exact.  Codes are
+// lo + (binade above the smallest) << MB: a round-up past the largest
+// mantissa carries into the next binade.  Branch-free like rne_code.
 template <class F>
-__device__ __forceinline__ uint32_t sr_code(float v, float u) {
-  constexpr float MIN_NORMAL = pow2(1 - F::BIAS);
-  constexpr float STEP = pow2(1 - F::BIAS - F::MB);
-  // subnormal range: lo = floor(v / step)
-  const float qs = __builtin_floorf(fminf(v, MIN_NORMAL) * pow2(F::MB + F::BIAS - 1));
-  const uint32_t lo_s = static_cast<uint32_t>(qs);
-  const float lov_s = qs * STEP;
-  // normal range: truncate the mantissa to MB bits
-  constexpr int SH = 23 - F::MB;
-  const uint32_t b = __float_as_uint(v);
-  const uint32_t t = b & ~((1u << SH) - 1u);
-  const uint32_t lo_n = (t >> SH) - static_cast<uint32_t>((127 - F::BIAS) << F::MB);
-  const float lov_n = __uint_as_float(t);
-  const float delta_n = __uint_as_float((b & 0x7F800000u) - (static_cast<uint32_t>(F::MB) << 23));
-  const bool sub = v < MIN_NORMAL;
-  const uint32_t lo = sub ? lo_s : lo_n;
-  const float diff = v - (sub ? lov_s : lov_n);
-  const float thr = u * (sub ? STEP : delta_n);
-  const uint32_t c = lo + (thr < diff ? 1u : 0u);
+__device__ __forceinline__ uint32_t sr_code(float v, uint32_t u24) {
+  constexpr int EMIN = 127 + 1 - F::BIAS;  // fp32 biased exponent of the smallest normal
+  const int eb = max(static_cast<int>(__builtin_amdgcn_ubfe(__float_as_uint(v), 23, 8)), EMIN);
+  const float q = __builtin_amdgcn_ldexpf(v, 127 + F::MB - eb);  // in [0, 2^(MB+1)) below +inf
+  const float fr = __builtin_amdgcn_fractf(q);
+  const uint32_t lo = static_cast<uint32_t>(q);
+  const uint32_t up = static_cast<float>(u24) < fr * 0x1p24f ? 1u : 0u;
+  const uint32_t c = lo + (static_cast<uint32_t>(eb - EMIN) << F::MB) + up;
   return v < F::MAXV ? c : static_cast<uint32_t>(F::MAXCODE);
 }
 
@@ -118,18 +113,18 @@ __device__ __forceinline__ uint64_t splitmix64(uint64_t z) {
   return z ^ (z >> 31);
 }
 constexpr uint64_t kGolden64 = 0x9E3779B97F4A7C15ull;
-__device__ __forceinline__ float u24(uint32_t bits) {
-  return static_cast<float>(bits) * (1.0f / 16777216.0f);
-}
-// the two uniforms of elements 2k, 2k+1 from gk = kGolden64 * (k + 1)
-__device__ __forceinline__ void sr_uniform_pair(uint64_t seed, uint64_t gk, float& u_even, float& u_odd) {
+// the 24-bit uniforms of elements 2k, 2k+1 from gk = kGolden64 * (k + 1),
+// taken from the two 32-bit halves of the output (32-bit shifts only, so
+// that the conversions to float stay 32-bit)
+__device__ __forceinline__ void sr_bits_pair(uint64_t seed, uint64_t gk, uint32_t& u_even, uint32_t& u_odd) {
   const uint64_t h = splitmix64(seed ^ gk);
-  u_even = u24(static_cast<uint32_t>(h >> 40));
-  u_odd = u24(static_cast<uint32_t>(h >> 16) & 0xFFFFFFu);
+  const uint32_t hi = static_cast<uint32_t>(h >> 32), lo = static_cast<uint32_t>(h);
+  u_even = hi >> 8;
+  u_odd = __builtin_amdgcn_alignbit(hi, lo, 16) & 0xFFFFFFu;
 }
-__device__ __forceinline__ float sr_uniform(uint64_t seed, uint64_t idx) {
-  float ue, uo;
-  sr_uniform_pair(seed, kGolden64 * ((idx >> 1) + 1ull), ue, uo);
+__device__ __forceinline__ uint32_t sr_bits(uint64_t seed, uint64_t idx) {
+  uint32_t ue, uo;
+  sr_bits_pair(seed, kGolden64 * ((idx >> 1) + 1ull), ue, uo);
   return (idx & 1ull) ? uo : ue;
 }
 

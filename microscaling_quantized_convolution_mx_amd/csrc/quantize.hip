@@ -368,17 +368,17 @@ __global__ __launch_bounds__(ONE ? kOneThreads : kThreads) void k_quantize(const
                (static_cast<uint64_t>(__builtin_bit_cast(uint32_t, hi)) << 32);
       }
     } else {
-      float u[8];
+      uint32_t u[8];
       if constexpr (SR) {
         if constexpr (ROLE == MX_ROLE_WEIGHT) {
 #pragma unroll
-          for (int j = 0; j < 8; ++j) u[j] = sr_uniform(seed, static_cast<uint64_t>(cur.rowbase + j * cur.col));
+          for (int j = 0; j < 8; ++j) u[j] = sr_bits(seed, static_cast<uint64_t>(cur.rowbase + j * cur.col));
         } else {
           // a row is 8 consecutive elements from an even index: 4 draws
           uint64_t gk = kGolden64 * (static_cast<uint64_t>(cur.rowbase >> 1) + 1ull);
 #pragma unroll
           for (int j = 0; j < 8; j += 2) {
-            sr_uniform_pair(seed, gk, u[j], u[j + 1]);
+            sr_bits_pair(seed, gk, u[j], u[j + 1]);
             gk += kGolden64;
           }
         }
@@ -428,17 +428,18 @@ __global__ __launch_bounds__(kThreads) void k_quantize_wide(const float* __restr
   const int64_t gstride = static_cast<int64_t>(gridDim.x) * kGroupsPerWG;
   int64_t grp = static_cast<int64_t>(blockIdx.x) * kGroupsPerWG + (threadIdx.x >> 6);
   const int64_t row = d.d3;  // N
+  const uint64_t gk_row = kGolden64 * static_cast<uint64_t>(row >> 1);  // N is a multiple of 8
   struct Rows {
     float4 x[8];  // columns 4h..4h+3 of rows 0..7
     int64_t base;  // source offset of column 4h of row 0
   };
+  // launched only for tensors of more than kOneBlocks blocks: block 0 exists
   auto load = [&](Rows& R, int64_t g) {
     int64_t b = g * kWideBlocks + (lane >> 1);
     b = b < d.nblocks ? b : 0;  // past the tensor: block 0, loaded, never stored
     R.base = block_addr<ROLE>(d, b).base + 4 * h;
 #pragma unroll
-    for (int r = 0; r < 8; ++r)
-      R.x[r] = d.nblocks ? load_stream(src + R.base + r * row) : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int r = 0; r < 8; ++r) R.x[r] = load_stream(src + R.base + r * row);
   };
   Rows cur;
   load(cur, grp);  // requested before the partials: the two loads overlap
@@ -514,6 +515,10 @@ __global__ __launch_bounds__(kThreads) void k_quantize_wide(const float* __restr
 
       // the 4 codes of each row of this lane, BITS each
       uint32_t chunk[8];
+      // counters of the SR draws: row r of this lane starts at element
+      // base + r N (even), so its first pair is k0 + r N / 2 with k0 = base / 2
+      // and gk = kGolden64 (k + 1) advances by a constant from row to row
+      const uint64_t gk0 = kGolden64 * (static_cast<uint64_t>(cur.base >> 1) + 1ull);
       if constexpr (SR && FMT == FMT_E2M1) {
         // Stochastic rounding on the hardware conversion, where it provably
         // matches sr_code.  Probed on this GPU: for |v| >= 1,
@@ -537,13 +542,12 @@ __global__ __launch_bounds__(kThreads) void k_quantize_wide(const float* __restr
         typedef float float2v __attribute__((ext_vector_type(2)));
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-          const uint64_t gk = kGolden64 * (static_cast<uint64_t>((cur.base + r * row) >> 1) + 1ull);
+          const uint64_t gk = gk0 + r * gk_row;
           uint32_t c = 0;
 #pragma unroll
           for (int q = 0; q < 2; ++q) {
-            const uint64_t hsh = splitmix64(seed ^ (gk + q * kGolden64));
-            const uint32_t ue = static_cast<uint32_t>(hsh >> 40);
-            const uint32_t uo = static_cast<uint32_t>(hsh >> 16) & 0xFFFFFFu;
+            uint32_t ue, uo;
+            sr_bits_pair(seed, gk + q * kGolden64, ue, uo);
             const int j = 4 * r + 2 * q;
             const float ae = v[j], ao = v[j + 1];
             auto below_one = [](float a, uint32_t u24) {
@@ -582,12 +586,12 @@ __global__ __launch_bounds__(kThreads) void k_quantize_wide(const float* __restr
       } else {
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-          float u[4];
+          uint32_t u[4];
           if constexpr (SR) {
             // elements base + r N + j; pairs from an even index
-            uint64_t gk = kGolden64 * (static_cast<uint64_t>((cur.base + r * row) >> 1) + 1ull);
-            sr_uniform_pair(seed, gk, u[0], u[1]);
-            sr_uniform_pair(seed, gk + kGolden64, u[2], u[3]);
+            const uint64_t gk = gk0 + r * gk_row;
+            sr_bits_pair(seed, gk, u[0], u[1]);
+            sr_bits_pair(seed, gk + kGolden64, u[2], u[3]);
           }
           uint32_t c = 0;
 #pragma unroll

@@ -140,17 +140,17 @@ __global__ __launch_bounds__(kMxWaves * 64) void k_quantize_mx(const float* __re
       w[q] = t;
     }
   } else {
-    float u[16];
+    uint32_t u[16];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       if constexpr (ROLE == MX_ROLE_WEIGHT) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) u[4 * q + j] = sr_uniform(seed, static_cast<uint64_t>(s0[q] + j * step));
+        for (int j = 0; j < 4; ++j) u[4 * q + j] = sr_bits(seed, static_cast<uint64_t>(s0[q] + j * step));
       } else {
         // 4 consecutive elements from an even index: 2 draws
         const uint64_t gk = kGolden64 * (static_cast<uint64_t>(s0[q] >> 1) + 1ull);
-        sr_uniform_pair(seed, gk, u[4 * q], u[4 * q + 1]);
-        sr_uniform_pair(seed, gk + kGolden64, u[4 * q + 2], u[4 * q + 3]);
+        sr_bits_pair(seed, gk, u[4 * q], u[4 * q + 1]);
+        sr_bits_pair(seed, gk + kGolden64, u[4 * q + 2], u[4 * q + 3]);
       }
     }
 #pragma unroll
