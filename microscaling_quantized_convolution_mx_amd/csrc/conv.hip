@@ -75,6 +75,21 @@ __device__ __forceinline__ f16x8 decode_frag(uint32_t codes, uint32_t sw) {
   return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
+// Half h (values 4h..4h+3) of decode_frag, for placing between MFMAs.
+__device__ __forceinline__ void decode_half(f16x8& f, uint32_t codes, uint32_t sw, int h) {
+  const float sc = __uint_as_float(sw);
+  const f16x2 m2 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(sw, sw, 0x01000100u));
+  if (h == 0) {
+    const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, sc, 0) * m2;
+    const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, sc, 1) * m2;
+    f[0] = p0[0]; f[1] = p0[1]; f[2] = p1[0]; f[3] = p1[1];
+  } else {
+    const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, sc, 2) * m2;
+    const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, sc, 3) * m2;
+    f[4] = p2[0]; f[5] = p2[1]; f[6] = p3[0]; f[7] = p3[1];
+  }
+}
+
 // two workgroups per CU: at most 256 registers per wave
 template <int OP, int MT, int NT, int WM, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_conv4(const ConvParams p) {
@@ -222,9 +237,16 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
 
 // E2M1, 256x256 tile, 4 waves of 128x128, one workgroup per CU (the 256
 // accumulator registers of a wave fill the AGPR file).  LDS holds the raw
-// 4-bit codes of two K steps; each wave decodes its MFMA fragments from
+// 4-bit codes of three K steps; each wave decodes its MFMA fragments from
 // them (conversion with the block scale's exponent, then a packed multiply
 // by its mantissa factor: exact in fp16).
+//
+// A wave hides VALU work behind its own MFMAs only a few operations at a
+// time (on this GPU about 4 VALU operations per 32x32x16 MFMA; past that
+// every operation adds its issue time), so each fragment is decoded in the
+// column before the one that uses it, in halves placed after single MFMAs,
+// and the raw fragments of the next stage are read a whole step ahead into
+// a second register set.
 //
 // Per stage and operand, 32 pitches of 136 bytes (the 8-byte pad staggers
 // the banks):
@@ -240,7 +262,8 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
 // that their codes, whatever they are, decode to zero.
 //
 // Block fetches run two steps ahead in two register sets; the loop is
-// unrolled twice so that sets and stages are static.
+// unrolled twice so that the register sets are static (the stage offsets
+// rotate at run time).
 template <int OP>
 __global__ __launch_bounds__(256) void k_conv4w(const ConvParams p) {
   constexpr int MT = 256, NT = 256, WM = 2, KB = 4;
@@ -250,8 +273,9 @@ __global__ __launch_bounds__(256) void k_conv4w(const ConvParams p) {
   constexpr int PITCH = 136, OPND = 32 * PITCH, SCL = 32 * 16;
   constexpr int A_C = 0, B_C = OPND, A_S = 2 * OPND, B_S = 2 * OPND + SCL;
   constexpr int STAGE = 2 * OPND + 2 * SCL;
-  constexpr int LUT = 2 * STAGE;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE + 1024];
+  constexpr int NST = 3;
+  constexpr int LUT = NST * STAGE;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[NST * STAGE + 1024];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -286,15 +310,15 @@ __global__ __launch_bounds__(256) void k_conv4w(const ConvParams p) {
   auto write_rows = [&](const RawBlock<FMT_E2M1>& g, uint8_t* base, int r0) {
     if constexpr (A_ROWS == B_ROWS) {
 #pragma unroll
-      for (int r = r0; r < r0 + 4; ++r)
+      for (int r = r0; r < r0 + 2; ++r)
         *reinterpret_cast<uint32_t*>(base + st_code + r * (A_ROWS ? 16 : PITCH)) = g.w[r];
     } else {
       if (__builtin_amdgcn_readfirstlane(static_cast<int>(rows))) {
 #pragma unroll
-        for (int r = r0; r < r0 + 4; ++r) *reinterpret_cast<uint32_t*>(base + st_code + r * 16) = g.w[r];
+        for (int r = r0; r < r0 + 2; ++r) *reinterpret_cast<uint32_t*>(base + st_code + r * 16) = g.w[r];
       } else {
 #pragma unroll
-        for (int r = r0; r < r0 + 4; ++r) *reinterpret_cast<uint32_t*>(base + st_code + r * PITCH) = g.w[r];
+        for (int r = r0; r < r0 + 2; ++r) *reinterpret_cast<uint32_t*>(base + st_code + r * PITCH) = g.w[r];
       }
     }
   };
@@ -319,81 +343,99 @@ __global__ __launch_bounds__(256) void k_conv4w(const ConvParams p) {
   typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
   typedef int i32x2 __attribute__((ext_vector_type(2)));
   typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
-  u32x2 ra[RM], sa[RM], rb[RN], sbv[RN];  // raw fragments of a stage (.x slice 0, .y slice 1)
+  u32x2 ra[2][RM], sa[2][RM], rb[2][RN], sbv[2][RN];  // raw fragments of two stages (.x slice 0, .y slice 1)
   auto read_code = [&](const uint8_t* q, bool line) -> u32x2 {
     if (line) return *reinterpret_cast<const u32x2*>(q);
     return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr4_b64_v2i32((lds_i32x2*)(q)));
   };
-  auto read_raw = [&](const uint8_t* base) {
-#pragma unroll
-    for (int i = 0; i < RM; ++i) {
-      ra[i] = read_code(base + a_code + i * (A_ROWS ? 4 * PITCH : 16), A_ROWS);
-      sa[i] = *reinterpret_cast<const u32x2*>(base + a_scale + i * 64);
-    }
-#pragma unroll
-    for (int j = 0; j < RN; ++j) {
-      rb[j] = read_code(base + b_code + j * (B_ROWS ? 4 * PITCH : 16), B_ROWS);
-      sbv[j] = *reinterpret_cast<const u32x2*>(base + b_scale + j * 64);
-    }
+  // part q (0..3) of the raw fragments of a stage: A and B fragment q with
+  // their scale words
+  auto read_raw = [&](auto set_c, const uint8_t* base, int q) {
+    constexpr int Q = decltype(set_c)::value;
+    ra[Q][q] = read_code(base + a_code + q * (A_ROWS ? 4 * PITCH : 16), A_ROWS);
+    sa[Q][q] = *reinterpret_cast<const u32x2*>(base + a_scale + q * 64);
+    rb[Q][q] = read_code(base + b_code + q * (B_ROWS ? 4 * PITCH : 16), B_ROWS);
+    sbv[Q][q] = *reinterpret_cast<const u32x2*>(base + b_scale + q * 64);
   };
   f16x8 fa0[RM], fa1[RM];  // A fragments of slice 0 and slice 1
 
-  // One column j of a slice: 4 MFMAs with the B fragment fb, then the work
-  // item placed after them; a scheduling barrier closes the group.
-  auto column = [&](const f16x8 (&fa)[RM], const f16x8& fb, int j, auto&& work) {
-#pragma unroll
-    for (int i = 0; i < RM; ++i)
-      acc[i][j] = mfma32<true>(reinterpret_cast<const uint16_t*>(&fa[i]),
-                               reinterpret_cast<const uint16_t*>(&fb), acc[i][j]);
-    work();
+  // One column j of a slice: MFMA i is followed by work unit i (a few VALU
+  // operations and LDS accesses), each closed by a scheduling barrier, so
+  // that the wave issues the decode work between MFMAs instead of in runs.
+  auto column = [&](const f16x8 (&fa)[RM], const f16x8& fb, int j, auto&& u0, auto&& u1, auto&& u2, auto&& u3) {
+    acc[0][j] = mfma32<true>(reinterpret_cast<const uint16_t*>(&fa[0]), reinterpret_cast<const uint16_t*>(&fb), acc[0][j]);
+    u0();
+    __builtin_amdgcn_sched_barrier(0);
+    acc[1][j] = mfma32<true>(reinterpret_cast<const uint16_t*>(&fa[1]), reinterpret_cast<const uint16_t*>(&fb), acc[1][j]);
+    u1();
+    __builtin_amdgcn_sched_barrier(0);
+    acc[2][j] = mfma32<true>(reinterpret_cast<const uint16_t*>(&fa[2]), reinterpret_cast<const uint16_t*>(&fb), acc[2][j]);
+    u2();
+    __builtin_amdgcn_sched_barrier(0);
+    acc[3][j] = mfma32<true>(reinterpret_cast<const uint16_t*>(&fa[3]), reinterpret_cast<const uint16_t*>(&fb), acc[3][j]);
+    u3();
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // Step s (fragments of stage s%2 in registers, slice-0 A decoded; set G
-  // holds the block of step s+1):
-  //   slice 0: decode the slice-1 A fragments and each column's B fragment;
-  //            stage G into stage (s+1)%2 (free since the barrier of step
-  //            s-1), then refill G with the block of step s+3
-  //   slice 1: decode the B fragments, barrier, read stage (s+1)%2, decode
-  //            its slice-0 A fragments
-  auto step = [&](auto nxt_c, RawBlock<FMT_E2M1>& G) {
-    constexpr int NXT = decltype(nxt_c)::value;
-    uint8_t* nbase = lds + NXT * STAGE;
-    column(fa0, decode_frag(rb[0].x, sbv[0].x), 0, [&] {
-      fa1[0] = decode_frag(ra[0].y, sa[0].y);
-      lookup_scale(G);
-      write_rows(G, nbase, 0);
-    });
-    column(fa0, decode_frag(rb[1].x, sbv[1].x), 1, [&] {
-      fa1[1] = decode_frag(ra[1].y, sa[1].y);
-      write_rows(G, nbase, 4);
-    });
-    column(fa0, decode_frag(rb[2].x, sbv[2].x), 2, [&] {
-      fa1[2] = decode_frag(ra[2].y, sa[2].y);
-      fetch(G);
-    });
-    column(fa0, decode_frag(rb[3].x, sbv[3].x), 3, [&] {
-      fa1[3] = decode_frag(ra[3].y, sa[3].y);
-      *reinterpret_cast<uint32_t*>(nbase + st_scale) = sws;
-    });
-    f16x8 fb1, fb2, fb3;
-    column(fa1, decode_frag(rb[0].y, sbv[0].y), 0, [&] {
-      fb1 = decode_frag(rb[1].y, sbv[1].y);
-      fb2 = decode_frag(rb[2].y, sbv[2].y);
-    });
-    column(fa1, fb1, 1, [&] {
-      fb3 = decode_frag(rb[3].y, sbv[3].y);
-      __syncthreads();
-      read_raw(nbase);
-    });
-    column(fa1, fb2, 2, [&] {
-      fa0[0] = decode_frag(ra[0].x, sa[0].x);
-      fa0[1] = decode_frag(ra[1].x, sa[1].x);
-    });
-    column(fa1, fb3, 3, [&] {
-      fa0[2] = decode_frag(ra[2].x, sa[2].x);
-      fa0[3] = decode_frag(ra[3].x, sa[3].x);
-    });
+  // Step s on stage s%3 (raw fragments in set P; slice-0 A fragments and the
+  // slice-0 column-0 B fragment fbc decoded).  Every fragment is decoded in
+  // the column before the one that uses it, in halves after single MFMAs:
+  // slice 0 decodes the slice-1 A fragments and the next B fragment; slice 1
+  // the next B fragment and the next step's slice-0 A fragments (set Q,
+  // read from stage (s+1)%3 during slice-0 column 0).  The block of step
+  // s+2 (in G) is staged into stage (s+2)%3 and G refilled with the block of
+  // step s+4; one barrier per step, at its end.
+  f16x8 fbc;
+  auto step = [&](auto set_c, RawBlock<FMT_E2M1>& G, int nxt_off, int wr_off) {
+    constexpr int P = decltype(set_c)::value, Q = P ^ 1;
+    uint8_t* wbase = lds + wr_off;
+    const uint8_t* nbase = lds + nxt_off;
+    f16x8 fbA, fbB;
+    // slice 0
+    column(fa0, fbc, 0,
+           [&] { read_raw(IC<Q>{}, nbase, 0); decode_half(fa1[0], ra[P][0].y, sa[P][0].y, 0); },
+           [&] { read_raw(IC<Q>{}, nbase, 1); decode_half(fa1[0], ra[P][0].y, sa[P][0].y, 1); },
+           [&] { read_raw(IC<Q>{}, nbase, 2); decode_half(fbA, rb[P][1].x, sbv[P][1].x, 0); },
+           [&] { read_raw(IC<Q>{}, nbase, 3); decode_half(fbA, rb[P][1].x, sbv[P][1].x, 1); });
+    column(fa0, fbA, 1,
+           [&] { lookup_scale(G); decode_half(fa1[1], ra[P][1].y, sa[P][1].y, 0); },
+           [&] { write_rows(G, wbase, 0); decode_half(fa1[1], ra[P][1].y, sa[P][1].y, 1); },
+           [&] { write_rows(G, wbase, 2); decode_half(fbB, rb[P][2].x, sbv[P][2].x, 0); },
+           [&] { write_rows(G, wbase, 4); decode_half(fbB, rb[P][2].x, sbv[P][2].x, 1); });
+    column(fa0, fbB, 2,
+           [&] { write_rows(G, wbase, 6); decode_half(fa1[2], ra[P][2].y, sa[P][2].y, 0); },
+           [&] { fetch(G); decode_half(fa1[2], ra[P][2].y, sa[P][2].y, 1); },
+           [&] { *reinterpret_cast<uint32_t*>(wbase + st_scale) = sws; decode_half(fbA, rb[P][3].x, sbv[P][3].x, 0); },
+           [&] { decode_half(fbA, rb[P][3].x, sbv[P][3].x, 1); });
+    column(fa0, fbA, 3,
+           [&] { decode_half(fa1[3], ra[P][3].y, sa[P][3].y, 0); },
+           [&] { decode_half(fa1[3], ra[P][3].y, sa[P][3].y, 1); },
+           [&] { decode_half(fbB, rb[P][0].y, sbv[P][0].y, 0); },
+           [&] { decode_half(fbB, rb[P][0].y, sbv[P][0].y, 1); });
+    // slice 1 (fa0 is free: it takes the next step's slice-0 A fragments)
+    column(fa1, fbB, 0,
+           [&] { decode_half(fbA, rb[P][1].y, sbv[P][1].y, 0); },
+           [&] { decode_half(fbA, rb[P][1].y, sbv[P][1].y, 1); },
+           [&] { decode_half(fa0[0], ra[Q][0].x, sa[Q][0].x, 0); },
+           [&] { decode_half(fa0[0], ra[Q][0].x, sa[Q][0].x, 1); });
+    column(fa1, fbA, 1,
+           [&] { decode_half(fbB, rb[P][2].y, sbv[P][2].y, 0); },
+           [&] { decode_half(fbB, rb[P][2].y, sbv[P][2].y, 1); },
+           [&] { decode_half(fa0[1], ra[Q][1].x, sa[Q][1].x, 0); },
+           [&] { decode_half(fa0[1], ra[Q][1].x, sa[Q][1].x, 1); });
+    column(fa1, fbB, 2,
+           [&] { decode_half(fbA, rb[P][3].y, sbv[P][3].y, 0); },
+           [&] { decode_half(fbA, rb[P][3].y, sbv[P][3].y, 1); },
+           [&] { decode_half(fa0[2], ra[Q][2].x, sa[Q][2].x, 0); },
+           [&] { decode_half(fa0[2], ra[Q][2].x, sa[Q][2].x, 1); });
+    column(fa1, fbA, 3,
+           [&] { decode_half(fa0[3], ra[Q][3].x, sa[Q][3].x, 0); },
+           [&] { decode_half(fa0[3], ra[Q][3].x, sa[Q][3].x, 1); },
+           [&] { decode_half(fbc, rb[Q][0].x, sbv[Q][0].x, 0); },
+           [&] {
+             decode_half(fbc, rb[Q][0].x, sbv[Q][0].x, 1);
+             __syncthreads();
+           });
   };
 
   const int nsteps = (t.kb_end - t.kb_begin + KB - 1) / KB;
@@ -404,18 +446,32 @@ __global__ __launch_bounds__(256) void k_conv4w(const ConvParams p) {
     __syncthreads();  // scale-word table
     lookup_scale(g0);
     write_rows(g0, lds, 0);
+    write_rows(g0, lds, 2);
     write_rows(g0, lds, 4);
+    write_rows(g0, lds, 6);
     *reinterpret_cast<uint32_t*>(lds + st_scale) = sws;
+    lookup_scale(g1);
+    write_rows(g1, lds + STAGE, 0);
+    write_rows(g1, lds + STAGE, 2);
+    write_rows(g1, lds + STAGE, 4);
+    write_rows(g1, lds + STAGE, 6);
+    *reinterpret_cast<uint32_t*>(lds + STAGE + st_scale) = sws;
     fetch(g0);
+    fetch(g1);
     __syncthreads();
-    read_raw(lds);
 #pragma unroll
-    for (int i = 0; i < RM; ++i) fa0[i] = decode_frag(ra[i].x, sa[i].x);
+    for (int q = 0; q < 4; ++q) read_raw(IC<0>{}, lds, q);
+#pragma unroll
+    for (int i = 0; i < RM; ++i) fa0[i] = decode_frag(ra[0][i].x, sa[0][i].x);
+    fbc = decode_frag(rb[0][0].x, sbv[0][0].x);
     // an odd step count runs one more step, on padding blocks only (zero
     // scale words: it adds exact zeros)
+    int c = 0;  // stage of step s
     for (int s = 0; s < nsteps; s += 2) {
-      step(IC<1>{}, g1);
-      step(IC<0>{}, g0);
+      const int c1 = c == 2 ? 0 : c + 1, c2 = c1 == 2 ? 0 : c1 + 1;
+      step(IC<0>{}, g0, c1 * STAGE, c2 * STAGE);
+      step(IC<1>{}, g1, c2 * STAGE, c * STAGE);
+      c = c2;
     }
   }
   store_tile<OP, MT, NT, KB, WTM, WTN, RM, RN>(p, t, acc, lane, wm, wn);

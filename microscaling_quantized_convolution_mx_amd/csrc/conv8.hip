@@ -26,7 +26,11 @@
 //
 // Tile: 256x256, 4 waves of 128x128 (one workgroup per CU: a wave's 16
 // accumulator tiles fill its 256 AGPRs), K steps of 4 k-blocks (32 K values:
-// two 16-wide MFMA slices), two LDS stages, block fetches two steps ahead.
+// two 16-wide MFMA slices), three LDS stages, block fetches two steps ahead.
+// As in the E2M1 kernel, every fragment is decoded in the column before
+// the one that uses it, in halves placed after single MFMAs (a wave hides
+// only about 4 VALU operations behind each MFMA), and the raw fragments of
+// the next stage are read a whole step ahead into a second register set.
 // Stage layout, per operand:
 //   block rows along M/N (fwd A, wgrad A and B): 32 line blocks of 8 lines
 //     of 32 bytes (the 4 k-blocks of a row in the order 0, 2, 1, 3, so that
@@ -74,6 +78,15 @@ __device__ __forceinline__ f16x8 decode8(uint32_t lo, uint32_t hi, uint32_t sw) 
   const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, sc, true) * m2;
   return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
+// Half of decode8: values 0..3 from lo (h = 0) or 4..7 from hi (h = 1), for
+// placing between MFMAs.
+__device__ __forceinline__ void decode8_half(f16x8& f, uint32_t w, uint32_t sw, int h) {
+  const float sc = __uint_as_float(sw);
+  const f16x2 m2 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(sw, sw, 0x01000100u));
+  const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, sc, false) * m2;
+  const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, sc, true) * m2;
+  f[4 * h] = a[0]; f[4 * h + 1] = a[1]; f[4 * h + 2] = b[0]; f[4 * h + 3] = b[1];
+}
 
 template <int OP>
 __global__ __launch_bounds__(256) void k_conv8w(const ConvParams p) {
@@ -89,9 +102,10 @@ __global__ __launch_bounds__(256) void k_conv8w(const ConvParams p) {
   constexpr int SCL = 32 * 16;
   constexpr int A_C = 0, B_C = A_SZ, A_S = A_SZ + B_SZ, B_S = A_S + SCL;
   constexpr int STAGE = A_S + 2 * SCL;
-  constexpr int LUT = 2 * STAGE;
+  constexpr int NST = 3;
+  constexpr int LUT = NST * STAGE;
   static_assert(STAGE % 16 == 0, "16-byte aligned stages");
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE + 1024];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[NST * STAGE + 1024];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -131,7 +145,7 @@ __global__ __launch_bounds__(256) void k_conv8w(const ConvParams p) {
   // finite (a quantized tensor holds no NaN code), so it decodes to zeros.
   auto write_rows = [&](const RawBlock<FMT_E4M3>& g, uint8_t* base, int r0) {
 #pragma unroll
-    for (int r = r0; r < r0 + 4; ++r)
+    for (int r = r0; r < r0 + 2; ++r)
       *reinterpret_cast<u32x2v*>(base + st_code + r * st_row) = u32x2v{g.w[2 * r], g.w[2 * r + 1]};
   };
 
@@ -152,9 +166,9 @@ __global__ __launch_bounds__(256) void k_conv8w(const ConvParams p) {
   const int b_code = B_C + (B_ROWS ? wn * 16 * PL + line_off : krow_off + wn * 128);
   const int a_scale = A_S + (wm * 16 + (l32 >> 3)) * 16 + half * 8;
   const int b_scale = B_S + (wn * 16 + (l32 >> 3)) * 16 + half * 8;
-  // raw fragments of a stage: .xy slice 0, .zw slice 1; scale words .x, .y
-  u32x4v ra[RM], rb[RN];
-  u32x2v sa[RM], sbv[RN];
+  // raw fragments of two stages: .xy slice 0, .zw slice 1; scale words .x, .y
+  u32x4v ra[2][RM], rb[2][RN];
+  u32x2v sa[2][RM], sbv[2][RN];
   auto read_code = [&](const uint8_t* q, bool line) -> u32x4v {
     if (line) return *reinterpret_cast<const u32x4v*>(q);
     const auto s0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2v*)(q));
@@ -162,79 +176,100 @@ __global__ __launch_bounds__(256) void k_conv8w(const ConvParams p) {
     return u32x4v{static_cast<uint32_t>(s0[0]), static_cast<uint32_t>(s0[1]), static_cast<uint32_t>(s1[0]),
                   static_cast<uint32_t>(s1[1])};
   };
-  auto read_raw = [&](const uint8_t* base) {
-#pragma unroll
-    for (int i = 0; i < RM; ++i) {
-      ra[i] = read_code(base + a_code + i * (A_ROWS ? 4 * PL : 32), A_ROWS);
-      sa[i] = *reinterpret_cast<const u32x2v*>(base + a_scale + i * 64);
-    }
-#pragma unroll
-    for (int j = 0; j < RN; ++j) {
-      rb[j] = read_code(base + b_code + j * (B_ROWS ? 4 * PL : 32), B_ROWS);
-      sbv[j] = *reinterpret_cast<const u32x2v*>(base + b_scale + j * 64);
-    }
+  // part q (0..3) of the raw fragments of a stage: A and B fragment q with
+  // their scale words
+  auto read_raw = [&](auto set_c, const uint8_t* base, int q) {
+    constexpr int Q = decltype(set_c)::value;
+    ra[Q][q] = read_code(base + a_code + q * (A_ROWS ? 4 * PL : 32), A_ROWS);
+    sa[Q][q] = *reinterpret_cast<const u32x2v*>(base + a_scale + q * 64);
+    rb[Q][q] = read_code(base + b_code + q * (B_ROWS ? 4 * PL : 32), B_ROWS);
+    sbv[Q][q] = *reinterpret_cast<const u32x2v*>(base + b_scale + q * 64);
   };
   auto dec = [&](const u32x4v& r, const u32x2v& s, int slice) -> f16x8 {
     return slice ? decode8(r.z, r.w, s.y) : decode8(r.x, r.y, s.x);
   };
+  // half h of the slice-`slice` fragment of raw r into f
+  auto dech = [&](f16x8& f, const u32x4v& r, const u32x2v& s, int slice, int h) {
+    if (slice) decode8_half(f, h ? r.w : r.z, s.y, h);
+    else decode8_half(f, h ? r.y : r.x, s.x, h);
+  };
   f16x8 fa0[RM], fa1[RM];  // A fragments of slice 0 and slice 1
 
-  // One column j of a slice: 4 MFMAs with the B fragment fb, then the work
-  // item placed after them; a scheduling barrier closes the group.
-  auto column = [&](const f16x8 (&fa)[RM], const f16x8& fb, int j, auto&& work) {
-#pragma unroll
-    for (int i = 0; i < RM; ++i)
-      acc[i][j] = mfma32<true>(reinterpret_cast<const uint16_t*>(&fa[i]),
-                               reinterpret_cast<const uint16_t*>(&fb), acc[i][j]);
-    work();
+  // One column j of a slice: MFMA i is followed by work unit i (a few VALU
+  // operations and LDS accesses), each closed by a scheduling barrier.
+  auto column = [&](const f16x8 (&fa)[RM], const f16x8& fb, int j, auto&& u0, auto&& u1, auto&& u2, auto&& u3) {
+    acc[0][j] = mfma32<true>(reinterpret_cast<const uint16_t*>(&fa[0]), reinterpret_cast<const uint16_t*>(&fb), acc[0][j]);
+    u0();
+    __builtin_amdgcn_sched_barrier(0);
+    acc[1][j] = mfma32<true>(reinterpret_cast<const uint16_t*>(&fa[1]), reinterpret_cast<const uint16_t*>(&fb), acc[1][j]);
+    u1();
+    __builtin_amdgcn_sched_barrier(0);
+    acc[2][j] = mfma32<true>(reinterpret_cast<const uint16_t*>(&fa[2]), reinterpret_cast<const uint16_t*>(&fb), acc[2][j]);
+    u2();
+    __builtin_amdgcn_sched_barrier(0);
+    acc[3][j] = mfma32<true>(reinterpret_cast<const uint16_t*>(&fa[3]), reinterpret_cast<const uint16_t*>(&fb), acc[3][j]);
+    u3();
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // Step s (fragments of stage s%2 in registers, slice-0 A decoded; set G
-  // holds the block of step s+1):
-  //   slice 0: decode the slice-1 A fragments and each column's B fragment;
-  //            stage G into stage (s+1)%2 (free since the barrier of step
-  //            s-1), then refill G with the block of step s+3
-  //   slice 1: decode the B fragments, barrier, read stage (s+1)%2, decode
-  //            its slice-0 A fragments
-  auto step = [&](auto nxt_c, RawBlock<FMT_E4M3>& G) {
-    constexpr int NXT = decltype(nxt_c)::value;
-    uint8_t* nbase = lds + NXT * STAGE;
-    column(fa0, dec(rb[0], sbv[0], 0), 0, [&] {
-      fa1[0] = dec(ra[0], sa[0], 1);
-      lookup_scale(G);
-      write_rows(G, nbase, 0);
-    });
-    column(fa0, dec(rb[1], sbv[1], 0), 1, [&] {
-      fa1[1] = dec(ra[1], sa[1], 1);
-      write_rows(G, nbase, 4);
-    });
-    column(fa0, dec(rb[2], sbv[2], 0), 2, [&] {
-      fa1[2] = dec(ra[2], sa[2], 1);
-      fetch(G);
-    });
-    column(fa0, dec(rb[3], sbv[3], 0), 3, [&] {
-      fa1[3] = dec(ra[3], sa[3], 1);
-      *reinterpret_cast<uint32_t*>(nbase + st_scale) = sws;
-    });
-    f16x8 fb1, fb2, fb3;
-    column(fa1, dec(rb[0], sbv[0], 1), 0, [&] {
-      fb1 = dec(rb[1], sbv[1], 1);
-      fb2 = dec(rb[2], sbv[2], 1);
-    });
-    column(fa1, fb1, 1, [&] {
-      fb3 = dec(rb[3], sbv[3], 1);
-      __syncthreads();
-      read_raw(nbase);
-    });
-    column(fa1, fb2, 2, [&] {
-      fa0[0] = dec(ra[0], sa[0], 0);
-      fa0[1] = dec(ra[1], sa[1], 0);
-    });
-    column(fa1, fb3, 3, [&] {
-      fa0[2] = dec(ra[2], sa[2], 0);
-      fa0[3] = dec(ra[3], sa[3], 0);
-    });
+  // Step s on stage s%3 (raw fragments in set P; slice-0 A fragments and the
+  // slice-0 column-0 B fragment fbc decoded): slice 0 decodes the slice-1 A
+  // fragments and the next B fragment; slice 1 the next B fragment and the
+  // next step's slice-0 A fragments (set Q, read from stage (s+1)%3 during
+  // slice-0 column 0).  The block of step s+2 (in G) is staged into stage
+  // (s+2)%3 and G refilled with the block of step s+4; one barrier per step,
+  // at its end.
+  f16x8 fbc;
+  auto step = [&](auto set_c, RawBlock<FMT_E4M3>& G, int nxt_off, int wr_off) {
+    constexpr int P = decltype(set_c)::value, Q = P ^ 1;
+    uint8_t* wbase = lds + wr_off;
+    const uint8_t* nbase = lds + nxt_off;
+    f16x8 fbA, fbB;
+    // slice 0
+    column(fa0, fbc, 0,
+           [&] { read_raw(IC<Q>{}, nbase, 0); dech(fa1[0], ra[P][0], sa[P][0], 1, 0); },
+           [&] { read_raw(IC<Q>{}, nbase, 1); dech(fa1[0], ra[P][0], sa[P][0], 1, 1); },
+           [&] { read_raw(IC<Q>{}, nbase, 2); dech(fbA, rb[P][1], sbv[P][1], 0, 0); },
+           [&] { read_raw(IC<Q>{}, nbase, 3); dech(fbA, rb[P][1], sbv[P][1], 0, 1); });
+    column(fa0, fbA, 1,
+           [&] { lookup_scale(G); dech(fa1[1], ra[P][1], sa[P][1], 1, 0); },
+           [&] { write_rows(G, wbase, 0); dech(fa1[1], ra[P][1], sa[P][1], 1, 1); },
+           [&] { write_rows(G, wbase, 2); dech(fbB, rb[P][2], sbv[P][2], 0, 0); },
+           [&] { write_rows(G, wbase, 4); dech(fbB, rb[P][2], sbv[P][2], 0, 1); });
+    column(fa0, fbB, 2,
+           [&] { write_rows(G, wbase, 6); dech(fa1[2], ra[P][2], sa[P][2], 1, 0); },
+           [&] { fetch(G); dech(fa1[2], ra[P][2], sa[P][2], 1, 1); },
+           [&] { *reinterpret_cast<uint32_t*>(wbase + st_scale) = sws; dech(fbA, rb[P][3], sbv[P][3], 0, 0); },
+           [&] { dech(fbA, rb[P][3], sbv[P][3], 0, 1); });
+    column(fa0, fbA, 3,
+           [&] { dech(fa1[3], ra[P][3], sa[P][3], 1, 0); },
+           [&] { dech(fa1[3], ra[P][3], sa[P][3], 1, 1); },
+           [&] { dech(fbB, rb[P][0], sbv[P][0], 1, 0); },
+           [&] { dech(fbB, rb[P][0], sbv[P][0], 1, 1); });
+    // slice 1 (fa0 is free: it takes the next step's slice-0 A fragments)
+    column(fa1, fbB, 0,
+           [&] { dech(fbA, rb[P][1], sbv[P][1], 1, 0); },
+           [&] { dech(fbA, rb[P][1], sbv[P][1], 1, 1); },
+           [&] { dech(fa0[0], ra[Q][0], sa[Q][0], 0, 0); },
+           [&] { dech(fa0[0], ra[Q][0], sa[Q][0], 0, 1); });
+    column(fa1, fbA, 1,
+           [&] { dech(fbB, rb[P][2], sbv[P][2], 1, 0); },
+           [&] { dech(fbB, rb[P][2], sbv[P][2], 1, 1); },
+           [&] { dech(fa0[1], ra[Q][1], sa[Q][1], 0, 0); },
+           [&] { dech(fa0[1], ra[Q][1], sa[Q][1], 0, 1); });
+    column(fa1, fbB, 2,
+           [&] { dech(fbA, rb[P][3], sbv[P][3], 1, 0); },
+           [&] { dech(fbA, rb[P][3], sbv[P][3], 1, 1); },
+           [&] { dech(fa0[2], ra[Q][2], sa[Q][2], 0, 0); },
+           [&] { dech(fa0[2], ra[Q][2], sa[Q][2], 0, 1); });
+    column(fa1, fbA, 3,
+           [&] { dech(fa0[3], ra[Q][3], sa[Q][3], 0, 0); },
+           [&] { dech(fa0[3], ra[Q][3], sa[Q][3], 0, 1); },
+           [&] { dech(fbc, rb[Q][0], sbv[Q][0], 0, 0); },
+           [&] {
+             dech(fbc, rb[Q][0], sbv[Q][0], 0, 1);
+             __syncthreads();
+           });
   };
 
   const int nsteps = (t.kb_end - t.kb_begin + KB - 1) / KB;
@@ -245,18 +280,32 @@ __global__ __launch_bounds__(256) void k_conv8w(const ConvParams p) {
     __syncthreads();  // scale-word table
     lookup_scale(g0);
     write_rows(g0, lds, 0);
+    write_rows(g0, lds, 2);
     write_rows(g0, lds, 4);
+    write_rows(g0, lds, 6);
     *reinterpret_cast<uint32_t*>(lds + st_scale) = sws;
+    lookup_scale(g1);
+    write_rows(g1, lds + STAGE, 0);
+    write_rows(g1, lds + STAGE, 2);
+    write_rows(g1, lds + STAGE, 4);
+    write_rows(g1, lds + STAGE, 6);
+    *reinterpret_cast<uint32_t*>(lds + STAGE + st_scale) = sws;
     fetch(g0);
+    fetch(g1);
     __syncthreads();
-    read_raw(lds);
 #pragma unroll
-    for (int i = 0; i < RM; ++i) fa0[i] = dec(ra[i], sa[i], 0);
+    for (int q = 0; q < 4; ++q) read_raw(IC<0>{}, lds, q);
+#pragma unroll
+    for (int i = 0; i < RM; ++i) fa0[i] = dec(ra[0][i], sa[0][i], 0);
+    fbc = dec(rb[0][0], sbv[0][0], 0);
     // an odd step count runs one more step, on padding blocks only (zero
     // scale words: it adds exact zeros)
+    int c = 0;  // stage of step s
     for (int s = 0; s < nsteps; s += 2) {
-      step(IC<1>{}, g1);
-      step(IC<0>{}, g0);
+      const int c1 = c == 2 ? 0 : c + 1, c2 = c1 == 2 ? 0 : c1 + 1;
+      step(IC<0>{}, g0, c1 * STAGE, c2 * STAGE);
+      step(IC<1>{}, g1, c2 * STAGE, c * STAGE);
+      c = c2;
     }
   }
   // the fp16 fragments held g * B * 2^-2: one accumulator unit is 2^-4
