@@ -71,6 +71,10 @@ def parse():
                          "the quantizations it reads; layers stay in order)")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="only time the vendor dense GEMM (torch.matmul: hipBLASLt) in fp16 and bf16 on the "
+                         "workload's first layer's three GEMM shapes and on 8192^3, as context for the MX GEMMs "
+                         "(same flops, 16-bit operands, no decode, no gather)")
     ap.add_argument("--verbose", action="store_true")
     return ap.parse_args()
 
@@ -161,6 +165,37 @@ def mfma_dtype(block, fmt, mx):
     return "fp4" if block == 32 else "f16"
 
 
+def library_gemm(a, torch, dev, WL):
+    """Dense 16-bit GEMM rates of the vendor library on the MX GEMMs' shapes:
+    fwd C_out x (N Ho Wo) x (C_in Kh Kw), wgrad C_out x (C_in Kh Kw) x (N Ho Wo),
+    and a square 8192 GEMM.  One JSON line per case."""
+    lay = WL.workloads()[a.workload].layers[0]
+    cols = lay.n * lay.h_out * lay.w_out
+    kk = lay.c_in * lay.k_h * lay.k_w
+    cases = [("square", 8192, 8192, 8192), ("fwd", lay.c_out, cols, kk), ("wgrad", lay.c_out, kk, cols)]
+    for dt in (torch.float16, torch.bfloat16):
+        for name, m, n, k in cases:
+            x = torch.randn(m, k, device=dev, dtype=dt)
+            y = torch.randn(k, n, device=dev, dtype=dt)
+            for _ in range(3):
+                z = torch.matmul(x, y)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 10
+            e0.record()
+            for _ in range(reps):
+                z = torch.matmul(x, y)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            tf = 2.0 * m * n * k / (us * 1e-6) / 1e12
+            print(json.dumps({"library_gemm": name, "dtype": str(dt).replace("torch.", ""), "m": m, "n": n, "k": k,
+                              "us": round(us, 1), "tflops": round(tf, 1), "frac_of_2p5_pflops": round(tf / 2500, 4)}),
+                  flush=True)
+            del x, y, z
+            torch.cuda.empty_cache()
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -175,6 +210,10 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if a.library_gemm:
+        library_gemm(a, torch, dev, WL)
+        return
 
     if a.copy_calib:
         n = a.copy_calib * (1 << 20) // 4
