@@ -711,6 +711,18 @@ WgradPlan wgrad_plan_mx(const Geom& g) {
   return {Tile{T, T, 2, 4, 4}, static_cast<int>(splits)};
 }
 
+// Band order of a fwd / dgrad launch's column tiles (TileCtx::init): rows
+// of `row_pos` output positions, `rows` of them, each a whole number of
+// NT-column tiles; bands of 4 rows.
+void set_band(ConvParams& p, int rows, int row_pos, int nt) {
+  const int64_t cb_per_row = static_cast<int64_t>(row_pos) * p.nb;
+  const int tile_cb = nt / 8;
+  if (rows >= 8 && cb_per_row % tile_cb == 0) {
+    p.band_tpr = static_cast<int32_t>(cb_per_row / tile_cb);
+    p.band_rows = 4;
+  }
+}
+
 // Forward launch geometry: tile, grid and waves per workgroup.
 struct FwdPlan {
   Tile t;
@@ -755,6 +767,7 @@ hipError_t launch_conv_fwd(const Geom& g, const mx_qtensor* wq, const mx_qtensor
   if (p.ncb > 0) {
     const FwdPlan pl = fwd_plan(g, p);
     nslots = static_cast<int64_t>(pl.grid.x) * pl.grid.y * pl.grid.z * pl.t.waves;
+    set_band(p, g.ho, g.wo, pl.t.nt);
     if (!launch_op<OP_FWD>(p, g.fmt, g.afmt, pl.t, pl.grid, s)) return hipErrorNotSupported;
   }
   if (y_amax != nullptr)
@@ -781,6 +794,7 @@ hipError_t launch_conv_dgrad(const Geom& g, const mx_qtensor* wq, const mx_qtens
   }
   const Tile t = pick_tile(p.M, static_cast<int64_t>(p.ncb) * 8, g.sh * g.sw);
   dim3 grid((p.ncb * 8 + t.nt - 1) / t.nt, (p.M + t.mt - 1) / t.mt, g.sh * g.sw);
+  if (g.sh == 1 && g.sw == 1) set_band(p, g.h, g.w, t.nt);  // one phase: the positions are (h, w)
   if (!launch_op<OP_DGRAD>(p, g.fmt, g.fmt, t, grid, s)) return hipErrorNotSupported;
   return hipGetLastError();
 }

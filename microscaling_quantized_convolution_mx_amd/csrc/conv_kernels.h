@@ -59,6 +59,9 @@ struct ConvParams {
   float* out;
   uint32_t* amax_out;  // fwd: per-wave max |y| slots (slot 1 + global wave index; nullptr: not wanted)
   int32_t stream_out;  // fwd / dgrad: write the output with nontemporal stores (outputs above kStreamOutBytes)
+  // fwd / dgrad: column tiles per row of output positions and the band
+  // height of the band order (TileCtx::init); 0: launch order
+  int32_t band_tpr, band_rows;
 };
 
 // Tile of one launch: MT x NT outputs, waves along M, waves, k-blocks per stage.
@@ -324,6 +327,21 @@ struct TileCtx {
       const int t = nl / gridDim.x;
       by = t % gridDim.y;
       bz = t / gridDim.y;
+    }
+    // Band order (fwd / dgrad, where a row of output positions is a whole
+    // number of column tiles): consecutive tiles walk down band_rows rows of
+    // positions before moving right, so that the tiles one XCD runs at once
+    // form a patch of positions whose input blocks, reused across the taps,
+    // stay in that XCD's L2 (in row order the rows above and below have left
+    // it by the time they are reused).  A bijection on the column tiles.
+    if constexpr (OP != OP_WGRAD) {
+      if (p.band_tpr > 0) {
+        const int tpr = p.band_tpr, R = p.band_rows, rows = gridDim.x / tpr;
+        const int b = bx / (R * tpr), off = bx - b * (R * tpr);
+        const int rb = min(R, rows - b * R);
+        const int c = off / rb, rr = off - c * rb;
+        bx = (b * R + rr) * tpr + c;
+      }
     }
     rb0 = by * (MT / 8);
     cb0 = bx * (NT / 8);
