@@ -140,6 +140,8 @@ def lib():
     L.orc_quantize_after_im2col.restype = ctypes.c_int
     L.orc_threads.restype = ctypes.c_int
     L.orc_threads.argtypes = []
+    L.orc_set_threads.restype = None
+    L.orc_set_threads.argtypes = [ctypes.c_int]
     L.orc_quantize_after_im2col.argtypes = [ctypes.POINTER(OrcConv), ctypes.c_int, _P, _P, _P, _P, _P]
     _lib = L
     return L
@@ -148,6 +150,11 @@ def lib():
 def threads() -> int:
     """Threads the oracle's OpenMP loops run on."""
     return lib().orc_threads()
+
+
+def set_threads(n: int) -> None:
+    """Threads for the oracle's OpenMP loops (for timing; results do not depend on it)."""
+    lib().orc_set_threads(int(n))
 
 
 def _ptr(a: np.ndarray):

@@ -1033,3 +1033,7 @@ int orc_quantize_after_im2col(const orc_conv* cv, int fmt, const float* x, uint8
 
 /* Threads the OpenMP loops above run on (for reporting only). */
 int orc_threads(void) { return omp_get_max_threads(); }
+
+/* Sets the threads of the OpenMP loops (timing only: the results do not
+   depend on it, every loop writes disjoint outputs). */
+void orc_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }

@@ -132,3 +132,33 @@ def test_im2col_rows_and_columns(orc):
             hh, ww = ho + kh - 1, wo + kw - 1
             exp = -1 if not (0 <= hh < 5 and 0 <= ww < 6) else ((hh * 6 + ww) * 16 + ci) * 8 + n
             assert O.im2col_src(cv, k, j) == exp
+
+
+def test_results_do_not_depend_on_the_thread_count(orc):
+    # the OpenMP loops write disjoint outputs: one thread and all threads give
+    # the same bits (the single-threaded CPU timing relies on it)
+    lay = WL.ConvLayer(8, 16, 16, 16, 16, 3, 3, 1, 1, 1, 1)
+    cv = O.conv(lay.n, lay.c_in, lay.c_out, lay.h, lay.w, lay.k_h, lay.k_w,
+                lay.stride_h, lay.stride_w, lay.pad_h, lay.pad_w)
+    x = WL.gen_x(lay, "normal", 31).numpy()
+    w = WL.gen_w(lay, 32).numpy()
+    dy = WL.gen_dy(lay, 1.0, 33).numpy()
+    nt = O.threads()
+
+    def run():
+        qx = O.quantize(O.ACT, O.E2M1, x)
+        qw = O.quantize(O.WEIGHT, O.E2M1, w)
+        qdy = O.quantize(O.GRAD, O.E2M1, dy, O.SR, 7)
+        xe, we, dye = qx.exact(), qw.exact(), qdy.exact()
+        return (qx.codes.copy(), qdy.codes.copy(), O.conv_fwd(cv, we, xe)[0], O.conv_dgrad(cv, we, dye)[0],
+                O.conv_wgrad(cv, dye, xe)[0])
+
+    try:
+        O.set_threads(1)
+        one = run()
+    finally:
+        O.set_threads(nt)
+    many = run()
+    assert O.threads() == nt
+    for a, b in zip(one, many):
+        assert np.array_equal(a, b)
