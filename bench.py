@@ -705,12 +705,34 @@ def cpu_baseline(wl, fmts, afmt, budget_s, with_replay=True):
             flops += 3 * lay.flops()
             done += 1
             li += 1
-        return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-                "cpu_model": cpu_model(), "nproc": os.cpu_count(),
-                "sample": f"full quantize X/W/dY + fp64 fwd/dgrad/wgrad of {done} layer(s) of the "
-                          f"{nl}-layer stack ({WL.FMT_NAMES[fmts[0]]}) taken in order from the first, "
-                          f"{flops / 1e9:.2f} GFLOP in {spent:.1f} s",
-                "seconds": spent}
+        out = {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+               "cpu_model": cpu_model(), "nproc": os.cpu_count(),
+               "sample": f"full quantize X/W/dY + fp64 fwd/dgrad/wgrad of {done} layer(s) of the "
+                         f"{nl}-layer stack ({WL.FMT_NAMES[fmts[0]]}) taken in order from the first, "
+                         f"{flops / 1e9:.2f} GFLOP in {spent:.1f} s",
+               "seconds": spent}
+        if nl == 1:
+            # the single conv is also timed on one thread (same passes, same inputs)
+            try:
+                O.set_threads(1)
+                t1 = 0.0
+                reps = 0
+                while t1 < min(budget_s, 5.0) and reps < done:
+                    t0 = time.perf_counter()
+                    qx = O.quantize(O.ACT, fmt_x, x)
+                    qw = O.quantize(O.WEIGHT, fmt_w, w)
+                    qdy = O.quantize(O.GRAD, fmt_w, dy, O.SR, WL.seed_for(wl.cfg_index, 0, 4))
+                    xe, we, dye = qx.exact(), qw.exact(), qdy.exact()
+                    O.conv_fwd(cv, we, xe)
+                    O.conv_dgrad(cv, we, dye)
+                    O.conv_wgrad(cv, dye, xe)
+                    t1 += time.perf_counter() - t0
+                    reps += 1
+            finally:
+                O.set_threads(threads)
+            out["single_thread"] = {"value": reps * 3 * wl.layers[0].flops() / t1 / 1e12, "unit": "TFLOP/s",
+                                    "cores": 1, "passes": reps, "seconds": t1}
+        return out
 
     # sampled stress layer
     npts = {"fwd": 65536, "dgrad": 65536, "wgrad": 4096}
