@@ -519,52 +519,7 @@ __global__ __launch_bounds__(kThreads) void k_quantize_wide(const float* __restr
       // base + r N (even), so its first pair is k0 + r N / 2 with k0 = base / 2
       // and gk = kGolden64 (k + 1) advances by a constant from row to row
       const uint64_t gk0 = kGolden64 * (static_cast<uint64_t>(cur.base >> 1) + 1ull);
-      if constexpr (SR && FMT == FMT_E2M1) {
-        // Stochastic rounding on the hardware conversion, where it provably
-        // matches sr_code.  Probed on this GPU: for |v| >= 1,
-        // v_cvt_scalef32_sr_pk_fp4_f32 gives the first element the code of
-        // lo, or of hi when frac + s / 2^32 >= 1 (lo <= |v| < hi the
-        // neighbouring grid points, frac = (|v| - lo) / (hi - lo), s the
-        // seed), saturates at |v| >= 6 and keeps the sign of v; the second
-        // element does the same with s << 1.  (1.2 million random pairs over
-        // [-64, 64], and u set to the exact threshold +-2 for 200000 values in
-        // each of [1, 2), [2, 4), [4, 6): no difference.)  With
-        // s = 2^32 - 1 - u24 * 2^8 the test reads frac >= u + 2^-32, which is
-        // frac > u (sr_code's rule) because frac has at most 22 fractional
-        // bits there; the second element gets s >> 1 (its test frac >=
-        // u + 2^-31 is the same rule for the same reason).  Below 1 the
-        // conversion keeps fewer random bits than frac has (it differs from
-        // the rule at the threshold), so there the rule itself is applied to
-        // the input: lo is 0 or 0.5, round up iff u24 < (|v| - lo) * 2^25
-        // (exact in fp32), and the conversion then receives the grid value
-        // it keeps unchanged.  The elements of a pair draw independent
-        // uniforms, so each gets a conversion of its own.
-        typedef float float2v __attribute__((ext_vector_type(2)));
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const uint64_t gk = gk0 + r * gk_row;
-          uint32_t c = 0;
-#pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            uint32_t ue, uo;
-            sr_bits_pair(seed, gk + q * kGolden64, ue, uo);
-            const int j = 4 * r + 2 * q;
-            const float ae = v[j], ao = v[j + 1];
-            auto below_one = [](float a, uint32_t u24) {
-              const float lo = a < 0.5f ? 0.0f : 0.5f;
-              return static_cast<float>(u24) < (a - lo) * 0x1p25f ? lo + 0.5f : lo;
-            };
-            const float ie = ae < 1.0f ? below_one(ae, ue) : ae;
-            const float io = ao < 1.0f ? below_one(ao, uo) : ao;
-            const float2v pe = {__builtin_copysignf(ie, xs[j]), 0.0f};
-            const float2v po = {0.0f, __builtin_copysignf(io, xs[j + 1])};
-            const uint32_t be = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, pe, ~(ue << 8), 1.0f, 0);
-            const uint32_t bo = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, po, (~(uo << 8)) >> 1, 1.0f, 0);
-            c |= ((be & 0x0Fu) | (bo & 0xF0u)) << (8 * q);
-          }
-          chunk[r] = c;
-        }
-      } else if constexpr (!SR && (FMT == FMT_E2M1 || FMT == FMT_E4M3)) {
+      if constexpr (!SR && (FMT == FMT_E2M1 || FMT == FMT_E4M3)) {
         // hardware round to nearest even on copysign(min(v, max), x)
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
