@@ -1,0 +1,324 @@
+// Convolution GEMMs for the FP6 element formats (E2M3, E3M2) on the 256x256
+// tile (MicroQonv, arXiv 2609.28358, §IV-B; the FP6 elements of §IV-E and
+// MicroQonv+ in §VI-B).
+//
+// Every staged block is decoded once, by the thread that stages it, into
+// exact fp16 values g * B (two 32-value FP6 conversions, which apply the
+// exponent of B, and packed multiplies by its mantissa factor mB; see
+// BlockScale), and the MFMA fragments are read from LDS as they are.
+//
+// What differs from the generic kernel (conv_kernels.h), which decodes the
+// same way: the A- and B-staging waves run one instruction stream (staging
+// addresses and strides are data, not branches), and each block is fetched
+// two K steps before its decode into one of two register sets, refilled
+// right after the decode has read it.  In the generic kernel a block has
+// one K step to arrive, and the 48-byte FP6 blocks, many of them from L2,
+// were not covered by it: without its global loads that kernel ran ~23%
+// faster.  With one instruction stream the compiler also keeps the wait for
+// a fetch at the decode that needs it, instead of at the top of the step.
+//
+// LDS per stage and operand (fp16):
+//   lines (block rows along M/N: fwd A, wgrad A and B): 256 lines of the
+//     stage's 32 K values, pitch 80 bytes, line L stored at L ^ ((L >> 2) & 4)
+//     (the two halves of every second 8-line block swapped): the 16-byte
+//     fragment reads of 16 consecutive lines and the 16-byte staging writes
+//     of 4 line blocks x 4 k-blocks each hit 16 distinct bank quads;
+//   k rows (block rows along K: fwd B, dgrad A and B): 32 k rows of 256
+//     fp16 columns, pitch 576 bytes, plus 64 bytes after every 8 rows.  The
+//     16-bit transposing LDS read (ds_read_b64_tr_b16: within each group of
+//     16 lanes, lanes 4e .. 4e+3 supply row e of a 4 x 16 matrix of 16-bit
+//     values, 4 each, and lane o receives column o) gives each lane 4
+//     consecutive K values of its column; two of them make an MFMA fragment.
+//     A pass of 32 lanes reads 4 rows x 64 bytes at row offsets 64 bytes
+//     apart modulo the 256-byte bank row, and the staging writes of 4 column
+//     blocks x 4 k-blocks fall 16 and 64 bytes apart: both conflict-free.
+// Tile: 4 waves of 128x128 (a wave's 16 accumulator tiles fill its 256
+// AGPRs), K steps of 4 k-blocks (two 16-wide MFMA slices), three LDS
+// stages; the fragments of the next slice are read during the current one.
+#include "conv_kernels.h"
+
+namespace mx {
+namespace {
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Raw FP6 block between its global load and its decode: two 6-word groups,
+// each loaded by one vector load straight into the register tuple that the
+// 32-value conversion reads.  The address of group 1 passes through an empty
+// asm statement, so that the compiler cannot merge the loads into 16-byte
+// pieces that straddle the two groups (the register copies that then build
+// the tuples wait for the newest loads).  For the same reason the scale code
+// comes from the aligned 32-bit word of the scales array that holds it (the
+// array is padded past its last block): a loop-carried byte gets a
+// zero-extension at the top of the loop body, which waits for its load
+// there.  As in RawWords, a block outside the tensor loads block 0, mask 0.
+struct Raw6 {
+  u32x6 g[2];
+  uint32_t sword;  // scales word holding the block's scale code
+  uint32_t sbit;   // bit offset of the code in sword
+  uint32_t mask;   // ~0 for a block of the tensor, 0 for padding
+
+  __device__ __forceinline__ void load(const uint8_t* codes, const uint8_t* scales, uint32_t blk, bool ok) {
+    typedef unsigned int u32x6a __attribute__((ext_vector_type(6), aligned(8)));
+    typedef __attribute__((address_space(1))) const u32x6a gu32x6a;  // global memory
+    const uint64_t b = ok ? blk : 0u;
+    const uint64_t a0 = reinterpret_cast<uint64_t>(codes) + b * 48;
+    uint64_t a1 = a0 + 24;
+    asm volatile("" : "+v"(a1));
+    g[0] = *reinterpret_cast<gu32x6a*>(a0);
+    g[1] = *reinterpret_cast<gu32x6a*>(a1);
+    sword = *reinterpret_cast<const uint32_t*>(scales + (b & ~static_cast<uint64_t>(3)));
+    sbit = static_cast<uint32_t>(b & 3u) * 8u;
+    mask = ok ? ~0u : 0u;
+  }
+  __device__ __forceinline__ uint32_t scale_code() const { return __builtin_amdgcn_ubfe(sword, sbit, 8) & mask; }
+};
+
+template <int OP, int FMT>
+__global__ __launch_bounds__(256) void k_conv6s(const ConvParams p) {
+  static_assert(Fmt<FMT>::BITS == 6, "FP6 element formats");
+  constexpr int MT = 256, NT = 256, WM = 2, KB = 4;
+  constexpr int WTM = 128, WTN = 128, RM = 4, RN = 4;
+  constexpr bool A_ROWS = (OP != OP_DGRAD);
+  constexpr bool B_ROWS = (OP == OP_WGRAD);
+  constexpr int PL = 80;           // line pitch
+  constexpr int PK = 576;          // k-row pitch
+  constexpr int GK = 8 * PK + 64;  // the 8 k rows of one k-block + pad
+  constexpr int SZL = 256 * PL, SZK = KB * GK;
+  constexpr int A_SZ = A_ROWS ? SZL : SZK, B_SZ = B_ROWS ? SZL : SZK;
+  constexpr int A_C = 0, B_C = A_SZ;
+  constexpr int STAGE = A_SZ + B_SZ;
+  constexpr int NST = 3;
+  static_assert(STAGE % 16 == 0, "16-byte aligned stages");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[NST * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % WM, wn = wave / WM;
+  TileCtx<OP, MT, NT, KB> t;
+  if (!t.init(p, tid)) return;
+  const bool is_a = t.is_a;  // uniform per wave: the first two waves stage A
+
+  // staging addresses of this thread's block: rows 0-3 from st0, rows 4-7
+  // from st1, st_pitch apart.  Lines: row r is line 8 lblk + r (the swizzle
+  // swaps the halves of line blocks with bit 1 set), at k-block kbl; k rows:
+  // row r is k row 8 kbl + r, at column block lblk.
+  const bool rows = is_a ? A_ROWS : B_ROWS;
+  const int opbase = is_a ? A_C : B_C;
+  const int sw = (t.lblk & 2) << 1;
+  const int st0 = opbase + (rows ? (t.lblk * 8 + sw) * PL + t.kbl * 16 : t.kbl * GK + t.lblk * 16);
+  const int st1 = rows ? opbase + (t.lblk * 8 + 4 - sw) * PL + t.kbl * 16 : st0 + 4 * PK;
+  const int st_pitch = rows ? PL : PK;
+
+  const uint8_t* my_codes = is_a ? p.a_codes : p.b_codes;
+  const uint8_t* my_scales = is_a ? p.a_scales : p.b_scales;
+  KWalk<OP, MT, NT, KB> walk;
+  walk.init(p, t);
+  uint32_t s_fetch = 0;  // k offset (s * KB) of the next fetch
+  auto fetch = [&](Raw6& g) {
+    uint32_t blk;
+    const bool ok = walk.next(s_fetch, blk);
+    g.load(my_codes, my_scales, blk, ok);
+    s_fetch += KB;
+  };
+
+  // decode of the staged block: scale, then group G (rows 4G .. 4G+3) into
+  // 16 words of fp16 pairs (row-major), then the mantissa factor.  A padding
+  // block (block 0's codes, scale code masked to 0) converts to finite
+  // values (FP6 has no NaN or Inf code) that mB = 0 turns into zeros.
+  float sc;
+  f16x2 m2;
+  uint32_t dw[16];
+  auto set_scale = [&](const Raw6& g) {
+    const BlockScale bs(g.scale_code());
+    sc = bs.b;
+    const _Float16 m = static_cast<_Float16>(bs.mb);
+    m2 = f16x2{m, m};
+  };
+  auto convert = [&](const Raw6& g, int G) {
+    const auto v = [&] {
+      if constexpr (FMT == FMT_E3M2) return __builtin_amdgcn_cvt_scalef32_pk32_f16_bf6(g.g[G], sc);
+      else return __builtin_amdgcn_cvt_scalef32_pk32_f16_fp6(g.g[G], sc);
+    }();
+    struct Words { uint32_t u[16]; };
+    const Words wv = __builtin_bit_cast(Words, v);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) dw[k] = wv.u[k];
+  };
+  auto scale_words = [&](int k0) {
+#pragma unroll
+    for (int k = k0; k < k0 + 8; ++k) dw[k] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, dw[k]) * m2);
+  };
+  // rows r, r+1 of group G (r even, 0..2) of the decoded block into stage base
+  auto write_rows = [&](uint8_t* base, int G, int r) {
+    const int a = (G ? st1 : st0) + r * st_pitch;
+    *reinterpret_cast<uint4*>(base + a) = make_uint4(dw[4 * r], dw[4 * r + 1], dw[4 * r + 2], dw[4 * r + 3]);
+    *reinterpret_cast<uint4*>(base + a + st_pitch) =
+        make_uint4(dw[4 * r + 4], dw[4 * r + 5], dw[4 * r + 6], dw[4 * r + 7]);
+  };
+  auto stage_block = [&](const Raw6& g, uint8_t* base) {
+    set_scale(g);
+#pragma unroll
+    for (int G = 0; G < 2; ++G) {
+      convert(g, G);
+      scale_words(0);
+      scale_words(8);
+      write_rows(base, G, 0);
+      write_rows(base, G, 2);
+    }
+  };
+
+  f32x16 acc[RM][RN];
+#pragma unroll
+  for (int i = 0; i < RM; ++i)
+#pragma unroll
+    for (int j = 0; j < RN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  // fragment read offsets (slice 0; slice 1 is 32 bytes further for lines,
+  // 2 GK for k rows).  Lines: line wX*128 + i*32 + lane%32 (swizzled), K
+  // half lane/32; fragment i adds 32 lines.  K rows: the lane supplies row
+  // e = (lane%16)/4 (and 4 + e) of k-block lane/32, columns 4 (lane%4) ..
+  // +3 of the 16-column group (lane/16)%2; fragment i adds 32 columns.
+  const int l32 = lane & 31, half = lane >> 5;
+  const int line_off = (l32 ^ ((l32 >> 2) & 4)) * PL + half * 16;
+  const int krow_off = half * GK + ((lane & 15) >> 2) * PK + (((lane >> 4) & 1) * 16 + (lane & 3) * 4) * 2;
+  const int a_frag = A_C + (A_ROWS ? wm * 128 * PL + line_off : wm * 256 + krow_off);
+  const int b_frag = B_C + (B_ROWS ? wn * 128 * PL + line_off : wn * 256 + krow_off);
+  auto read_frag = [&](const uint8_t* q, bool line) -> f16x8 {
+    if (line) return *reinterpret_cast<const f16x8*>(q);
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(q));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(q + 4 * PK));
+    return __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  // fragment i of A (j of B) of slice `slice` of the stage at `base`
+  auto frag_a = [&](const uint8_t* base, int slice, int i) {
+    return read_frag(base + a_frag + (A_ROWS ? i * 32 * PL + slice * 32 : i * 64 + slice * 2 * GK), A_ROWS);
+  };
+  auto frag_b = [&](const uint8_t* base, int slice, int j) {
+    return read_frag(base + b_frag + (B_ROWS ? j * 32 * PL + slice * 32 : j * 64 + slice * 2 * GK), B_ROWS);
+  };
+  f16x8 fa0[RM], fb0[RN], fa1[RM], fb1[RN];  // fragments of slice 0 and slice 1
+
+  // One column j of a slice: MFMA i is followed by work unit i, each closed
+  // by a scheduling barrier (a wave hides only a few VALU operations and
+  // LDS accesses behind each MFMA).
+  auto column = [&](const f16x8 (&fa)[RM], const f16x8& fb, int j, auto&& u0, auto&& u1, auto&& u2, auto&& u3) {
+    acc[0][j] = mfma32<true>(reinterpret_cast<const uint16_t*>(&fa[0]), reinterpret_cast<const uint16_t*>(&fb), acc[0][j]);
+    u0();
+    __builtin_amdgcn_sched_barrier(0);
+    acc[1][j] = mfma32<true>(reinterpret_cast<const uint16_t*>(&fa[1]), reinterpret_cast<const uint16_t*>(&fb), acc[1][j]);
+    u1();
+    __builtin_amdgcn_sched_barrier(0);
+    acc[2][j] = mfma32<true>(reinterpret_cast<const uint16_t*>(&fa[2]), reinterpret_cast<const uint16_t*>(&fb), acc[2][j]);
+    u2();
+    __builtin_amdgcn_sched_barrier(0);
+    acc[3][j] = mfma32<true>(reinterpret_cast<const uint16_t*>(&fa[3]), reinterpret_cast<const uint16_t*>(&fb), acc[3][j]);
+    u3();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto none = [] {};
+
+  // Step s on the stage at cur (its slice-0 fragments in fa0/fb0): slice 0
+  // reads the slice-1 fragments; the block in G (step s+2) is decoded and
+  // written into the stage at wr across both slices, and G is refilled with
+  // the block of step s+4; slice 1 reads the slice-0 fragments of the next
+  // stage (nxt, complete since the previous step's barrier).  One barrier,
+  // at the end: wr complete, cur free.
+  auto step = [&](Raw6& G, const uint8_t* cur, const uint8_t* nxt, uint8_t* wr) {
+    column(fa0, fb0[0], 0,
+           [&] { fa1[0] = frag_a(cur, 1, 0); },
+           [&] { fb1[0] = frag_b(cur, 1, 0); },
+           [&] { fa1[1] = frag_a(cur, 1, 1); },
+           [&] { fb1[1] = frag_b(cur, 1, 1); });
+    column(fa0, fb0[1], 1,
+           [&] { fa1[2] = frag_a(cur, 1, 2); },
+           [&] { fb1[2] = frag_b(cur, 1, 2); },
+           [&] { fa1[3] = frag_a(cur, 1, 3); },
+           [&] { fb1[3] = frag_b(cur, 1, 3); });
+    column(fa0, fb0[2], 2,
+           [&] { set_scale(G); },
+           [&] { convert(G, 0); },
+           [&] { scale_words(0); },
+           [&] { scale_words(8); });
+    column(fa0, fb0[3], 3,
+           [&] { write_rows(wr, 0, 0); },
+           [&] { write_rows(wr, 0, 2); },
+           [&] { convert(G, 1); },
+           [&] { scale_words(0); });
+    column(fa1, fb1[0], 0,
+           [&] { scale_words(8); },
+           [&] { write_rows(wr, 1, 0); },
+           [&] { write_rows(wr, 1, 2); },
+           [&] { fetch(G); });
+    column(fa1, fb1[1], 1,
+           [&] { fa0[0] = frag_a(nxt, 0, 0); },
+           [&] { fb0[0] = frag_b(nxt, 0, 0); },
+           [&] { fa0[1] = frag_a(nxt, 0, 1); },
+           [&] { fb0[1] = frag_b(nxt, 0, 1); });
+    column(fa1, fb1[2], 2,
+           [&] { fa0[2] = frag_a(nxt, 0, 2); },
+           [&] { fb0[2] = frag_b(nxt, 0, 2); },
+           [&] { fa0[3] = frag_a(nxt, 0, 3); },
+           [&] { fb0[3] = frag_b(nxt, 0, 3); });
+    column(fa1, fb1[3], 3, none, none, none, [&] { __syncthreads(); });
+  };
+
+  const int nsteps = (t.kb_end - t.kb_begin + KB - 1) / KB;
+  if (nsteps > 0) {
+    Raw6 g0, g1;  // blocks of even and odd steps
+    fetch(g0);
+    fetch(g1);
+    stage_block(g0, lds);
+    stage_block(g1, lds + STAGE);
+    fetch(g0);
+    fetch(g1);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < RM; ++i) fa0[i] = frag_a(lds, 0, i);
+#pragma unroll
+    for (int j = 0; j < RN; ++j) fb0[j] = frag_b(lds, 0, j);
+    // an odd step count runs one more step, on padding blocks only (zero
+    // values: it adds exact zeros)
+    int c = 0;  // stage of step s
+    for (int s = 0; s < nsteps; s += 2) {
+      const int c1 = c == 2 ? 0 : c + 1, c2 = c1 == 2 ? 0 : c1 + 1;
+      step(g0, lds + c * STAGE, lds + c1 * STAGE, lds + c2 * STAGE);
+      step(g1, lds + c1 * STAGE, lds + c2 * STAGE, lds + c * STAGE);
+      c = c2;
+    }
+  }
+  store_tile<OP, MT, NT, KB, WTM, WTN, RM, RN>(p, t, acc, lane, wm, wn);
+}
+
+}  // namespace
+
+namespace gemm {
+
+// The 256x256 FP6 kernel; false (nothing launched) for another format or
+// where its K walk needs the division-based block search (an innermost K
+// extent below 4 k-blocks).
+bool launch_conv6(int op, int fmt, const ConvParams& p, dim3 grid, hipStream_t s) {
+  if (!kwalk_ok(op, p, 4) || (fmt != FMT_E2M3 && fmt != FMT_E3M2)) return false;
+  const bool e3 = fmt == FMT_E3M2;
+  switch (op) {
+    case OP_FWD:
+      if (e3) hipLaunchKernelGGL((k_conv6s<OP_FWD, FMT_E3M2>), grid, dim3(256), 0, s, p);
+      else hipLaunchKernelGGL((k_conv6s<OP_FWD, FMT_E2M3>), grid, dim3(256), 0, s, p);
+      break;
+    case OP_DGRAD:
+      if (e3) hipLaunchKernelGGL((k_conv6s<OP_DGRAD, FMT_E3M2>), grid, dim3(256), 0, s, p);
+      else hipLaunchKernelGGL((k_conv6s<OP_DGRAD, FMT_E2M3>), grid, dim3(256), 0, s, p);
+      break;
+    default:
+      if (e3) hipLaunchKernelGGL((k_conv6s<OP_WGRAD, FMT_E3M2>), grid, dim3(256), 0, s, p);
+      else hipLaunchKernelGGL((k_conv6s<OP_WGRAD, FMT_E2M3>), grid, dim3(256), 0, s, p);
+      break;
+  }
+  return true;
+}
+
+}  // namespace gemm
+}  // namespace mx
