@@ -14,7 +14,7 @@ namespace gemm {
 
 bool launch_mixed(int op, const ConvParams& p, int fmt_a, int fmt_b, const Tile& t, dim3 grid, hipStream_t s) {
   if (fmt_a == FMT_E3M2 && fmt_b == FMT_E3M2) {
-    if (t.mt == 256 && t.nt == 256 && launch_conv6(op, FMT_E3M2, p, grid, s)) return true;
+    if (t.mt == 256 && t.nt == 256 && launch_staged(op, FMT_E3M2, p, grid, s)) return true;
     switch (op) {
       case OP_FWD: launch_generic<OP_FWD, FMT_E3M2, FMT_E3M2>(p, t, grid, s); return true;
       case OP_DGRAD: launch_generic<OP_DGRAD, FMT_E3M2, FMT_E3M2>(p, t, grid, s); return true;

@@ -1,11 +1,14 @@
 // Convolution GEMMs for the FP6 element formats (E2M3, E3M2) on the 256x256
-// tile (MicroQonv, arXiv 2609.28358, §IV-B; the FP6 elements of §IV-E and
+// tile, every block decoded once, at staging, into exact fp16 values in LDS
+// (MicroQonv, arXiv 2609.28358, §IV-B; the FP6 elements of §IV-E and
 // MicroQonv+ in §VI-B).
 //
-// Every staged block is decoded once, by the thread that stages it, into
-// exact fp16 values g * B (two 32-value FP6 conversions, which apply the
-// exponent of B, and packed multiplies by its mantissa factor mB; see
-// BlockScale), and the MFMA fragments are read from LDS as they are.
+// The thread that stages a block decodes it into g * B (two 32-value FP6
+// conversions, which apply the exponent of B, and packed multiplies by its
+// mantissa factor mB; see BlockScale), and the MFMA fragments are read from
+// LDS as they are.  Both steps are exact (g * B has at most 8 significant
+// bits and lies in [2^-13, 12544]), so the fp16 MFMA sums the exact products
+// of Eq. 7.
 //
 // What differs from the generic kernel (conv_kernels.h), which decodes the
 // same way: the A- and B-staging waves run one instruction stream (staging
@@ -43,22 +46,33 @@ namespace {
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
+// The scale code of a block comes from the aligned 32-bit word of the scales
+// array that holds it (the array is padded past its last block), so that the
+// value carried across the K loop is a whole loaded word: a loop-carried
+// byte gets a zero-extension at the top of the loop body, which waits for
+// its load there.  As in RawWords, a block outside the tensor loads block 0
+// and carries mask 0.
+struct RawScale {
+  uint32_t sword;  // scales word holding the block's scale code
+  uint32_t sbit;   // bit offset of the code in sword
+  uint32_t mask;   // ~0 for a block of the tensor, 0 for padding
+  __device__ __forceinline__ void load(const uint8_t* scales, uint64_t b, bool ok) {
+    sword = *reinterpret_cast<const uint32_t*>(scales + (b & ~static_cast<uint64_t>(3)));
+    sbit = static_cast<uint32_t>(b & 3u) * 8u;
+    mask = ok ? ~0u : 0u;
+  }
+  __device__ __forceinline__ uint32_t code() const { return __builtin_amdgcn_ubfe(sword, sbit, 8) & mask; }
+};
+
 // Raw FP6 block between its global load and its decode: two 6-word groups,
 // each loaded by one vector load straight into the register tuple that the
 // 32-value conversion reads.  The address of group 1 passes through an empty
 // asm statement, so that the compiler cannot merge the loads into 16-byte
-// pieces that straddle the two groups (the register copies that then build
-// the tuples wait for the newest loads).  For the same reason the scale code
-// comes from the aligned 32-bit word of the scales array that holds it (the
-// array is padded past its last block): a loop-carried byte gets a
-// zero-extension at the top of the loop body, which waits for its load
-// there.  As in RawWords, a block outside the tensor loads block 0, mask 0.
+// pieces that straddle the groups (the register copies that would then build
+// the tuples wait for the newest loads).
 struct Raw6 {
   u32x6 g[2];
-  uint32_t sword;  // scales word holding the block's scale code
-  uint32_t sbit;   // bit offset of the code in sword
-  uint32_t mask;   // ~0 for a block of the tensor, 0 for padding
-
+  RawScale s;
   __device__ __forceinline__ void load(const uint8_t* codes, const uint8_t* scales, uint32_t blk, bool ok) {
     typedef unsigned int u32x6a __attribute__((ext_vector_type(6), aligned(8)));
     typedef __attribute__((address_space(1))) const u32x6a gu32x6a;  // global memory
@@ -68,15 +82,11 @@ struct Raw6 {
     asm volatile("" : "+v"(a1));
     g[0] = *reinterpret_cast<gu32x6a*>(a0);
     g[1] = *reinterpret_cast<gu32x6a*>(a1);
-    sword = *reinterpret_cast<const uint32_t*>(scales + (b & ~static_cast<uint64_t>(3)));
-    sbit = static_cast<uint32_t>(b & 3u) * 8u;
-    mask = ok ? ~0u : 0u;
+    s.load(scales, b, ok);
   }
-  __device__ __forceinline__ uint32_t scale_code() const { return __builtin_amdgcn_ubfe(sword, sbit, 8) & mask; }
 };
-
 template <int OP, int FMT>
-__global__ __launch_bounds__(256) void k_conv6s(const ConvParams p) {
+__global__ __launch_bounds__(256) void k_convs(const ConvParams p) {
   static_assert(Fmt<FMT>::BITS == 6, "FP6 element formats");
   constexpr int MT = 256, NT = 256, WM = 2, KB = 4;
   constexpr int WTM = 128, WTN = 128, RM = 4, RN = 4;
@@ -92,6 +102,7 @@ __global__ __launch_bounds__(256) void k_conv6s(const ConvParams p) {
   constexpr int NST = 3;
   static_assert(STAGE % 16 == 0, "16-byte aligned stages");
   __shared__ __attribute__((aligned(16))) uint8_t lds[NST * STAGE];
+  using Raw = Raw6;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -116,27 +127,28 @@ __global__ __launch_bounds__(256) void k_conv6s(const ConvParams p) {
   KWalk<OP, MT, NT, KB> walk;
   walk.init(p, t);
   uint32_t s_fetch = 0;  // k offset (s * KB) of the next fetch
-  auto fetch = [&](Raw6& g) {
+  auto fetch = [&](Raw& g) {
     uint32_t blk;
     const bool ok = walk.next(s_fetch, blk);
     g.load(my_codes, my_scales, blk, ok);
     s_fetch += KB;
   };
 
-  // decode of the staged block: scale, then group G (rows 4G .. 4G+3) into
-  // 16 words of fp16 pairs (row-major), then the mantissa factor.  A padding
-  // block (block 0's codes, scale code masked to 0) converts to finite
-  // values (FP6 has no NaN or Inf code) that mB = 0 turns into zeros.
-  float sc;
-  f16x2 m2;
+  // Decode of the staged block into dw: 4 rows (a group) of 4 words of fp16
+  // pairs, row-major.  A padding block (block 0's codes, scale code masked
+  // to 0) converts to finite values (FP6 has no NaN or Inf code) that
+  // mB = 0 turns into zeros.
+  float sc;  // scale operand of the conversions (only its exponent is used)
+  f16x2 m2;  // mantissa factor mB, twice
   uint32_t dw[16];
-  auto set_scale = [&](const Raw6& g) {
-    const BlockScale bs(g.scale_code());
+  auto set_scale = [&](const Raw& g) {
+    const BlockScale bs(g.s.code());
     sc = bs.b;
     const _Float16 m = static_cast<_Float16>(bs.mb);
     m2 = f16x2{m, m};
   };
-  auto convert = [&](const Raw6& g, int G) {
+  // group G (rows 4G .. 4G+3) in one conversion
+  auto convert_group = [&](const Raw& g, int G) {
     const auto v = [&] {
       if constexpr (FMT == FMT_E3M2) return __builtin_amdgcn_cvt_scalef32_pk32_f16_bf6(g.g[G], sc);
       else return __builtin_amdgcn_cvt_scalef32_pk32_f16_fp6(g.g[G], sc);
@@ -157,11 +169,24 @@ __global__ __launch_bounds__(256) void k_conv6s(const ConvParams p) {
     *reinterpret_cast<uint4*>(base + a + st_pitch) =
         make_uint4(dw[4 * r + 4], dw[4 * r + 5], dw[4 * r + 6], dw[4 * r + 7]);
   };
-  auto stage_block = [&](const Raw6& g, uint8_t* base) {
+  // Staging work of one step, as units K = 0 .. NSUB-1 placed after MFMA
+  // SUB0 + K.  The block's set is refilled (fetch) after the last unit that
+  // reads it.
+  constexpr int NSUB = 12, SUB0 = 8;
+  auto stage_sub = [&]<int K>(Raw& g, uint8_t* wr) {
+    if constexpr (K == 0) set_scale(g);
+    else if constexpr (K == 1 || K == 6) convert_group(g, K == 6);
+    else if constexpr (K == 2 || K == 8) scale_words(0);
+    else if constexpr (K == 3 || K == 9) scale_words(8);
+    else if constexpr (K == 4 || K == 10) write_rows(wr, K == 10, 0);
+    else if constexpr (K == 5 || K == 11) write_rows(wr, K == 11, 2);
+    else if constexpr (K == 7) fetch(g);
+  };
+  auto stage_block = [&](Raw& g, uint8_t* base) {
     set_scale(g);
 #pragma unroll
     for (int G = 0; G < 2; ++G) {
-      convert(g, G);
+      convert_group(g, G);
       scale_words(0);
       scale_words(8);
       write_rows(base, G, 0);
@@ -202,73 +227,40 @@ __global__ __launch_bounds__(256) void k_conv6s(const ConvParams p) {
   };
   f16x8 fa0[RM], fb0[RN], fa1[RM], fb1[RN];  // fragments of slice 0 and slice 1
 
-  // One column j of a slice: MFMA i is followed by work unit i, each closed
-  // by a scheduling barrier (a wave hides only a few VALU operations and
-  // LDS accesses behind each MFMA).
-  auto column = [&](const f16x8 (&fa)[RM], const f16x8& fb, int j, auto&& u0, auto&& u1, auto&& u2, auto&& u3) {
-    acc[0][j] = mfma32<true>(reinterpret_cast<const uint16_t*>(&fa[0]), reinterpret_cast<const uint16_t*>(&fb), acc[0][j]);
-    u0();
-    __builtin_amdgcn_sched_barrier(0);
-    acc[1][j] = mfma32<true>(reinterpret_cast<const uint16_t*>(&fa[1]), reinterpret_cast<const uint16_t*>(&fb), acc[1][j]);
-    u1();
-    __builtin_amdgcn_sched_barrier(0);
-    acc[2][j] = mfma32<true>(reinterpret_cast<const uint16_t*>(&fa[2]), reinterpret_cast<const uint16_t*>(&fb), acc[2][j]);
-    u2();
-    __builtin_amdgcn_sched_barrier(0);
-    acc[3][j] = mfma32<true>(reinterpret_cast<const uint16_t*>(&fa[3]), reinterpret_cast<const uint16_t*>(&fb), acc[3][j]);
-    u3();
+  // Step s on the stage at cur (its slice-0 fragments in fa0/fb0): MFMA M
+  // (slice M / 16, column (M % 16) / 4, row M % 4) is followed by its work
+  // and a scheduling barrier (a wave hides only a few VALU operations and
+  // LDS accesses behind each MFMA): after MFMAs 0-7 the slice-1 fragments
+  // of cur, after 20-27 the slice-0 fragments of the next stage (nxt,
+  // complete since the previous step's barrier), and the staging units of
+  // the block in G (step s+2) into the stage at wr, which refill G with the
+  // block of step s+4.  One barrier, at the end: wr complete, cur free.
+  auto slot = [&]<int M>(Raw& G, const uint8_t* cur, const uint8_t* nxt, uint8_t* wr) {
+    constexpr int i = M % 4, j = (M % 16) / 4;
+    if constexpr (M < 16)
+      acc[i][j] = mfma32<true>(reinterpret_cast<const uint16_t*>(&fa0[i]), reinterpret_cast<const uint16_t*>(&fb0[j]), acc[i][j]);
+    else
+      acc[i][j] = mfma32<true>(reinterpret_cast<const uint16_t*>(&fa1[i]), reinterpret_cast<const uint16_t*>(&fb1[j]), acc[i][j]);
+    if constexpr (M < 8) {
+      if constexpr (M % 2 == 0) fa1[M / 2] = frag_a(cur, 1, M / 2);
+      else fb1[M / 2] = frag_b(cur, 1, M / 2);
+    } else if constexpr (M >= 20 && M < 28) {
+      if constexpr (M % 2 == 0) fa0[(M - 20) / 2] = frag_a(nxt, 0, (M - 20) / 2);
+      else fb0[(M - 20) / 2] = frag_b(nxt, 0, (M - 20) / 2);
+    }
+    if constexpr (M >= SUB0 && M < SUB0 + NSUB) stage_sub.template operator()<M - SUB0>(G, wr);
+    if constexpr (M == 31) __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
   };
-  auto none = [] {};
-
-  // Step s on the stage at cur (its slice-0 fragments in fa0/fb0): slice 0
-  // reads the slice-1 fragments; the block in G (step s+2) is decoded and
-  // written into the stage at wr across both slices, and G is refilled with
-  // the block of step s+4; slice 1 reads the slice-0 fragments of the next
-  // stage (nxt, complete since the previous step's barrier).  One barrier,
-  // at the end: wr complete, cur free.
-  auto step = [&](Raw6& G, const uint8_t* cur, const uint8_t* nxt, uint8_t* wr) {
-    column(fa0, fb0[0], 0,
-           [&] { fa1[0] = frag_a(cur, 1, 0); },
-           [&] { fb1[0] = frag_b(cur, 1, 0); },
-           [&] { fa1[1] = frag_a(cur, 1, 1); },
-           [&] { fb1[1] = frag_b(cur, 1, 1); });
-    column(fa0, fb0[1], 1,
-           [&] { fa1[2] = frag_a(cur, 1, 2); },
-           [&] { fb1[2] = frag_b(cur, 1, 2); },
-           [&] { fa1[3] = frag_a(cur, 1, 3); },
-           [&] { fb1[3] = frag_b(cur, 1, 3); });
-    column(fa0, fb0[2], 2,
-           [&] { set_scale(G); },
-           [&] { convert(G, 0); },
-           [&] { scale_words(0); },
-           [&] { scale_words(8); });
-    column(fa0, fb0[3], 3,
-           [&] { write_rows(wr, 0, 0); },
-           [&] { write_rows(wr, 0, 2); },
-           [&] { convert(G, 1); },
-           [&] { scale_words(0); });
-    column(fa1, fb1[0], 0,
-           [&] { scale_words(8); },
-           [&] { write_rows(wr, 1, 0); },
-           [&] { write_rows(wr, 1, 2); },
-           [&] { fetch(G); });
-    column(fa1, fb1[1], 1,
-           [&] { fa0[0] = frag_a(nxt, 0, 0); },
-           [&] { fb0[0] = frag_b(nxt, 0, 0); },
-           [&] { fa0[1] = frag_a(nxt, 0, 1); },
-           [&] { fb0[1] = frag_b(nxt, 0, 1); });
-    column(fa1, fb1[2], 2,
-           [&] { fa0[2] = frag_a(nxt, 0, 2); },
-           [&] { fb0[2] = frag_b(nxt, 0, 2); },
-           [&] { fa0[3] = frag_a(nxt, 0, 3); },
-           [&] { fb0[3] = frag_b(nxt, 0, 3); });
-    column(fa1, fb1[3], 3, none, none, none, [&] { __syncthreads(); });
+  auto step = [&](Raw& G, const uint8_t* cur, const uint8_t* nxt, uint8_t* wr) {
+    [&]<int... M>(std::integer_sequence<int, M...>) {
+      (slot.template operator()<M>(G, cur, nxt, wr), ...);
+    }(std::make_integer_sequence<int, 32>());
   };
 
   const int nsteps = (t.kb_end - t.kb_begin + KB - 1) / KB;
   if (nsteps > 0) {
-    Raw6 g0, g1;  // blocks of even and odd steps
+    Raw g0, g1;  // blocks of even and odd steps
     fetch(g0);
     fetch(g1);
     stage_block(g0, lds);
@@ -293,6 +285,15 @@ __global__ __launch_bounds__(256) void k_conv6s(const ConvParams p) {
   store_tile<OP, MT, NT, KB, WTM, WTN, RM, RN>(p, t, acc, lane, wm, wn);
 }
 
+template <int FMT>
+void launch_fmt_staged(int op, const ConvParams& p, dim3 grid, hipStream_t s) {
+  switch (op) {
+    case OP_FWD: hipLaunchKernelGGL((k_convs<OP_FWD, FMT>), grid, dim3(256), 0, s, p); break;
+    case OP_DGRAD: hipLaunchKernelGGL((k_convs<OP_DGRAD, FMT>), grid, dim3(256), 0, s, p); break;
+    default: hipLaunchKernelGGL((k_convs<OP_WGRAD, FMT>), grid, dim3(256), 0, s, p); break;
+  }
+}
+
 }  // namespace
 
 namespace gemm {
@@ -300,24 +301,13 @@ namespace gemm {
 // The 256x256 FP6 kernel; false (nothing launched) for another format or
 // where its K walk needs the division-based block search (an innermost K
 // extent below 4 k-blocks).
-bool launch_conv6(int op, int fmt, const ConvParams& p, dim3 grid, hipStream_t s) {
-  if (!kwalk_ok(op, p, 4) || (fmt != FMT_E2M3 && fmt != FMT_E3M2)) return false;
-  const bool e3 = fmt == FMT_E3M2;
-  switch (op) {
-    case OP_FWD:
-      if (e3) hipLaunchKernelGGL((k_conv6s<OP_FWD, FMT_E3M2>), grid, dim3(256), 0, s, p);
-      else hipLaunchKernelGGL((k_conv6s<OP_FWD, FMT_E2M3>), grid, dim3(256), 0, s, p);
-      break;
-    case OP_DGRAD:
-      if (e3) hipLaunchKernelGGL((k_conv6s<OP_DGRAD, FMT_E3M2>), grid, dim3(256), 0, s, p);
-      else hipLaunchKernelGGL((k_conv6s<OP_DGRAD, FMT_E2M3>), grid, dim3(256), 0, s, p);
-      break;
-    default:
-      if (e3) hipLaunchKernelGGL((k_conv6s<OP_WGRAD, FMT_E3M2>), grid, dim3(256), 0, s, p);
-      else hipLaunchKernelGGL((k_conv6s<OP_WGRAD, FMT_E2M3>), grid, dim3(256), 0, s, p);
-      break;
+bool launch_staged(int op, int fmt, const ConvParams& p, dim3 grid, hipStream_t s) {
+  if (!kwalk_ok(op, p, 4)) return false;
+  switch (fmt) {
+    case FMT_E2M3: launch_fmt_staged<FMT_E2M3>(op, p, grid, s); return true;
+    case FMT_E3M2: launch_fmt_staged<FMT_E3M2>(op, p, grid, s); return true;
+    default: return false;
   }
-  return true;
 }
 
 }  // namespace gemm
