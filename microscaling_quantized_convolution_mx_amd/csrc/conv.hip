@@ -628,7 +628,7 @@ void launch_fmt(const ConvParams& p, const Tile& t, dim3 grid, hipStream_t s) {
     if (t.mt == 256 && t.nt == 256 && launch_conv8(OP, p, grid, s)) return;
   } else if constexpr (FMT == FMT_E2M3) {
     // E2M3 on the 256x256 tile: fetched two K steps ahead, fp16 in LDS
-    if (t.mt == 256 && t.nt == 256 && launch_staged(OP, FMT_E2M3, p, grid, s)) return;
+    if (t.mt == 256 && t.nt == 256 && launch_staged(OP, FMT_E2M3, FMT_E2M3, p, grid, s)) return;
   }
   launch_generic<OP, FMT, FMT>(p, t, grid, s);
 }

@@ -80,11 +80,12 @@ bool launch_mixed(int op, const ConvParams& p, int fmt_a, int fmt_b, const Tile&
 // (nothing launched) where its K walk does not apply.
 bool launch_conv8(int op, const ConvParams& p, dim3 grid, hipStream_t s);
 
-// Launches the 256x256 FP6 (E2M3 or E3M2, both operands) GEMM that fetches
+// Launches the 256x256 GEMM of FP6 activations (E2M3 or E3M2 throughout, or
+// E2M1 A with FP6 B in the forward and weight-gradient GEMMs) that fetches
 // every block two K steps ahead and decodes it once into fp16 in LDS
 // (defined in conv_staged.hip).  Returns false (nothing launched) for another
-// format or where its K walk does not apply.
-bool launch_staged(int op, int fmt, const ConvParams& p, dim3 grid, hipStream_t s);
+// format pair or where its K walk does not apply.
+bool launch_staged(int op, int fmt_a, int fmt_b, const ConvParams& p, dim3 grid, hipStream_t s);
 
 // Launches the E8M0 32x32-block GEMM on the scaled FP4 MFMA (defined in
 // conv_mx.hip): tile x tile outputs per workgroup (tile 256 or 128), the

@@ -6,15 +6,17 @@
 //     weight-gradient (dY x X'^T) GEMMs; the data gradient (W^T x dY) has no
 //     activation operand and runs all-E2M1.
 // Both FP6 formats and E2M1 decode exactly to fp16, so a mixed pair shares
-// the fp16 MFMA.
+// the fp16 MFMA.  On the 256x256 tile these pairs run on the kernel of FP6
+// activations in conv_staged.hip.
 #include "conv_kernels.h"
 
 namespace mx {
 namespace gemm {
 
 bool launch_mixed(int op, const ConvParams& p, int fmt_a, int fmt_b, const Tile& t, dim3 grid, hipStream_t s) {
+  // the 256x256 tile: FP6 activations on the kernel that decodes at staging
+  if (t.mt == 256 && t.nt == 256 && launch_staged(op, fmt_a, fmt_b, p, grid, s)) return true;
   if (fmt_a == FMT_E3M2 && fmt_b == FMT_E3M2) {
-    if (t.mt == 256 && t.nt == 256 && launch_staged(op, FMT_E3M2, p, grid, s)) return true;
     switch (op) {
       case OP_FWD: launch_generic<OP_FWD, FMT_E3M2, FMT_E3M2>(p, t, grid, s); return true;
       case OP_DGRAD: launch_generic<OP_DGRAD, FMT_E3M2, FMT_E3M2>(p, t, grid, s); return true;

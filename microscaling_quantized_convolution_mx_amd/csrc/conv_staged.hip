@@ -1,14 +1,15 @@
-// Convolution GEMMs for the FP6 element formats (E2M3, E3M2) on the 256x256
-// tile, every block decoded once, at staging, into exact fp16 values in LDS
-// (MicroQonv, arXiv 2609.28358, §IV-B; the FP6 elements of §IV-E and
-// MicroQonv+ in §VI-B).
+// Convolution GEMMs with FP6 activations on the 256x256 tile, every block
+// decoded once, at staging, into exact fp16 values in LDS (MicroQonv, arXiv
+// 2609.28358, §IV-B): an FP6 element format (E2M3, E3M2) throughout (the FP6
+// elements of §IV-E), or MicroQonv+'s pair of §IV-D / Table VI, E2M1 weights
+// and gradients with FP6 activations (the forward and weight-gradient GEMMs).
 //
-// The thread that stages a block decodes it into g * B (two 32-value FP6
-// conversions, which apply the exponent of B, and packed multiplies by its
-// mantissa factor mB; see BlockScale), and the MFMA fragments are read from
-// LDS as they are.  Both steps are exact (g * B has at most 8 significant
-// bits and lies in [2^-13, 12544]), so the fp16 MFMA sums the exact products
-// of Eq. 7.
+// The thread that stages a block decodes it into g * B (FP6: two 32-value
+// conversions, which apply the exponent of B; E2M1: 32 two-value
+// conversions; then packed multiplies by the mantissa factor mB, see
+// BlockScale), and the MFMA fragments are read from LDS as they are.  Both
+// steps are exact (g * B has at most 8 significant bits and lies in
+// [2^-13, 12544]), so the fp16 MFMA sums the exact products of Eq. 7.
 //
 // What differs from the generic kernel (conv_kernels.h), which decodes the
 // same way: the A- and B-staging waves run one instruction stream (staging
@@ -64,30 +65,43 @@ struct RawScale {
   __device__ __forceinline__ uint32_t code() const { return __builtin_amdgcn_ubfe(sword, sbit, 8) & mask; }
 };
 
-// Raw FP6 block between its global load and its decode: two 6-word groups,
-// each loaded by one vector load straight into the register tuple that the
-// 32-value conversion reads.  The address of group 1 passes through an empty
-// asm statement, so that the compiler cannot merge the loads into 16-byte
-// pieces that straddle the groups (the register copies that would then build
-// the tuples wait for the newest loads).
+// Raw block between its global load and its decode: two 6-word groups.  An
+// FP6 block (48 bytes) fills both, each loaded by one vector load straight
+// into the register tuple that the 32-value conversion reads; the address of
+// group 1 passes through an empty asm statement, so that the compiler cannot
+// merge the loads into 16-byte pieces that straddle the groups (the register
+// copies that would then build the tuples wait for the newest loads).  An
+// E2M1 block (32 bytes) fills group 0 and the first two words of group 1.
 struct Raw6 {
   u32x6 g[2];
   RawScale s;
+  template <bool FP6>
   __device__ __forceinline__ void load(const uint8_t* codes, const uint8_t* scales, uint32_t blk, bool ok) {
     typedef unsigned int u32x6a __attribute__((ext_vector_type(6), aligned(8)));
+    typedef unsigned int u32x2a __attribute__((ext_vector_type(2), aligned(8)));
     typedef __attribute__((address_space(1))) const u32x6a gu32x6a;  // global memory
+    typedef __attribute__((address_space(1))) const u32x2a gu32x2a;
     const uint64_t b = ok ? blk : 0u;
-    const uint64_t a0 = reinterpret_cast<uint64_t>(codes) + b * 48;
+    const uint64_t a0 = reinterpret_cast<uint64_t>(codes) + b * (FP6 ? 48 : 32);
     uint64_t a1 = a0 + 24;
     asm volatile("" : "+v"(a1));
     g[0] = *reinterpret_cast<gu32x6a*>(a0);
-    g[1] = *reinterpret_cast<gu32x6a*>(a1);
+    if constexpr (FP6) {
+      g[1] = *reinterpret_cast<gu32x6a*>(a1);
+    } else {
+      const u32x2a t = *reinterpret_cast<gu32x2a*>(a1);
+      g[1] = u32x6{t.x, t.y, 0u, 0u, 0u, 0u};
+    }
     s.load(scales, b, ok);
   }
+  __device__ __forceinline__ uint32_t word(int i) const { return i < 6 ? g[0][i] : g[1][i - 6]; }
 };
-template <int OP, int FMT>
+// FMTA: element format of the A operand (FP6, or E2M1 in MicroQonv+'s pair);
+// FMTB: that of B, FP6.
+template <int OP, int FMTA, int FMTB>
 __global__ __launch_bounds__(256) void k_convs(const ConvParams p) {
-  static_assert(Fmt<FMT>::BITS == 6, "FP6 element formats");
+  static_assert(Fmt<FMTB>::BITS == 6 && (FMTA == FMTB || FMTA == FMT_E2M1), "FP6 activations");
+  constexpr bool MIXED = FMTA != FMTB;
   constexpr int MT = 256, NT = 256, WM = 2, KB = 4;
   constexpr int WTM = 128, WTN = 128, RM = 4, RN = 4;
   constexpr bool A_ROWS = (OP != OP_DGRAD);
@@ -130,7 +144,8 @@ __global__ __launch_bounds__(256) void k_convs(const ConvParams p) {
   auto fetch = [&](Raw& g) {
     uint32_t blk;
     const bool ok = walk.next(s_fetch, blk);
-    g.load(my_codes, my_scales, blk, ok);
+    if (MIXED && is_a) g.template load<false>(my_codes, my_scales, blk, ok);
+    else g.template load<true>(my_codes, my_scales, blk, ok);
     s_fetch += KB;
   };
 
@@ -147,16 +162,29 @@ __global__ __launch_bounds__(256) void k_convs(const ConvParams p) {
     const _Float16 m = static_cast<_Float16>(bs.mb);
     m2 = f16x2{m, m};
   };
-  // group G (rows 4G .. 4G+3) in one conversion
+  // FP6 group G (rows 4G .. 4G+3) in one conversion
   auto convert_group = [&](const Raw& g, int G) {
     const auto v = [&] {
-      if constexpr (FMT == FMT_E3M2) return __builtin_amdgcn_cvt_scalef32_pk32_f16_bf6(g.g[G], sc);
+      if constexpr (FMTB == FMT_E3M2) return __builtin_amdgcn_cvt_scalef32_pk32_f16_bf6(g.g[G], sc);
       else return __builtin_amdgcn_cvt_scalef32_pk32_f16_fp6(g.g[G], sc);
     }();
     struct Words { uint32_t u[16]; };
     const Words wv = __builtin_bit_cast(Words, v);
 #pragma unroll
     for (int k = 0; k < 16; ++k) dw[k] = wv.u[k];
+  };
+  // E2M1 row r (into dw row r % 4), two values per conversion
+  auto convert_row = [&](const Raw& g, int r) {
+    const uint32_t w = g.word(r);
+    const f16x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc, 0);
+    const f16x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc, 1);
+    const f16x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc, 2);
+    const f16x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc, 3);
+    const int q = 4 * (r & 3);
+    dw[q] = __builtin_bit_cast(uint32_t, v0);
+    dw[q + 1] = __builtin_bit_cast(uint32_t, v1);
+    dw[q + 2] = __builtin_bit_cast(uint32_t, v2);
+    dw[q + 3] = __builtin_bit_cast(uint32_t, v3);
   };
   auto scale_words = [&](int k0) {
 #pragma unroll
@@ -169,11 +197,12 @@ __global__ __launch_bounds__(256) void k_convs(const ConvParams p) {
     *reinterpret_cast<uint4*>(base + a + st_pitch) =
         make_uint4(dw[4 * r + 4], dw[4 * r + 5], dw[4 * r + 6], dw[4 * r + 7]);
   };
-  // Staging work of one step, as units K = 0 .. NSUB-1 placed after MFMA
-  // SUB0 + K.  The block's set is refilled (fetch) after the last unit that
-  // reads it.
-  constexpr int NSUB = 12, SUB0 = 8;
-  auto stage_sub = [&]<int K>(Raw& g, uint8_t* wr) {
+  // Staging work of one step, as units placed after MFMAs: FP6 units K =
+  // 0..11 after MFMA 8 + K, E2M1 units K = 0..17 after MFMA K.  The block's
+  // set is refilled (fetch) after the last unit that reads it (both after
+  // MFMA 15).  In MicroQonv+'s pair the A-staging waves run the E2M1 units
+  // and the B-staging waves the FP6 units (a wave-uniform branch per slot).
+  auto stage_fp6 = [&]<int K>(Raw& g, uint8_t* wr) {
     if constexpr (K == 0) set_scale(g);
     else if constexpr (K == 1 || K == 6) convert_group(g, K == 6);
     else if constexpr (K == 2 || K == 8) scale_words(0);
@@ -182,11 +211,41 @@ __global__ __launch_bounds__(256) void k_convs(const ConvParams p) {
     else if constexpr (K == 5 || K == 11) write_rows(wr, K == 11, 2);
     else if constexpr (K == 7) fetch(g);
   };
+  // rows 2P, 2P+1 in units 1 + 4P .. 4 + 4P (the last pair: 13, 14, then
+  // the refill, 16, 17)
+  auto stage_e2m1 = [&]<int K>(Raw& g, uint8_t* wr) {
+    if constexpr (K == 0) set_scale(g);
+    else if constexpr (K == 15) fetch(g);
+    else {
+      constexpr int P = K < 15 ? (K - 1) / 4 : 3, U = K < 15 ? (K - 1) % 4 : K - 14;
+      if constexpr (U == 0 || U == 1) convert_row(g, 2 * P + U);
+      else if constexpr (U == 2) scale_words(8 * (P & 1));
+      else write_rows(wr, P >> 1, 2 * (P & 1));
+    }
+  };
+  auto stage_slot = [&]<int M>(Raw& g, uint8_t* wr) {
+    constexpr bool F = M >= 8 && M < 20, E = M < 18;
+    if constexpr (!MIXED) {
+      if constexpr (F) stage_fp6.template operator()<M - 8>(g, wr);
+    } else if constexpr (F && E) {
+      if (is_a) stage_e2m1.template operator()<M>(g, wr);
+      else stage_fp6.template operator()<M - 8>(g, wr);
+    } else if constexpr (E) {
+      if (is_a) stage_e2m1.template operator()<M>(g, wr);
+    } else if constexpr (F) {
+      if (!is_a) stage_fp6.template operator()<M - 8>(g, wr);
+    }
+  };
   auto stage_block = [&](Raw& g, uint8_t* base) {
     set_scale(g);
 #pragma unroll
     for (int G = 0; G < 2; ++G) {
-      convert_group(g, G);
+      if (MIXED && is_a) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) convert_row(g, 4 * G + r);
+      } else {
+        convert_group(g, G);
+      }
       scale_words(0);
       scale_words(8);
       write_rows(base, G, 0);
@@ -248,7 +307,7 @@ __global__ __launch_bounds__(256) void k_convs(const ConvParams p) {
       if constexpr (M % 2 == 0) fa0[(M - 20) / 2] = frag_a(nxt, 0, (M - 20) / 2);
       else fb0[(M - 20) / 2] = frag_b(nxt, 0, (M - 20) / 2);
     }
-    if constexpr (M >= SUB0 && M < SUB0 + NSUB) stage_sub.template operator()<M - SUB0>(G, wr);
+    stage_slot.template operator()<M>(G, wr);
     if constexpr (M == 31) __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -285,12 +344,14 @@ __global__ __launch_bounds__(256) void k_convs(const ConvParams p) {
   store_tile<OP, MT, NT, KB, WTM, WTN, RM, RN>(p, t, acc, lane, wm, wn);
 }
 
-template <int FMT>
+template <int FMTA, int FMTB>
 void launch_fmt_staged(int op, const ConvParams& p, dim3 grid, hipStream_t s) {
   switch (op) {
-    case OP_FWD: hipLaunchKernelGGL((k_convs<OP_FWD, FMT>), grid, dim3(256), 0, s, p); break;
-    case OP_DGRAD: hipLaunchKernelGGL((k_convs<OP_DGRAD, FMT>), grid, dim3(256), 0, s, p); break;
-    default: hipLaunchKernelGGL((k_convs<OP_WGRAD, FMT>), grid, dim3(256), 0, s, p); break;
+    case OP_FWD: hipLaunchKernelGGL((k_convs<OP_FWD, FMTA, FMTB>), grid, dim3(256), 0, s, p); break;
+    case OP_DGRAD:
+      if constexpr (FMTA == FMTB) hipLaunchKernelGGL((k_convs<OP_DGRAD, FMTA, FMTB>), grid, dim3(256), 0, s, p);
+      break;
+    default: hipLaunchKernelGGL((k_convs<OP_WGRAD, FMTA, FMTB>), grid, dim3(256), 0, s, p); break;
   }
 }
 
@@ -298,16 +359,23 @@ void launch_fmt_staged(int op, const ConvParams& p, dim3 grid, hipStream_t s) {
 
 namespace gemm {
 
-// The 256x256 FP6 kernel; false (nothing launched) for another format or
-// where its K walk needs the division-based block search (an innermost K
-// extent below 4 k-blocks).
-bool launch_staged(int op, int fmt, const ConvParams& p, dim3 grid, hipStream_t s) {
+// The 256x256 kernel of FP6 activations; false (nothing launched) for a
+// format pair it does not take (FP6 throughout; E2M1 with FP6 activations in
+// the forward and weight-gradient GEMMs) or where its K walk needs the
+// division-based block search (an innermost K extent below 4 k-blocks).
+bool launch_staged(int op, int fmt_a, int fmt_b, const ConvParams& p, dim3 grid, hipStream_t s) {
   if (!kwalk_ok(op, p, 4)) return false;
-  switch (fmt) {
-    case FMT_E2M3: launch_fmt_staged<FMT_E2M3>(op, p, grid, s); return true;
-    case FMT_E3M2: launch_fmt_staged<FMT_E3M2>(op, p, grid, s); return true;
-    default: return false;
+  if (fmt_a == fmt_b) {
+    if (fmt_a == FMT_E2M3) launch_fmt_staged<FMT_E2M3, FMT_E2M3>(op, p, grid, s);
+    else if (fmt_a == FMT_E3M2) launch_fmt_staged<FMT_E3M2, FMT_E3M2>(op, p, grid, s);
+    else return false;
+    return true;
   }
+  if (fmt_a != FMT_E2M1 || op == OP_DGRAD) return false;
+  if (fmt_b == FMT_E3M2) launch_fmt_staged<FMT_E2M1, FMT_E3M2>(op, p, grid, s);
+  else if (fmt_b == FMT_E2M3) launch_fmt_staged<FMT_E2M1, FMT_E2M3>(op, p, grid, s);
+  else return false;
+  return true;
 }
 
 }  // namespace gemm
