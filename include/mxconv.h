@@ -38,8 +38,9 @@
  *   sign is the top bit of each code.  scales: one E4M3 byte per block, in
  *   block order; the buffer continues, from the next multiple of 16 bytes,
  *   with 2 KiB that mx_quantize_cbf uses as scratch for its amax reduction
- *   (mx_scale_bytes() counts both).  tensor_scale: one fp32.  amax: one
- *   fp32, max |x|.
+ *   (mx_scale_bytes() counts both; the GEMMs may read the scales as aligned
+ *   4-byte words, which stay below that multiple of 16).  tensor_scale: one
+ *   fp32.  amax: one fp32, max |x|.
  * - C_in, C_out and N must be multiples of 8 (zero-pad otherwise: padding
  *   changes neither the amax nor any result) and block must be 8.  N may be 0.
  * - block = 32 selects the original microscaling format instead (§II-D: a
