@@ -227,3 +227,42 @@ def test_e4m3_block_scales_in_the_subnormal_range():
         ref, s = fn(cv, we, e, idx)
         assert np.all(s[np.isin(idx, small)] > 0)
         assert_close(got.view(-1)[torch.from_numpy(idx).to(DEV)].cpu().numpy(), ref, s, name)
+
+
+# The 256x256 kernel of FP6 activations with ragged edges: 264 rows (a
+# second row tile of 8), 122,400 columns (a last column tile of 32), 9 K
+# steps (an odd count) across the taps and the zero padding.  fwd on the
+# first shape (C_out = 264), dgrad on the second (C_in = 264); outputs
+# sampled, as in the full-size checks (the oracle evaluates them one by one).
+FP6_TILE_SHAPES = [((136, 32, 264, 30, 30, 3, 3, 1, 1, 1, 1), "fwd"),
+                   ((136, 264, 32, 30, 30, 3, 3, 1, 1, 1, 1), "dgrad")]
+
+
+@pytest.mark.parametrize("fmts", [(mx.MX_E2M3, 0), (mx.MX_E3M2, 0), (mx.MX_E2M1, mx.MX_E3M2), (mx.MX_E2M1, mx.MX_E2M3)],
+                         ids=["e2m3", "e3m2", "w4-x6e3m2", "w4-x6e2m3"])
+@pytest.mark.parametrize("shape,op", FP6_TILE_SHAPES, ids=["fwd", "dgrad"])
+def test_fp6_tile_ragged_edges(fmts, shape, op):
+    fmt, act_fmt = fmts
+    if act_fmt and op == "dgrad":
+        pytest.skip("the data gradient has no activation operand (all-E2M1)")
+    say("fp6 tile ragged", fmt, act_fmt, shape, op)
+    lay, x, w, dy = layer_inputs(shape, 700 + FP6_TILE_SHAPES.index((shape, op)))
+    d = mx.desc_from_layer(lay, fmt, act_fmt)
+    (qx, qw, qdy), (y, dx, _) = run_layer(d, x, w, dy, seed_sr=11, ops=(op,))
+    ow = oracle_quantize(d, mx.MX_ROLE_WEIGHT, w)
+    cv = oracle_conv(d)
+    rng = np.random.default_rng(710 + FP6_TILE_SHAPES.index((shape, op)))
+    if op == "fwd":
+        got, other, fn = y, oracle_quantize(d, mx.MX_ROLE_ACT, x), O.conv_fwd_points
+    else:
+        got, other, fn = dx, oracle_quantize(d, mx.MX_ROLE_GRAD, dy, mx.MX_SR, 11), O.conv_dgrad_points
+    # outputs [position][row][n]: samples in the ragged row tile (rows 256..263),
+    # in the last position (its columns include the ragged column tile's 32),
+    # and anywhere
+    n, rows = got.numel(), (d.c_out if op == "fwd" else d.c_in)
+    npos = n // (rows * d.n)
+    edge = (rng.integers(0, npos, 4096) * rows + rng.integers(256, rows, 4096)) * d.n + rng.integers(0, d.n, 4096)
+    tail = rng.integers(n - rows * d.n, n, 4096)
+    idx = np.unique(np.concatenate([edge, tail, rng.integers(0, n, 16384), [n - 1]])).astype(np.int64)
+    ref, s = fn(cv, ow.exact(), other.exact(), idx)
+    assert_close(got.view(-1)[torch.from_numpy(idx).to(DEV)].cpu().numpy(), ref, s, op)
