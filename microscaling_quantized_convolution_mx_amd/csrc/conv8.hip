@@ -140,7 +140,7 @@ __global__ __launch_bounds__(256) void k_conv8w(const ConvParams p) {
   auto lookup_scale = [&](const RawBlock<FMT_E4M3>& g) {
     sws = *reinterpret_cast<const uint32_t*>(lds + LUT + ((g.scale & g.mask) << 2));
   };
-  // rows r0 .. r0+3 of the staged block into stage `base`.  A padding block
+  // rows r0, r0+1 of the staged block into stage `base`.  A padding block
   // carries the codes of block 0 with a zero scale word: its codes are
   // finite (a quantized tensor holds no NaN code), so it decodes to zeros.
   auto write_rows = [&](const RawBlock<FMT_E4M3>& g, uint8_t* base, int r0) {

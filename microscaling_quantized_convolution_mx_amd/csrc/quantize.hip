@@ -327,13 +327,15 @@ __global__ __launch_bounds__(ONE ? kOneThreads : kThreads) void k_quantize(const
     const bool dd_ok = (dd >= 0x1p-125f) & (dd <= 0x1p125f);
     const float thr = fmaxf(0x1p-100f, dd * 0x1p-98f);
     float v[8];
-    bool any_slow = false;
+    // a tiny nonzero element, 0 < |x| < thr: 2 bits(|x|) - 1 below
+    // 2 bits(thr) - 1 as unsigned (a zero wraps to the maximum)
+    uint32_t mn = ~0u;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float ax = fabsf(cur.x[j]);
-      v[j] = div_by_recip(ax, dd, y);
-      any_slow |= (ax != 0.0f) & (ax < thr);
+      v[j] = div_by_recip(fabsf(cur.x[j]), dd, y);
+      mn = min(mn, (__float_as_uint(cur.x[j]) << 1) - 1u);
     }
+    bool any_slow = mn < (__float_as_uint(thr) << 1) - 1u;
     any_slow = (any_slow | !dd_ok) & (dd != 0.0f);
     if (any_slow) {  // rare: tiny elements or an extreme block scale
 #pragma unroll
@@ -495,13 +497,17 @@ __global__ __launch_bounds__(kThreads) void k_quantize_wide(const float* __restr
         xs[4 * r] = cur.x[r].x; xs[4 * r + 1] = cur.x[r].y;
         xs[4 * r + 2] = cur.x[r].z; xs[4 * r + 3] = cur.x[r].w;
       }
-      bool any_slow = false;
+      // a tiny nonzero element, 0 < |x| < thr: 2 bits(|x|) - 1 below
+      // 2 bits(thr) - 1 as unsigned (a zero wraps to the maximum), tested
+      // on the minimum over the lane's elements (vector operations only)
+      uint32_t mn = ~0u;
 #pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        const float ax = fabsf(xs[j]);
-        v[j] = div_by_recip(ax, dd, y);
-        any_slow |= (ax != 0.0f) & (ax < thr);
+      for (int j = 0; j < 32; j += 2) {
+        v[j] = div_by_recip(fabsf(xs[j]), dd, y);
+        v[j + 1] = div_by_recip(fabsf(xs[j + 1]), dd, y);
+        mn = min(mn, min((__float_as_uint(xs[j]) << 1) - 1u, (__float_as_uint(xs[j + 1]) << 1) - 1u));
       }
+      bool any_slow = mn < (__float_as_uint(thr) << 1) - 1u;
       any_slow = (any_slow | !dd_ok) & (dd != 0.0f);
       if (any_slow) {  // rare: tiny elements or an extreme block scale
 #pragma unroll
