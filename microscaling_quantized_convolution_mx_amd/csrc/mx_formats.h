@@ -73,25 +73,34 @@ __device__ __forceinline__ uint32_t rne_code(float v) {
   return v < F::MAXV ? c : static_cast<uint32_t>(F::MAXCODE);
 }
 
-// Stochastic rounding of v >= 0 (v may be +inf) with the uniform u24 / 2^24:
-// with lo <= v < hi the neighbouring grid points, round up iff
-// u24 / 2^24 < (v - lo) / (hi - lo).  The grid step at v is 2^(e - MB) for v
-// in the normal binade [2^e, 2^(e+1)) and the subnormal step 2^(1-BIAS-MB)
-// below the smallest normal; q = v / step is an exact power-of-two rescale,
-// lo is its integer part and the fraction of q is (v - lo) / (hi - lo), so
-// the comparison u24 < frac(q) * 2^24 is exact.  Codes are
-// lo + (binade above the smallest) << MB: a round-up past the largest
-// mantissa carries into the next binade.  Branch-free like rne_code.
+// Stochastic rounding of v >= +0 (v may be +inf) with the uniform u / 2^24
+// (u a 24-bit integer), passed as its complement ub = 2^24 - 1 - u: with
+// lo <= v < hi the neighbouring grid points, round up iff
+// u / 2^24 < (v - lo) / (hi - lo).  v is clamped to the format maximum
+// first.  The grid step at v is 2^(e - MB) in the normal binade
+// [2^e, 2^(e+1)) and the subnormal step 2^(1-BIAS-MB) below the smallest
+// normal, so Q = v / step * 2^24 is an exact power-of-two rescale of v,
+// below 2^(MB+25); lo / step is its integer part over 2^24 and the rule is
+// u < X with X = Q - (lo / step) 2^24 in [0, 2^24).  For an integer u,
+// u < X exactly when u < ceil(X), so with C = ceil(Q) = L 2^24 + F
+// (0 <= F < 2^24) the rounded index lo / step + up is L + (u < F): where
+// ceil(X) reaches 2^24 it has carried into L and F = 0.  u < F is the carry
+// of F + ub out of the low 24 bits, so the index is (C + ub) >> 24.  Codes
+// are that index plus (binade above the smallest) << MB: a round-up past the
+// largest mantissa carries into the next binade.  Branch-free.
 template <class F>
-__device__ __forceinline__ uint32_t sr_code(float v, uint32_t u24) {
+__device__ __forceinline__ uint32_t sr_code(float v, uint32_t ub) {
   constexpr int EMIN = 127 + 1 - F::BIAS;  // fp32 biased exponent of the smallest normal
-  const int eb = max(static_cast<int>(__builtin_amdgcn_ubfe(__float_as_uint(v), 23, 8)), EMIN);
-  const float q = __builtin_amdgcn_ldexpf(v, 127 + F::MB - eb);  // in [0, 2^(MB+1)) below +inf
-  const float fr = __builtin_amdgcn_fractf(q);
-  const uint32_t lo = static_cast<uint32_t>(q);
-  const uint32_t up = static_cast<float>(u24) < fr * 0x1p24f ? 1u : 0u;
-  const uint32_t c = lo + (static_cast<uint32_t>(eb - EMIN) << F::MB) + up;
-  return v < F::MAXV ? c : static_cast<uint32_t>(F::MAXCODE);
+  // v is +0 or positive (+inf and NaN lie above the maximum as bit
+  // patterns): the clamp is the unsigned minimum of the bit patterns
+  v = __uint_as_float(min(__float_as_uint(v), __float_as_uint(F::MAXV)));
+  const uint32_t e = __builtin_amdgcn_ubfe(__float_as_uint(v), 23, 8);
+  const uint32_t eb = e > static_cast<uint32_t>(EMIN) ? e - EMIN : 0u;  // binades above the smallest
+  const float q = __builtin_amdgcn_ldexpf(v, (151 + F::MB - EMIN) - static_cast<int>(eb));
+  // -ceil(Q) = floor(-Q) in one conversion (Q < 2^28: no saturation)
+  int m;
+  asm("v_cvt_flr_i32_f32 %0, -%1" : "=v"(m) : "v"(q));
+  return (eb << F::MB) + ((ub - static_cast<uint32_t>(m)) >> 24);
 }
 
 // Value of a magnitude code as fp32 (exact).
@@ -104,27 +113,29 @@ __device__ __forceinline__ float code_value(uint32_t mag) {
   return e ? normal : sub;
 }
 
-// SplitMix64 output function (Steele, Lea & Flood, OOPSLA 2014).  The
-// stochastic-rounding uniform of element idx takes 24 bits of the output for
-// counter idx / 2: bits 40..63 for an even idx, bits 16..39 for an odd one.
-__device__ __forceinline__ uint64_t splitmix64(uint64_t z) {
+// SplitMix64 output function (Steele, Lea & Flood, OOPSLA 2014), returned
+// complemented (~z for the output z).  The stochastic-rounding uniform of
+// element idx takes 24 bits of the output for counter idx / 2: bits 40..63
+// for an even idx, bits 16..39 for an odd one; the same bits of the
+// complement are 2^24 - 1 - u, the form sr_code takes.
+__device__ __forceinline__ uint64_t splitmix64_not(uint64_t z) {
   z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
   z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
-  return z ^ (z >> 31);
+  return ~(z ^ (z >> 31));
 }
 constexpr uint64_t kGolden64 = 0x9E3779B97F4A7C15ull;
-// the 24-bit uniforms of elements 2k, 2k+1 from gk = kGolden64 * (k + 1),
-// taken from the two 32-bit halves of the output (32-bit shifts only, so
-// that the conversions to float stay 32-bit)
-__device__ __forceinline__ void sr_bits_pair(uint64_t seed, uint64_t gk, uint32_t& u_even, uint32_t& u_odd) {
-  const uint64_t h = splitmix64(seed ^ gk);
+// the complemented 24-bit uniforms of elements 2k, 2k+1 from
+// gk = kGolden64 * (k + 1), taken from the two 32-bit halves of the output
+// (a shift and a byte gather)
+__device__ __forceinline__ void sr_ubar_pair(uint64_t seed, uint64_t gk, uint32_t& ub_even, uint32_t& ub_odd) {
+  const uint64_t h = splitmix64_not(seed ^ gk);
   const uint32_t hi = static_cast<uint32_t>(h >> 32), lo = static_cast<uint32_t>(h);
-  u_even = hi >> 8;
-  u_odd = __builtin_amdgcn_alignbit(hi, lo, 16) & 0xFFFFFFu;
+  ub_even = hi >> 8;
+  ub_odd = __builtin_amdgcn_perm(hi, lo, 0x0c040302u);  // bytes 2, 3 of lo and 0 of hi: bits 16..39
 }
-__device__ __forceinline__ uint32_t sr_bits(uint64_t seed, uint64_t idx) {
+__device__ __forceinline__ uint32_t sr_ubar(uint64_t seed, uint64_t idx) {
   uint32_t ue, uo;
-  sr_bits_pair(seed, kGolden64 * ((idx >> 1) + 1ull), ue, uo);
+  sr_ubar_pair(seed, kGolden64 * ((idx >> 1) + 1ull), ue, uo);
   return (idx & 1ull) ? uo : ue;
 }
 

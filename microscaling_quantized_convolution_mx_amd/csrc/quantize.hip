@@ -9,11 +9,14 @@
 // Two kernels per tensor, no atomics:
 //   k_amax_part       each workgroup writes the max |x| of its grid-stride
 //                     share as one 32-bit partial into a scratch tail behind
-//                     the block scales (the scales buffer is sized for it);
+//                     the block scales (the scales buffer is sized for it),
+//                     with a flag bit for magnitudes below 2^-64;
 //   k_quantize_wide   activations and gradients: every wave reduces the
-//                     partials to the tensor amax and T, then quantizes 32
-//                     blocks per iteration (the next 32 in flight), two lanes
-//                     per block, each row load of a wave 1 KiB contiguous;
+//                     partials to the tensor amax and T, each workgroup
+//                     tabulates dd = B T and RN(1 / dd) for the 127 block-scale
+//                     codes in LDS, then quantizes 32 blocks per iteration
+//                     (the next 32 in flight), two lanes per block, each row
+//                     load of a wave 1 KiB contiguous;
 //   k_quantize        weights (strided rows): the same arithmetic with one
 //                     lane per block row, 8 blocks per wave iteration.
 // Tensors of at most kOneBlocks blocks take k_quantize in a single
@@ -71,12 +74,23 @@ __device__ __forceinline__ uint32_t max4(uint4 v) {
 // Max |x| as the unsigned max of the bit patterns with the sign cleared:
 // exact, order-independent, and Inf/NaN come out at or above 0x7F800000.
 // Workgroup b writes its share's max to part[b]; every workgroup writes.
+// Bit 31 of part[b] (never set in a max of cleared sign bits) flags a
+// nonzero element of the share below 2^-64 in magnitude: a tensor with no
+// flag and amax <= 2^34 has no element that the quantizer's reciprocal
+// quotient must divide instead (k_quantize_wide).
 // 16 waves per workgroup: with at most kAmaxMaxPartials workgroups, 8 loads
 // of 16 bytes in flight per lane still make 128 KiB per CU.
 constexpr int kAmaxThreads = 1024;
+constexpr uint32_t kPartTiny = 0x80000000u;
+// 2 bits(|x|) - 1 (a zero wraps to the maximum) and its bound for 2^-64
+__device__ __forceinline__ uint32_t tiny_key(uint32_t v) { return (v << 1) - 1u; }
+constexpr uint32_t kTinyKey64 = (0x1F800000u << 1) - 1u;
+__device__ __forceinline__ uint32_t min4key(uint4 v) {
+  return min(min(tiny_key(v.x), tiny_key(v.y)), min(tiny_key(v.z), tiny_key(v.w)));
+}
 __global__ __launch_bounds__(kAmaxThreads) void k_amax_part(const uint4* __restrict__ src, int64_t n4,
                                                             uint32_t* __restrict__ part) {
-  uint32_t m = 0;
+  uint32_t m = 0, mk = ~0u;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kAmaxThreads;
   int64_t i = static_cast<int64_t>(blockIdx.x) * kAmaxThreads + threadIdx.x;
   for (; i + 7 * stride < n4; i += 8 * stride) {
@@ -84,17 +98,24 @@ __global__ __launch_bounds__(kAmaxThreads) void k_amax_part(const uint4* __restr
 #pragma unroll
     for (int k = 0; k < 8; ++k) v[k] = load_stream(src + i + k * stride);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) m = max(m, max4(v[k]));
+    for (int k = 0; k < 8; ++k) {
+      m = max(m, max4(v[k]));
+      mk = min(mk, min4key(v[k]));
+    }
   }
-  for (; i < n4; i += stride) m = max(m, max4(load_stream(src + i)));
+  for (; i < n4; i += stride) {
+    const uint4 v = load_stream(src + i);
+    m = max(m, max4(v));
+    mk = min(mk, min4key(v));
+  }
   for (int off = 32; off > 0; off >>= 1) m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), off)));
   __shared__ uint32_t wmax[kAmaxThreads / 64];
   if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
-  __syncthreads();
+  const int tiny = __syncthreads_or(mk < kTinyKey64);
   if (threadIdx.x == 0) {
     uint32_t r = wmax[0];
     for (int k = 1; k < kAmaxThreads / 64; ++k) r = max(r, wmax[k]);
-    part[blockIdx.x] = r;
+    part[blockIdx.x] = r | (tiny ? kPartTiny : 0u);
   }
 }
 
@@ -224,6 +245,12 @@ struct RowIn {
   }
 };
 
+// One entry of the per-workgroup table of block-scale codes (below).
+struct ScaleEntry {
+  float dd, y;
+  uint32_t tiny, all_slow;
+};
+
 // ONE: a single 1024-thread workgroup that also computes the amax (nparts
 // >= 0) over the whole tensor first, for tensors of at most kOneBlocks
 // blocks (up to 4 loads of 16 bytes per thread): one launch instead of two.
@@ -270,7 +297,7 @@ __global__ __launch_bounds__(ONE ? kOneThreads : kThreads) void k_quantize(const
       }
       for (; i < n4; i += kOneThreads) m = max(m, max4(s4[i]));
     } else {
-      for (int i = lane; i < nparts; i += 64) m = max(m, part[i]);
+      for (int i = lane; i < nparts; i += 64) m = max(m, part[i] & ~kPartTiny);
     }
     for (int off = 32; off > 0; off >>= 1) m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), off)));
     if constexpr (ONE) {
@@ -309,7 +336,7 @@ __global__ __launch_bounds__(ONE ? kOneThreads : kThreads) void k_quantize(const
     }
     float am = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(cur.x[j]));
+    for (int j = 0; j < 8; j += 2) am = fmaxf(fmaxf(am, fabsf(cur.x[j])), fabsf(cur.x[j + 1]));
     am = max8(am);
 
     // Quotients a / b are computed as RN(a / b) from y = RN(1/b) without a
@@ -322,8 +349,9 @@ __global__ __launch_bounds__(ONE ? kOneThreads : kThreads) void k_quantize(const
     const float B = code_value<ScaleFmt>(bcode);
     const float dd = B * T;
     // Elements: |x| / dd is at most 8 * MAXV because dd is the block amax
-    // over MAXV rounded to an E4M3 block scale; a zero block scale gives 0.
-    const float y = 1.0f / dd;
+    // over MAXV rounded to an E4M3 block scale.  A zero block scale gives
+    // y = 0, so every quotient is 0 (q = 0, residual a, a * 0 + 0).
+    const float y = (dd == 0.0f) ? 0.0f : 1.0f / dd;
     const bool dd_ok = (dd >= 0x1p-125f) & (dd <= 0x1p125f);
     const float thr = fmaxf(0x1p-100f, dd * 0x1p-98f);
     float v[8];
@@ -352,7 +380,7 @@ __global__ __launch_bounds__(ONE ? kOneThreads : kThreads) void k_quantize(const
       // maximum first
       float sv[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) sv[j] = __builtin_copysignf(fminf((dd == 0.0f) ? 0.0f : v[j], F::MAXV), cur.x[j]);
+      for (int j = 0; j < 8; ++j) sv[j] = __builtin_copysignf(fminf(v[j], F::MAXV), cur.x[j]);
       if constexpr (FMT == FMT_E2M1) {
         uint32_t w = 0;
         w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, sv[0], sv[1], 1.0f, 0);
@@ -370,29 +398,28 @@ __global__ __launch_bounds__(ONE ? kOneThreads : kThreads) void k_quantize(const
                (static_cast<uint64_t>(__builtin_bit_cast(uint32_t, hi)) << 32);
       }
     } else {
-      uint32_t u[8];
+      uint32_t ub[8];  // complemented SR uniforms
       if constexpr (SR) {
         if constexpr (ROLE == MX_ROLE_WEIGHT) {
 #pragma unroll
-          for (int j = 0; j < 8; ++j) u[j] = sr_bits(seed, static_cast<uint64_t>(cur.rowbase + j * cur.col));
+          for (int j = 0; j < 8; ++j) ub[j] = sr_ubar(seed, static_cast<uint64_t>(cur.rowbase + j * cur.col));
         } else {
           // a row is 8 consecutive elements from an even index: 4 draws
           uint64_t gk = kGolden64 * (static_cast<uint64_t>(cur.rowbase >> 1) + 1ull);
 #pragma unroll
           for (int j = 0; j < 8; j += 2) {
-            sr_bits_pair(seed, gk, u[j], u[j + 1]);
+            sr_ubar_pair(seed, gk, ub[j], ub[j + 1]);
             gk += kGolden64;
           }
         }
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float vj = (dd == 0.0f) ? 0.0f : v[j];
         uint32_t mag;
         if constexpr (SR) {
-          mag = sr_code<F>(vj, u[j]);
+          mag = sr_code<F>(v[j], ub[j]);
         } else {
-          mag = rne_code<F>(vj);
+          mag = rne_code<F>(v[j]);
         }
         const uint32_t code = F::SIGNED ? (mag | ((__float_as_uint(cur.x[j]) >> 31) << F::SIGN)) : mag;
         bits |= static_cast<uint64_t>(code) << (F::BITS * j);
@@ -447,11 +474,22 @@ __global__ __launch_bounds__(kThreads) void k_quantize_wide(const float* __restr
   load(cur, grp);  // requested before the partials: the two loads overlap
 
   uint32_t ab;
+  bool tiny_free = false;  // no element of the tensor is tiny for any block scale
   if (nparts >= 0) {
-    uint32_t m = 0;
-    for (int i = lane; i < nparts; i += 64) m = max(m, part[i]);
-    for (int off = 32; off > 0; off >>= 1) m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), off)));
+    uint32_t m = 0, f = 0;
+    for (int i = lane; i < nparts; i += 64) {
+      const uint32_t p = part[i];
+      m = max(m, p & ~kPartTiny);
+      f |= p;
+    }
+    for (int off = 32; off > 0; off >>= 1) {
+      m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), off)));
+      f |= static_cast<uint32_t>(__shfl_xor(static_cast<int>(f), off));
+    }
     ab = m;
+    // every nonzero |x| >= 2^-64, and every block's dd <= amax / MAXV <=
+    // 2^34, so the bound max(2^-100, dd 2^-98) is at most 2^-64
+    tiny_free = __builtin_amdgcn_readfirstlane(((f & kPartTiny) == 0u) & (ab <= 0x50800000u)) != 0;
   } else {
     ab = __float_as_uint(*amax) & 0x7FFFFFFFu;
   }
@@ -465,6 +503,26 @@ __global__ __launch_bounds__(kThreads) void k_quantize_wide(const float* __restr
   const float y_den = 1.0f / den;
   const bool den_ok = (den >= 0x1p-125f) & (den <= 0x1p125f);
   const float thr_den = fmaxf(0x1p-100f, den * 0x1p-98f);
+  // Per block-scale code c (0..126): dd = B(c) T, y = RN(1 / dd) (0 where
+  // dd = 0, which makes every quotient 0), the tiny-element bound
+  // 2 bits(thr) - 1 (0 where dd = 0: nothing is tiny) and 1 where dd is
+  // outside the range of the reciprocal quotient (every element divides).
+  __shared__ ScaleEntry stab[128];
+  if (threadIdx.x < 128) {
+    const float dd = code_value<ScaleFmt>(threadIdx.x) * T;
+    const bool dd_ok = (dd >= 0x1p-125f) & (dd <= 0x1p125f);
+    const float thr = fmaxf(0x1p-100f, dd * 0x1p-98f);
+    ScaleEntry e;
+    e.dd = dd;
+    e.y = (dd == 0.0f) ? 0.0f : 1.0f / dd;
+    e.tiny = (dd == 0.0f) ? 0u : (__float_as_uint(thr) << 1) - 1u;
+    e.all_slow = (!dd_ok & (dd != 0.0f)) ? 1u : 0u;
+    stab[threadIdx.x] = e;
+  }
+  __syncthreads();
+  // the seed in registers before the loop: a wait for its scalar load inside
+  // the loop would also wait for the table reads there
+  if constexpr (SR) asm volatile("" ::"s"(seed));
 
   for (; grp < ngroups; grp += gstride) {
     const int64_t blk = grp * kWideBlocks + (lane >> 1);
@@ -476,21 +534,24 @@ __global__ __launch_bounds__(kThreads) void k_quantize_wide(const float* __restr
 #pragma unroll
     for (int k = 0; k < B; ++k) words[k] = 0u;
     if (!nonfinite) {
+      // a running chain of maxima (three-operand maxima on the raw loads)
       float am = 0.0f;
 #pragma unroll
-      for (int r = 0; r < 8; ++r)
-        am = fmaxf(fmaxf(am, fmaxf(fabsf(cur.x[r].x), fabsf(cur.x[r].y))),
-                   fmaxf(fabsf(cur.x[r].z), fabsf(cur.x[r].w)));
+      for (int r = 0; r < 8; ++r) {
+        am = fmaxf(fmaxf(am, fabsf(cur.x[r].x)), fabsf(cur.x[r].y));
+        am = fmaxf(fmaxf(am, fabsf(cur.x[r].z)), fabsf(cur.x[r].w));
+      }
       am = fmaxf(am, swap_pair(am));
 
       float braw = div_by_recip(am, den, y_den);
-      if (!((T == 0.0f) | (den_ok & ((am == 0.0f) | (am >= thr_den))))) braw = am / den;
+      const bool braw_div = !((T == 0.0f) | (den_ok & ((am == 0.0f) | (am >= thr_den))));
+      if (__builtin_amdgcn_ballot_w64(braw_div)) {  // rare: skipped by the whole wave otherwise
+        if (braw_div) braw = am / den;
+        asm volatile("" : "+v"(braw));  // keeps the division inside the branch
+      }
       braw = (T == 0.0f) ? 0.0f : braw;
       bcode = rne_e4m3_hw(braw);
-      const float dd = code_value<ScaleFmt>(bcode) * T;
-      const float y = 1.0f / dd;
-      const bool dd_ok = (dd >= 0x1p-125f) & (dd <= 0x1p125f);
-      const float thr = fmaxf(0x1p-100f, dd * 0x1p-98f);
+      const ScaleEntry se = stab[bcode];
       float xs[32], v[32];
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
@@ -499,32 +560,49 @@ __global__ __launch_bounds__(kThreads) void k_quantize_wide(const float* __restr
       }
       // a tiny nonzero element, 0 < |x| < thr: 2 bits(|x|) - 1 below
       // 2 bits(thr) - 1 as unsigned (a zero wraps to the maximum), tested
-      // on the minimum over the lane's elements (vector operations only)
+      // on the minimum over the lane's elements (vector operations only),
+      // while the table entry is read
       uint32_t mn = ~0u;
+      if (!tiny_free) {
 #pragma unroll
-      for (int j = 0; j < 32; j += 2) {
-        v[j] = div_by_recip(fabsf(xs[j]), dd, y);
-        v[j + 1] = div_by_recip(fabsf(xs[j + 1]), dd, y);
-        mn = min(mn, min((__float_as_uint(xs[j]) << 1) - 1u, (__float_as_uint(xs[j + 1]) << 1) - 1u));
+        for (int j = 0; j < 32; j += 2) mn = min(min(mn, tiny_key(__float_as_uint(xs[j]))), tiny_key(__float_as_uint(xs[j + 1])));
       }
-      bool any_slow = mn < (__float_as_uint(thr) << 1) - 1u;
-      any_slow = (any_slow | !dd_ok) & (dd != 0.0f);
+      // SR draws (complemented uniforms) of element 4 r + j: counters of row
+      // r of this lane start at element base + r N (even), so its first pair
+      // is k0 + r N / 2 with k0 = base / 2 and gk = kGolden64 (k + 1)
+      // advances by a constant from row to row (a running 64-bit sum, not a
+      // product per row).  Rows 0 and 1 are drawn here, while the table
+      // entry is read.
+      uint32_t ub[32];
+      uint64_t gk = kGolden64 * (static_cast<uint64_t>(cur.base >> 1) + 1ull);
+      auto draw_row = [&](int r) {
+        sr_ubar_pair(seed, gk, ub[4 * r], ub[4 * r + 1]);
+        sr_ubar_pair(seed, gk + kGolden64, ub[4 * r + 2], ub[4 * r + 3]);
+        gk += gk_row;
+      };
+      if constexpr (SR) {
+        draw_row(0);
+        draw_row(1);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) asm volatile("" : "+v"(ub[k]));  // drawn here, not at their use
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      const float dd = se.dd, y = se.y;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) v[j] = div_by_recip(fabsf(xs[j]), dd, y);
+      const bool any_slow = (mn < se.tiny) | (se.all_slow != 0u);
       if (any_slow) {  // rare: tiny elements or an extreme block scale
+        const bool dd_ok = se.all_slow == 0u;
+        const float thr = fmaxf(0x1p-100f, dd * 0x1p-98f);
 #pragma unroll
         for (int j = 0; j < 32; ++j) {
           const float ax = fabsf(xs[j]);
           if (!dd_ok | ((ax != 0.0f) & (ax < thr))) v[j] = ax / dd;
         }
       }
-#pragma unroll
-      for (int j = 0; j < 32; ++j) v[j] = (dd == 0.0f) ? 0.0f : v[j];
 
       // the 4 codes of each row of this lane, BITS each
       uint32_t chunk[8];
-      // counters of the SR draws: row r of this lane starts at element
-      // base + r N (even), so its first pair is k0 + r N / 2 with k0 = base / 2
-      // and gk = kGolden64 (k + 1) advances by a constant from row to row
-      const uint64_t gk0 = kGolden64 * (static_cast<uint64_t>(cur.base >> 1) + 1ull);
       if constexpr (!SR && (FMT == FMT_E2M1 || FMT == FMT_E4M3)) {
         // hardware round to nearest even on copysign(min(v, max), x)
 #pragma unroll
@@ -547,18 +625,14 @@ __global__ __launch_bounds__(kThreads) void k_quantize_wide(const float* __restr
       } else {
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-          uint32_t u[4];
           if constexpr (SR) {
-            // elements base + r N + j; pairs from an even index
-            const uint64_t gk = gk0 + r * gk_row;
-            sr_bits_pair(seed, gk, u[0], u[1]);
-            sr_bits_pair(seed, gk + kGolden64, u[2], u[3]);
+            if (r >= 2) draw_row(r);
           }
           uint32_t c = 0;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             uint32_t mag;
-            if constexpr (SR) mag = sr_code<F>(v[4 * r + j], u[j]);
+            if constexpr (SR) mag = sr_code<F>(v[4 * r + j], ub[4 * r + j]);
             else mag = rne_code<F>(v[4 * r + j]);
             const uint32_t code = F::SIGNED ? (mag | ((__float_as_uint(xs[4 * r + j]) >> 31) << F::SIGN)) : mag;
             c |= code << (B * j);

@@ -140,22 +140,22 @@ __global__ __launch_bounds__(kMxWaves * 64) void k_quantize_mx(const float* __re
       w[q] = t;
     }
   } else {
-    uint32_t u[16];
+    uint32_t ub[16];  // complemented SR uniforms
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       if constexpr (ROLE == MX_ROLE_WEIGHT) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) u[4 * q + j] = sr_bits(seed, static_cast<uint64_t>(s0[q] + j * step));
+        for (int j = 0; j < 4; ++j) ub[4 * q + j] = sr_ubar(seed, static_cast<uint64_t>(s0[q] + j * step));
       } else {
         // 4 consecutive elements from an even index: 2 draws
         const uint64_t gk = kGolden64 * (static_cast<uint64_t>(s0[q] >> 1) + 1ull);
-        sr_bits_pair(seed, gk, u[4 * q], u[4 * q + 1]);
-        sr_bits_pair(seed, gk + kGolden64, u[4 * q + 2], u[4 * q + 3]);
+        sr_ubar_pair(seed, gk, ub[4 * q], ub[4 * q + 1]);
+        sr_ubar_pair(seed, gk + kGolden64, ub[4 * q + 2], ub[4 * q + 3]);
       }
     }
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const uint32_t mag = nonfinite ? 0u : sr_code<F>(fabsf(x[j]) * inv, u[j]);
+      const uint32_t mag = nonfinite ? 0u : sr_code<F>(fabsf(x[j]) * inv, ub[j]);
       const uint32_t sign = nonfinite ? 0u : (__float_as_uint(x[j]) >> 31);
       w[j >> 2] |= (mag | (sign << F::SIGN)) << (4 * (j & 3));
     }
