@@ -78,7 +78,10 @@ __device__ __forceinline__ f16x8 decode_frag(uint32_t codes, uint32_t sw) {
 // Half h (values 4h..4h+3) of decode_frag, for placing between MFMAs.
 __device__ __forceinline__ void decode_half(f16x8& f, uint32_t codes, uint32_t sw, int h) {
   const float sc = __uint_as_float(sw);
-  const f16x2 m2 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(sw, sw, 0x01000100u));
+  // the mantissa factor in both halves: a splat of the low half, which the
+  // packed multiply takes through its operand select (no extra instruction)
+  const f16x2 sw2 = __builtin_bit_cast(f16x2, sw);
+  const f16x2 m2 = {sw2[0], sw2[0]};
   if (h == 0) {
     const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, sc, 0) * m2;
     const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, sc, 1) * m2;
