@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256) void k_conv8w(const ConvParams p) {
   constexpr int SCL = 32 * 16;
   constexpr int A_C = 0, B_C = A_SZ, A_S = A_SZ + B_SZ, B_S = A_S + SCL;
   constexpr int STAGE = A_S + 2 * SCL;
-  constexpr int NST = 3;
+  constexpr int NST = 4;
   constexpr int LUT = NST * STAGE;
   static_assert(STAGE % 16 == 0, "16-byte aligned stages");
   __shared__ __attribute__((aligned(16))) uint8_t lds[NST * STAGE + 1024];
@@ -215,18 +215,18 @@ __global__ __launch_bounds__(256) void k_conv8w(const ConvParams p) {
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // Step s on stage s%3 (raw fragments in set P; slice-0 A fragments and the
+  // Step s on stage s%4 (raw fragments in set P; slice-0 A fragments and the
   // slice-0 column-0 B fragment fbc decoded): slice 0 decodes the slice-1 A
   // fragments and the next B fragment; slice 1 the next B fragment and the
-  // next step's slice-0 A fragments (set Q, read from stage (s+1)%3 during
+  // next step's slice-0 A fragments (set Q, read from stage (s+1)%4 during
   // slice-0 column 0).  The block of step s+2 (in G) is staged into stage
-  // (s+2)%3 and G refilled with the block of step s+4; one barrier per step,
-  // at its end.
+  // (s+2)%4 and G refilled with the block of step s+4; one barrier per step,
+  // at its end.  The stage offsets are compile-time constants (nxt_c, wr_c).
   f16x8 fbc;
-  auto step = [&](auto set_c, RawBlock<FMT_E4M3>& G, int nxt_off, int wr_off) {
+  auto step = [&](auto set_c, RawBlock<FMT_E4M3>& G, auto nxt_c, auto wr_c) {
     constexpr int P = decltype(set_c)::value, Q = P ^ 1;
-    uint8_t* wbase = lds + wr_off;
-    const uint8_t* nbase = lds + nxt_off;
+    uint8_t* wbase = lds + decltype(wr_c)::value;
+    const uint8_t* nbase = lds + decltype(nxt_c)::value;
     f16x8 fbA, fbB;
     // slice 0
     column(fa0, fbc, 0,
@@ -301,14 +301,17 @@ __global__ __launch_bounds__(256) void k_conv8w(const ConvParams p) {
 #pragma unroll
     for (int i = 0; i < RM; ++i) fa0[i] = dec(ra[0][i], sa[0][i], 0);
     fbc = dec(rb[0][0], sbv[0][0], 0);
-    // an odd step count runs one more step, on padding blocks only (zero
-    // scale words: it adds exact zeros)
-    int c = 0;  // stage of step s
-    for (int s = 0; s < nsteps; s += 2) {
-      const int c1 = c == 2 ? 0 : c + 1, c2 = c1 == 2 ? 0 : c1 + 1;
-      step(IC<0>{}, g0, c1 * STAGE, c2 * STAGE);
-      step(IC<1>{}, g1, c2 * STAGE, c * STAGE);
-      c = c2;
+    // Step s computes from stage s % 4, reads stage (s + 1) % 4 and writes
+    // stage (s + 2) % 4 with register set s % 2: one loop iteration runs the
+    // four steps of the pattern, so every stage offset is an immediate of
+    // its LDS instruction (no address arithmetic per step).  The step count
+    // is rounded up to a multiple of four; the extra steps see padding
+    // blocks only (zero scale words: they add exact zeros).
+    for (int s = 0; s < nsteps; s += 4) {
+      step(IC<0>{}, g0, IC<STAGE>{}, IC<2 * STAGE>{});
+      step(IC<1>{}, g1, IC<2 * STAGE>{}, IC<3 * STAGE>{});
+      step(IC<0>{}, g0, IC<3 * STAGE>{}, IC<0>{});
+      step(IC<1>{}, g1, IC<0>{}, IC<STAGE>{});
     }
   }
   // the fp16 fragments held g * B * 2^-2: one accumulator unit is 2^-4
