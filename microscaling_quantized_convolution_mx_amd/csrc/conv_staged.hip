@@ -37,8 +37,9 @@
 //     apart modulo the 256-byte bank row, and the staging writes of 4 column
 //     blocks x 4 k-blocks fall 16 and 64 bytes apart: both conflict-free.
 // Tile: 4 waves of 128x128 (a wave's 16 accumulator tiles fill its 256
-// AGPRs), K steps of 4 k-blocks (two 16-wide MFMA slices), three LDS
-// stages; the fragments of the next slice are read during the current one.
+// AGPRs), K steps of 4 k-blocks (two 16-wide MFMA slices), four LDS
+// stages (160 KB for the weight gradient, whose operands are both staged as
+// lines); the fragments of the next slice are read during the current one.
 #include "conv_kernels.h"
 
 namespace mx {
@@ -113,7 +114,7 @@ __global__ __launch_bounds__(256) void k_convs(const ConvParams p) {
   constexpr int A_SZ = A_ROWS ? SZL : SZK, B_SZ = B_ROWS ? SZL : SZK;
   constexpr int A_C = 0, B_C = A_SZ;
   constexpr int STAGE = A_SZ + B_SZ;
-  constexpr int NST = 3;
+  constexpr int NST = 4;
   static_assert(STAGE % 16 == 0, "16-byte aligned stages");
   __shared__ __attribute__((aligned(16))) uint8_t lds[NST * STAGE];
   using Raw = Raw6;
@@ -331,14 +332,17 @@ __global__ __launch_bounds__(256) void k_convs(const ConvParams p) {
     for (int i = 0; i < RM; ++i) fa0[i] = frag_a(lds, 0, i);
 #pragma unroll
     for (int j = 0; j < RN; ++j) fb0[j] = frag_b(lds, 0, j);
-    // an odd step count runs one more step, on padding blocks only (zero
-    // values: it adds exact zeros)
-    int c = 0;  // stage of step s
-    for (int s = 0; s < nsteps; s += 2) {
-      const int c1 = c == 2 ? 0 : c + 1, c2 = c1 == 2 ? 0 : c1 + 1;
-      step(g0, lds + c * STAGE, lds + c1 * STAGE, lds + c2 * STAGE);
-      step(g1, lds + c1 * STAGE, lds + c2 * STAGE, lds + c * STAGE);
-      c = c2;
+    // Step s computes from stage s % 4, reads ahead from stage (s + 1) % 4
+    // and writes stage (s + 2) % 4 with register set s % 2: one loop
+    // iteration runs the four steps of the pattern, so every stage offset is
+    // an immediate of its LDS instruction (no address arithmetic per step).
+    // The step count is rounded up to a multiple of four; the extra steps
+    // see padding blocks only (zero values: they add exact zeros).
+    for (int s = 0; s < nsteps; s += 4) {
+      step(g0, lds, lds + STAGE, lds + 2 * STAGE);
+      step(g1, lds + STAGE, lds + 2 * STAGE, lds + 3 * STAGE);
+      step(g0, lds + 2 * STAGE, lds + 3 * STAGE, lds);
+      step(g1, lds + 3 * STAGE, lds, lds + STAGE);
     }
   }
   store_tile<OP, MT, NT, KB, WTM, WTN, RM, RN>(p, t, acc, lane, wm, wn);
