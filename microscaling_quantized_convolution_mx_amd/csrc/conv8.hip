@@ -219,11 +219,11 @@ __global__ __launch_bounds__(256) void k_conv8w(const ConvParams p) {
   // slice-0 column-0 B fragment fbc decoded): slice 0 decodes the slice-1 A
   // fragments and the next B fragment; slice 1 the next B fragment and the
   // next step's slice-0 A fragments (set Q, read from stage (s+1)%4 during
-  // slice-0 column 0).  The block of step s+2 (in G) is staged into stage
-  // (s+2)%4 and G refilled with the block of step s+4; one barrier per step,
-  // at its end.  The stage offsets are compile-time constants (nxt_c, wr_c).
+  // slice-0 column 0).  The block in G is staged into stage wr_c and G
+  // refilled two steps ahead; a barrier at the end where bar_c is set.  Stage
+  // offsets are compile-time constants.
   f16x8 fbc;
-  auto step = [&](auto set_c, RawBlock<FMT_E4M3>& G, auto nxt_c, auto wr_c) {
+  auto step = [&](auto set_c, RawBlock<FMT_E4M3>& G, auto nxt_c, auto wr_c, auto bar_c) {
     constexpr int P = decltype(set_c)::value, Q = P ^ 1;
     uint8_t* wbase = lds + decltype(wr_c)::value;
     const uint8_t* nbase = lds + decltype(nxt_c)::value;
@@ -271,28 +271,28 @@ __global__ __launch_bounds__(256) void k_conv8w(const ConvParams p) {
            [&] { dech(fbc, rb[Q][0], sbv[Q][0], 0, 0); },
            [&] {
              dech(fbc, rb[Q][0], sbv[Q][0], 0, 1);
-             __syncthreads();
+             if constexpr (decltype(bar_c)::value) __syncthreads();
            });
   };
 
   const int nsteps = (t.kb_end - t.kb_begin + KB - 1) / KB;
   if (nsteps > 0) {
-    RawBlock<FMT_E4M3> g0, g1;  // blocks of even and odd steps
+    RawBlock<FMT_E4M3> g0, g1;  // the blocks that even and odd steps stage
+    auto stage_block = [&](const RawBlock<FMT_E4M3>& g, uint8_t* base) {
+      lookup_scale(g);
+      write_rows(g, base, 0);
+      write_rows(g, base, 2);
+      write_rows(g, base, 4);
+      write_rows(g, base, 6);
+      *reinterpret_cast<uint32_t*>(base + st_scale) = sws;
+    };
     fetch(g0);
     fetch(g1);
     __syncthreads();  // scale-word table
-    lookup_scale(g0);
-    write_rows(g0, lds, 0);
-    write_rows(g0, lds, 2);
-    write_rows(g0, lds, 4);
-    write_rows(g0, lds, 6);
-    *reinterpret_cast<uint32_t*>(lds + st_scale) = sws;
-    lookup_scale(g1);
-    write_rows(g1, lds + STAGE, 0);
-    write_rows(g1, lds + STAGE, 2);
-    write_rows(g1, lds + STAGE, 4);
-    write_rows(g1, lds + STAGE, 6);
-    *reinterpret_cast<uint32_t*>(lds + STAGE + st_scale) = sws;
+    stage_block(g0, lds);
+    stage_block(g1, lds + STAGE);
+    fetch(g0);
+    stage_block(g0, lds + 2 * STAGE);
     fetch(g0);
     fetch(g1);
     __syncthreads();
@@ -301,17 +301,22 @@ __global__ __launch_bounds__(256) void k_conv8w(const ConvParams p) {
 #pragma unroll
     for (int i = 0; i < RM; ++i) fa0[i] = dec(ra[0][i], sa[0][i], 0);
     fbc = dec(rb[0][0], sbv[0][0], 0);
-    // Step s computes from stage s % 4, reads stage (s + 1) % 4 and writes
-    // stage (s + 2) % 4 with register set s % 2: one loop iteration runs the
-    // four steps of the pattern, so every stage offset is an immediate of
-    // its LDS instruction (no address arithmetic per step).  The step count
-    // is rounded up to a multiple of four; the extra steps see padding
-    // blocks only (zero scale words: they add exact zeros).
+    // Step s computes from stage s % 4, reads stage (s + 1) % 4 (all of its
+    // raw fragments) and stages the block of step s + 3 into stage
+    // (s + 3) % 4 from register set s % 2, which it then refills with the
+    // block of step s + 5.  A barrier ends every even step only: a stage
+    // written in step s is read in step s + 2, and the one it overwrites was
+    // last read in step s - 2, so a barrier at the end of s or s + 1, and one
+    // at the end of s - 2 or s - 1, orders both.  One loop iteration runs the
+    // four steps of the pattern, so every stage offset is an immediate of its
+    // LDS instruction (no address arithmetic per step).  The step count is
+    // rounded up to a multiple of four; the extra steps see padding blocks
+    // only (zero scale words: they add exact zeros).
     for (int s = 0; s < nsteps; s += 4) {
-      step(IC<0>{}, g0, IC<STAGE>{}, IC<2 * STAGE>{});
-      step(IC<1>{}, g1, IC<2 * STAGE>{}, IC<3 * STAGE>{});
-      step(IC<0>{}, g0, IC<3 * STAGE>{}, IC<0>{});
-      step(IC<1>{}, g1, IC<0>{}, IC<STAGE>{});
+      step(IC<0>{}, g0, IC<STAGE>{}, IC<3 * STAGE>{}, IC<1>{});
+      step(IC<1>{}, g1, IC<2 * STAGE>{}, IC<0>{}, IC<0>{});
+      step(IC<0>{}, g0, IC<3 * STAGE>{}, IC<STAGE>{}, IC<1>{});
+      step(IC<1>{}, g1, IC<0>{}, IC<2 * STAGE>{}, IC<0>{});
     }
   }
   // the fp16 fragments held g * B * 2^-2: one accumulator unit is 2^-4
