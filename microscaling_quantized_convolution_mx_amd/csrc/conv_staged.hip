@@ -39,7 +39,8 @@
 // Tile: 4 waves of 128x128 (a wave's 16 accumulator tiles fill its 256
 // AGPRs), K steps of 4 k-blocks (two 16-wide MFMA slices), four LDS
 // stages (160 KB for the weight gradient, whose operands are both staged as
-// lines); the fragments of the next slice are read during the current one.
+// lines); every fragment of a stage is read in the step before its use, so
+// one barrier serves two K steps.
 #include "conv_kernels.h"
 
 namespace mx {
@@ -287,62 +288,76 @@ __global__ __launch_bounds__(256) void k_convs(const ConvParams p) {
   };
   f16x8 fa0[RM], fb0[RN], fa1[RM], fb1[RN];  // fragments of slice 0 and slice 1
 
-  // Step s on the stage at cur (its slice-0 fragments in fa0/fb0): MFMA M
+  // One step (its fragments of both slices in fa0/fb0 and fa1/fb1): MFMA M
   // (slice M / 16, column (M % 16) / 4, row M % 4) is followed by its work
   // and a scheduling barrier (a wave hides only a few VALU operations and
-  // LDS accesses behind each MFMA): after MFMAs 0-7 the slice-1 fragments
-  // of cur, after 20-27 the slice-0 fragments of the next stage (nxt,
-  // complete since the previous step's barrier), and the staging units of
-  // the block in G (step s+2) into the stage at wr, which refill G with the
-  // block of step s+4.  One barrier, at the end: wr complete, cur free.
-  auto slot = [&]<int M>(Raw& G, const uint8_t* cur, const uint8_t* nxt, uint8_t* wr) {
+  // LDS accesses behind each MFMA): after MFMAs 20-27 the slice-0 fragments
+  // of the next stage (nxt), and the slice-1 fragments of nxt each right
+  // after the last MFMA that reads its register (B column j after MFMA
+  // 19 + 4j, A row i after MFMA 28 + i), so that a stage is read only in
+  // the step before its own; and the staging units of the block in G into
+  // the stage at wr, which refill G two steps ahead.  A barrier at the end
+  // where BAR is set.
+  auto slot = [&]<int M, int BAR>(Raw& G, const uint8_t* nxt, uint8_t* wr) {
     constexpr int i = M % 4, j = (M % 16) / 4;
     if constexpr (M < 16)
       acc[i][j] = mfma32<true>(reinterpret_cast<const uint16_t*>(&fa0[i]), reinterpret_cast<const uint16_t*>(&fb0[j]), acc[i][j]);
     else
       acc[i][j] = mfma32<true>(reinterpret_cast<const uint16_t*>(&fa1[i]), reinterpret_cast<const uint16_t*>(&fb1[j]), acc[i][j]);
-    if constexpr (M < 8) {
-      if constexpr (M % 2 == 0) fa1[M / 2] = frag_a(cur, 1, M / 2);
-      else fb1[M / 2] = frag_b(cur, 1, M / 2);
-    } else if constexpr (M >= 20 && M < 28) {
+    if constexpr (M >= 20 && M < 28) {
       if constexpr (M % 2 == 0) fa0[(M - 20) / 2] = frag_a(nxt, 0, (M - 20) / 2);
       else fb0[(M - 20) / 2] = frag_b(nxt, 0, (M - 20) / 2);
     }
+    if constexpr (M == 19 || M == 23 || M == 27 || M == 31) fb1[(M - 19) / 4] = frag_b(nxt, 1, (M - 19) / 4);
+    if constexpr (M >= 28) fa1[M - 28] = frag_a(nxt, 1, M - 28);
     stage_slot.template operator()<M>(G, wr);
-    if constexpr (M == 31) __syncthreads();
+    if constexpr (M == 31 && BAR) __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
   };
-  auto step = [&](Raw& G, const uint8_t* cur, const uint8_t* nxt, uint8_t* wr) {
+  auto step = [&](Raw& G, const uint8_t* nxt, uint8_t* wr, auto bar_c) {
     [&]<int... M>(std::integer_sequence<int, M...>) {
-      (slot.template operator()<M>(G, cur, nxt, wr), ...);
+      (slot.template operator()<M, decltype(bar_c)::value>(G, nxt, wr), ...);
     }(std::make_integer_sequence<int, 32>());
   };
 
   const int nsteps = (t.kb_end - t.kb_begin + KB - 1) / KB;
   if (nsteps > 0) {
-    Raw g0, g1;  // blocks of even and odd steps
+    Raw g0, g1;  // the blocks that even and odd steps stage
     fetch(g0);
     fetch(g1);
     stage_block(g0, lds);
     stage_block(g1, lds + STAGE);
     fetch(g0);
+    stage_block(g0, lds + 2 * STAGE);
+    fetch(g0);
     fetch(g1);
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < RM; ++i) fa0[i] = frag_a(lds, 0, i);
+    for (int i = 0; i < RM; ++i) {
+      fa0[i] = frag_a(lds, 0, i);
+      fa1[i] = frag_a(lds, 1, i);
+    }
 #pragma unroll
-    for (int j = 0; j < RN; ++j) fb0[j] = frag_b(lds, 0, j);
-    // Step s computes from stage s % 4, reads ahead from stage (s + 1) % 4
-    // and writes stage (s + 2) % 4 with register set s % 2: one loop
-    // iteration runs the four steps of the pattern, so every stage offset is
-    // an immediate of its LDS instruction (no address arithmetic per step).
-    // The step count is rounded up to a multiple of four; the extra steps
-    // see padding blocks only (zero values: they add exact zeros).
+    for (int j = 0; j < RN; ++j) {
+      fb0[j] = frag_b(lds, 0, j);
+      fb1[j] = frag_b(lds, 1, j);
+    }
+    // Step s computes stage s % 4 (its fragments read in step s - 1), reads
+    // stage (s + 1) % 4 and stages the block of step s + 3 into stage
+    // (s + 3) % 4 from register set s % 2, which it then refills with the
+    // block of step s + 5.  A barrier ends every even step only: a stage
+    // written in step s is read in step s + 2, and the one it overwrites was
+    // last read in step s - 2, so a barrier at the end of s or s + 1, and one
+    // at the end of s - 2 or s - 1, orders both.  One loop iteration runs the
+    // four steps of the pattern, so every stage offset is an immediate of its
+    // LDS instruction.  The step count is rounded up to a multiple of four;
+    // the extra steps see padding blocks only (zero values: they add exact
+    // zeros).
     for (int s = 0; s < nsteps; s += 4) {
-      step(g0, lds, lds + STAGE, lds + 2 * STAGE);
-      step(g1, lds + STAGE, lds + 2 * STAGE, lds + 3 * STAGE);
-      step(g0, lds + 2 * STAGE, lds + 3 * STAGE, lds);
-      step(g1, lds + 3 * STAGE, lds, lds + STAGE);
+      step(g0, lds + STAGE, lds + 3 * STAGE, IC<1>{});
+      step(g1, lds + 2 * STAGE, lds, IC<0>{});
+      step(g0, lds + 3 * STAGE, lds + STAGE, IC<1>{});
+      step(g1, lds, lds + 2 * STAGE, IC<0>{});
     }
   }
   store_tile<OP, MT, NT, KB, WTM, WTN, RM, RN>(p, t, acc, lane, wm, wn);
