@@ -266,3 +266,26 @@ def test_fp6_tile_ragged_edges(fmts, shape, op):
     idx = np.unique(np.concatenate([edge, tail, rng.integers(0, n, 16384), [n - 1]])).astype(np.int64)
     ref, s = fn(cv, ow.exact(), other.exact(), idx)
     assert_close(got.view(-1)[torch.from_numpy(idx).to(DEV)].cpu().numpy(), ref, s, op)
+
+
+# The 256x256 kernels run their K loop in iterations of four steps (the
+# step count rounded up with padding blocks) with a barrier after every
+# second step: 1x1 layers whose K is 2, 3 and 5 steps of 32, on the forward
+# (C_out = 256) and data-gradient (C_in = 256) GEMMs, 131072 columns so that
+# the 256x256 tile is the one chosen.
+@pytest.mark.parametrize("fmt", [mx.MX_E2M1, mx.MX_E2M3, mx.MX_E4M3], ids=["e2m1", "e2m3", "e4m3"])
+@pytest.mark.parametrize("op,kch", [("fwd", 64), ("fwd", 96), ("fwd", 160), ("dgrad", 64), ("dgrad", 96), ("dgrad", 160)])
+def test_k_step_counts_256(fmt, op, kch):
+    shape = (128, kch, 256, 32, 32, 1, 1, 1, 1, 0, 0) if op == "fwd" else (128, 256, kch, 32, 32, 1, 1, 1, 1, 0, 0)
+    say("k steps", op, kch, fmt)
+    lay, x, w, dy = layer_inputs(shape, 300 + kch)
+    d = mx.desc_from_layer(lay, fmt)
+    (qx, qw, qdy), (y, dx, _) = run_layer(d, x, w, dy, seed_sr=5, ops=(op,))
+    ow = oracle_quantize(d, mx.MX_ROLE_WEIGHT, w)
+    cv = oracle_conv(d)
+    if op == "fwd":
+        ref, s = O.conv_fwd(cv, ow.exact(), oracle_quantize(d, mx.MX_ROLE_ACT, x).exact())
+        assert_close(y.cpu().numpy(), ref, s, "fwd")
+    else:
+        ref, s = O.conv_dgrad(cv, ow.exact(), oracle_quantize(d, mx.MX_ROLE_GRAD, dy, mx.MX_SR, 5).exact())
+        assert_close(dx.cpu().numpy(), ref, s, "dgrad")
