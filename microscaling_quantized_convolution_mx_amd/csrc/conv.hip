@@ -240,7 +240,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
 
 // E2M1, 256x256 tile, 4 waves of 128x128, one workgroup per CU (the 256
 // accumulator registers of a wave fill the AGPR file).  LDS holds the raw
-// 4-bit codes of three K steps; each wave decodes its MFMA fragments from
+// 4-bit codes of four K steps; each wave decodes its MFMA fragments from
 // them (conversion with the block scale's exponent, then a packed multiply
 // by its mantissa factor: exact in fp16).
 //

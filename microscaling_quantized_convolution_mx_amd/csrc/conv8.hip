@@ -26,7 +26,7 @@
 //
 // Tile: 256x256, 4 waves of 128x128 (one workgroup per CU: a wave's 16
 // accumulator tiles fill its 256 AGPRs), K steps of 4 k-blocks (32 K values:
-// two 16-wide MFMA slices), three LDS stages, block fetches two steps ahead.
+// two 16-wide MFMA slices), four LDS stages, block fetches two steps ahead.
 // As in the E2M1 kernel, every fragment is decoded in the column before
 // the one that uses it, in halves placed after single MFMAs (a wave hides
 // only about 4 VALU operations behind each MFMA), and the raw fragments of
