@@ -289,3 +289,27 @@ def test_k_step_counts_256(fmt, op, kch):
     else:
         ref, s = O.conv_dgrad(cv, ow.exact(), oracle_quantize(d, mx.MX_ROLE_GRAD, dy, mx.MX_SR, 5).exact())
         assert_close(dx.cpu().numpy(), ref, s, "dgrad")
+
+
+# The 256x256 kernels share LDS stages across steps with one barrier per two
+# steps; any missed ordering between a stage's writes and reads would show
+# as outputs that change from run to run.  Forward and data gradient of a
+# 3x3 layer (27 K steps) on the 256x256 tile, five runs each, bit for bit.
+@pytest.mark.parametrize("fmt", [mx.MX_E2M1, mx.MX_E2M3, mx.MX_E4M3], ids=["e2m1", "e2m3", "e4m3"])
+def test_256_tile_runs_are_bitwise_repeatable(fmt):
+    shape = (128, 96, 256, 32, 32, 3, 3, 1, 1, 1, 1)
+    say("repeatable 256 tile", fmt)
+    lay, x, w, dy = layer_inputs(shape, 77)
+    d = mx.desc_from_layer(lay, fmt)   # fwd with C_out = 256 (the 256-row tile)
+    (qx, qw, _), (y0, _, _) = run_layer(d, x, w, dy, seed_sr=3, ops=("fwd",))
+    lay2, x2, w2, dy2 = layer_inputs((128, 256, 96, 32, 32, 3, 3, 1, 1, 1, 1), 78)
+    d2 = mx.desc_from_layer(lay2, fmt)  # dgrad with C_in = 256 (the 256-row tile)
+    (_, qw2, qdy2), (_, dxb0, _) = run_layer(d2, x2, w2, dy2, seed_sr=3, ops=("dgrad",))
+    for _ in range(4):
+        y, _, _, _ = conv_buffers(d)
+        _, dxb, _, _ = conv_buffers(d2)
+        mx.mx_conv_fwd(d, qw, qx, y)
+        mx.mx_conv_dgrad(d2, qw2, qdy2, dxb)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int32), y0.view(torch.int32)), "fwd differs between runs"
+        assert torch.equal(dxb.view(torch.int32), dxb0.view(torch.int32)), "dgrad differs between runs"
